@@ -1,0 +1,342 @@
+"""Plain fp64 CPU oracle for rotate-then-quantize int4 KV-cache compression.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+in ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or run anything in this package.  It shares no code, table,
+constant generator or helper with the HIP library and imports nothing from it.
+
+Everything here is written to be checked by eye against the source pages:
+explicit O(d^2) matrices, scalar rounding rules, no blocking or fusion.
+
+Sources (cited by page title and section):
+  [P1] "Quantization Speed Is Often a Kernel Problem" -- the method page.
+  [P3] "Day 9 - Quantization: Shrink the Bytes Themselves".
+  [P4] "Quantization & Serving".
+  [P5] "Chapter 25 - Quantization: The Hardware View".
+
+What the pages fix and what is a reading (each reading is listed in the design doc):
+  * Each K/V vector is rotated, quantized to int4, and later dequantized and
+    rotated back [P1, "First, the 17%"].
+  * SRFT = multiply by a fixed random +-1 pattern, then an FFT (rfft on the
+    way in, irfft on the way out) [P1, "First, the 17%"].  Reading: the
+    orthonormal real DFT, with the d/2+1 complex bins packed into d reals as
+    [X0, sqrt2*Re X1, sqrt2*Im X1, ..., sqrt2*Im X_{d/2-1}, X_{d/2}].
+  * SRHT = sign-randomized Hadamard transform, the control rotation
+    [P1, "First, the 17%"].  Reading: (1/sqrt d) * Sylvester H_d.
+  * Symmetric absmax quantization, zero point 0 [P3, "What Quantization Is,
+    Mathematically"; P4].  Reading: scale = fp16(absmax / 8) (the int4
+    worked examples on P3 divide by 8), code = clamp(round-half-even(z/s),
+    -8, 7) (the clamp range of the symmetric quantizer code on P5, "Python:
+    Quantize, Simulate the Integer GEMM, and Compute the Savings").
+  * Scales are fp16 values [P3, "How Many Numbers Should One Scale Cover"];
+    one absmax scale per group of consecutive values [P1, "Fusing four steps
+    into two kernels is not enough"].
+  * Two int4 codes per byte, w0 in the low nibble, w1 in the high nibble,
+    mapped from 0..15 to signed [P5, "Kernels: Marlin, CUTLASS, and Why INT4
+    Packing Needs Special Code"].  Reading: two's complement nibbles.
+  * The +-1 pattern: the pages only say "fixed random".  Reading: sign i of
+    seed S is -1 iff bit 63 of the (i+1)-th output of the published SplitMix64
+    generator (Steele, Lea, Flood 2014) started at state S is set; the seed of
+    row r is S + ((r div rows_per_seed) mod seed_period), with 0 meaning
+    "one seed for all rows" / "no modulo".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+SPLITMIX64_GAMMA = 0x9E3779B97F4A7C15
+INT4_MIN = -8
+INT4_MAX = 7
+FP16_MAX = 65504.0
+
+# ---------------------------------------------------------------------------
+# Sign pattern (the "fixed random +-1 pattern" of [P1, "First, the 17%"])
+# ---------------------------------------------------------------------------
+
+
+def splitmix64_stream(state: int, count: int) -> list[int]:
+    """The first ``count`` outputs of SplitMix64 started at ``state``.
+
+    Published generator (Steele, Lea & Flood, "Fast splittable pseudorandom
+    number generators", OOPSLA 2014; Vigna's reference implementation): the
+    state advances by the golden-ratio increment, and each output is the
+    state passed through two xor-shift-multiply rounds and a final xor-shift.
+    """
+    out = []
+    s = state & MASK64
+    for _ in range(count):
+        s = (s + SPLITMIX64_GAMMA) & MASK64
+        z = s
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        out.append(z ^ (z >> 31))
+    return out
+
+
+def sign_vector(seed: int, d: int) -> np.ndarray:
+    """D in {+1,-1}^d for one seed: -1 where bit 63 of output i is set."""
+    return np.array(
+        [-1.0 if (o >> 63) & 1 else 1.0 for o in splitmix64_stream(seed, d)],
+        dtype=np.float64,
+    )
+
+
+def row_seed(seed: int, row: int, rows_per_seed: int, seed_period: int) -> int:
+    """Seed of row ``row``: seed + ((row // rows_per_seed) % seed_period).
+
+    rows_per_seed == 0 means every row uses ``seed``; seed_period == 0 means
+    the block index is not wrapped.  Arithmetic is modulo 2^64.
+    """
+    if rows_per_seed == 0:
+        return seed & MASK64
+    block = row // rows_per_seed
+    if seed_period != 0:
+        block %= seed_period
+    return (seed + block) & MASK64
+
+
+def sign_matrix(n: int, d: int, seed: int, rows_per_seed: int = 0,
+                seed_period: int = 0, row0: int = 0) -> np.ndarray:
+    """[n, d] matrix of per-row sign vectors for rows row0 .. row0+n-1."""
+    cache: dict[int, np.ndarray] = {}
+    out = np.empty((n, d), dtype=np.float64)
+    for i in range(n):
+        s = row_seed(seed, row0 + i, rows_per_seed, seed_period)
+        if s not in cache:
+            cache[s] = sign_vector(s, d)
+        out[i] = cache[s]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Rotations R (d x d, orthonormal)
+# ---------------------------------------------------------------------------
+
+
+def srft_matrix(d: int) -> np.ndarray:
+    """Packed orthonormal real DFT, written out from its definition.
+
+    X_k = (1/sqrt d) * sum_n u_n * exp(-2*pi*i*k*n/d), k = 0..d/2 (the rfft of
+    [P1, "First, the 17%"] with orthonormal scaling).  Rows of R, in order:
+      row 0        : X_0                      (real)
+      row 2k-1     : sqrt(2) * Re X_k,  k = 1 .. d/2-1
+      row 2k       : sqrt(2) * Im X_k,  k = 1 .. d/2-1
+      row d-1      : X_{d/2}                  (real)
+    The sqrt(2) on interior bins makes R^T R = I.
+    """
+    if d < 2 or d % 2:
+        raise ValueError("d must be even and >= 2")
+    n = np.arange(d)
+    half = d // 2
+    R = np.empty((d, d), dtype=np.float64)
+    R[0, :] = 1.0 / math.sqrt(d)
+    for k in range(1, half):
+        # reduce k*n mod d before forming the angle to keep it small
+        ang = 2.0 * math.pi * ((k * n) % d) / d
+        R[2 * k - 1, :] = math.sqrt(2.0 / d) * np.cos(ang)
+        R[2 * k, :] = -math.sqrt(2.0 / d) * np.sin(ang)
+    R[d - 1, :] = np.where(n % 2 == 0, 1.0, -1.0) / math.sqrt(d)
+    return R
+
+
+def srht_matrix(d: int) -> np.ndarray:
+    """(1/sqrt d) * H_d with H[i][k] = (-1)^popcount(i & k) (Sylvester order).
+
+    The sign-randomized Hadamard control of [P1, "First, the 17%"].
+    """
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    H = np.empty((d, d), dtype=np.float64)
+    for i in range(d):
+        for k in range(d):
+            H[i, k] = -1.0 if bin(i & k).count("1") % 2 else 1.0
+    return H / math.sqrt(d)
+
+
+_MATRIX_CACHE: dict[tuple[str, int], np.ndarray] = {}
+
+
+def rotation_matrix(rot: str, d: int) -> np.ndarray:
+    key = (rot, d)
+    if key not in _MATRIX_CACHE:
+        if rot == "srft":
+            _MATRIX_CACHE[key] = srft_matrix(d)
+        elif rot == "srht":
+            _MATRIX_CACHE[key] = srht_matrix(d)
+        elif rot == "none":
+            _MATRIX_CACHE[key] = np.eye(d)
+        else:
+            raise ValueError(f"unknown rotation {rot!r}")
+    return _MATRIX_CACHE[key]
+
+
+# ---------------------------------------------------------------------------
+# Symmetric absmax int4 quantizer
+# ---------------------------------------------------------------------------
+
+
+def fp16_scale_from_absmax(a: np.ndarray) -> np.ndarray:
+    """s = fp16(absmax / 8), round-to-nearest-even, saturated at 65504.
+
+    Divisor 8: the int4 worked examples of [P3, "What Quantization Is,
+    Mathematically"] (range -8..8 over 16 cells gives scale 1) and [P3, "How
+    Many Numbers Should One Scale Cover"] (a group whose largest value is 20
+    gets scale 20/8 = 2.5).  fp16 storage: same section of P3.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = (a / 8.0).astype(np.float16)
+    return np.where(np.isinf(s), np.float16(FP16_MAX), s).astype(np.float16)
+
+
+def quantize_with_scale(z: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """q = clamp(round_half_even(z / s), -8, 7); q = 0 where s == 0.
+
+    The rounding-and-clamp step of the symmetric quantizer ([P3, "What
+    Quantization Is, Mathematically"]; clamp to [-qmax-1, qmax] as in the
+    quantizer code of [P5, "Python: Quantize, Simulate ..."]; its round is
+    half-to-even).  ``s`` is the stored fp16 scale, widened exactly.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+    safe = np.where(s64 > 0, s64, 1.0)
+    r = np.where(s64 > 0, z / safe, 0.0)
+    return np.clip(np.rint(r), INT4_MIN, INT4_MAX).astype(np.int8)
+
+
+def quantize_groups(z: np.ndarray, group: int):
+    """Per-row, per-group absmax int4 quantization of the last axis.
+
+    Groups are consecutive runs of ``group`` values ([P1, "Fusing four steps
+    into two kernels is not enough": one absmax per 32 values]; group == d
+    is the per-token recipe).  Returns (q int8 [..., d], s float16
+    [..., d/group], a float64 [..., d/group]) where a is the exact absmax.
+    """
+    z = np.asarray(z, dtype=np.float64)
+    d = z.shape[-1]
+    if d % group:
+        raise ValueError("group must divide d")
+    zg = z.reshape(z.shape[:-1] + (d // group, group))
+    a = np.max(np.abs(zg), axis=-1)
+    s = fp16_scale_from_absmax(a)
+    q = quantize_with_scale(zg, s[..., None])
+    return q.reshape(z.shape), s, a
+
+
+def dequantize_groups(q: np.ndarray, s: np.ndarray, group: int) -> np.ndarray:
+    """x_hat = s * q (zero point 0), per group, in fp64."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    qg = q.reshape(q.shape[:-1] + (d // group, group))
+    s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+    return (qg * s64[..., None]).reshape(q.shape)
+
+
+# ---------------------------------------------------------------------------
+# Nibble packing ([P5, "Kernels: Marlin, CUTLASS, and Why INT4 Packing ..."])
+# ---------------------------------------------------------------------------
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """byte m = (q[2m] & 0xF) | ((q[2m+1] & 0xF) << 4): w0 low, w1 high."""
+    q = np.asarray(q, dtype=np.int64)
+    lo = q[..., 0::2] & 0xF
+    hi = q[..., 1::2] & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray) -> np.ndarray:
+    """w0 = byte & 0x0F, w1 = (byte >> 4) & 0x0F, each sign-extended."""
+    b = np.asarray(b, dtype=np.int64)
+    lo = b & 0xF
+    hi = (b >> 4) & 0xF
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The two fused operations, as plain steps
+# ---------------------------------------------------------------------------
+
+
+def rotate_fwd(x_f16: np.ndarray, seed: int, rows_per_seed: int = 0,
+               seed_period: int = 0, rot: str = "srft", row0: int = 0) -> np.ndarray:
+    """z = R (D (.) x) per row, fp64.  Sign first, then the transform."""
+    x = np.asarray(x_f16, dtype=np.float16).astype(np.float64)
+    n, d = x.shape
+    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0)
+    u = D * x
+    return u @ rotation_matrix(rot, d).T
+
+
+def rotate_inv(z: np.ndarray, seed: int, rows_per_seed: int = 0,
+               seed_period: int = 0, rot: str = "srft", row0: int = 0) -> np.ndarray:
+    """u = D (.) (R^T z) per row, fp64 (before the fp16 rounding of y)."""
+    z = np.asarray(z, dtype=np.float64)
+    n, d = z.shape
+    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0)
+    return D * (z @ rotation_matrix(rot, d))
+
+
+def quant_fwd(x_f16: np.ndarray, group: int, seed: int, rows_per_seed: int = 0,
+              seed_period: int = 0, rot: str = "srft", row0: int = 0):
+    """Forward: sign, rotate, per-group absmax int4, pack.
+
+    Returns (codes uint8 [n, d/2], scales float16 [n, d/group]).
+    """
+    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0)
+    q, s, _ = quantize_groups(z, group)
+    return pack_nibbles(q), s
+
+
+def dequant_inv(codes: np.ndarray, scales: np.ndarray, d: int, group: int,
+                seed: int, rows_per_seed: int = 0, seed_period: int = 0,
+                rot: str = "srft", row0: int = 0, return_fp64: bool = False):
+    """Inverse: unpack, dequantize, inverse-rotate, sign, round to fp16."""
+    q = unpack_nibbles(codes)
+    if q.shape[-1] != d:
+        raise ValueError("codes do not match d")
+    zhat = dequantize_groups(q, scales, group)
+    u = rotate_inv(zhat, seed, rows_per_seed, seed_period, rot, row0)
+    with np.errstate(over="ignore"):
+        y = u.astype(np.float16)
+    return (y, u) if return_fp64 else y
+
+
+def forward_detail(x_f16: np.ndarray, group: int, seed: int, rows_per_seed: int = 0,
+                   seed_period: int = 0, rot: str = "srft", row0: int = 0) -> dict:
+    """All intermediate values of the forward step, for tolerance checks."""
+    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0)
+    q, s, a = quantize_groups(z, group)
+    return {"z": z, "q": q, "s": s, "a": a, "codes": pack_nibbles(q)}
+
+
+# ---------------------------------------------------------------------------
+# Generic granularity helper for the MSE-ordering check of [P4]
+# ---------------------------------------------------------------------------
+
+
+def int4_roundtrip_blocks(w: np.ndarray, block_rows: int, block_cols: int) -> np.ndarray:
+    """Quantize-dequantize ``w`` with one absmax scale per (block_rows x block_cols) tile.
+
+    (rows, cols) = whole matrix -> per-tensor; (1, cols) -> per-row (channel);
+    (1, g) -> per-group.  Same scale and rounding rules as the method.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    r, c = w.shape
+    if r % block_rows or c % block_cols:
+        raise ValueError("blocks must tile the matrix")
+    t = w.reshape(r // block_rows, block_rows, c // block_cols, block_cols)
+    a = np.max(np.abs(t), axis=(1, 3))
+    s = fp16_scale_from_absmax(a)
+    sb = s[:, None, :, None]
+    q = quantize_with_scale(t, sb)
+    return (q.astype(np.float64) * sb.astype(np.float64)).reshape(r, c)

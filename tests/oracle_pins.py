@@ -1,0 +1,363 @@
+"""Pin checks for the oracle, written against what the pages and mathematics fix.
+
+Each ``check_*`` takes the implementation under test as an argument, so the
+same check serves the real oracle (tests/test_oracle_pins.py) and deliberately
+broken copies of it (tests/test_oracle_mutations.py).  A check raises
+AssertionError when the implementation disagrees with the pin.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _read_fixture(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append(line)
+    return rows
+
+
+def _kv_fixture(name):
+    out = {}
+    for line in _read_fixture(name):
+        key, val = line.split(":", 1)
+        out[key.strip()] = [float(v) for v in val.split()]
+    return out
+
+
+# --- sign generator -------------------------------------------------------
+
+
+def check_splitmix64_published(splitmix64_stream):
+    """Published SplitMix64 outputs (golden file)."""
+    for line in _read_fixture("splitmix64_vectors.txt"):
+        vals = [int(v) for v in line.split()]
+        seed, expect = vals[0], vals[1:]
+        got = splitmix64_stream(seed, len(expect))
+        assert list(got) == expect, f"splitmix64({seed}) = {got} != {expect}"
+
+
+def check_sign_vector_from_published(sign_vector):
+    """Signs of seed 1234567 follow from the top bits of the published outputs.
+
+    6457827717110365317 < 2^63 -> +1, 3203168211198807973 -> +1,
+    9817491932198370423 >= 2^63 -> -1, 4593380528125082431 -> +1,
+    16408922859458223821 -> -1.
+    """
+    got = sign_vector(1234567, 5)
+    assert np.array_equal(got, [1.0, 1.0, -1.0, 1.0, -1.0]), got
+    # seed 0: first output 16294208416658607535 >= 2^63 -> -1
+    assert sign_vector(0, 1)[0] == -1.0
+
+
+def check_row_seed(row_seed):
+    """Hand-evaluated cases of seed + ((r // rows_per_seed) % seed_period)."""
+    cases = [
+        # seed, row, rps, period, expected
+        (100, 0, 0, 0, 100),
+        (100, 12345, 0, 0, 100),
+        (100, 9, 10, 0, 100),
+        (100, 10, 10, 0, 101),
+        (100, 25, 10, 0, 102),
+        (100, 25, 10, 2, 100),
+        (100, 35, 10, 2, 101),
+        (100, 40960 * 33 + 7, 40960, 32, 101),
+        ((1 << 64) - 1, 10, 10, 0, 0),  # wraps modulo 2^64
+    ]
+    for seed, row, rps, per, exp in cases:
+        got = row_seed(seed, row, rps, per)
+        assert got == exp, (seed, row, rps, per, got, exp)
+
+
+# --- rotations ------------------------------------------------------------
+
+
+def check_orthonormal(matrix_fn, ds=(2, 4, 8, 16)):
+    """R^T R = I and R R^T = I, element by element, and ||R x|| = ||x||."""
+    rng = np.random.default_rng(7)
+    for d in ds:
+        R = matrix_fn(d)
+        assert R.shape == (d, d)
+        G = np.zeros((d, d))
+        for i in range(d):  # brute force dot products
+            for j in range(d):
+                G[i, j] = sum(R[k, i] * R[k, j] for k in range(d))
+        assert np.max(np.abs(G - np.eye(d))) < 1e-12, f"R^T R != I at d={d}"
+        assert np.max(np.abs(R @ R.T - np.eye(d))) < 1e-12
+        for _ in range(5):
+            x = rng.standard_normal(d)
+            assert abs(np.linalg.norm(R @ x) - np.linalg.norm(x)) < 1e-12 * max(1, np.linalg.norm(x))
+
+
+def pack_rfft_reference(x):
+    """numpy.fft.rfft(norm='ortho') packed as [X0, s*ReX1, s*ImX1, ..., X_{d/2}], s = sqrt 2.
+
+    Written from view_as_real(rfft) with the two always-zero imaginary parts
+    (of X0 and X_{d/2}) dropped; independent of the explicit DFT matrix.
+    """
+    d = x.shape[-1]
+    X = np.fft.rfft(x, norm="ortho")
+    z = np.empty(x.shape[:-1] + (d,))
+    z[..., 0] = X[..., 0].real
+    z[..., 1:d - 1:2] = math.sqrt(2) * X[..., 1:d // 2].real
+    z[..., 2:d - 1:2] = math.sqrt(2) * X[..., 1:d // 2].imag
+    z[..., d - 1] = X[..., d // 2].real
+    return z
+
+
+def check_srft_vs_library(srft_matrix, ds=(4, 8, 16, 64, 128, 256)):
+    rng = np.random.default_rng(11)
+    for d in ds:
+        R = srft_matrix(d)
+        x = rng.standard_normal((7, d))
+        assert np.max(np.abs(x @ R.T - pack_rfft_reference(x))) < 1e-12, f"d={d}"
+
+
+def check_srft_closed_forms(srft_matrix, ds=(8, 64, 256)):
+    """Inputs whose packed orthonormal DFT is known in closed form."""
+    for d in ds:
+        R = srft_matrix(d)
+        n = np.arange(d)
+        # unit impulse at 0: every X_k = 1/sqrt d
+        z = R @ np.eye(d)[0]
+        exp = np.zeros(d)
+        exp[0] = exp[d - 1] = 1 / math.sqrt(d)
+        exp[1:d - 1:2] = math.sqrt(2 / d)
+        assert np.allclose(z, exp, atol=1e-13), "impulse"
+        # constant 1: X0 = sqrt d, everything else 0
+        z = R @ np.ones(d)
+        exp = np.zeros(d)
+        exp[0] = math.sqrt(d)
+        assert np.allclose(z, exp, atol=1e-12), "constant"
+        # (-1)^n: only the Nyquist bin, X_{d/2} = sqrt d
+        z = R @ np.where(n % 2 == 0, 1.0, -1.0)
+        exp = np.zeros(d)
+        exp[d - 1] = math.sqrt(d)
+        assert np.allclose(z, exp, atol=1e-12), "nyquist"
+        for m in (1, d // 4, d // 2 - 1):
+            # cos(2 pi m n / d): X_m = sqrt(d)/2 -> z_{2m-1} = sqrt(d/2)
+            z = R @ np.cos(2 * math.pi * m * n / d)
+            exp = np.zeros(d)
+            exp[2 * m - 1] = math.sqrt(d / 2)
+            assert np.allclose(z, exp, atol=1e-12), f"cos m={m}"
+            # sin(2 pi m n / d): X_m = -i sqrt(d)/2 -> z_{2m} = -sqrt(d/2)
+            z = R @ np.sin(2 * math.pi * m * n / d)
+            exp = np.zeros(d)
+            exp[2 * m] = -math.sqrt(d / 2)
+            assert np.allclose(z, exp, atol=1e-12), f"sin m={m}"
+
+
+def check_srht(srht_matrix, ds=(1, 2, 4, 8, 16, 64, 128, 256)):
+    import scipy.linalg
+    for d in ds:
+        H = srht_matrix(d) * math.sqrt(d)
+        assert np.array_equal(np.rint(H), H)
+        assert np.array_equal(H, scipy.linalg.hadamard(d).astype(np.float64)), f"d={d}"
+        assert np.array_equal(H @ H.T, d * np.eye(d))
+
+
+# --- quantizer ------------------------------------------------------------
+
+
+def check_ruler(fp16_scale_from_absmax, quantize_with_scale):
+    fx = _kv_fixture("ruler_example.txt")
+    vals = np.array(fx["values"])
+    s = fp16_scale_from_absmax(np.max(np.abs(vals)))
+    assert float(s) == fx["scale"][0], s
+    q = quantize_with_scale(vals, s)
+    # interior values land exactly on cells; -8 is a code, +8 is clipped to 7
+    assert np.array_equal(q, np.clip(vals, -8, 7)), q
+
+
+def check_outlier(fp16_scale_from_absmax, quantize_with_scale):
+    fx = _kv_fixture("outlier_example.txt")
+    vals = np.array(fx["values"])
+    s = fp16_scale_from_absmax(np.max(np.abs(vals)))
+    assert float(s) == fx["scale"][0], s
+    q_small = quantize_with_scale(np.array(fx["small"]), s)
+    assert len(set(q_small.tolist())) == 1, q_small  # one shared cell
+    assert q_small[0] == 0
+
+
+def check_half_step_bound(fp16_scale_from_absmax, quantize_with_scale):
+    """|z - s q| <= s/2 before clipping ([P4]); <= s when the absmax element clips."""
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        z = rng.standard_normal(32) * rng.choice([1e-3, 1.0, 30.0])
+        if trial % 3 == 0:
+            z[rng.integers(32)] *= 20.0
+        s = fp16_scale_from_absmax(np.max(np.abs(z)))
+        q = quantize_with_scale(z, s)
+        s64 = float(s)
+        r = z / s64
+        err = np.abs(z - s64 * q)
+        inside = (r <= 7.5) & (r >= -8.5)
+        assert np.all(err[inside] <= s64 / 2 * (1 + 1e-12))
+        # fp16 rounding of s moves absmax/s at most 2^-11 relative away from 8
+        assert np.all(err <= s64 * (1 + 8 * 2.0 ** -11) + 1e-300)
+
+
+def check_bruteforce_argmin(quantize_with_scale):
+    """q = argmin_{c in [-8,7]} |z - s c|, ties to the even code."""
+    rng = np.random.default_rng(5)
+    s = np.float16(0.375)
+    s64 = float(s)
+    zs = list(rng.uniform(-10, 10, size=2000) * s64)
+    zs += [(k + 0.5) * s64 for k in range(-10, 10)]  # exact ties
+    zs += [-8.5 * s64, 7.5 * s64, 0.0, -0.0]
+    for z in zs:
+        cands = np.arange(-8, 8)
+        err = np.abs(z - s64 * cands)
+        best = cands[err == err.min()]
+        want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+        got = int(quantize_with_scale(np.array([z]), s)[0])
+        assert got == want, (z / s64, got, want)
+
+
+def check_scale_rounding(fp16_scale_from_absmax):
+    """fp16 round-to-nearest-even of absmax/8, saturating at 65504."""
+    cases = [
+        (8.0, 1.0),
+        (8 * (1 + 2.0 ** -11), 1.0),  # tie -> even mantissa
+        (8 * (1 + 3 * 2.0 ** -11), 1 + 2.0 ** -9),  # tie -> even mantissa
+        (8 * (1 + 2.0 ** -11 + 2.0 ** -30), 1 + 2.0 ** -10),  # just above tie
+        (20.0, 2.5),
+        (0.0, 0.0),
+        (8 * 2.0 ** -24, 2.0 ** -24),  # smallest subnormal
+        (8 * 2.0 ** -25, 0.0),  # tie between 0 and 2^-24 -> 0
+        (8 * 70000.0, 65504.0),  # saturate
+        (8 * 65504.0, 65504.0),
+    ]
+    for a, want in cases:
+        got = float(fp16_scale_from_absmax(np.array(a)))
+        assert got == want, (a, got, want)
+
+
+def check_zero_group(quantize_groups, dequantize_groups):
+    z = np.zeros((3, 64))
+    z[1, 32:] = 1.0
+    # nonzero values whose absmax/8 is below half the smallest fp16 subnormal:
+    # the scale rounds to 0 and every code of the group must be 0
+    z[2, :32] = np.linspace(-1e-9, 1e-9, 32)
+    q, s, _ = quantize_groups(z, 32)
+    assert float(s[0, 0]) == 0 and float(s[0, 1]) == 0 and float(s[1, 0]) == 0
+    assert float(s[2, 0]) == 0
+    assert np.all(q[0] == 0) and np.all(q[1, :32] == 0) and np.all(q[2, :32] == 0)
+    assert np.all(dequantize_groups(q, s, 32)[0] == 0)
+
+
+def check_mse_ordering(int4_roundtrip_blocks):
+    """Per-tensor >= per-channel >= per-group 4-bit MSE on a matrix with small
+    and large regions ([P4]: the tests it describes)."""
+    rng = np.random.default_rng(9)
+    w = rng.standard_normal((64, 256))
+    w[5:9, :] *= 20.0       # large rows
+    w[:, 100:104] *= 20.0   # large columns (hurt per-row, not per-group)
+    def mse(br, bc):
+        return float(np.mean((int4_roundtrip_blocks(w, br, bc) - w) ** 2))
+    t, c, g = mse(64, 256), mse(1, 256), mse(1, 32)
+    assert t > c > g, (t, c, g)
+
+
+# --- packing --------------------------------------------------------------
+
+
+def check_nibbles(pack_nibbles, unpack_nibbles):
+    allb = np.arange(256, dtype=np.uint8)[None, :]
+    assert np.array_equal(pack_nibbles(unpack_nibbles(allb)), allb)
+    for line in _read_fixture("nibble_layout.txt"):
+        w0, w1, b = line.split()
+        got = int(pack_nibbles(np.array([[int(w0), int(w1)]]))[0, 0])
+        assert got == int(b, 16), (w0, w1, hex(got), b)
+        un = unpack_nibbles(np.array([[int(b, 16)]], dtype=np.uint8))[0]
+        assert un.tolist() == [int(w0), int(w1)]
+
+
+# --- whole pipeline -------------------------------------------------------
+
+
+def check_impulse_end_to_end(oracle):
+    """x = c * e_0 gives z = c * D_0 * R[:, 0], known in closed form."""
+    for d, g in ((64, 32), (128, 32), (256, 32), (64, 64)):
+        c = 3.0
+        x = np.zeros((1, d), dtype=np.float16)
+        x[0, 0] = c
+        seed = 4242
+        d0 = oracle.sign_vector(seed, d)[0]
+        codes, scales = oracle.quant_fwd(x, g, seed)
+        # every group holds a sqrt(2/d) * c entry, the largest magnitude
+        big = math.sqrt(2.0 / d) * c
+        s_exp = np.float16(big / 8)
+        assert np.all(scales == s_exp), (scales, s_exp)
+        q = oracle.unpack_nibbles(codes)[0]
+        s64 = float(s_exp)
+        z = np.zeros(d)
+        z[0] = z[d - 1] = d0 * c / math.sqrt(d)
+        z[1:d - 1:2] = d0 * big
+        q_exp = np.clip(np.rint(z / s64), -8, 7)
+        assert np.array_equal(q, q_exp), (q[:8], q_exp[:8])
+
+
+def check_roundtrip_energy(oracle):
+    """||y_fp64 - x|| = ||z_hat - z|| (R and D are orthogonal)."""
+    rng = np.random.default_rng(13)
+    for rot in ("srft", "srht"):
+        for d, g in ((64, 32), (128, 32), (256, 32)):
+            x = (rng.standard_normal((9, d)) * 2).astype(np.float16)
+            det = oracle.forward_detail(x, g, 77, rot=rot)
+            codes, scales = det["codes"], det["s"]
+            _, u = oracle.dequant_inv(codes, scales, d, g, 77, rot=rot, return_fp64=True)
+            zhat = oracle.dequantize_groups(det["q"], det["s"], g)
+            lhs = np.linalg.norm(u - x.astype(np.float64), axis=1)
+            rhs = np.linalg.norm(zhat - det["z"], axis=1)
+            assert np.allclose(lhs, rhs, rtol=1e-9, atol=1e-12), (rot, d)
+
+
+def check_rotation_helps(oracle):
+    """Rotating before quantizing lowers int4 error on outlier data ([P1,
+    "Before you celebrate, check the quality bill"]); SRFT and SRHT land
+    close to each other ([P1, "First, the 17%"])."""
+    rng = np.random.default_rng(21)
+    d, g = 64, 32
+    x = rng.standard_normal((2000, d))
+    x[:, [3, 17]] *= 20.0
+    x = x.astype(np.float16)
+    x64 = x.astype(np.float64)
+    err = {}
+    for rot in ("none", "srft", "srht"):
+        det = oracle.forward_detail(x, g, 5, rot=rot)
+        _, u = oracle.dequant_inv(det["codes"], det["s"], d, g, 5, rot=rot, return_fp64=True)
+        err[rot] = float(np.mean((u - x64) ** 2))
+    assert err["srft"] < 0.5 * err["none"], err
+    assert err["srht"] < 0.5 * err["none"], err
+    # the pages compare the two on perplexity, not MSE; on this impulse-like
+    # outlier data the flat Hadamard image of a spike is slightly better, so
+    # the check only asks that neither is far from the other
+    assert 1 / 1.5 < err["srft"] / err["srht"] < 1.5, err
+
+
+def check_group_scales(quantize_groups):
+    """Each group gets its own absmax/8 (hand-evaluated)."""
+    z = np.zeros((1, 128))
+    z[0, 5] = -8.0      # group 0 absmax 8   -> scale 1
+    z[0, 40] = 16.0     # group 1 absmax 16  -> scale 2
+    z[0, 70] = 0.5      # group 2 absmax 0.5 -> scale 1/16
+    z[0, 127] = -20.0   # group 3 absmax 20  -> scale 2.5
+    z[0, 100] = 2.5     # group 3: 2.5 / 2.5 = 1
+    q, s, _ = quantize_groups(z, 32)
+    assert s.astype(np.float64).tolist() == [[1.0, 2.0, 0.0625, 2.5]], s
+    assert q[0, 5] == -8 and q[0, 40] == 7 and q[0, 70] == 7 and q[0, 127] == -8
+    assert q[0, 100] == 1
+    q, s, _ = quantize_groups(z, 64)
+    assert s.astype(np.float64).tolist() == [[2.0, 2.5]], s
+    assert q[0, 5] == -4 and q[0, 100] == 1

@@ -1,0 +1,111 @@
+"""Plant plausible mistakes in a copy of the oracle (CPU only) and check that
+at least one pin catches each of them.  The real oracle is never modified."""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins as P
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "rtq_oracle.py")
+
+
+def mutated(old, new):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/present: {old!r}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def all_pins(m):
+    """Run every pin against module ``m``; return the names that failed."""
+    checks = {
+        "splitmix": lambda: P.check_splitmix64_published(m.splitmix64_stream),
+        "signs": lambda: P.check_sign_vector_from_published(m.sign_vector),
+        "row_seed": lambda: P.check_row_seed(m.row_seed),
+        "srft_orth": lambda: P.check_orthonormal(m.srft_matrix),
+        "srft_lib": lambda: P.check_srft_vs_library(m.srft_matrix),
+        "srft_closed": lambda: P.check_srft_closed_forms(m.srft_matrix),
+        "srht": lambda: P.check_srht(m.srht_matrix),
+        "ruler": lambda: P.check_ruler(m.fp16_scale_from_absmax, m.quantize_with_scale),
+        "outlier": lambda: P.check_outlier(m.fp16_scale_from_absmax, m.quantize_with_scale),
+        "half_step": lambda: P.check_half_step_bound(m.fp16_scale_from_absmax, m.quantize_with_scale),
+        "argmin": lambda: P.check_bruteforce_argmin(m.quantize_with_scale),
+        "scale_round": lambda: P.check_scale_rounding(m.fp16_scale_from_absmax),
+        "zero_group": lambda: P.check_zero_group(m.quantize_groups, m.dequantize_groups),
+        "group_scales": lambda: P.check_group_scales(m.quantize_groups),
+        "mse_order": lambda: P.check_mse_ordering(m.int4_roundtrip_blocks),
+        "nibbles": lambda: P.check_nibbles(m.pack_nibbles, m.unpack_nibbles),
+        "impulse": lambda: P.check_impulse_end_to_end(m),
+        "roundtrip": lambda: P.check_roundtrip_energy(m),
+    }
+    failed = []
+    for name, fn in checks.items():
+        try:
+            with __import__("numpy").errstate(all="ignore"):
+                fn()
+        except Exception:
+            failed.append(name)
+    return failed
+
+
+MUTATIONS = {
+    "srft drops sqrt2 on interior bins": (
+        "R[2 * k - 1, :] = math.sqrt(2.0 / d) * np.cos(ang)",
+        "R[2 * k - 1, :] = math.sqrt(1.0 / d) * np.cos(ang)"),
+    "srft uses exp(+i...)": (
+        "R[2 * k, :] = -math.sqrt(2.0 / d) * np.sin(ang)",
+        "R[2 * k, :] = math.sqrt(2.0 / d) * np.sin(ang)"),
+    "srft swaps Re/Im slots": (
+        "R[2 * k - 1, :] = math.sqrt(2.0 / d) * np.cos(ang)\n        R[2 * k, :] = -math.sqrt(2.0 / d) * np.sin(ang)",
+        "R[2 * k, :] = math.sqrt(2.0 / d) * np.cos(ang)\n        R[2 * k - 1, :] = -math.sqrt(2.0 / d) * np.sin(ang)"),
+    "srft nyquist sign": (
+        "R[d - 1, :] = np.where(n % 2 == 0, 1.0, -1.0) / math.sqrt(d)",
+        "R[d - 1, :] = np.where(n % 2 == 0, -1.0, 1.0) / math.sqrt(d)"),
+    "hadamard uses OR": (
+        'H[i, k] = -1.0 if bin(i & k).count("1") % 2 else 1.0',
+        'H[i, k] = -1.0 if bin(i | k).count("1") % 2 else 1.0'),
+    "scale divides by 7": ("s = (a / 8.0).astype(np.float16)", "s = (a / 7.0).astype(np.float16)"),
+    "scale rounds through fp32": (
+        "s = (a / 8.0).astype(np.float16)", "s = (a / 8.0).astype(np.float32).astype(np.float16)"),
+    "scale not saturated": (
+        "return np.where(np.isinf(s), np.float16(FP16_MAX), s).astype(np.float16)",
+        "return s.astype(np.float16)"),
+    "clamp to [-7, 7]": ("INT4_MIN = -8", "INT4_MIN = -7"),
+    "round half away from zero": (
+        "return np.clip(np.rint(r), INT4_MIN, INT4_MAX).astype(np.int8)",
+        "return np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), INT4_MIN, INT4_MAX).astype(np.int8)"),
+    "truncate instead of round": (
+        "return np.clip(np.rint(r), INT4_MIN, INT4_MAX).astype(np.int8)",
+        "return np.clip(np.trunc(r), INT4_MIN, INT4_MAX).astype(np.int8)"),
+    "zero scale divides by zero": (
+        "r = np.where(s64 > 0, z / safe, 0.0)", "r = z / s64"),
+    "absmax over the whole row": (
+        "a = np.max(np.abs(zg), axis=-1)",
+        "a = np.repeat(np.max(np.abs(zg), axis=(-1, -2))[..., None], zg.shape[-2], axis=-1)"),
+    "nibbles swapped": ("return (lo | (hi << 4)).astype(np.uint8)", "return (hi | (lo << 4)).astype(np.uint8)"),
+    "unpack without sign extension": ("lo = np.where(lo >= 8, lo - 16, lo)", "lo = lo"),
+    "splitmix wrong multiplier": ("0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
+    "sign from bit 0": ("[-1.0 if (o >> 63) & 1 else 1.0", "[-1.0 if o & 1 else 1.0"),
+    "row seed without modulo": ("block %= seed_period", "block = block"),
+    "inverse uses R instead of R^T": (
+        "return D * (z @ rotation_matrix(rot, d))", "return D * (z @ rotation_matrix(rot, d).T)"),
+    "inverse forgets the signs": (
+        "return D * (z @ rotation_matrix(rot, d))", "return z @ rotation_matrix(rot, d)"),
+    "forward rotates before the sign flip": (
+        "u = D * x\n    return u @ rotation_matrix(rot, d).T",
+        "return D * (x @ rotation_matrix(rot, d).T)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    old, new = MUTATIONS[name]
+    failed = all_pins(mutated(old, new))
+    assert failed, f"no pin catches the planted mistake: {name}"
+
+
+def test_unmutated_copy_passes_every_pin():
+    assert all_pins(mutated("INT4_MAX = 7", "INT4_MAX = 7")) == []
