@@ -1,0 +1,155 @@
+"""rotate_then_quantize_amd -- fused rotate-then-quantize int4 K/V kernels for MI355X.
+
+A thin binding over ``librtq.so`` (C ABI in ``include/rtq.h``).  It only checks
+and marshals arguments: every step of the method runs in the HIP kernels.
+PyTorch provides the device memory and the current stream.  There is no CPU
+fallback: if the library is missing, every call raises.
+
+    codes, scales = srft_quant_fwd(x, group, seed)        # x: [n, d] fp16 on the GPU
+    y = srft_dequant_inv(codes, scales, d, group, seed)   # y: [n, d] fp16
+
+The method ("Quantization Speed Is Often a Kernel Problem", sections "First,
+the 17%" and "Fusing four steps into two kernels is not enough"): rotate each
+K/V vector (SRFT, or the SRHT control), quantize it to int4 with one absmax
+fp16 scale per group, and undo both when it is read back.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
+    "RTQError", "library", "library_path", "SUPPORTED",
+]
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG_DIR, "librtq.so")
+_lib = None
+
+RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_HIP = 0, 1, 2, 3
+# (d, group) pairs the library is built for
+SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+
+
+class RTQError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def library():
+    """The loaded ctypes handle of librtq.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RTQError(-1, f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m rotate_then_quantize_amd._build")
+        lib = ctypes.CDLL(_LIB_PATH)
+        fwd_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                    ctypes.c_int32, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        for name in ("srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv"):
+            fn = getattr(lib, name)
+            fn.argtypes = fwd_args
+            fn.restype = ctypes.c_int
+        lib.rtq_status_string.argtypes = [ctypes.c_int]
+        lib.rtq_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != RTQ_OK:
+        msg = library().rtq_status_string(status).decode()
+        raise RTQError(status, msg)
+
+
+def _stream_handle(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtype, name, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _fwd(cname, x, group, seed, rows_per_seed, seed_period, codes, scales, stream):
+    import torch
+    _need(x, torch.float16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [n, d]")
+    n, d = x.shape
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    if codes is None:
+        codes = torch.empty((n, d // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, d // group), dtype=torch.float16, device=x.device)
+    _need(codes, torch.uint8, "codes", (n, d // 2))
+    _need(scales, torch.float16, "scales", (n, d // group))
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+        n, d, group, seed & ((1 << 64) - 1), rows_per_seed, seed_period, _stream_handle(x, stream)))
+    return codes, scales
+
+
+def _inv(cname, codes, scales, d, group, seed, rows_per_seed, seed_period, out, stream):
+    import torch
+    _need(codes, torch.uint8, "codes")
+    if codes.dim() != 2 or codes.shape[1] * 2 != d:
+        raise ValueError("codes must be [n, d/2]")
+    n = codes.shape[0]
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    _need(scales, torch.float16, "scales", (n, d // group))
+    if out is None:
+        out = torch.empty((n, d), dtype=torch.float16, device=codes.device)
+    _need(out, torch.float16, "out", (n, d))
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        n, d, group, seed & ((1 << 64) - 1), rows_per_seed, seed_period, _stream_handle(codes, stream)))
+    return out
+
+
+def srft_quant_fwd(x, group, seed, rows_per_seed=0, seed_period=0, codes=None, scales=None, stream=None):
+    """Forward step with the SRFT rotation: returns (codes [n, d/2] uint8, scales [n, d/group] fp16)."""
+    return _fwd("srft_quant_fwd", x, group, seed, rows_per_seed, seed_period, codes, scales, stream)
+
+
+def srft_dequant_inv(codes, scales, d, group, seed, rows_per_seed=0, seed_period=0, out=None, stream=None):
+    """Inverse step with the SRFT rotation: returns y [n, d] fp16."""
+    return _inv("srft_dequant_inv", codes, scales, d, group, seed, rows_per_seed, seed_period, out, stream)
+
+
+def srht_quant_fwd(x, group, seed, rows_per_seed=0, seed_period=0, codes=None, scales=None, stream=None):
+    """Forward step with the SRHT (Walsh-Hadamard) control rotation."""
+    return _fwd("srht_quant_fwd", x, group, seed, rows_per_seed, seed_period, codes, scales, stream)
+
+
+def srht_dequant_inv(codes, scales, d, group, seed, rows_per_seed=0, seed_period=0, out=None, stream=None):
+    """Inverse step with the SRHT (Walsh-Hadamard) control rotation."""
+    return _inv("srht_dequant_inv", codes, scales, d, group, seed, rows_per_seed, seed_period, out, stream)
+
+
+def quant_fwd(rot, *args, **kw):
+    return (srft_quant_fwd if rot == "srft" else srht_quant_fwd)(*args, **kw)
+
+
+def dequant_inv(rot, *args, **kw):
+    return (srft_dequant_inv if rot == "srft" else srht_dequant_inv)(*args, **kw)

@@ -1,0 +1,492 @@
+// rtq_device.hpp -- register-resident building blocks for the fused
+// rotate-then-quantize kernels on CDNA4 (gfx950, wave64).
+//
+// Every transform here works on one K/V vector held entirely in the registers
+// of one lane (d <= 128) or of two lanes (d = 256), with compile-time
+// register indices: no LDS, no cross-lane traffic and no loops at run time.
+//
+// Method sources (page title, section):
+//   "Quantization Speed Is Often a Kernel Problem", "First, the 17%":
+//     rotate each K/V vector, quantize to int4, dequantize and rotate back;
+//     SRFT = fixed random +-1 pattern then an FFT (rfft / irfft); SRHT =
+//     sign-randomized Hadamard transform as the control.
+//   same page, "Fusing four steps into two kernels is not enough": forward =
+//     rotate + quantize in one kernel, inverse = dequantize + inverse-rotate
+//     in one kernel; one absmax scale per group of 32 values.
+//   "Day 9 - Quantization: Shrink the Bytes Themselves", "What Quantization
+//     Is, Mathematically" / "How Many Numbers Should One Scale Cover":
+//     symmetric int4, scale = absmax / 8, scales stored as fp16.
+//   "Chapter 25 - Quantization: The Hardware View", "Kernels: Marlin,
+//     CUTLASS, and Why INT4 Packing Needs Special Code": two int4 per byte,
+//     w0 in the low nibble.
+#pragma once
+
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtq {
+
+// ---------------------------------------------------------------------------
+// Compile-time helpers
+// ---------------------------------------------------------------------------
+
+template <int... Is> struct iseq {};
+template <int N, int... Is> struct make_iseq : make_iseq<N - 1, N - 1, Is...> {};
+template <int... Is> struct make_iseq<0, Is...> { using type = iseq<Is...>; };
+template <int I> struct ic { static constexpr int value = I; };
+
+template <typename F, int... Is>
+__device__ __forceinline__ void sfor_impl(F& f, iseq<Is...>) {
+  (f(ic<Is>{}), ...);
+}
+// Unrolled loop whose index is a compile-time constant: f(ic<0>{}) .. f(ic<N-1>{}).
+template <int N, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(f, typename make_iseq<N>::type{});
+}
+#define RTQ_CI(x) (decltype(x)::value)
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n / 2); }
+constexpr int bitrev(int x, int bits) {
+  int r = 0;
+  for (int i = 0; i < bits; ++i) r = (r << 1) | ((x >> i) & 1);
+  return r;
+}
+
+// cos(2*pi*t/n) and sin(2*pi*t/n) in double at compile time: exact integer
+// reduction of the angle to [0, pi/4], then Taylor series.
+constexpr double kPi = 3.141592653589793238462643383279502884;
+constexpr double taylor_sin(double x) {
+  double x2 = x * x, term = x, sum = x;
+  for (int k = 1; k < 16; ++k) {
+    term *= -x2 / ((2.0 * k) * (2.0 * k + 1.0));
+    sum += term;
+  }
+  return sum;
+}
+constexpr double taylor_cos(double x) {
+  double x2 = x * x, term = 1.0, sum = 1.0;
+  for (int k = 1; k < 16; ++k) {
+    term *= -x2 / ((2.0 * k - 1.0) * (2.0 * k));
+    sum += term;
+  }
+  return sum;
+}
+constexpr double cos2pi(long long t, long long n) {
+  t %= n;
+  if (t < 0) t += n;
+  const long long q = (4 * t) / n;      // quadrant
+  const long long r = 4 * t - q * n;    // angle inside the quadrant = (pi/2) r / n
+  double c, s;
+  if (2 * r <= n) {
+    const double phi = (kPi / 2.0) * (double)r / (double)n;
+    c = taylor_cos(phi);
+    s = taylor_sin(phi);
+  } else {
+    const double psi = (kPi / 2.0) * (double)(n - r) / (double)n;
+    c = taylor_sin(psi);
+    s = taylor_cos(psi);
+  }
+  switch (q) {
+    case 0: return c;
+    case 1: return -s;
+    case 2: return -c;
+    default: return s;
+  }
+}
+constexpr double sin2pi(long long t, long long n) { return cos2pi(4 * t - n, 4 * n); }
+constexpr double csqrt(double x) {
+  double r = x > 1.0 ? x : 1.0;
+  for (int i = 0; i < 200; ++i) r = 0.5 * (r + x / r);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// fp16 and bit helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float lo_f(uint32_t w) {
+  return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu)));
+}
+__device__ __forceinline__ float hi_f(uint32_t w) {
+  return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
+}
+// Two floats to packed fp16 (round to nearest even): low half = a.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const __half2 h = __floats2half2_rn(a, b);
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// fp16 + fp16 and fp16 - fp16 into fp32 with one v_fma_mix_f32 each (the sum
+// of two fp16 values is exact in fp32).  SEL_A / SEL_B pick the half (0 = low,
+// 1 = high) of each packed operand.
+template <int SEL_A, int SEL_B>
+__device__ __forceinline__ float mix_add(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (SEL_A == 0 && SEL_B == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  else if constexpr (SEL_A == 1 && SEL_B == 1)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  else if constexpr (SEL_A == 0 && SEL_B == 1)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+// a - b
+template <int SEL_A, int SEL_B>
+__device__ __forceinline__ float mix_sub(uint32_t a, uint32_t b) {
+  float r;
+  if constexpr (SEL_A == 0 && SEL_B == 0)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(b), "v"(a));
+  else if constexpr (SEL_A == 1 && SEL_B == 1)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(b), "v"(a));
+  else if constexpr (SEL_A == 0 && SEL_B == 1)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(b), "v"(a));
+  else
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(r) : "v"(b), "v"(a));
+  return r;
+}
+
+// Nibble order of a 32-bit word reversed (nibble i <-> nibble 7-i).
+__device__ __forceinline__ uint32_t nibble_reverse(uint32_t x) {
+  x = __builtin_amdgcn_perm(x, x, 0x00010203u);  // byte reverse
+  return ((x >> 4) & 0x0f0f0f0fu) | ((x << 4) & 0xf0f0f0f0u);
+}
+
+// ---------------------------------------------------------------------------
+// Sign pattern: SplitMix64 (Steele, Lea & Flood 2014).  Output i (0-based) of
+// the stream started at state S is mix(S + (i+1)*gamma); the sign of element i
+// is -1 iff its bit 63 is set.  The final xor-shift of the mixer leaves bit 63
+// unchanged, so it is skipped.
+// ---------------------------------------------------------------------------
+
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+
+__device__ __forceinline__ uint32_t sign_bit(uint64_t seed, uint32_t i) {
+  uint64_t z = seed + (uint64_t)(i + 1u) * kGamma;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return (uint32_t)(z >> 63);
+}
+
+// XOR masks that flip the fp16 sign bits of elements 8k .. 8k+7 (four packed
+// pairs, low half = even element).
+__device__ __forceinline__ uint4 chunk_sign_masks(uint64_t seed, uint32_t k) {
+  uint32_t m[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t e = 8u * k + 2u * t;
+    m[t] = (sign_bit(seed, e) << 15) | (sign_bit(seed, e + 1u) << 31);
+  }
+  return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+__device__ __forceinline__ uint64_t row_seed(uint64_t seed, int64_t row, int64_t rows_per_seed,
+                                             int32_t seed_period) {
+  if (rows_per_seed == 0) return seed;
+  uint64_t block = (uint64_t)(row / rows_per_seed);
+  if (seed_period != 0) block %= (uint64_t)seed_period;
+  return seed + block;
+}
+
+__device__ __forceinline__ uint4 xor4(uint4 a, uint4 b) {
+  return make_uint4(a.x ^ b.x, a.y ^ b.y, a.z ^ b.z, a.w ^ b.w);
+}
+
+// ---------------------------------------------------------------------------
+// Complex radix-2 FFT (decimation in time), forward sign exp(-2 pi i / L).
+// ---------------------------------------------------------------------------
+
+// (a, b) <- (a + w b, a - w b), w = exp(-2 pi i J / L).
+template <int J, int L>
+__device__ __forceinline__ void bfly(float& ar, float& ai, float& br, float& bi) {
+  if constexpr (J == 0) {
+    const float tr = ar - br, ti = ai - bi;
+    ar = ar + br;
+    ai = ai + bi;
+    br = tr;
+    bi = ti;
+  } else if constexpr (4 * J == L) {  // w = -i, w b = (bi, -br)
+    const float tr = ar - bi, ti = ai + br;
+    ar = ar + bi;
+    ai = ai - br;
+    br = tr;
+    bi = ti;
+  } else {
+    constexpr float c = (float)cos2pi(J, L);
+    constexpr float s = (float)sin2pi(J, L);
+    // w b = (c br + s bi) + i (c bi - s br)
+    const float pr = __builtin_fmaf(c, br, __builtin_fmaf(s, bi, ar));
+    const float pi = __builtin_fmaf(c, bi, __builtin_fmaf(-s, br, ai));
+    br = __builtin_fmaf(2.0f, ar, -pr);
+    bi = __builtin_fmaf(2.0f, ai, -pi);
+    ar = pr;
+    ai = pi;
+  }
+}
+
+// Stages of length 4 .. M on data already in bit-reversed order after stage 1.
+template <int M>
+__device__ __forceinline__ void fft_stages_from4(float (&re)[M], float (&im)[M]) {
+  constexpr int LOG = ilog2(M);
+  sfor<LOG - 1>([&](auto S) {
+    constexpr int len = 4 << RTQ_CI(S);
+    constexpr int half = len / 2;
+    sfor<M / len>([&](auto B) {
+      sfor<half>([&](auto J) {
+        constexpr int p = RTQ_CI(B) * len + RTQ_CI(J);
+        bfly<RTQ_CI(J), len>(re[p], im[p], re[p + half], im[p + half]);
+      });
+    });
+  });
+}
+
+// W = DFT_M(w), w_m = lo(h[m]) + i hi(h[m]) (packed fp16 pairs).  Natural order
+// in and out; the bit reversal is register renaming only.
+template <int M>
+__device__ __forceinline__ void cfft_from_f16(const uint32_t (&h)[M], float (&re)[M], float (&im)[M]) {
+  constexpr int LOG = ilog2(M);
+  sfor<M / 2>([&](auto I) {
+    constexpr int i = RTQ_CI(I);
+    constexpr int e = bitrev(2 * i, LOG);  // pair (e, e + M/2)
+    re[2 * i] = mix_add<0, 0>(h[e], h[e + M / 2]);
+    im[2 * i] = mix_add<1, 1>(h[e], h[e + M / 2]);
+    re[2 * i + 1] = mix_sub<0, 0>(h[e], h[e + M / 2]);
+    im[2 * i + 1] = mix_sub<1, 1>(h[e], h[e + M / 2]);
+  });
+  fft_stages_from4<M>(re, im);
+}
+
+// Same for fp32 input arrays (natural order).
+template <int M>
+__device__ __forceinline__ void cfft_f32(const float (&xr)[M], const float (&xi)[M], float (&re)[M],
+                                         float (&im)[M]) {
+  constexpr int LOG = ilog2(M);
+  sfor<M / 2>([&](auto I) {
+    constexpr int i = RTQ_CI(I);
+    constexpr int e = bitrev(2 * i, LOG);
+    re[2 * i] = xr[e] + xr[e + M / 2];
+    im[2 * i] = xi[e] + xi[e + M / 2];
+    re[2 * i + 1] = xr[e] - xr[e + M / 2];
+    im[2 * i + 1] = xi[e] - xi[e + M / 2];
+  });
+  fft_stages_from4<M>(re, im);
+}
+
+// ---------------------------------------------------------------------------
+// Real DFT of length D = 2M from one complex DFT of length M.
+// ---------------------------------------------------------------------------
+
+// Scale sets for the real-DFT bins: bin 0 is multiplied by S0, bin M by SM,
+// bins 1..M-1 by SI.
+template <int D>
+struct OrthoPacked {  // the packed orthonormal rfft: z[0]=X0, ..., sqrt2 on interior bins
+  static constexpr double s0 = 1.0 / csqrt((double)D);
+  static constexpr double sm = 1.0 / csqrt((double)D);
+  static constexpr double si = csqrt(2.0 / (double)D);
+};
+
+// Bins U_k (k = 0..M) of the real sequence u, u_{2m} = lo(h[m]),
+// u_{2m+1} = hi(h[m]):  U_k = sum_n u_n exp(-2 pi i k n / D), scaled per SC.
+// With W = DFT_M(u_{2m} + i u_{2m+1}):
+//   U_k = (W_k + conj W_{M-k})/2 - (i/2) exp(-2 pi i k / D) (W_k - conj W_{M-k}).
+template <int D, class SC>
+__device__ __forceinline__ void rfft_bins(const uint32_t (&h)[D / 2], float (&ur)[D / 2 + 1],
+                                          float (&ui)[D / 2 + 1]) {
+  constexpr int M = D / 2;
+  float re[M], im[M];
+  cfft_from_f16<M>(h, re, im);
+  constexpr float s0 = (float)SC::s0, sm = (float)SC::sm, si = (float)SC::si;
+  ur[0] = s0 * (re[0] + im[0]);
+  ui[0] = 0.0f;
+  ur[M] = sm * (re[0] - im[0]);
+  ui[M] = 0.0f;
+  ur[M / 2] = si * re[M / 2];
+  ui[M / 2] = -si * im[M / 2];
+  sfor<M / 2 - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    constexpr float hh = (float)(SC::si * 0.5);
+    constexpr float a = (float)(SC::si * 0.5 * sin2pi(k, D));  // (si/2) * i * w^k = a + i b
+    constexpr float b = (float)(SC::si * 0.5 * cos2pi(k, D));
+    const float Ar = re[k] + re[M - k], Ai = im[k] - im[M - k];
+    const float Br = re[k] - re[M - k], Bi = im[k] + im[M - k];
+    const float Qr = __builtin_fmaf(a, Br, -b * Bi);
+    const float Qi = __builtin_fmaf(a, Bi, b * Br);
+    ur[k] = __builtin_fmaf(hh, Ar, -Qr);
+    ui[k] = __builtin_fmaf(hh, Ai, -Qi);
+    ur[M - k] = __builtin_fmaf(hh, Ar, Qr);
+    ui[M - k] = -__builtin_fmaf(hh, Ai, Qi);
+  });
+}
+
+// z = R u for the packed orthonormal SRFT of length D (D <= 128, one lane).
+template <int D>
+__device__ __forceinline__ void srft_fwd(const uint32_t (&h)[D / 2], float (&z)[D]) {
+  constexpr int M = D / 2;
+  float ur[M + 1], ui[M + 1];
+  rfft_bins<D, OrthoPacked<D>>(h, ur, ui);
+  z[0] = ur[0];
+  sfor<M - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    z[2 * k - 1] = ur[k];
+    z[2 * k] = ui[k];
+  });
+  z[D - 1] = ur[M];
+}
+
+// u = KAPPA * R^T z for the packed orthonormal SRFT of length D (the
+// orthonormal irfft of the unpacked bins, times KAPPA).  Computed as
+// u_{2n} + i u_{2n+1} = conj(DFT_M(V))_n with V built from z.
+template <int D, class KAPPA>
+__device__ __forceinline__ void srft_inv(const float (&z)[D], float (&u)[D]) {
+  constexpr int M = D / 2;
+  constexpr double cout = KAPPA::value / (csqrt(2.0) * csqrt((double)D));
+  float vr[M], vi[M];
+  {
+    constexpr float c = (float)(cout * csqrt(2.0));
+    vr[0] = c * (z[0] + z[D - 1]);
+    vi[0] = c * (z[D - 1] - z[0]);
+    constexpr float c2 = (float)(cout * 2.0);
+    vr[M / 2] = c2 * z[M - 1];
+    vi[M / 2] = c2 * z[M];
+  }
+  sfor<M / 2 - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    constexpr float co = (float)cout;
+    constexpr float ms = (float)(-cout * sin2pi(k, D));  // cout * i * w^-k = ms + i mc'
+    constexpr float mc = (float)(cout * cos2pi(k, D));
+    const float Ar = z[2 * k - 1] + z[2 * (M - k) - 1], Ai = z[2 * k] - z[2 * (M - k)];
+    const float Br = z[2 * k - 1] - z[2 * (M - k) - 1], Bi = z[2 * k] + z[2 * (M - k)];
+    const float Qr = __builtin_fmaf(ms, Br, -mc * Bi);
+    const float Qi = __builtin_fmaf(mc, Br, ms * Bi);
+    vr[k] = __builtin_fmaf(co, Ar, Qr);
+    vi[k] = -__builtin_fmaf(co, Ai, Qi);
+    vr[M - k] = __builtin_fmaf(co, Ar, -Qr);
+    vi[M - k] = __builtin_fmaf(co, Ai, -Qi);
+  });
+  float wr[M], wi[M];
+  cfft_f32<M>(vr, vi, wr, wi);
+  sfor<M>([&](auto N) {
+    constexpr int m = RTQ_CI(N);
+    u[2 * m] = wr[m];
+    u[2 * m + 1] = -wi[m];
+  });
+}
+
+struct One { static constexpr double value = 1.0; };
+struct Sqrt2 { static constexpr double value = 1.4142135623730950488016887242097; };
+
+// ---------------------------------------------------------------------------
+// Walsh-Hadamard transform (Sylvester order), unnormalized.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ __forceinline__ void fwht_stages_from2(float (&v)[N]) {
+  constexpr int LOG = ilog2(N);
+  sfor<LOG - 1>([&](auto S) {
+    constexpr int h = 2 << RTQ_CI(S);
+    sfor<N / (2 * h)>([&](auto B) {
+      sfor<h>([&](auto J) {
+        constexpr int p = RTQ_CI(B) * 2 * h + RTQ_CI(J);
+        const float a = v[p], b = v[p + h];
+        v[p] = a + b;
+        v[p + h] = a - b;
+      });
+    });
+  });
+}
+
+// y = H_N u, u_{2m} = lo(h[m]), u_{2m+1} = hi(h[m]).
+template <int N>
+__device__ __forceinline__ void fwht_from_f16(const uint32_t (&h)[N / 2], float (&y)[N]) {
+  sfor<N / 2>([&](auto M) {
+    constexpr int m = RTQ_CI(M);
+    y[2 * m] = mix_add<0, 1>(h[m], h[m]);
+    y[2 * m + 1] = mix_sub<0, 1>(h[m], h[m]);
+  });
+  fwht_stages_from2<N>(y);
+}
+
+// In place, fp32.
+template <int N>
+__device__ __forceinline__ void fwht_f32(float (&v)[N]) {
+  sfor<N / 2>([&](auto M) {
+    constexpr int m = RTQ_CI(M);
+    const float a = v[2 * m], b = v[2 * m + 1];
+    v[2 * m] = a + b;
+    v[2 * m + 1] = a - b;
+  });
+  fwht_stages_from2<N>(v);
+}
+
+// ---------------------------------------------------------------------------
+// Symmetric absmax int4 quantizer and nibble packing.
+// ---------------------------------------------------------------------------
+
+// Per group of G consecutive values of (zs * z): s = fp16_rne(absmax / 8)
+// saturated at 65504; q = clamp(rne(zs * z / s), -8, 7), q = 0 when s == 0.
+// Codes: cw[w] holds values 8w .. 8w+7, value 2i in the low nibble of byte i.
+// The rounding uses fma(z, 1/s, 1.5 * 2^23): the fp32 result lies in
+// [2^23, 2^24) where the spacing is 1, so the single rounding of the fma is
+// round-half-even of z/s, and the low 4 bits of the result are q mod 16.
+template <int D, int G>
+__device__ __forceinline__ void quantize_pack(const float (&z)[D], float zs, uint32_t (&cw)[D / 8],
+                                              uint32_t (&sb)[D / G]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  sfor<D / G>([&](auto GI) {
+    constexpr int g0 = RTQ_CI(GI) * G;
+    float a = 0.0f;
+    sfor<G>([&](auto I) { a = fmaxf(a, fabsf(z[g0 + RTQ_CI(I)])); });
+    a *= zs;
+    uint32_t bits = __half_as_ushort(__float2half_rn(a * 0.125f));
+    bits = bits < 0x7bffu ? bits : 0x7bffu;  // saturate (inf -> 65504)
+    sb[RTQ_CI(GI)] = bits;
+    const float s = __half2float(__ushort_as_half((unsigned short)bits));
+    const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
+    sfor<G / 8>([&](auto W) {
+      constexpr int base = g0 + RTQ_CI(W) * 8;
+      uint32_t b[8];
+      sfor<8>([&](auto I) {
+        const float t = __builtin_fmaf(z[base + RTQ_CI(I)], inv, kMagic);
+        b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic - 8.0f, kMagic + 7.0f));
+      });
+      // low bytes of the even codes -> E, of the odd codes -> O
+      const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) |
+                         __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
+      const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) |
+                         __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
+      cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+    });
+  });
+}
+
+// z = zs * s * q for every value (inverse of quantize_pack's codes).  The
+// nibble is biased by 8 (xor 0x8) so it reads as q + 8 in 0..15, converted by
+// one v_cvt_f32_ubyte; then fma(q + 8, s, -8 s) = s q exactly.
+template <int D, int G>
+__device__ __forceinline__ void dequant_unpack(const uint32_t (&cw)[D / 8], const uint32_t (&sb)[D / G],
+                                               float zs, float (&z)[D]) {
+  sfor<D / G>([&](auto GI) {
+    constexpr int g0 = RTQ_CI(GI) * G;
+    const float s = __half2float(__ushort_as_half((unsigned short)sb[RTQ_CI(GI)])) * zs;
+    const float m8 = -8.0f * s;
+    sfor<G / 8>([&](auto W) {
+      constexpr int base = g0 + RTQ_CI(W) * 8;
+      const uint32_t x = cw[base / 8] ^ 0x88888888u;
+      const uint32_t lo = x & 0x0f0f0f0fu;
+      const uint32_t hi = (x >> 4) & 0x0f0f0f0fu;
+      z[base + 0] = __builtin_fmaf((float)(lo & 0xffu), s, m8);
+      z[base + 1] = __builtin_fmaf((float)(hi & 0xffu), s, m8);
+      z[base + 2] = __builtin_fmaf((float)((lo >> 8) & 0xffu), s, m8);
+      z[base + 3] = __builtin_fmaf((float)((hi >> 8) & 0xffu), s, m8);
+      z[base + 4] = __builtin_fmaf((float)((lo >> 16) & 0xffu), s, m8);
+      z[base + 5] = __builtin_fmaf((float)((hi >> 16) & 0xffu), s, m8);
+      z[base + 6] = __builtin_fmaf((float)(lo >> 24), s, m8);
+      z[base + 7] = __builtin_fmaf((float)(hi >> 24), s, m8);
+    });
+  });
+}
+
+}  // namespace rtq

@@ -1,0 +1,106 @@
+"""The C ABI on the host: library loads, exports every declared symbol, and
+rejects bad arguments before any HIP call (CPU only, no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import rotate_then_quantize_amd as rtq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rtq.library_path()),
+                                reason="librtq.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z_0-9]*\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["rtq_status_string", "srft_dequant_inv", "srft_quant_fwd",
+                                    "srht_dequant_inv", "srht_quant_fwd"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rtq.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", rtq.library_path()], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert set(declared_functions()) <= exported
+    # nothing else of ours leaks out of the shared object
+    ours = {s for s in exported if "rtq" in s or "srft" in s or "srht" in s}
+    assert ours == set(declared_functions()), ours
+
+
+def test_status_strings():
+    lib = rtq.library()
+    for st, key in [(0, "RTQ_OK"), (1, "INVALID_ARG"), (2, "UNSUPPORTED"), (3, "RTQ_ERR_HIP")]:
+        assert key in lib.rtq_status_string(st).decode()
+    assert lib.rtq_status_string(99)
+
+
+FWD = ["srft_quant_fwd", "srht_quant_fwd"]
+INV = ["srft_dequant_inv", "srht_dequant_inv"]
+A, B, C = 0x10000, 0x200000, 0x3000000  # distinct 16-byte aligned fake addresses (never dereferenced)
+
+
+def call(name, p0, p1, p2, n, d, g, seed=1, rps=0, per=0):
+    fn = getattr(rtq.library(), name)
+    return fn(ctypes.c_void_p(p0), ctypes.c_void_p(p1), ctypes.c_void_p(p2), n, d, g, seed, rps, per, None)
+
+
+@pytest.mark.parametrize("name", FWD + INV)
+def test_rejects_bad_arguments_without_launching(name):
+    assert call(name, A, B, C, -1, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, C, 10, 64, 32, rps=-1) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, C, 10, 64, 32, per=-1) == rtq.RTQ_ERR_INVALID_ARG
+    for d, g in [(96, 32), (32, 32), (512, 32), (64, 16), (64, 128), (128, 256), (64, 48), (256, 256)]:
+        assert call(name, A, B, C, 10, d, g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
+    # null and misaligned pointers
+    assert call(name, 0, B, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, 0, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, 0, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A + 8, B, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B + 4, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, C + 2, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    # size overflow
+    assert call(name, A, B, C, 1 << 62, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", FWD + INV)
+def test_zero_rows_is_a_no_op(name):
+    assert call(name, 0, 0, 0, 0, 64, 32) == rtq.RTQ_OK
+    assert call(name, A, B, C, 0, 256, 32) == rtq.RTQ_OK
+
+
+@pytest.mark.parametrize("name", FWD)
+def test_forward_rejects_overlapping_buffers(name):
+    n, d, g = 100, 64, 32  # x: 12800 B, codes: 3200 B, scales: 400 B
+    assert call(name, A, A + 1024, C, n, d, g) == rtq.RTQ_ERR_INVALID_ARG   # codes inside x
+    assert call(name, A, B, A + 4096, n, d, g) == rtq.RTQ_ERR_INVALID_ARG   # scales inside x
+    assert call(name, A, B, B + 3184, n, d, g) == rtq.RTQ_ERR_INVALID_ARG   # scales overlap codes
+
+
+@pytest.mark.parametrize("name", INV)
+def test_inverse_rejects_overlapping_buffers(name):
+    n, d, g = 100, 64, 32
+    assert call(name, A + 1024, B, A, n, d, g) == rtq.RTQ_ERR_INVALID_ARG   # codes inside y
+    assert call(name, A, B, A + 3000, n, d, g) == rtq.RTQ_ERR_INVALID_ARG        # y overlaps codes
+    assert call(name, A, B, B - 16, n, d, g) == rtq.RTQ_ERR_INVALID_ARG         # y overlaps scales
+
+
+def test_python_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        rtq.srft_quant_fwd(x, 32, 1)
+    with pytest.raises(TypeError):
+        rtq.srft_quant_fwd(x.float(), 32, 1)
