@@ -1,0 +1,257 @@
+#!/usr/bin/env python3
+"""Throughput of the fused SRFT int4 forward + inverse kernels on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic K/V input:
+the forward launch (sign flip, SRFT, per-group absmax, int4 rounding, nibble
+packing) over every row, then the inverse launch (unpack, dequantize, inverse
+SRFT, sign flip, fp16 store) over every row.  The default workload is the
+SmolLM2-360M-shaped prefill KV cache (32 layers x 2 x 5 KV heads x 4096
+tokens, d = 64, groups of 32, per-layer sign seeds): 1,310,720 vectors.
+
+Inputs are resident in HBM before timing starts.  Several replicas of the
+buffers are cycled so the 256 MB last-level cache cannot hold a step's data.
+Prints one JSON line on stdout (human-readable notes go to stderr).
+
+  python bench.py [--steps K] [--warmup W] [--workload 1..5] [--rot srft|srht]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, public figure
+METRIC = "K/V vectors/s and HBM GB/s (% of peak), fused SRFT-int4 quant+dequant, 1 GPU"
+KERNEL_SOURCES = [os.path.join(ROOT, "rotate_then_quantize_amd", "csrc", f) for f in ("rtq.hip", "rtq_device.hpp", "rtq_div.hpp")]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload_name: str, rot: str, kernel: str):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{rot}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x_gpu, rot, seconds):
+    """The oracle, as it is, on consecutive 65536-row chunks of the same
+    workload until ``seconds`` of CPU time are spent (input copy excluded)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    chunk = 65536
+    done, spent, r0 = 0, 0.0, 0
+    while spent < seconds and r0 < w.n_rows:
+        r1 = min(w.n_rows, r0 + chunk)
+        xs = x_gpu[r0:r1].cpu().numpy()
+        t0 = time.perf_counter()
+        codes, scales = oracle.quant_fwd(xs, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, rot, row0=r0)
+        oracle.dequant_inv(codes, scales, w.d, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, rot, row0=r0)
+        spent += time.perf_counter() - t0
+        done += r1 - r0
+        r0 = r1
+    return {
+        "value": done / spent,
+        "unit": "vectors/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {done} of {w.n_rows} rows of the same workload, forward + inverse, "
+                  f"fp64 numpy oracle in {chunk}-row chunks ({spent:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--rot", choices=["srft", "srht"], default="srft")
+    ap.add_argument("--replicas", type=int, default=0, help="buffer sets cycled per step (0 = enough to exceed 1 GiB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU: this build has no multi-GPU path (rows are independent; "
+            "see DESIGN.md for how the work would shard). Run with --gpus 1.")
+        sys.exit(2)
+
+    import torch
+    import rotate_then_quantize_amd as rtq
+    from rotate_then_quantize_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calibrate_copy:
+        nbytes = args.calibrate_copy << 20
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {nbytes} bytes 5 times")
+        return
+
+    w = W.WORKLOADS[args.workload]
+    rot = args.rot
+    if rot not in w.rots:
+        log(f"note: workload {w.name} is specified with {w.rots}; running {rot} anyway")
+    lib = rtq.library()
+    fwd_fn = lib.srft_quant_fwd if rot == "srft" else lib.srht_quant_fwd
+    inv_fn = lib.srft_dequant_inv if rot == "srft" else lib.srht_dequant_inv
+
+    # rows of one step: decode = new token's rows forward, whole cache inverse
+    n_inv = w.n_rows
+    n_fwd = w.new_rows if w.new_tokens else w.n_rows
+    bpv = w.bytes_per_vector()
+    footprint = n_fwd * 2 * w.d + n_inv * (w.d // 2 + 2 * (w.d // w.group)) + n_inv * 2 * w.d
+    replicas = args.replicas or max(1, math.ceil((1 << 30) / footprint))
+    log(f"workload {w.name}: fwd rows {n_fwd}, inv rows {n_inv}, d={w.d}, group={w.group}, rot={rot}, "
+        f"{replicas} buffer replica(s) of {footprint / 1e6:.1f} MB")
+
+    x0 = W.generate(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    sets = []
+    for r in range(replicas):
+        x = x0 if r == 0 else x0.clone()
+        codes = torch.empty((n_inv, w.d // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((n_inv, w.d // w.group), dtype=torch.float16, device=dev)
+        y = torch.empty((n_inv, w.d), dtype=torch.float16, device=dev)
+        xin = x[n_inv - n_fwd:] if w.new_tokens else x
+        cin, sin = (codes[n_inv - n_fwd:], scales[n_inv - n_fwd:]) if w.new_tokens else (codes, scales)
+        if w.new_tokens:  # the cached prefix is already quantized
+            st = fwd_fn(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(codes.data_ptr()),
+                        ctypes.c_void_p(scales.data_ptr()), n_inv, w.d, w.group, w.sign_seed,
+                        w.rows_per_seed, w.seed_period, sh)
+            assert st == 0, lib.rtq_status_string(st)
+        fa = (ctypes.c_void_p(xin.data_ptr()), ctypes.c_void_p(cin.data_ptr()), ctypes.c_void_p(sin.data_ptr()),
+              n_fwd, w.d, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, sh)
+        ia = (ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+              n_inv, w.d, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, sh)
+        sets.append((fa, ia, (x, codes, scales, y)))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        fa, ia, _ = sets[i % replicas]
+        if ev is not None:
+            ev[0].record(stream)
+        s1 = fwd_fn(*fa)
+        if ev is not None:
+            ev[1].record(stream)
+        s2 = inv_fn(*ia)
+        if ev is not None:
+            ev[2].record(stream)
+        if s1 or s2:
+            raise RuntimeError(lib.rtq_status_string(s1 or s2).decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    inv_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    fwd_bytes, inv_bytes = n_fwd * bpv, n_inv * bpv
+    fwd_gbps, inv_gbps = fwd_bytes / fwd_ms / 1e6, inv_bytes / inv_ms / 1e6
+    vectors = max(n_fwd, n_inv)
+    value = vectors * args.steps / (t1 - t0)
+    step_gbps = (fwd_bytes + inv_bytes) / (ms_step * 1e6)
+    dominant = "inv" if inv_ms >= fwd_ms else "fwd"
+    dom_ms, dom_bytes = (inv_ms, inv_bytes) if dominant == "inv" else (fwd_ms, fwd_bytes)
+    achieved = dom_bytes / dom_ms / 1e6
+    kname = {"fwd": "quant_fwd", "inv": "dequant_inv"}[dominant]
+    traffic = read_traffic(w.name, rot, kname)
+    log(f"step {ms_step * 1e3:.1f} us | fwd {fwd_ms * 1e3:.1f} us {fwd_gbps:.0f} GB/s "
+        f"({100 * fwd_gbps / HBM_PEAK_GBPS:.1f}%) | inv {inv_ms * 1e3:.1f} us {inv_gbps:.0f} GB/s "
+        f"({100 * inv_gbps / HBM_PEAK_GBPS:.1f}%) | step {step_gbps:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "rows_forward": n_fwd, "rows_inverse": n_inv, "d": w.d, "group": w.group,
+            "rotation": rot, "rows_per_seed": w.rows_per_seed, "seed_period": w.seed_period,
+            "io": "fp16 in/out, int4 codes, fp16 scales", "buffer_replicas": replicas,
+        },
+        "hbm_gbps": {"step": step_gbps, "forward": fwd_gbps, "inverse": inv_gbps,
+                     "peak": HBM_PEAK_GBPS, "bytes_per_vector": bpv},
+        "kernel_us": {"forward": fwd_ms * 1e3, "inverse": inv_ms * 1e3},
+        "roofline": {
+            "kernel": f"{rot}_{kname} d={w.d} g={w.group}",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x0, rot, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -22,7 +22,9 @@
  *    scales   : [n][d/group] IEEE fp16; scale j of a row covers packed
  *                            coordinates [j*group, (j+1)*group)
  *  Shapes: d in {64, 128, 256}; group in {32, 64, 128, 256} with group <= d.
- *    group == d is the per-token recipe (one scale per vector).
+ *    group == d is the per-token recipe (one scale per vector).  Rows per
+ *    call: 0 <= n <= 0xFFFFFF00 (row indices are 32-bit on the device); a
+ *    larger n returns RTQ_ERR_INVALID_ARG.
  *  Signs: row r uses the sign vector of seed'(r) =
  *    seed + ((r / rows_per_seed) % seed_period)   (mod 2^64),
  *    where rows_per_seed == 0 means one seed for every row and

@@ -14,197 +14,309 @@
 //     tile); d = 256 vectors span two lanes, lane v (even samples for SRFT,
 //     first half for SRHT) and lane v+32 (32 rows per tile).
 //   * Rows are read and written with fully coalesced 16-byte accesses and
-//     transposed to / from the owning lane through a padded, wave-private LDS
-//     tile (no barriers between waves).  The +-1 signs are applied on the
-//     16-byte chunks during that transposition: a lane always handles the
-//     same chunk position, so its XOR masks are computed once per seed.
+//     transposed to / from the owning lane through a wave-private LDS tile:
+//     forward tiles arrive by direct-to-LDS loads (global_load_lds_dwordx4)
+//     with an xor swizzle that keeps the per-row LDS reads conflict free, and
+//     the packed codes leave through LDS as full 1 KB stores.
+//   * The +-1 signs of a tile come from one SplitMix64 evaluation per lane, a
+//     ballot, and scalar bit extraction, then one v_xor per packed pair.
 //   * The transforms, the absmax reduction, rounding, clamping and nibble
 //     packing are straight-line register code (rtq_device.hpp); there is no
 //     dense contraction and no MFMA.
+//   * Row indices are 32-bit (any tensor that fits in HBM has fewer than 2^32
+//     rows); addresses are a wave-uniform 64-bit tile base plus 32-bit lane
+//     offsets; the seed rule divides with precomputed multipliers
+//     (rtq_div.hpp).
 #include <hip/hip_runtime.h>
 
-#include <mutex>
 #include <stdint.h>
 
 #include "rtq.h"
 #include "rtq_device.hpp"
+#include "rtq_div.hpp"
 
 namespace rtq {
 
 enum Rot : int { kSRFT = 0, kSRHT = 1 };
 
-__device__ __forceinline__ void lds_sync() { __syncthreads(); }  // one-wave workgroup
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
 
-// Cached XOR masks of this lane's chunk position for the seed of the current
-// tile, recomputed only when the seed changes.
-struct SignCache {
+// Every workgroup is a single wave, and a wave's LDS instructions execute in
+// order, so exchanging data between its lanes through LDS only needs the
+// compiler kept from reordering the accesses.  (__syncthreads would also wait
+// for every outstanding global store and load of the wave.)
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_wave_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt lgkmcnt(0): this wave's LDS reads have returned.
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// vmcnt(N) (gfx9 encoding: expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Sign masks
+// ---------------------------------------------------------------------------
+
+// XOR masks for the D/2 packed fp16 pairs of one row (pair m = elements 2m,
+// 2m+1) as wave-uniform values: lane l computes the sign bits of elements
+// l, l + 64, ... and a ballot gathers them.
+template <int D>
+__device__ __forceinline__ void uniform_sign_masks(uint64_t s, int lane, uint32_t (&sm)[D / 2]) {
+  sfor<D / 64>([&](auto Q) {
+    constexpr int q = RTQ_CI(Q);
+    const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
+    sfor<32>([&](auto M) {
+      constexpr int m = RTQ_CI(M);
+      const uint32_t b0 = (uint32_t)(bits >> (2 * m)) & 1u, b1 = (uint32_t)(bits >> (2 * m + 1)) & 1u;
+      sm[32 * q + m] = (b0 << 15) | (b1 << 31);
+    });
+  });
+}
+
+// Signs of each lane's own row (the lane holds row row0 + lane).  When every
+// row of the tile has the same seed the masks are wave-uniform (cached across
+// tiles); a tile that straddles a seed boundary builds per-lane masks in a
+// plain loop.
+template <int D>
+struct RowSigns {
+  uint32_t sm[D / 2];
+  uint64_t seed_cached;
+  bool valid;
+
+  __device__ __forceinline__ void apply(uint32_t (&h)[D / 2], const SeedRule& sr, uint32_t row0, int rows,
+                                        int lane) {
+    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+    if (b0 == b1) {
+      const uint64_t s = seed_of_block(b0, sr);
+      if (!valid || seed_cached != s) {
+        uniform_sign_masks<D>(s, lane, sm);
+        seed_cached = s;
+        valid = true;
+      }
+      sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] ^= sm[RTQ_CI(M)]; });
+      return;
+    }
+    const uint64_t mine = seed_of_block(seed_block(row0 + (uint32_t)(lane < rows ? lane : rows - 1), sr), sr);
+    sfor<D / 64>([&](auto Q) {
+      uint64_t bits = 0;
+#pragma unroll 1
+      for (uint32_t e = 0; e < 64; ++e) bits |= (uint64_t)sign_bit(mine, 64u * RTQ_CI(Q) + e) << e;
+      sfor<32>([&](auto M) {
+        constexpr int m = RTQ_CI(M);
+        const uint32_t b0 = (uint32_t)(bits >> (2 * m)) & 1u, b1 = (uint32_t)(bits >> (2 * m + 1)) & 1u;
+        h[32 * RTQ_CI(Q) + m] ^= (b0 << 15) | (b1 << 31);
+      });
+    });
+  }
+};
+
+// Signs of a fixed 16-byte chunk position (elements 8k .. 8k+7) of whatever
+// row a lane stages; cached per seed.  Used by the two-lane d = 256 kernels.
+struct ChunkSigns {
   uint64_t seed;
   uint4 m;
   bool valid;
+
+  // Masks for the tile's seed; returns false if the tile straddles a seed
+  // boundary (then the caller derives the masks row by row).
+  __device__ __forceinline__ bool prepare(const SeedRule& sr, uint32_t row0, int rows, uint32_t kpos) {
+    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+    if (b0 != b1) return false;
+    const uint64_t s = seed_of_block(b0, sr);
+    if (!valid || seed != s) {
+      m = chunk_sign_masks(s, kpos);
+      seed = s;
+      valid = true;
+    }
+    return true;
+  }
 };
 
-// Prepare the cache for a tile [row0, row0 + rows); returns whether every row
-// of the tile uses the same seed.
-__device__ __forceinline__ bool tile_signs(SignCache& sc, uint64_t seed, int64_t row0, int rows, int64_t rps,
-                                           int32_t period, uint32_t kpos) {
-  const bool uniform = (rps == 0) || (row0 / rps == (row0 + rows - 1) / rps);
-  if (uniform) {
-    const uint64_t s = row_seed(seed, row0, rps, period);
-    if (!sc.valid || sc.seed != s) {
-      sc.m = chunk_sign_masks(s, kpos);
-      sc.seed = s;
-      sc.valid = true;
-    }
-  }
-  return uniform;
+__device__ __forceinline__ void wave_tile_range(uint32_t n_tiles, int32_t per_wave, uint32_t& t0, uint32_t& t1) {
+  t0 = blockIdx.x * (uint32_t)per_wave;
+  t1 = t0 + (uint32_t)per_wave < n_tiles ? t0 + (uint32_t)per_wave : n_tiles;
 }
 
 // ---------------------------------------------------------------------------
 // d = 64 / 128: one lane per vector, 64 vectors per tile.
 // ---------------------------------------------------------------------------
 
-template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, int64_t n, uint64_t seed,
-                                                      int64_t rps, int32_t period) {
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int LROW = CPR + 1;  // padded LDS row (uint4), keeps ds_read_b128 conflict free
-  __shared__ uint4 lds[64 * LROW];
-  const int lane = threadIdx.x;
-  const uint32_t kpos = lane % CPR;
-  const int64_t tiles = (n + 63) / 64;
-  SignCache sc;
-  sc.valid = false;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row0 = t * 64;
-    const int rows = (int)(n - row0 < 64 ? n - row0 : 64);
-    const bool uniform = tile_signs(sc, seed, row0, rows, rps, period, kpos);
-    // coalesced load of the tile, sign flip, transpose into LDS
-    if (uniform) {
-      uint4 v[CPR];
-      sfor<CPR>([&](auto J) {
-        const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
-        v[RTQ_CI(J)] = rl < rows ? x[(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
-      });
-      sfor<CPR>([&](auto J) {
-        const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
-        lds[rl * LROW + kpos] = xor4(v[RTQ_CI(J)], sc.m);
-      });
-    } else {  // the tile crosses a seed boundary: signs per row
-#pragma unroll 1
-      for (int j = 0; j < CPR; ++j) {
-        const int rl = (j * 64 + lane) / CPR;
-        const uint4 q = rl < rows ? x[(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
-        lds[rl * LROW + kpos] = xor4(q, chunk_sign_masks(row_seed(seed, row0 + rl, rps, period), kpos));
-      }
-    }
-    lds_sync();
-    uint32_t h[D / 2];
-    sfor<CPR>([&](auto C) {
-      const uint4 q = lds[lane * LROW + RTQ_CI(C)];
-      h[4 * RTQ_CI(C) + 0] = q.x;
-      h[4 * RTQ_CI(C) + 1] = q.y;
-      h[4 * RTQ_CI(C) + 2] = q.z;
-      h[4 * RTQ_CI(C) + 3] = q.w;
-    });
-    lds_sync();
-    float z[D];
-    float zs;
-    if constexpr (ROT == kSRFT) {
-      srft_fwd<D>(h, z);
-      zs = 1.0f;
-    } else {
-      fwht_from_f16<D>(h, z);
-      zs = (float)(1.0 / csqrt((double)D));
-    }
-    uint32_t cw[D / 8], sb[D / G];
-    quantize_pack<D, G>(z, zs, cw, sb);
-    if (lane < rows) {
-      const int64_t row = row0 + lane;
-      sfor<D / 32>([&](auto C) {
-        codes[row * (D / 32) + RTQ_CI(C)] =
-            make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]);
-      });
-      if constexpr (D / G == 1) {
-        reinterpret_cast<uint16_t*>(scales)[row] = (uint16_t)sb[0];
-      } else if constexpr (D / G == 2) {
-        reinterpret_cast<uint32_t*>(scales)[row] = sb[0] | (sb[1] << 16);
-      } else {
-        reinterpret_cast<uint2*>(scales)[row] = make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16));
-      }
-    }
+// Direct-to-LDS staging of one tile.  Load instruction j of lane i fills LDS
+// slot 64j + i (hardware layout); slot s holds row r = s / CPR, chunk
+// k = (s % CPR) ^ (r & 7).  The xor swizzle makes the owning lane's
+// ds_read_b128 of its row conflict free while every row's chunks still come
+// from one contiguous row in HBM.  A partial tile reloads its last row.
+template <int CPR>
+__device__ __forceinline__ void load_tile_to_lds(const uint4* __restrict__ xt, int rows, uint4* buf, int lane) {
+  auto issue = [&](auto J, int rmax) {
+    const int slot = RTQ_CI(J) * 64 + lane;
+    const int r = slot / CPR;
+    const int k = (slot % CPR) ^ (r & 7);
+    const int rr = r < rmax ? r : rmax - 1;
+    const uint32_t off = (uint32_t)(rr * CPR + k) * 16u;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)xt + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16,
+                                     0, 0);
+  };
+  if (rows == 64) {
+    sfor<CPR>([&](auto J) { issue(J, 64); });
+  } else {
+    sfor<CPR>([&](auto J) { issue(J, rows); });
   }
 }
 
+template <int CPR>
+__device__ __forceinline__ void read_own_row(const uint4* buf, int lane, uint32_t (&h)[CPR * 4]) {
+  const int sw = lane & 7;
+  sfor<CPR>([&](auto C) {
+    const uint4 q = buf[lane * CPR + (RTQ_CI(C) ^ sw)];
+    h[4 * RTQ_CI(C) + 0] = q.x;
+    h[4 * RTQ_CI(C) + 1] = q.y;
+    h[4 * RTQ_CI(C) + 2] = q.z;
+    h[4 * RTQ_CI(C) + 3] = q.w;
+  });
+}
+
+template <int D, int G, int ROT>
+__device__ __forceinline__ void quantize_row(const uint32_t (&h)[D / 2], uint32_t (&cw)[D / 8],
+                                             uint32_t (&sb)[D / G]) {
+  float z[D];
+  float zs;
+  if constexpr (ROT == kSRFT) {
+    srft_fwd_unscaled<D>(h, z);
+    zs = SrftScale<D>::value;
+  } else {
+    fwht_from_f16<D>(h, z);
+    zs = InvSqrt<D>::value;
+  }
+  quantize_pack<D, G>(z, zs, cw, sb);
+}
+
+// scales of one row, packed as written to memory (fp16 pairs, low half first)
+template <int D, int G>
+__device__ __forceinline__ void store_row_scales(uint8_t* __restrict__ st, uint32_t r, const uint32_t (&sb)[D / G]) {
+  if constexpr (D / G == 1) {
+    reinterpret_cast<uint16_t*>(st)[r] = (uint16_t)sb[0];
+  } else if constexpr (D / G == 2) {
+    reinterpret_cast<uint32_t*>(st)[r] = sb[0] | (sb[1] << 16);
+  } else {
+    reinterpret_cast<uint2*>(st)[r] = make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16));
+  }
+}
+
+template <int D, int G>
+__device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, uint32_t r, uint32_t (&sb)[D / G]) {
+  if constexpr (D / G == 1) {
+    sb[0] = reinterpret_cast<const uint16_t*>(st)[r];
+  } else if constexpr (D / G == 2) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(st)[r];
+    sb[0] = w & 0xffffu;
+    sb[1] = w >> 16;
+  } else {
+    const uint2 w = reinterpret_cast<const uint2*>(st)[r];
+    sb[0] = w.x & 0xffffu;
+    sb[1] = w.x >> 16;
+    sb[2] = w.y & 0xffffu;
+    sb[3] = w.y >> 16;
+  }
+}
+
+// Forward step, one 64-row tile per wave.
+template <int D, int G, int ROT>
+__global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
+                                                      int32_t per_wave) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per input row
+  constexpr int CW = D / 32;  // 16-byte chunks per code row
+  __shared__ uint4 buf[64 * CPR];
+  (void)per_wave;
+  const int lane = threadIdx.x;
+  const uint32_t row0 = blockIdx.x * 64u;
+  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+  load_tile_to_lds<CPR>(x + (size_t)row0 * CPR, rows, buf, lane);
+  wait_vmcnt<0>();
+  lds_sync();
+  uint32_t h[D / 2];
+  read_own_row<CPR>(buf, lane, h);
+  RowSigns<D> signs;
+  signs.valid = false;
+  signs.apply(h, sr, row0, rows, lane);
+  uint32_t cw[D / 8], sb[D / G];
+  quantize_row<D, G, ROT>(h, cw, sb);
+  // codes leave through LDS (the input tile is no longer needed)
+  lds_sync();
+  sfor<CW>([&](auto C) {
+    buf[lane * CW + RTQ_CI(C)] =
+        make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]);
+  });
+  lds_sync();
+  uint4* ct = codes + (size_t)row0 * CW;
+  sfor<CW>([&](auto J) {
+    const int c = RTQ_CI(J) * 64 + lane;  // chunk of the tile's code block (row c / CW)
+    if (c / CW < rows) ct[(uint32_t)c] = buf[c];
+  });
+  if (lane < rows) store_row_scales<D, G>(scales + (size_t)row0 * (2 * D / G), (uint32_t)lane, sb);
+}
+
+// Inverse step, `per_wave` consecutive 64-row tiles per wave.
 template <int D, int G, int ROT>
 __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                      int64_t n, uint64_t seed, int64_t rps, int32_t period) {
+                                                      uint32_t n, SeedRule sr, int32_t per_wave) {
   constexpr int CPR = D / 8;
-  constexpr int LROW = CPR + 1;
+  constexpr int CW = D / 32;
+  constexpr int LROW = CPR + 1;  // padded LDS row (uint4)
   __shared__ uint4 lds[64 * LROW];
   const int lane = threadIdx.x;
   const uint32_t kpos = lane % CPR;
-  const int64_t tiles = (n + 63) / 64;
-  SignCache sc;
-  sc.valid = false;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row0 = t * 64;
-    const int rows = (int)(n - row0 < 64 ? n - row0 : 64);
-    const bool uniform = tile_signs(sc, seed, row0, rows, rps, period, kpos);
+  uint32_t t, tiles;
+  wave_tile_range((n + 63u) / 64u, per_wave, t, tiles);
+  RowSigns<D> signs;
+  signs.valid = false;
+  for (; t < tiles; ++t) {
+    const uint32_t row0 = t * 64u;
+    const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+    const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
+    const uint4* ct = codes + (size_t)row0 * CW;
     uint32_t cw[D / 8], sb[D / G];
-    {
-      const int64_t row = row0 + (lane < rows ? lane : 0);
-      sfor<D / 32>([&](auto C) {
-        const uint4 q = codes[row * (D / 32) + RTQ_CI(C)];
-        cw[4 * RTQ_CI(C) + 0] = q.x;
-        cw[4 * RTQ_CI(C) + 1] = q.y;
-        cw[4 * RTQ_CI(C) + 2] = q.z;
-        cw[4 * RTQ_CI(C) + 3] = q.w;
-      });
-      if constexpr (D / G == 1) {
-        sb[0] = reinterpret_cast<const uint16_t*>(scales)[row];
-      } else if constexpr (D / G == 2) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(scales)[row];
-        sb[0] = w & 0xffffu;
-        sb[1] = w >> 16;
-      } else {
-        const uint2 w = reinterpret_cast<const uint2*>(scales)[row];
-        sb[0] = w.x & 0xffffu;
-        sb[1] = w.x >> 16;
-        sb[2] = w.y & 0xffffu;
-        sb[3] = w.y >> 16;
-      }
-    }
+    sfor<CW>([&](auto C) {
+      const uint4 q = ct[r * CW + RTQ_CI(C)];
+      cw[4 * RTQ_CI(C) + 0] = q.x;
+      cw[4 * RTQ_CI(C) + 1] = q.y;
+      cw[4 * RTQ_CI(C) + 2] = q.z;
+      cw[4 * RTQ_CI(C) + 3] = q.w;
+    });
+    load_row_scales<D, G>(scales + (size_t)row0 * (2 * D / G), r, sb);
     float z[D], u[D];
     if constexpr (ROT == kSRFT) {
       dequant_unpack<D, G>(cw, sb, 1.0f, z);
       srft_inv<D, One>(z, u);
     } else {
-      dequant_unpack<D, G>(cw, sb, (float)(1.0 / csqrt((double)D)), u);
+      dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
       fwht_f32<D>(u);
     }
-    // fp16 row into LDS, then coalesced sign flip and store
+    uint32_t h[D / 2];
+    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+    signs.apply(h, sr, row0, rows, lane);
+    // own row into LDS, then coalesced chunks out
     sfor<CPR>([&](auto C) {
       constexpr int c = RTQ_CI(C);
-      lds[lane * LROW + c] = make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
-                                        pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+      lds[lane * LROW + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
     });
     lds_sync();
-    if (uniform) {
-      sfor<CPR>([&](auto J) {
-        const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
-        if (rl < rows) y[(row0 + rl) * CPR + kpos] = xor4(lds[rl * LROW + kpos], sc.m);
-      });
-    } else {
-#pragma unroll 1
-      for (int j = 0; j < CPR; ++j) {
-        const int rl = (j * 64 + lane) / CPR;
-        if (rl < rows)
-          y[(row0 + rl) * CPR + kpos] =
-              xor4(lds[rl * LROW + kpos], chunk_sign_masks(row_seed(seed, row0 + rl, rps, period), kpos));
-      }
-    }
+    uint4* yt = y + (size_t)row0 * CPR;
+    sfor<CPR>([&](auto J) {
+      const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
+      if (rl < rows) yt[(uint32_t)(RTQ_CI(J) * 64 + lane)] = lds[rl * LROW + kpos];
+    });
+    wait_lds_reads();
     lds_sync();
   }
 }
@@ -222,29 +334,25 @@ __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ 
 //     lane applies H_128 and the halves combine as F0 + F1 / F0 - F1.
 // ---------------------------------------------------------------------------
 
-struct Srft256Sub {  // scales of the length-128 sub-DFT bins: X-scaled for d = 256
-  static constexpr double s0 = 1.0 / 16.0;
-  static constexpr double sm = 0.08838834764831844055010554526311;  // sqrt(2/256)
-  static constexpr double si = 0.08838834764831844055010554526311;
-};
 
 template <int G, int ROT>
 __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, int64_t n, uint64_t seed,
-                                                      int64_t rps, int32_t period) {
+                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
+                                                      int32_t per_wave) {
   constexpr int D = 256, CPR = 32, LROW = CPR + 1;
   __shared__ uint4 lds[32 * LROW];
   const int lane = threadIdx.x;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
   const float sigma = p ? -1.0f : 1.0f;
-  const int64_t tiles = (n + 31) / 32;
-  SignCache sc;
-  sc.valid = false;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row0 = t * 32;
-    const int rows = (int)(n - row0 < 32 ? n - row0 : 32);
-    const bool uniform = tile_signs(sc, seed, row0, rows, rps, period, kpos);
+  uint32_t t0, tiles;
+  wave_tile_range((n + 31u) / 32u, per_wave, t0, tiles);
+  ChunkSigns cs;
+  cs.valid = false;
+  for (uint32_t t = t0; t < tiles; ++t) {
+    const uint32_t row0 = t * 32u;
+    const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
+    const bool uniform = cs.prepare(sr, row0, rows, kpos);
     auto put = [&](int rl, uint4 q) {
       if constexpr (ROT == kSRFT) {
         // de-interleave: evens to the first half of the LDS row, odds to the second
@@ -256,18 +364,19 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
       }
     };
     if (uniform) {
+      const uint4* xt = x + (size_t)row0 * CPR;
       uint4 in[16];
       sfor<16>([&](auto J) {
         const int rl = 2 * RTQ_CI(J) + p;
-        in[RTQ_CI(J)] = rl < rows ? x[(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
+        in[RTQ_CI(J)] = rl < rows ? xt[(uint32_t)(rl * CPR) + kpos] : make_uint4(0, 0, 0, 0);
       });
-      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], sc.m)); });
+      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cs.m)); });
     } else {
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
         const int rl = 2 * j + p;
-        const uint4 q = rl < rows ? x[(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
-        put(rl, xor4(q, chunk_sign_masks(row_seed(seed, row0 + rl, rps, period), kpos)));
+        const uint4 q = rl < rows ? x[(size_t)(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
+        put(rl, xor4(q, chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos)));
       }
     }
     lds_sync();
@@ -279,17 +388,19 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
       h[4 * RTQ_CI(C) + 2] = q.z;
       h[4 * RTQ_CI(C) + 3] = q.w;
     });
+    wait_lds_reads();
     lds_sync();
     float L[128];
     float zs;
     if constexpr (ROT == kSRFT) {
       float fr[65], fi[65];
-      rfft_bins<128, Srft256Sub>(h, fr, fi);
+      rdft<128, 1, 0, 64>(h, fr, fi);  // unnormalized; sqrt(2/256) is applied by the quantizer
       const int src_e = v, src_o = v + 32;
       // slot 0: E_0 + sigma * O_0 (real)
       {
         const float e0 = __shfl(fr[0], src_e), o0 = __shfl(fr[0], src_o);
-        L[0] = __builtin_fmaf(sigma, o0, e0);
+        constexpr float r2 = 0.70710678118654752440f;  // real end bins: 1/16 = sqrt(2/256) / sqrt(2)
+        L[0] = __builtin_fmaf(sigma, o0, e0) * r2;
       }
       sfor<63>([&](auto A) {
         constexpr int a = RTQ_CI(A) + 1;
@@ -307,7 +418,7 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
         const float e64 = __shfl(fr[64], src_e), o64 = __shfl(fr[64], src_o);
         L[127] = p ? -o64 : e64;
       }
-      zs = 1.0f;
+      zs = SrftScale<256>::value;
     } else {
       float f[128];
       fwht_from_f16<128>(h, f);
@@ -329,7 +440,7 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
       sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
     }
     if (v < rows) {
-      const int64_t row = row0 + v;
+      const size_t row = (size_t)row0 + v;
       sfor<4>([&](auto C) {
         codes[row * 8 + 4 * p + RTQ_CI(C)] =
             make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]);
@@ -349,23 +460,24 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
 template <int G, int ROT>
 __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                      int64_t n, uint64_t seed, int64_t rps, int32_t period) {
+                                                      uint32_t n, SeedRule sr, int32_t per_wave) {
   constexpr int CPR = 32, LROW = CPR + 1;
   __shared__ uint4 lds[32 * LROW];
   const int lane = threadIdx.x;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
   const float sigma = p ? -1.0f : 1.0f;
-  const int64_t tiles = (n + 31) / 32;
-  SignCache sc;
-  sc.valid = false;
-  for (int64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
-    const int64_t row0 = t * 32;
-    const int rows = (int)(n - row0 < 32 ? n - row0 : 32);
-    const bool uniform = tile_signs(sc, seed, row0, rows, rps, period, kpos);
+  uint32_t t0, tiles;
+  wave_tile_range((n + 31u) / 32u, per_wave, t0, tiles);
+  ChunkSigns cs;
+  cs.valid = false;
+  for (uint32_t t = t0; t < tiles; ++t) {
+    const uint32_t row0 = t * 32u;
+    const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
+    const bool uniform = cs.prepare(sr, row0, rows, kpos);
     uint32_t cw[16], sb[128 / G];
     {
-      const int64_t row = row0 + (v < rows ? v : 0);
+      const size_t row = (size_t)row0 + (v < rows ? v : 0);
       sfor<4>([&](auto C) {
         const uint4 q = codes[row * 8 + 4 * p + RTQ_CI(C)];
         cw[4 * RTQ_CI(C) + 0] = q.x;
@@ -450,19 +562,22 @@ __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ 
         return lds[rl * LROW + kpos];
       }
     };
+    uint4* yt = y + (size_t)row0 * CPR;
     if (uniform) {
       sfor<16>([&](auto J) {
         const int rl = 2 * RTQ_CI(J) + p;
-        if (rl < rows) y[(row0 + rl) * CPR + kpos] = xor4(get(rl), sc.m);
+        if (rl < rows) yt[(uint32_t)(rl * CPR) + kpos] = xor4(get(rl), cs.m);
       });
     } else {
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
         const int rl = 2 * j + p;
         if (rl < rows)
-          y[(row0 + rl) * CPR + kpos] = xor4(get(rl), chunk_sign_masks(row_seed(seed, row0 + rl, rps, period), kpos));
+          yt[(uint32_t)(rl * CPR) + kpos] =
+              xor4(get(rl), chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos));
       }
     }
+    wait_lds_reads();
     lds_sync();
   }
 }
@@ -471,59 +586,24 @@ __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ 
 // Host side: validation, launch configuration, dispatch.
 // ---------------------------------------------------------------------------
 
-struct Args {
-  const void* in0;
-  const void* in1;  // scales for the inverse, unused for the forward
-  void* out0;
-  void* out1;       // scales for the forward, unused for the inverse
-  int64_t n;
-  uint64_t seed;
-  int64_t rps;
-  int32_t period;
-  hipStream_t stream;
-};
-
 using KernelFn = const void*;
 
-int device_cu_count() {
-  static std::mutex mu;
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  std::lock_guard<std::mutex> g(mu);
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = cus;
-  }
-  return cache[dev];
+// Rows per call: row indices are 32-bit on the device.
+constexpr int64_t kMaxRows = 0xffffff00ll;
+
+// Tiles per wave.  The grid is derived from the row count alone (no occupancy
+// query): each one-wave workgroup takes this many consecutive tiles and the
+// hardware dispatcher keeps every CU filled.  The forward takes one tile per
+// wave; the inverse amortizes its cached sign masks over a few tiles.
+int32_t tiles_per_wave(bool fwd, int d, int64_t tiles) {
+  if (fwd) return d == 256 ? 2 : 1;
+  if (tiles < 16384) return 1;
+  return d == 64 ? 2 : 4;
 }
 
-// Resident waves per CU for a kernel: occupancy query, cached per (kernel, device).
-int blocks_per_cu(KernelFn fn) {
-  static std::mutex mu;
-  struct Entry { KernelFn fn; int dev; int blocks; };
-  static Entry cache[256];
-  static int used = 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  {
-    std::lock_guard<std::mutex> g(mu);
-    for (int i = 0; i < used; ++i)
-      if (cache[i].fn == fn && cache[i].dev == dev) return cache[i].blocks;
-  }
-  int blocks = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fn, 64, 0) != hipSuccess || blocks <= 0) blocks = 4;
-  std::lock_guard<std::mutex> g(mu);
-  if (used < 256) cache[used++] = Entry{fn, dev, blocks};
-  return blocks;
-}
-
-rtq_status launch(KernelFn fn, int64_t tiles, void** kargs, hipStream_t stream) {
-  const int cus = device_cu_count();
-  if (cus <= 0) return RTQ_ERR_HIP;
-  const int64_t resident = (int64_t)cus * blocks_per_cu(fn);
-  const int64_t grid = tiles < resident ? tiles : resident;
+rtq_status launch(KernelFn fn, int64_t tiles, int32_t per_wave, void** kargs, hipStream_t stream) {
+  const int64_t grid = (tiles + per_wave - 1) / per_wave;
+  if (grid <= 0 || grid > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
   const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
@@ -567,13 +647,25 @@ rtq_status check_shape(int32_t d, int32_t g) {
   return RTQ_OK;
 }
 
+// The row seed rule as the kernels apply it: rows_per_seed >= n selects one
+// seed for all rows, exactly as rows_per_seed == 0 does.
+SeedRule make_seed_rule(uint64_t seed, int64_t rps, int32_t period, int64_t n) {
+  SeedRule s;
+  s.seed = seed;
+  s.rps = (rps == 0 || rps >= n) ? 0u : (uint32_t)rps;
+  s.period = (uint32_t)period;
+  s.by_rps = make_div32(s.rps ? s.rps : 1u);
+  s.by_period = make_div32(s.period ? s.period : 1u);
+  return s;
+}
+
 rtq_status run(bool fwd, int rot, const void* in0, const void* in1, void* out0, void* out1, int64_t n, int32_t d,
                int32_t g, uint64_t seed, int64_t rps, int32_t period, hipStream_t stream) {
   if (n < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   const rtq_status shape = check_shape(d, g);
   if (shape != RTQ_OK) return shape;
   if (n == 0) return RTQ_OK;
-  if (n > (INT64_MAX / 4) / d) return RTQ_ERR_INVALID_ARG;
+  if (n > kMaxRows) return RTQ_ERR_INVALID_ARG;
   const int64_t fp16_bytes = n * 2 * d, code_bytes = n * (d / 2), scale_bytes = n * 2 * (d / g);
   if (fwd) {
     // in0 = x, out0 = codes, out1 = scales
@@ -593,18 +685,21 @@ rtq_status run(bool fwd, int rot, const void* in0, const void* in1, void* out0, 
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   const int vpt = d == 256 ? 32 : 64;
   const int64_t tiles = (n + vpt - 1) / vpt;
+  int32_t per_wave = tiles_per_wave(fwd, d, tiles);
+  uint32_t n32 = (uint32_t)n;
+  SeedRule sr = make_seed_rule(seed, rps, period, n);
   if (fwd) {
     const void* x = in0;
     void* codes = out0;
     void* scales = out1;
-    void* kargs[] = {&x, &codes, &scales, &n, &seed, &rps, &period};
-    return launch(fn, tiles, kargs, stream);
+    void* kargs[] = {&x, &codes, &scales, &n32, &sr, &per_wave};
+    return launch(fn, tiles, per_wave, kargs, stream);
   }
   const void* codes = in0;
   const void* scales = in1;
   void* y = out0;
-  void* kargs[] = {&codes, &scales, &y, &n, &seed, &rps, &period};
-  return launch(fn, tiles, kargs, stream);
+  void* kargs[] = {&codes, &scales, &y, &n32, &sr, &per_wave};
+  return launch(fn, tiles, per_wave, kargs, stream);
 }
 
 }  // namespace rtq

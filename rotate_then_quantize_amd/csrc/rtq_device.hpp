@@ -55,9 +55,10 @@ constexpr int bitrev(int x, int bits) {
 }
 
 // cos(2*pi*t/n) and sin(2*pi*t/n) in double at compile time: exact integer
-// reduction of the angle to [0, pi/4], then Taylor series.
+// reduction of the angle to [0, pi/4], then Taylor series.  consteval: these
+// must never run on the GPU.
 constexpr double kPi = 3.141592653589793238462643383279502884;
-constexpr double taylor_sin(double x) {
+consteval double taylor_sin(double x) {
   double x2 = x * x, term = x, sum = x;
   for (int k = 1; k < 16; ++k) {
     term *= -x2 / ((2.0 * k) * (2.0 * k + 1.0));
@@ -65,7 +66,7 @@ constexpr double taylor_sin(double x) {
   }
   return sum;
 }
-constexpr double taylor_cos(double x) {
+consteval double taylor_cos(double x) {
   double x2 = x * x, term = 1.0, sum = 1.0;
   for (int k = 1; k < 16; ++k) {
     term *= -x2 / ((2.0 * k - 1.0) * (2.0 * k));
@@ -73,7 +74,7 @@ constexpr double taylor_cos(double x) {
   }
   return sum;
 }
-constexpr double cos2pi(long long t, long long n) {
+consteval double cos2pi(long long t, long long n) {
   t %= n;
   if (t < 0) t += n;
   const long long q = (4 * t) / n;      // quadrant
@@ -95,8 +96,8 @@ constexpr double cos2pi(long long t, long long n) {
     default: return s;
   }
 }
-constexpr double sin2pi(long long t, long long n) { return cos2pi(4 * t - n, 4 * n); }
-constexpr double csqrt(double x) {
+consteval double sin2pi(long long t, long long n) { return cos2pi(4 * t - n, 4 * n); }
+consteval double csqrt(double x) {
   double r = x > 1.0 ? x : 1.0;
   for (int i = 0; i < 200; ++i) r = 0.5 * (r + x / r);
   return r;
@@ -276,6 +277,76 @@ __device__ __forceinline__ void cfft_f32(const float (&xr)[M], const float (&xi)
 }
 
 // ---------------------------------------------------------------------------
+// Real-input DFT by even/odd recursion (decimation in time on real data).
+//
+//   X_k = sum_n u_n exp(-2 pi i k n / N),  k = 0 .. N/2 (unnormalized).
+// With E, O the real DFTs of the even and odd samples (length N/2):
+//   X_k = E_k + w^k O_k  and  X_{N/2-k} = conj(E_k - w^k O_k),  k = 0 .. N/4,
+// where E_0, O_0, E_{N/4}, O_{N/4} are real.  Each bin pair costs six FMAs:
+// X_k from two fused multiply-adds per component, X_{N/2-k} as 2E - X_k.
+// The recursion ends at N = 4, whose first add/sub layer reads the fp16
+// samples directly (v_fma_mix).  Samples u_j live in packed pairs, u_j = half
+// (j % 2) of h[j / 2]; this call transforms u_{OFF}, u_{OFF+S}, ... .
+// ---------------------------------------------------------------------------
+
+template <int N, int S, int OFF, int H>
+__device__ __forceinline__ void rdft(const uint32_t (&h)[H], float (&xr)[N / 2 + 1], float (&xi)[N / 2 + 1]) {
+  if constexpr (N == 4) {
+    constexpr int a = OFF, b = OFF + S, c = OFF + 2 * S, d = OFF + 3 * S;
+    static_assert((a & 1) == (c & 1) && (b & 1) == (d & 1), "leaf pairs share a half");
+    const float t0 = mix_add<a & 1, c & 1>(h[a / 2], h[c / 2]);
+    const float t1 = mix_sub<a & 1, c & 1>(h[a / 2], h[c / 2]);
+    const float t2 = mix_add<b & 1, d & 1>(h[b / 2], h[d / 2]);
+    const float t3 = mix_sub<b & 1, d & 1>(h[b / 2], h[d / 2]);
+    xr[0] = t0 + t2;
+    xr[2] = t0 - t2;
+    xr[1] = t1;
+    xi[1] = -t3;
+    xi[0] = 0.0f;
+    xi[2] = 0.0f;
+  } else {
+    float er[N / 4 + 1], ei[N / 4 + 1], orr[N / 4 + 1], oi[N / 4 + 1];
+    rdft<N / 2, 2 * S, OFF, H>(h, er, ei);
+    rdft<N / 2, 2 * S, OFF + S, H>(h, orr, oi);
+    xr[0] = er[0] + orr[0];
+    xi[0] = 0.0f;
+    xr[N / 2] = er[0] - orr[0];
+    xi[N / 2] = 0.0f;
+    xr[N / 4] = er[N / 4];  // w^{N/4} = -i and E, O are real there
+    xi[N / 4] = -orr[N / 4];
+    sfor<N / 4 - 1>([&](auto K) {
+      constexpr int k = RTQ_CI(K) + 1;
+      constexpr float c = (float)cos2pi(k, N), s = (float)sin2pi(k, N);  // w^k = c - i s
+      xr[k] = __builtin_fmaf(c, orr[k], __builtin_fmaf(s, oi[k], er[k]));
+      xi[k] = __builtin_fmaf(c, oi[k], __builtin_fmaf(-s, orr[k], ei[k]));
+      xr[N / 2 - k] = __builtin_fmaf(2.0f, er[k], -xr[k]);
+      xi[N / 2 - k] = __builtin_fmaf(-2.0f, ei[k], xi[k]);
+    });
+  }
+}
+
+// Packed orthonormal SRFT of length D (one lane), returned divided by
+// sqrt(2/D): the quantizer multiplies it back (zs = SrftScale<D>), so the
+// interior bins cost nothing extra and only the two real end bins (scale
+// 1/sqrt(D) = sqrt(2/D) / sqrt(2)) take a multiply.
+template <int D> struct SrftScale { static constexpr float value = (float)csqrt(2.0 / (double)D); };
+
+template <int D>
+__device__ __forceinline__ void srft_fwd_unscaled(const uint32_t (&h)[D / 2], float (&z)[D]) {
+  constexpr int M = D / 2;
+  float xr[M + 1], xi[M + 1];
+  rdft<D, 1, 0, D / 2>(h, xr, xi);
+  constexpr float r2 = (float)(1.0 / csqrt(2.0));
+  z[0] = xr[0] * r2;
+  sfor<M - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    z[2 * k - 1] = xr[k];
+    z[2 * k] = xi[k];
+  });
+  z[D - 1] = xr[M] * r2;
+}
+
+// ---------------------------------------------------------------------------
 // Real DFT of length D = 2M from one complex DFT of length M.
 // ---------------------------------------------------------------------------
 
@@ -376,6 +447,9 @@ __device__ __forceinline__ void srft_inv(const float (&z)[D], float (&u)[D]) {
 }
 
 struct One { static constexpr double value = 1.0; };
+
+// 1/sqrt(D) as a compile-time fp32 constant (the SRHT normalization).
+template <int D> struct InvSqrt { static constexpr float value = (float)(1.0 / csqrt((double)D)); };
 struct Sqrt2 { static constexpr double value = 1.4142135623730950488016887242097; };
 
 // ---------------------------------------------------------------------------

@@ -71,8 +71,10 @@ def test_rejects_bad_arguments_without_launching(name):
     assert call(name, A + 8, B, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
     assert call(name, A, B + 4, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
     assert call(name, A, B, C + 2, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
-    # size overflow
+    # size overflow and the 32-bit row-index limit (0xFFFFFF00 rows per call)
     assert call(name, A, B, C, 1 << 62, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, C, 0xFFFFFF01, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
+    assert call(name, A, B, C, 1 << 32, 256, 32) == rtq.RTQ_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name", FWD + INV)
