@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -37,11 +38,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """Source with comments and blank runs removed: what the compiler sees."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code (comments ignored)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -65,6 +74,130 @@ def read_traffic(workload_name: str, rot: str, kernel: str):
         return None
 
 
+KERNEL_ROLES = (("fwd_", "quant_fwd"), ("inv_", "dequant_inv"))
+
+
+def short_kernel_name(name: str) -> str:
+    """'void rtq::fwd_lane_kernel<64, 32, 0>(...)' -> 'rtq::fwd_lane_kernel<64, 32, 0>'."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    name = name.replace("(anonymous namespace)", "{anon}")
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def kernel_role(name: str):
+    short = short_kernel_name(name)
+    if not short.startswith("rtq::"):
+        return None
+    for prefix, role in KERNEL_ROLES:
+        if short[5:].startswith(prefix):
+            return role
+    return None
+
+
+def find_csv(directory: str, suffix: str) -> str:
+    hits = []
+    for root, _, files in os.walk(directory):
+        hits += [os.path.join(root, f) for f in files if f.endswith(suffix)]
+    if len(hits) != 1:
+        raise SystemExit(f"expected one *{suffix} under {directory}, found {hits}")
+    return hits[0]
+
+
+def summarize_trace(trace_dir: str, w, rot: str, command: str) -> None:
+    """Write the rocprofv3 --kernel-trace --stats summary of a bench run."""
+    import csv
+    rows = list(csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel trace, workload {w.name} (d={w.d}, group={w.group}, {rot})",
+             f"# command: {command}",
+             f"# kernel_source_sha: {kernel_source_hash()}",
+             "# kernel | calls | average us | min us | max us | share of GPU time",
+             ]
+    for r in rows:
+        lines.append(f"{short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}%")
+    for r in rows:
+        role = kernel_role(r["Name"])
+        if role:
+            bytes_launch = (w.new_rows if (w.new_tokens and role == "quant_fwd") else w.n_rows) * w.bytes_per_vector()
+            lines.append(f"{role}_average_us: {float(r['AverageNs']) / 1e3:.3f}")
+            lines.append(f"{role}_algorithmic_GBps: {bytes_launch / float(r['AverageNs']):.1f}")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{rot}_{w.name}.txt")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"wrote {path}")
+
+
+def pmc_per_dispatch(directory: str, counter: str):
+    """{kernel short name: mean counter value per dispatch} from a rocprofv3 --pmc run."""
+    import csv
+    acc = {}
+    for r in csv.DictReader(open(find_csv(directory, "counter_collection.csv"))):
+        if r["Counter_Name"] != counter:
+            continue
+        acc.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib, w, rot, commands) -> None:
+    """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a plain device copy of
+    a known size."""
+    known_kib = cal_mib * 1024.0
+    cal = {}
+    for counter, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
+        vals, _ = pmc_per_dispatch(d, counter)
+        copies = {k: v for k, v in vals.items() if "copy" in k.lower()}
+        if not copies:
+            raise SystemExit(f"no copy kernel in {d}: {sorted(vals)}")
+        name, kib = max(copies.items(), key=lambda kv: kv[1])
+        cal[counter] = (known_kib / kib, name, kib)
+    fetch, nf = pmc_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write, nw = pmc_per_dispatch(write_dir, "WRITE_SIZE")
+    for kname in sorted(set(fetch) & set(write)):
+        role = kernel_role(kname)
+        if not role:
+            continue
+        rows = w.new_rows if (w.new_tokens and role == "quant_fwd") else w.n_rows
+        algo = rows * w.bytes_per_vector()
+        fb = fetch[kname] * cal["FETCH_SIZE"][0] * 1024.0
+        wb = write[kname] * cal["WRITE_SIZE"][0] * 1024.0
+        lines = [f"# HBM traffic of {kname}, workload {w.name} (d={w.d}, group={w.group}, {rot})"]
+        lines += [f"# command ({c}): {cmd}" for c, cmd in commands]
+        lines += [
+            f"kernel: {kname}",
+            f"kernel_source_sha: {kernel_source_hash()}",
+            f"dispatches_fetch: {nf[kname]}",
+            f"dispatches_write: {nw[kname]}",
+            f"fetch_kib_per_dispatch_raw: {fetch[kname]:.1f}",
+            f"write_kib_per_dispatch_raw: {write[kname]:.1f}",
+            f"copy_calibration_kernel: {cal['FETCH_SIZE'][1]}",
+            f"copy_calibration_bytes_each_way: {cal_mib} MiB",
+            f"copy_fetch_kib_raw: {cal['FETCH_SIZE'][2]:.1f}",
+            f"copy_write_kib_raw: {cal['WRITE_SIZE'][2]:.1f}",
+            f"fetch_scale: {cal['FETCH_SIZE'][0]:.4f}",
+            f"write_scale: {cal['WRITE_SIZE'][0]:.4f}",
+            f"hbm_read_bytes_per_launch: {fb:.0f}",
+            f"hbm_write_bytes_per_launch: {wb:.0f}",
+            f"hbm_bytes_per_launch: {fb + wb:.0f}",
+            f"algorithmic_bytes_per_launch: {algo}",
+            f"traffic_over_algorithmic: {(fb + wb) / algo:.4f}",
+        ]
+        path = os.path.join(ROOT, "profiles", f"traffic_{role}_{rot}_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"wrote {path}")
+
+
 def cpu_baseline(w, x_gpu, rot, seconds):
     """The oracle, as it is, on consecutive 65536-row chunks of the same
     workload until ``seconds`` of CPU time are spent (input copy excluded)."""
@@ -76,8 +209,8 @@ def cpu_baseline(w, x_gpu, rot, seconds):
     except Exception:
         threads = 1
     chunk = 65536
-    done, spent, r0 = 0, 0.0, 0
-    while spent < seconds and r0 < w.n_rows:
+    done, spent, r0, passes = 0, 0.0, 0, 0
+    while spent < seconds:
         r1 = min(w.n_rows, r0 + chunk)
         xs = x_gpu[r0:r1].cpu().numpy()
         t0 = time.perf_counter()
@@ -86,13 +219,16 @@ def cpu_baseline(w, x_gpu, rot, seconds):
         spent += time.perf_counter() - t0
         done += r1 - r0
         r0 = r1
+        if r0 >= w.n_rows:
+            r0, passes = 0, passes + 1
+    where = (f"{passes} full pass(es) plus {r0} rows" if passes else f"the first {done}") + f" of the {w.n_rows}-row workload"
     return {
         "value": done / spent,
         "unit": "vectors/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {done} of {w.n_rows} rows of the same workload, forward + inverse, "
-                  f"fp64 numpy oracle in {chunk}-row chunks ({spent:.1f} s)",
+        "sample": f"{done} rows ({where}), forward + inverse each, fp64 numpy oracle in {chunk}-row chunks, "
+                  f"{spent:.1f} s of oracle time (device-to-host copies excluded)",
     }
 
 
@@ -108,7 +244,24 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/kernel_trace_*.txt from a rocprofv3 --kernel-trace --stats CSV directory")
+    ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write profiles/traffic_*.txt from four rocprofv3 --pmc CSV directories")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
+
+    if args.summarize_trace or args.summarize_traffic:
+        from rotate_then_quantize_amd import workloads as W
+        w = W.WORKLOADS[args.workload]
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command))
+        if args.summarize_traffic:
+            names = ("FETCH_SIZE", "WRITE_SIZE", "copy FETCH_SIZE", "copy WRITE_SIZE")
+            cmds = list(zip(names, args.command[-4:])) if len(args.command) >= 4 else []
+            summarize_traffic(*args.summarize_traffic, args.calibrate_copy or 256, w, args.rot, cmds)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -176,8 +329,17 @@ def main():
         sets.append((fa, ia, (x, codes, scales, y)))
     torch.cuda.synchronize()
 
+    # Every replica's codes exist before the first inverse reads them.
+    for fa, _, _ in sets:
+        st = fwd_fn(*fa)
+        assert st == 0, lib.rtq_status_string(st)
+    torch.cuda.synchronize()
+
     def step(i, ev=None):
-        fa, ia, _ = sets[i % replicas]
+        # The inverse reads the replica the forward wrote two steps earlier, so
+        # its codes come from HBM rather than from the 256 MB last-level cache.
+        fa = sets[i % replicas][0]
+        ia = sets[(i + 1) % replicas][1]
         if ev is not None:
             ev[0].record(stream)
         s1 = fwd_fn(*fa)

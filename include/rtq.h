@@ -2,9 +2,9 @@
  * rtq.h -- C ABI of the rotate-then-quantize int4 KV-cache library for
  * AMD MI355X (gfx950).
  *
- * The method: every K/V vector of the cache is rotated, quantized to int4,
- * and dequantized and rotated back when attention reads it ("Quantization
- * Speed Is Often a Kernel Problem", section "First, the 17%").  The fused
+ * The method: each K/V vector is rotated and stored as int4 codes with fp16
+ * scales; reading the cache reverses both steps ("Quantization Speed Is
+ * Often a Kernel Problem", section "First, the 17%").  The fused
  * form runs rotate + quantize as one kernel and dequantize + inverse-rotate
  * as another (same page, section "Fusing four steps into two kernels is not
  * enough").  Each entry point below is one such fused kernel launch.
@@ -30,8 +30,9 @@
  *    where rows_per_seed == 0 means one seed for every row and
  *    seed_period == 0 means no modulo.  Sign i of seed S is -1 iff bit 63 of
  *    the (i+1)-th output of SplitMix64 (Steele, Lea & Flood 2014) started at
- *    state S is set.  The pages only ask for a fixed random +-1 pattern
- *    ("Quantization Speed Is Often a Kernel Problem", "First, the 17%").
+ *    state S is set.  The method page fixes only that the signs are a
+ *    constant pseudo-random +-1 vector ("Quantization Speed Is Often a
+ *    Kernel Problem", "First, the 17%").
  *  Pointers: device pointers (or any pointers the GPU can address), each
  *    16-byte aligned.  The caller owns every buffer; the library allocates
  *    nothing, keeps no state between calls, and is thread-safe.  Outputs must
@@ -66,9 +67,9 @@ typedef enum rtq_status {
 /*
  * srft_quant_fwd -- fused forward step with the SRFT rotation.
  *
- * For each row r: u = D(seed'(r)) * x[r] (sign flip; "Quantization Speed Is
- * Often a Kernel Problem", "First, the 17%": a fixed random +-1 pattern, then
- * an FFT); z = R u, R = orthonormal real DFT (rfft) packed to d reals as
+ * For each row r: u = D(seed'(r)) * x[r] (sign flip, which the SRFT applies
+ * before its FFT: "Quantization Speed Is Often a Kernel Problem", "First, the
+ * 17%"); z = R u, R = orthonormal real DFT (rfft) packed to d reals as
  *   z[0] = X_0, z[2k-1] = sqrt2*Re X_k, z[2k] = sqrt2*Im X_k (k=1..d/2-1),
  *   z[d-1] = X_{d/2},  X_k = d^-1/2 * sum_n u_n exp(-2 pi i k n / d);
  * then per group j: s_j = fp16_rne(max_i |z_i| / 8) (saturated at 65504),
@@ -92,8 +93,8 @@ rtq_status srft_quant_fwd(const void* x_f16, void* codes_u8, void* scales_f16,
  *
  * For each row r: z_hat_i = s_j * q_i (sign-extended nibbles); u = R^T z_hat
  * (the orthonormal irfft of the unpacked bins); y[r] = fp16_rne(D(seed'(r)) * u)
- * ("Quantization Speed Is Often a Kernel Problem", "First, the 17%":
- * dequantized and rotated back when attention reads it).
+ * ("Quantization Speed Is Often a Kernel Problem", "First, the 17%": the
+ * inverse runs when the cache is read).
  *
  *   codes_u8    in : [n][d/2] uint8
  *   scales_f16  in : [n][d/group] fp16

@@ -17,7 +17,7 @@ Sources (cited by page title and section):
 What the pages fix and what is a reading (each reading is listed in the design doc):
   * Each K/V vector is rotated, quantized to int4, and later dequantized and
     rotated back [P1, "First, the 17%"].
-  * SRFT = multiply by a fixed random +-1 pattern, then an FFT (rfft on the
+  * SRFT = flip signs with a constant pseudo-random +-1 vector, then take an FFT (rfft on the
     way in, irfft on the way out) [P1, "First, the 17%"].  Reading: the
     orthonormal real DFT, with the d/2+1 complex bins packed into d reals as
     [X0, sqrt2*Re X1, sqrt2*Im X1, ..., sqrt2*Im X_{d/2-1}, X_{d/2}].
@@ -32,9 +32,9 @@ What the pages fix and what is a reading (each reading is listed in the design doc):
     one absmax scale per group of consecutive values [P1, "Fusing four steps
     into two kernels is not enough"].
   * Two int4 codes per byte, w0 in the low nibble, w1 in the high nibble,
-    mapped from 0..15 to signed [P5, "Kernels: Marlin, CUTLASS, and Why INT4
+    read back as signed values [P5, "Kernels: Marlin, CUTLASS, and Why INT4
     Packing Needs Special Code"].  Reading: two's complement nibbles.
-  * The +-1 pattern: the pages only say "fixed random".  Reading: sign i of
+  * The +-1 vector: the pages do not say how it is drawn.  Reading: sign i of
     seed S is -1 iff bit 63 of the (i+1)-th output of the published SplitMix64
     generator (Steele, Lea, Flood 2014) started at state S is set; the seed of
     row r is S + ((r div rows_per_seed) mod seed_period), with 0 meaning
@@ -54,7 +54,7 @@ INT4_MAX = 7
 FP16_MAX = 65504.0
 
 # ---------------------------------------------------------------------------
-# Sign pattern (the "fixed random +-1 pattern" of [P1, "First, the 17%"])
+# Sign vector (the SRFT's +-1 sign flip, [P1, "First, the 17%"])
 # ---------------------------------------------------------------------------
 
 

@@ -7,9 +7,10 @@
 //
 // Method sources (page title, section):
 //   "Quantization Speed Is Often a Kernel Problem", "First, the 17%":
-//     rotate each K/V vector, quantize to int4, dequantize and rotate back;
-//     SRFT = fixed random +-1 pattern then an FFT (rfft / irfft); SRHT =
-//     sign-randomized Hadamard transform as the control.
+//     K/V vectors are rotated before int4 quantization and un-rotated after
+//     dequantization; SRFT flips signs with a seeded +-1 vector and then takes
+//     a real FFT (inverse: real inverse FFT); the Hadamard variant (SRHT) is
+//     the control.
 //   same page, "Fusing four steps into two kernels is not enough": forward =
 //     rotate + quantize in one kernel, inverse = dequantize + inverse-rotate
 //     in one kernel; one absmax scale per group of 32 values.
