@@ -3,9 +3,9 @@
 //
 // The method ("Quantization Speed Is Often a Kernel Problem", sections
 // "First, the 17%" and "Fusing four steps into two kernels is not enough"):
-// each K/V vector is multiplied by a fixed +-1 pattern and rotated (SRFT = real
-// FFT, SRHT = Hadamard control), quantized to int4 with one absmax fp16 scale
-// per group; the inverse dequantizes, rotates back and flips the signs.  One
+// each K/V vector gets its signs flipped by a seeded +-1 vector and is rotated
+// (SRFT = real FFT, SRHT = Hadamard control), then quantized to int4 with one
+// absmax fp16 scale per group; the inverse dequantizes, rotates back and flips the signs.  One
 // launch does the forward step for all rows, one launch the inverse.
 //
 // Mapping to CDNA4:
@@ -17,7 +17,8 @@
 //     transposed to / from the owning lane through a wave-private LDS tile:
 //     forward tiles arrive by direct-to-LDS loads (global_load_lds_dwordx4)
 //     with an xor swizzle that keeps the per-row LDS reads conflict free, and
-//     the packed codes leave through LDS as full 1 KB stores.
+//     the packed codes leave through LDS as full 1 KB stores.  All global
+//     accesses are non-temporal: each byte is used once.
 //   * The +-1 signs of a tile come from one SplitMix64 evaluation per lane, a
 //     ballot, and scalar bit extraction, then one v_xor per packed pair.
 //   * The transforms, the absmax reduction, rounding, clamping and nibble
@@ -42,6 +43,36 @@ enum Rot : int { kSRFT = 0, kSRHT = 1 };
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
+// Streaming global accesses.  Every input and output byte is touched exactly
+// once, so loads and stores carry the non-temporal ("nt") cache policy: the
+// stream does not displace other lines, and the outputs do not linger dirty
+// in L2 / last-level cache for the next launch to write back.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kCachePolicyNT = 2;  // "nt" bit of a global_load_lds cache-policy operand
+
+__device__ __forceinline__ void stream_store(uint4* p, uint4 v) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void stream_store(uint2* p, uint2 v) {
+  const u32x2_t w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(p));
+}
+__device__ __forceinline__ void stream_store(uint32_t* p, uint32_t v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void stream_store(uint16_t* p, uint16_t v) { __builtin_nontemporal_store(v, p); }
+
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  const u32x4_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ uint2 stream_load(const uint2* p) {
+  const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+  return make_uint2(w.x, w.y);
+}
+__device__ __forceinline__ uint32_t stream_load(const uint32_t* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ uint16_t stream_load(const uint16_t* p) { return __builtin_nontemporal_load(p); }
+
 // Every workgroup is a single wave, and a wave's LDS instructions execute in
 // order, so exchanging data between its lanes through LDS only needs the
 // compiler kept from reordering the accesses.  (__syncthreads would also wait
@@ -65,58 +96,56 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Sign masks
 // ---------------------------------------------------------------------------
 
-// XOR masks for the D/2 packed fp16 pairs of one row (pair m = elements 2m,
-// 2m+1) as wave-uniform values: lane l computes the sign bits of elements
-// l, l + 64, ... and a ballot gathers them.
+// XOR mask of packed pair m (elements 2m, 2m+1) from a word of 64 sign bits
+// (bit e = element e): bit 2m goes to bit 15 (low fp16), bit 2m+1 to bit 31.
+__device__ __forceinline__ uint32_t pair_mask(uint64_t bits, int m) {
+  const uint32_t v = (uint32_t)(bits >> (2 * m)) & 3u;
+  return (v * 0x40008000u) & 0x80008000u;
+}
+
+// h ^ m for a wave-uniform mask m kept in an SGPR: one VALU instruction.
+__device__ __forceinline__ uint32_t xor_uniform(uint32_t h, uint32_t m) {
+  uint32_t r;
+  asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(m), "v"(h));
+  return r;
+}
+
+// Sign masks of one seed for the D/2 packed pairs of a row, wave-uniform:
+// lane l evaluates the sign bits of elements l, l + 64, ... and a ballot
+// gathers them into scalar registers.
 template <int D>
-__device__ __forceinline__ void uniform_sign_masks(uint64_t s, int lane, uint32_t (&sm)[D / 2]) {
-  sfor<D / 64>([&](auto Q) {
-    constexpr int q = RTQ_CI(Q);
-    const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
-    sfor<32>([&](auto M) {
-      constexpr int m = RTQ_CI(M);
-      const uint32_t b0 = (uint32_t)(bits >> (2 * m)) & 1u, b1 = (uint32_t)(bits >> (2 * m + 1)) & 1u;
-      sm[32 * q + m] = (b0 << 15) | (b1 << 31);
+struct UniformSigns {
+  uint32_t m[D / 2];
+
+  __device__ __forceinline__ void compute(uint64_t s, int lane) {
+    sfor<D / 64>([&](auto Q) {
+      constexpr int q = RTQ_CI(Q);
+      const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
+      sfor<32>([&](auto M) { m[32 * q + RTQ_CI(M)] = pair_mask(bits, RTQ_CI(M)); });
     });
+  }
+
+  __device__ __forceinline__ void apply(uint32_t (&h)[D / 2]) const {
+    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = xor_uniform(h[RTQ_CI(M)], m[RTQ_CI(M)]); });
+  }
+};
+
+// Signs of a lane's own seed s, evaluated element by element; used only for
+// the few tiles whose rows straddle a seed boundary.
+template <int D>
+__device__ __forceinline__ void apply_lane_signs(uint32_t (&h)[D / 2], uint64_t s) {
+  sfor<D / 64>([&](auto Q) {
+    uint64_t bits = 0;
+#pragma unroll 1
+    for (uint32_t e = 0; e < 64; ++e) bits |= (uint64_t)sign_bit(s, 64u * RTQ_CI(Q) + e) << e;
+    sfor<32>([&](auto M) { h[32 * RTQ_CI(Q) + RTQ_CI(M)] ^= pair_mask(bits, RTQ_CI(M)); });
   });
 }
 
-// Signs of each lane's own row (the lane holds row row0 + lane).  When every
-// row of the tile has the same seed the masks are wave-uniform (cached across
-// tiles); a tile that straddles a seed boundary builds per-lane masks in a
-// plain loop.
-template <int D>
-struct RowSigns {
-  uint32_t sm[D / 2];
-  uint64_t seed_cached;
-  bool valid;
-
-  __device__ __forceinline__ void apply(uint32_t (&h)[D / 2], const SeedRule& sr, uint32_t row0, int rows,
-                                        int lane) {
-    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-    if (b0 == b1) {
-      const uint64_t s = seed_of_block(b0, sr);
-      if (!valid || seed_cached != s) {
-        uniform_sign_masks<D>(s, lane, sm);
-        seed_cached = s;
-        valid = true;
-      }
-      sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] ^= sm[RTQ_CI(M)]; });
-      return;
-    }
-    const uint64_t mine = seed_of_block(seed_block(row0 + (uint32_t)(lane < rows ? lane : rows - 1), sr), sr);
-    sfor<D / 64>([&](auto Q) {
-      uint64_t bits = 0;
-#pragma unroll 1
-      for (uint32_t e = 0; e < 64; ++e) bits |= (uint64_t)sign_bit(mine, 64u * RTQ_CI(Q) + e) << e;
-      sfor<32>([&](auto M) {
-        constexpr int m = RTQ_CI(M);
-        const uint32_t b0 = (uint32_t)(bits >> (2 * m)) & 1u, b1 = (uint32_t)(bits >> (2 * m + 1)) & 1u;
-        h[32 * RTQ_CI(Q) + m] ^= (b0 << 15) | (b1 << 31);
-      });
-    });
-  }
-};
+// Seed of the row a lane owns in a tile (rows past the end reuse the last).
+__device__ __forceinline__ uint64_t lane_seed(const SeedRule& sr, uint32_t row0, int rows, int lane) {
+  return seed_of_block(seed_block(row0 + (uint32_t)(lane < rows ? lane : rows - 1), sr), sr);
+}
 
 // Signs of a fixed 16-byte chunk position (elements 8k .. 8k+7) of whatever
 // row a lane stages; cached per seed.  Used by the two-lane d = 256 kernels.
@@ -162,8 +191,8 @@ __device__ __forceinline__ void load_tile_to_lds(const uint4* __restrict__ xt, i
     const int k = (slot % CPR) ^ (r & 7);
     const int rr = r < rmax ? r : rmax - 1;
     const uint32_t off = (uint32_t)(rr * CPR + k) * 16u;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)xt + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16,
-                                     0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)xt + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16, 0,
+                                     kCachePolicyNT);
   };
   if (rows == 64) {
     sfor<CPR>([&](auto J) { issue(J, 64); });
@@ -203,24 +232,24 @@ __device__ __forceinline__ void quantize_row(const uint32_t (&h)[D / 2], uint32_
 template <int D, int G>
 __device__ __forceinline__ void store_row_scales(uint8_t* __restrict__ st, uint32_t r, const uint32_t (&sb)[D / G]) {
   if constexpr (D / G == 1) {
-    reinterpret_cast<uint16_t*>(st)[r] = (uint16_t)sb[0];
+    stream_store(reinterpret_cast<uint16_t*>(st) + r, (uint16_t)sb[0]);
   } else if constexpr (D / G == 2) {
-    reinterpret_cast<uint32_t*>(st)[r] = sb[0] | (sb[1] << 16);
+    stream_store(reinterpret_cast<uint32_t*>(st) + r, sb[0] | (sb[1] << 16));
   } else {
-    reinterpret_cast<uint2*>(st)[r] = make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16));
+    stream_store(reinterpret_cast<uint2*>(st) + r, make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)));
   }
 }
 
 template <int D, int G>
 __device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, uint32_t r, uint32_t (&sb)[D / G]) {
   if constexpr (D / G == 1) {
-    sb[0] = reinterpret_cast<const uint16_t*>(st)[r];
+    sb[0] = stream_load(reinterpret_cast<const uint16_t*>(st) + r);
   } else if constexpr (D / G == 2) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(st)[r];
+    const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(st) + r);
     sb[0] = w & 0xffffu;
     sb[1] = w >> 16;
   } else {
-    const uint2 w = reinterpret_cast<const uint2*>(st)[r];
+    const uint2 w = stream_load(reinterpret_cast<const uint2*>(st) + r);
     sb[0] = w.x & 0xffffu;
     sb[1] = w.x >> 16;
     sb[2] = w.y & 0xffffu;
@@ -228,26 +257,24 @@ __device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, 
   }
 }
 
-// Forward step, one 64-row tile per wave.
-template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
-                                                      int32_t per_wave) {
+// One forward tile: rows row0 .. row0 + rows - 1, lane l owning row row0 + l.
+// kUniform: every row has seed s (masks are scalar); otherwise s is the
+// lane's own seed.
+template <int D, int G, int ROT, bool kUniform>
+__device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint4* __restrict__ ct,
+                                              uint8_t* __restrict__ st, int rows, uint64_t s, uint4* buf,
+                                              int lane) {
   constexpr int CPR = D / 8;  // 16-byte chunks per input row
   constexpr int CW = D / 32;  // 16-byte chunks per code row
-  __shared__ uint4 buf[64 * CPR];
-  (void)per_wave;
-  const int lane = threadIdx.x;
-  const uint32_t row0 = blockIdx.x * 64u;
-  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
-  load_tile_to_lds<CPR>(x + (size_t)row0 * CPR, rows, buf, lane);
+  load_tile_to_lds<CPR>(xt, rows, buf, lane);
+  UniformSigns<D> sg;
+  if constexpr (kUniform) sg.compute(s, lane);  // overlaps the loads
   wait_vmcnt<0>();
   lds_sync();
   uint32_t h[D / 2];
   read_own_row<CPR>(buf, lane, h);
-  RowSigns<D> signs;
-  signs.valid = false;
-  signs.apply(h, sr, row0, rows, lane);
+  if constexpr (kUniform) sg.apply(h);
+  else apply_lane_signs<D>(h, s);
   uint32_t cw[D / 8], sb[D / G];
   quantize_row<D, G, ROT>(h, cw, sb);
   // codes leave through LDS (the input tile is no longer needed)
@@ -257,67 +284,111 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
         make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]);
   });
   lds_sync();
-  uint4* ct = codes + (size_t)row0 * CW;
   sfor<CW>([&](auto J) {
     const int c = RTQ_CI(J) * 64 + lane;  // chunk of the tile's code block (row c / CW)
-    if (c / CW < rows) ct[(uint32_t)c] = buf[c];
+    if (c / CW < rows) stream_store(ct + (uint32_t)c, buf[c]);
   });
-  if (lane < rows) store_row_scales<D, G>(scales + (size_t)row0 * (2 * D / G), (uint32_t)lane, sb);
+  if (lane < rows) store_row_scales<D, G>(st, (uint32_t)lane, sb);
 }
 
-// Inverse step, `per_wave` consecutive 64-row tiles per wave.
+// Forward step, one 64-row tile per wave.
+template <int D, int G, int ROT>
+__global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
+                                                      int32_t per_wave) {
+  constexpr int CPR = D / 8;
+  constexpr int CW = D / 32;
+  __shared__ uint4 buf[64 * CPR];
+  (void)per_wave;
+  const int lane = threadIdx.x;
+  const uint32_t row0 = blockIdx.x * 64u;
+  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+  const uint4* xt = x + (size_t)row0 * CPR;
+  uint4* ct = codes + (size_t)row0 * CW;
+  uint8_t* st = scales + (size_t)row0 * (2 * D / G);
+  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+  if (b0 == b1) fwd_lane_tile<D, G, ROT, true>(xt, ct, st, rows, seed_of_block(b0, sr), buf, lane);
+  else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, lane_seed(sr, row0, rows, lane), buf, lane);
+}
+
+// One inverse tile (layout as fwd_lane_tile); `lds` is a padded row tile.
+template <int D, int G, int ROT, bool kUniform>
+__device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, const uint8_t* __restrict__ st,
+                                              uint4* __restrict__ yt, int rows, const UniformSigns<D>& sg,
+                                              uint64_t s, uint4* lds, int lane) {
+  constexpr int CPR = D / 8;
+  constexpr int CW = D / 32;
+  constexpr int LROW = CPR + 1;
+  const uint32_t kpos = lane % CPR;
+  const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
+  uint32_t cw[D / 8], sb[D / G];
+  sfor<CW>([&](auto C) {
+    const uint4 q = stream_load(ct + (r * CW + RTQ_CI(C)));
+    cw[4 * RTQ_CI(C) + 0] = q.x;
+    cw[4 * RTQ_CI(C) + 1] = q.y;
+    cw[4 * RTQ_CI(C) + 2] = q.z;
+    cw[4 * RTQ_CI(C) + 3] = q.w;
+  });
+  load_row_scales<D, G>(st, r, sb);
+  float z[D], u[D];
+  if constexpr (ROT == kSRFT) {
+    dequant_unpack<D, G>(cw, sb, 1.0f, z);
+    srft_inv<D, One>(z, u);
+  } else {
+    dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
+    fwht_f32<D>(u);
+  }
+  uint32_t h[D / 2];
+  sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+  if constexpr (kUniform) sg.apply(h);
+  else apply_lane_signs<D>(h, s);
+  // own row into LDS, then coalesced chunks out
+  sfor<CPR>([&](auto C) {
+    constexpr int c = RTQ_CI(C);
+    lds[lane * LROW + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
+  });
+  lds_sync();
+  sfor<CPR>([&](auto J) {
+    const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
+    if (rl < rows) stream_store(yt + (uint32_t)(RTQ_CI(J) * 64 + lane), lds[rl * LROW + kpos]);
+  });
+  wait_lds_reads();
+  lds_sync();
+}
+
+// Inverse step, `per_wave` consecutive 64-row tiles per wave; the scalar sign
+// masks are kept while the seed does not change.
 template <int D, int G, int ROT>
 __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
                                                       uint32_t n, SeedRule sr, int32_t per_wave) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
-  constexpr int LROW = CPR + 1;  // padded LDS row (uint4)
-  __shared__ uint4 lds[64 * LROW];
+  __shared__ uint4 lds[64 * (CPR + 1)];
   const int lane = threadIdx.x;
-  const uint32_t kpos = lane % CPR;
   uint32_t t, tiles;
   wave_tile_range((n + 63u) / 64u, per_wave, t, tiles);
-  RowSigns<D> signs;
-  signs.valid = false;
+  UniformSigns<D> sg;
+  uint64_t cached = 0;
+  bool have = false;
   for (; t < tiles; ++t) {
     const uint32_t row0 = t * 64u;
     const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
-    const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
     const uint4* ct = codes + (size_t)row0 * CW;
-    uint32_t cw[D / 8], sb[D / G];
-    sfor<CW>([&](auto C) {
-      const uint4 q = ct[r * CW + RTQ_CI(C)];
-      cw[4 * RTQ_CI(C) + 0] = q.x;
-      cw[4 * RTQ_CI(C) + 1] = q.y;
-      cw[4 * RTQ_CI(C) + 2] = q.z;
-      cw[4 * RTQ_CI(C) + 3] = q.w;
-    });
-    load_row_scales<D, G>(scales + (size_t)row0 * (2 * D / G), r, sb);
-    float z[D], u[D];
-    if constexpr (ROT == kSRFT) {
-      dequant_unpack<D, G>(cw, sb, 1.0f, z);
-      srft_inv<D, One>(z, u);
-    } else {
-      dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
-      fwht_f32<D>(u);
-    }
-    uint32_t h[D / 2];
-    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
-    signs.apply(h, sr, row0, rows, lane);
-    // own row into LDS, then coalesced chunks out
-    sfor<CPR>([&](auto C) {
-      constexpr int c = RTQ_CI(C);
-      lds[lane * LROW + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
-    });
-    lds_sync();
+    const uint8_t* st = scales + (size_t)row0 * (2 * D / G);
     uint4* yt = y + (size_t)row0 * CPR;
-    sfor<CPR>([&](auto J) {
-      const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
-      if (rl < rows) yt[(uint32_t)(RTQ_CI(J) * 64 + lane)] = lds[rl * LROW + kpos];
-    });
-    wait_lds_reads();
-    lds_sync();
+    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+    if (b0 == b1) {
+      const uint64_t s = seed_of_block(b0, sr);
+      if (!have || s != cached) {
+        sg.compute(s, lane);
+        cached = s;
+        have = true;
+      }
+      inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, sg, 0, lds, lane);
+    } else {
+      inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, sg, lane_seed(sr, row0, rows, lane), lds, lane);
+    }
   }
 }
 
@@ -368,14 +439,14 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
       uint4 in[16];
       sfor<16>([&](auto J) {
         const int rl = 2 * RTQ_CI(J) + p;
-        in[RTQ_CI(J)] = rl < rows ? xt[(uint32_t)(rl * CPR) + kpos] : make_uint4(0, 0, 0, 0);
+        in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
       });
       sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cs.m)); });
     } else {
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
         const int rl = 2 * j + p;
-        const uint4 q = rl < rows ? x[(size_t)(row0 + rl) * CPR + kpos] : make_uint4(0, 0, 0, 0);
+        const uint4 q = rl < rows ? stream_load(x + ((size_t)(row0 + rl) * CPR + kpos)) : make_uint4(0, 0, 0, 0);
         put(rl, xor4(q, chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos)));
       }
     }
@@ -442,16 +513,16 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
     if (v < rows) {
       const size_t row = (size_t)row0 + v;
       sfor<4>([&](auto C) {
-        codes[row * 8 + 4 * p + RTQ_CI(C)] =
-            make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]);
+        stream_store(codes + (row * 8 + 4 * p + RTQ_CI(C)),
+                     make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]));
       });
       // this lane's half of the row's scales: 128/G values
       if constexpr (128 / G == 1) {
-        reinterpret_cast<uint16_t*>(scales)[row * 2 + p] = (uint16_t)sb[0];
+        stream_store(reinterpret_cast<uint16_t*>(scales) + (row * 2 + p), (uint16_t)sb[0]);
       } else if constexpr (128 / G == 2) {
-        reinterpret_cast<uint32_t*>(scales)[row * 2 + p] = sb[0] | (sb[1] << 16);
+        stream_store(reinterpret_cast<uint32_t*>(scales) + (row * 2 + p), sb[0] | (sb[1] << 16));
       } else {
-        reinterpret_cast<uint2*>(scales)[row * 2 + p] = make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16));
+        stream_store(reinterpret_cast<uint2*>(scales) + (row * 2 + p), make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)));
       }
     }
   }
@@ -479,20 +550,20 @@ __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ 
     {
       const size_t row = (size_t)row0 + (v < rows ? v : 0);
       sfor<4>([&](auto C) {
-        const uint4 q = codes[row * 8 + 4 * p + RTQ_CI(C)];
+        const uint4 q = stream_load(codes + (row * 8 + 4 * p + RTQ_CI(C)));
         cw[4 * RTQ_CI(C) + 0] = q.x;
         cw[4 * RTQ_CI(C) + 1] = q.y;
         cw[4 * RTQ_CI(C) + 2] = q.z;
         cw[4 * RTQ_CI(C) + 3] = q.w;
       });
       if constexpr (128 / G == 1) {
-        sb[0] = reinterpret_cast<const uint16_t*>(scales)[row * 2 + p];
+        sb[0] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (row * 2 + p));
       } else if constexpr (128 / G == 2) {
-        const uint32_t w = reinterpret_cast<const uint32_t*>(scales)[row * 2 + p];
+        const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(scales) + (row * 2 + p));
         sb[0] = w & 0xffffu;
         sb[1] = w >> 16;
       } else {
-        const uint2 w = reinterpret_cast<const uint2*>(scales)[row * 2 + p];
+        const uint2 w = stream_load(reinterpret_cast<const uint2*>(scales) + (row * 2 + p));
         sb[0] = w.x & 0xffffu;
         sb[1] = w.x >> 16;
         sb[2] = w.y & 0xffffu;
@@ -566,15 +637,15 @@ __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ 
     if (uniform) {
       sfor<16>([&](auto J) {
         const int rl = 2 * RTQ_CI(J) + p;
-        if (rl < rows) yt[(uint32_t)(rl * CPR) + kpos] = xor4(get(rl), cs.m);
+        if (rl < rows) stream_store(yt + ((uint32_t)(rl * CPR) + kpos), xor4(get(rl), cs.m));
       });
     } else {
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
         const int rl = 2 * j + p;
         if (rl < rows)
-          yt[(uint32_t)(rl * CPR) + kpos] =
-              xor4(get(rl), chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos));
+          stream_store(yt + ((uint32_t)(rl * CPR) + kpos),
+                       xor4(get(rl), chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos)));
       }
     }
     wait_lds_reads();
