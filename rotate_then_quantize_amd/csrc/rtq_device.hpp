@@ -537,29 +537,40 @@ __device__ __forceinline__ void quantize_pack(const float (&z)[D], float zs, uin
   });
 }
 
-// z = zs * s * q for every value (inverse of quantize_pack's codes).  The
-// nibble is biased by 8 (xor 0x8) so it reads as q + 8 in 0..15, converted by
-// one v_cvt_f32_ubyte; then fma(q + 8, s, -8 s) = s q exactly.
+// fp16 half SEL of a, times b, plus c, in fp32 with a single rounding.
+template <int SEL>
+__device__ __forceinline__ float mix_fma(uint32_t a, float b, float c) {
+  float r;
+  if constexpr (SEL == 0)
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// z = s' * q for every value, s' = zs * s (inverse of quantize_pack's codes).
+// Two codes at a time become an fp16 pair: nibble j of a code word (value
+// 8w + j) and nibble j + 4 (value 8w + j + 4) are masked into the low and
+// high halves, biased to q + 8 by an xor with 8, and placed under the fp16
+// exponent of 1024 (0x6400), so each half reads 1024 + 8 + q.  One v_fma_mix
+// per value then gives (1032 + q) s' - 1032 s' = s' q.  For zs = 1 (and any
+// power of two) 1032 s' is exact in fp32 and so is the result.
 template <int D, int G>
 __device__ __forceinline__ void dequant_unpack(const uint32_t (&cw)[D / 8], const uint32_t (&sb)[D / G],
                                                float zs, float (&z)[D]) {
   sfor<D / G>([&](auto GI) {
     constexpr int g0 = RTQ_CI(GI) * G;
     const float s = __half2float(__ushort_as_half((unsigned short)sb[RTQ_CI(GI)])) * zs;
-    const float m8 = -8.0f * s;
+    const float c = -1032.0f * s;
     sfor<G / 8>([&](auto W) {
       constexpr int base = g0 + RTQ_CI(W) * 8;
-      const uint32_t x = cw[base / 8] ^ 0x88888888u;
-      const uint32_t lo = x & 0x0f0f0f0fu;
-      const uint32_t hi = (x >> 4) & 0x0f0f0f0fu;
-      z[base + 0] = __builtin_fmaf((float)(lo & 0xffu), s, m8);
-      z[base + 1] = __builtin_fmaf((float)(hi & 0xffu), s, m8);
-      z[base + 2] = __builtin_fmaf((float)((lo >> 8) & 0xffu), s, m8);
-      z[base + 3] = __builtin_fmaf((float)((hi >> 8) & 0xffu), s, m8);
-      z[base + 4] = __builtin_fmaf((float)((lo >> 16) & 0xffu), s, m8);
-      z[base + 5] = __builtin_fmaf((float)((hi >> 16) & 0xffu), s, m8);
-      z[base + 6] = __builtin_fmaf((float)(lo >> 24), s, m8);
-      z[base + 7] = __builtin_fmaf((float)(hi >> 24), s, m8);
+      const uint32_t x = cw[base / 8];
+      sfor<4>([&](auto J) {
+        constexpr int j = RTQ_CI(J);
+        const uint32_t pr = ((x >> (4 * j)) & 0x000f000fu) ^ 0x64086408u;
+        z[base + j] = mix_fma<0>(pr, s, c);
+        z[base + j + 4] = mix_fma<1>(pr, s, c);
+      });
     });
   });
 }
