@@ -311,25 +311,49 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
   else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, lane_seed(sr, row0, rows, lane), buf, lane);
 }
 
-// One inverse tile (layout as fwd_lane_tile); `lds` is a padded row tile.
+// Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
+// row order): load instruction j of lane i fills slot 64j + i with chunk
+// 64j + i, a partial tile repeating its last row.
+template <int CW>
+__device__ __forceinline__ void load_codes_to_lds(const uint4* __restrict__ ct, int rows, uint4* buf, int lane) {
+  sfor<CW>([&](auto J) {
+    const int c = RTQ_CI(J) * 64 + lane;
+    const int r = c / CW;
+    const int rr = r < rows ? r : rows - 1;
+    const uint32_t off = (uint32_t)(rr * CW + c % CW) * 16u;
+    __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)ct + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16,
+                                     0, kCachePolicyNT);
+  });
+}
+
+// One inverse tile: rows row0 .. row0 + rows - 1, lane l owning row row0 + l.
+// The code block arrives coalesced in LDS, each lane reads its own row, and
+// the fp16 output leaves through the same LDS buffer (padded rows) as
+// coalesced 16-byte stores.
 template <int D, int G, int ROT, bool kUniform>
 __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, const uint8_t* __restrict__ st,
-                                              uint4* __restrict__ yt, int rows, const UniformSigns<D>& sg,
-                                              uint64_t s, uint4* lds, int lane) {
+                                              uint4* __restrict__ yt, int rows, uint64_t s, uint4* lds,
+                                              int lane) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   constexpr int LROW = CPR + 1;
   const uint32_t kpos = lane % CPR;
   const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
-  uint32_t cw[D / 8], sb[D / G];
+  load_codes_to_lds<CW>(ct, rows, lds, lane);
+  uint32_t sb[D / G];
+  load_row_scales<D, G>(st, r, sb);
+  UniformSigns<D> sg;
+  if constexpr (kUniform) sg.compute(s, lane);  // overlaps the loads
+  wait_vmcnt<0>();
+  lds_sync();
+  uint32_t cw[D / 8];
   sfor<CW>([&](auto C) {
-    const uint4 q = stream_load(ct + (r * CW + RTQ_CI(C)));
+    const uint4 q = lds[r * CW + RTQ_CI(C)];
     cw[4 * RTQ_CI(C) + 0] = q.x;
     cw[4 * RTQ_CI(C) + 1] = q.y;
     cw[4 * RTQ_CI(C) + 2] = q.z;
     cw[4 * RTQ_CI(C) + 3] = q.w;
   });
-  load_row_scales<D, G>(st, r, sb);
   float z[D], u[D];
   if constexpr (ROT == kSRFT) {
     dequant_unpack<D, G>(cw, sb, 1.0f, z);
@@ -342,7 +366,9 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   if constexpr (kUniform) sg.apply(h);
   else apply_lane_signs<D>(h, s);
-  // own row into LDS, then coalesced chunks out
+  // own row into LDS (the code block has been read), then coalesced chunks out
+  wait_lds_reads();
+  lds_sync();
   sfor<CPR>([&](auto C) {
     constexpr int c = RTQ_CI(C);
     lds[lane * LROW + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
@@ -352,12 +378,9 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
     const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
     if (rl < rows) stream_store(yt + (uint32_t)(RTQ_CI(J) * 64 + lane), lds[rl * LROW + kpos]);
   });
-  wait_lds_reads();
-  lds_sync();
 }
 
-// Inverse step, `per_wave` consecutive 64-row tiles per wave; the scalar sign
-// masks are kept while the seed does not change.
+// Inverse step, one 64-row tile per wave.
 template <int D, int G, int ROT>
 __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
@@ -365,31 +388,16 @@ __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ 
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   __shared__ uint4 lds[64 * (CPR + 1)];
+  (void)per_wave;
   const int lane = threadIdx.x;
-  uint32_t t, tiles;
-  wave_tile_range((n + 63u) / 64u, per_wave, t, tiles);
-  UniformSigns<D> sg;
-  uint64_t cached = 0;
-  bool have = false;
-  for (; t < tiles; ++t) {
-    const uint32_t row0 = t * 64u;
-    const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
-    const uint4* ct = codes + (size_t)row0 * CW;
-    const uint8_t* st = scales + (size_t)row0 * (2 * D / G);
-    uint4* yt = y + (size_t)row0 * CPR;
-    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-    if (b0 == b1) {
-      const uint64_t s = seed_of_block(b0, sr);
-      if (!have || s != cached) {
-        sg.compute(s, lane);
-        cached = s;
-        have = true;
-      }
-      inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, sg, 0, lds, lane);
-    } else {
-      inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, sg, lane_seed(sr, row0, rows, lane), lds, lane);
-    }
-  }
+  const uint32_t row0 = blockIdx.x * 64u;
+  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+  const uint4* ct = codes + (size_t)row0 * CW;
+  const uint8_t* st = scales + (size_t)row0 * (2 * D / G);
+  uint4* yt = y + (size_t)row0 * CPR;
+  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+  if (b0 == b1) inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, seed_of_block(b0, sr), lds, lane);
+  else inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, lane_seed(sr, row0, rows, lane), lds, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -664,12 +672,13 @@ constexpr int64_t kMaxRows = 0xffffff00ll;
 
 // Tiles per wave.  The grid is derived from the row count alone (no occupancy
 // query): each one-wave workgroup takes this many consecutive tiles and the
-// hardware dispatcher keeps every CU filled.  The forward takes one tile per
-// wave; the inverse amortizes its cached sign masks over a few tiles.
+// hardware dispatcher keeps every CU filled.  The one-lane kernels take one
+// tile per wave; the two-lane d = 256 kernels amortize their cached sign
+// masks over a few tiles.
 int32_t tiles_per_wave(bool fwd, int d, int64_t tiles) {
-  if (fwd) return d == 256 ? 2 : 1;
-  if (tiles < 16384) return 1;
-  return d == 64 ? 2 : 4;
+  if (d != 256) return 1;
+  if (fwd) return 2;
+  return tiles < 16384 ? 1 : 4;
 }
 
 rtq_status launch(KernelFn fn, int64_t tiles, int32_t per_wave, void** kargs, hipStream_t stream) {
