@@ -117,7 +117,18 @@ template <int D>
 struct UniformSigns {
   uint32_t m[D / 2];
 
-  __device__ __forceinline__ void compute(uint64_t s, int lane) {
+  // Seed offset j (wave-uniform) of base seed s0: the sign words come from
+  // the host-filled table when it holds j, otherwise from a ballot.
+  __device__ __forceinline__ void setup(const SignTable& tb, uint32_t j, uint64_t s0, int lane) {
+    if (j < tb.seeds) {
+      sfor<D / 64>([&](auto Q) {
+        constexpr int q = RTQ_CI(Q);
+        const uint64_t bits = tb.w[j * (D / 64) + q];
+        sfor<32>([&](auto M) { m[32 * q + RTQ_CI(M)] = pair_mask(bits, RTQ_CI(M)); });
+      });
+      return;
+    }
+    const uint64_t s = s0 + j;
     sfor<D / 64>([&](auto Q) {
       constexpr int q = RTQ_CI(Q);
       const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
@@ -147,31 +158,18 @@ __device__ __forceinline__ uint64_t lane_seed(const SeedRule& sr, uint32_t row0,
   return seed_of_block(seed_block(row0 + (uint32_t)(lane < rows ? lane : rows - 1), sr), sr);
 }
 
-// Signs of a fixed 16-byte chunk position (elements 8k .. 8k+7) of whatever
-// row a lane stages; cached per seed.  Used by the two-lane d = 256 kernels.
-struct ChunkSigns {
-  uint64_t seed;
-  uint4 m;
-  bool valid;
-
-  // Masks for the tile's seed; returns false if the tile straddles a seed
-  // boundary (then the caller derives the masks row by row).
-  __device__ __forceinline__ bool prepare(const SeedRule& sr, uint32_t row0, int rows, uint32_t kpos) {
-    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-    if (b0 != b1) return false;
-    const uint64_t s = seed_of_block(b0, sr);
-    if (!valid || seed != s) {
-      m = chunk_sign_masks(s, kpos);
-      seed = s;
-      valid = true;
-    }
-    return true;
+// XOR masks flipping the fp16 sign bits of chunk k (elements 8k .. 8k+7) for
+// seed offset j (wave-uniform) of base seed s0, from the host-filled table
+// when it holds j (D = 256: four words per seed), otherwise evaluated here.
+__device__ __forceinline__ uint4 chunk_masks(const SignTable& tb, uint32_t j, uint64_t s0, uint32_t k) {
+  if (j < tb.seeds) {
+    const uint64_t w0 = tb.w[4 * j], w1 = tb.w[4 * j + 1], w2 = tb.w[4 * j + 2], w3 = tb.w[4 * j + 3];
+    const uint32_t q = k >> 3;
+    const uint64_t w = q == 0 ? w0 : q == 1 ? w1 : q == 2 ? w2 : w3;
+    const uint64_t byte = (w >> (8 * (k & 7))) & 0xffu;
+    return make_uint4(pair_mask(byte, 0), pair_mask(byte, 1), pair_mask(byte, 2), pair_mask(byte, 3));
   }
-};
-
-__device__ __forceinline__ void wave_tile_range(uint32_t n_tiles, int32_t per_wave, uint32_t& t0, uint32_t& t1) {
-  t0 = blockIdx.x * (uint32_t)per_wave;
-  t1 = t0 + (uint32_t)per_wave < n_tiles ? t0 + (uint32_t)per_wave : n_tiles;
+  return chunk_sign_masks(s0 + j, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -262,13 +260,13 @@ __device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, 
 // lane's own seed.
 template <int D, int G, int ROT, bool kUniform>
 __device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint4* __restrict__ ct,
-                                              uint8_t* __restrict__ st, int rows, uint64_t s, uint4* buf,
-                                              int lane) {
+                                              uint8_t* __restrict__ st, int rows, const SignTable& tb,
+                                              uint32_t j, uint64_t s, uint4* buf, int lane) {
   constexpr int CPR = D / 8;  // 16-byte chunks per input row
   constexpr int CW = D / 32;  // 16-byte chunks per code row
   load_tile_to_lds<CPR>(xt, rows, buf, lane);
   UniformSigns<D> sg;
-  if constexpr (kUniform) sg.compute(s, lane);  // overlaps the loads
+  if constexpr (kUniform) sg.setup(tb, j, s, lane);  // overlaps the loads
   wait_vmcnt<0>();
   lds_sync();
   uint32_t h[D / 2];
@@ -294,12 +292,10 @@ __device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint
 // Forward step, one 64-row tile per wave.
 template <int D, int G, int ROT>
 __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
-                                                      int32_t per_wave) {
+                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr, SignTable tb) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   __shared__ uint4 buf[64 * CPR];
-  (void)per_wave;
   const int lane = threadIdx.x;
   const uint32_t row0 = blockIdx.x * 64u;
   const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
@@ -307,8 +303,8 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
   uint4* ct = codes + (size_t)row0 * CW;
   uint8_t* st = scales + (size_t)row0 * (2 * D / G);
   const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-  if (b0 == b1) fwd_lane_tile<D, G, ROT, true>(xt, ct, st, rows, seed_of_block(b0, sr), buf, lane);
-  else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, lane_seed(sr, row0, rows, lane), buf, lane);
+  if (b0 == b1) fwd_lane_tile<D, G, ROT, true>(xt, ct, st, rows, tb, seed_offset(b0, sr), sr.seed, buf, lane);
+  else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, tb, 0, lane_seed(sr, row0, rows, lane), buf, lane);
 }
 
 // Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
@@ -332,8 +328,8 @@ __device__ __forceinline__ void load_codes_to_lds(const uint4* __restrict__ ct, 
 // coalesced 16-byte stores.
 template <int D, int G, int ROT, bool kUniform>
 __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, const uint8_t* __restrict__ st,
-                                              uint4* __restrict__ yt, int rows, uint64_t s, uint4* lds,
-                                              int lane) {
+                                              uint4* __restrict__ yt, int rows, const SignTable& tb, uint32_t j,
+                                              uint64_t s, uint4* lds, int lane) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   constexpr int LROW = CPR + 1;
@@ -343,7 +339,7 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   uint32_t sb[D / G];
   load_row_scales<D, G>(st, r, sb);
   UniformSigns<D> sg;
-  if constexpr (kUniform) sg.compute(s, lane);  // overlaps the loads
+  if constexpr (kUniform) sg.setup(tb, j, s, lane);  // overlaps the loads
   wait_vmcnt<0>();
   lds_sync();
   uint32_t cw[D / 8];
@@ -384,11 +380,10 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
 template <int D, int G, int ROT>
 __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                      uint32_t n, SeedRule sr, int32_t per_wave) {
+                                                      uint32_t n, SeedRule sr, SignTable tb) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   __shared__ uint4 lds[64 * (CPR + 1)];
-  (void)per_wave;
   const int lane = threadIdx.x;
   const uint32_t row0 = blockIdx.x * 64u;
   const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
@@ -396,8 +391,8 @@ __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ 
   const uint8_t* st = scales + (size_t)row0 * (2 * D / G);
   uint4* yt = y + (size_t)row0 * CPR;
   const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-  if (b0 == b1) inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, seed_of_block(b0, sr), lds, lane);
-  else inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, lane_seed(sr, row0, rows, lane), lds, lane);
+  if (b0 == b1) inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, tb, seed_offset(b0, sr), sr.seed, lds, lane);
+  else inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, tb, 0, lane_seed(sr, row0, rows, lane), lds, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -415,23 +410,21 @@ __global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ 
 
 
 template <int G, int ROT>
-__global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
-                                                      int32_t per_wave) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_pair_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                                      uint8_t* __restrict__ scales, uint32_t n, SeedRule sr, SignTable tb) {
   constexpr int D = 256, CPR = 32, LROW = CPR + 1;
   __shared__ uint4 lds[32 * LROW];
   const int lane = threadIdx.x;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
   const float sigma = p ? -1.0f : 1.0f;
-  uint32_t t0, tiles;
-  wave_tile_range((n + 31u) / 32u, per_wave, t0, tiles);
-  ChunkSigns cs;
-  cs.valid = false;
-  for (uint32_t t = t0; t < tiles; ++t) {
-    const uint32_t row0 = t * 32u;
+  {
+    const uint32_t row0 = blockIdx.x * 32u;
     const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
-    const bool uniform = cs.prepare(sr, row0, rows, kpos);
+    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+    const bool uniform = b0 == b1;
+    uint4 cm = make_uint4(0, 0, 0, 0);
+    if (uniform) cm = chunk_masks(tb, seed_offset(b0, sr), sr.seed, kpos);
     auto put = [&](int rl, uint4 q) {
       if constexpr (ROT == kSRFT) {
         // de-interleave: evens to the first half of the LDS row, odds to the second
@@ -449,7 +442,7 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
         const int rl = 2 * RTQ_CI(J) + p;
         in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
       });
-      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cs.m)); });
+      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cm)); });
     } else {
 #pragma unroll 1
       for (int j = 0; j < 16; ++j) {
@@ -474,17 +467,22 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
     if constexpr (ROT == kSRFT) {
       float fr[65], fi[65];
       rdft<128, 1, 0, 64>(h, fr, fi);  // unnormalized; sqrt(2/256) is applied by the quantizer
-      const int src_e = v, src_o = v + 32;
+      // Partner exchange by ds_bpermute.  Every 4 bins the next addresses are
+      // tied to the last result, so each group of shuffles issues only once
+      // the previous group has been consumed; this keeps the exchange from
+      // holding all 260 shuffled values at once (register pressure).
+      int addr_e = v * 4, addr_o = (v + 32) * 4;
+      auto shf = [](float x, int addr) { return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x))); };
       // slot 0: E_0 + sigma * O_0 (real)
       {
-        const float e0 = __shfl(fr[0], src_e), o0 = __shfl(fr[0], src_o);
+        const float e0 = shf(fr[0], addr_e), o0 = shf(fr[0], addr_o);
         constexpr float r2 = 0.70710678118654752440f;  // real end bins: 1/16 = sqrt(2/256) / sqrt(2)
         L[0] = __builtin_fmaf(sigma, o0, e0) * r2;
       }
       sfor<63>([&](auto A) {
         constexpr int a = RTQ_CI(A) + 1;
-        const float er = __shfl(fr[a], src_e), ei = __shfl(fi[a], src_e);
-        const float orr = __shfl(fr[a], src_o), oi = __shfl(fi[a], src_o);
+        const float er = shf(fr[a], addr_e), ei = shf(fi[a], addr_e);
+        const float orr = shf(fr[a], addr_o), oi = shf(fi[a], addr_o);
         constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);  // w^a = c - i s
         const float tr = __builtin_fmaf(c, orr, s * oi);
         const float ti = __builtin_fmaf(c, oi, -s * orr);
@@ -492,9 +490,10 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
         const float ri = __builtin_fmaf(sigma, ei, ti);
         L[2 * a - 1] = p ? ri : rr;
         L[2 * a] = p ? rr : ri;
+        if constexpr (a % 4 == 0) asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(L[2 * a]));
       });
       {  // slot 64: X_64 = E_64 - i O_64; lane 0 keeps Re, lane 1 keeps Im
-        const float e64 = __shfl(fr[64], src_e), o64 = __shfl(fr[64], src_o);
+        const float e64 = shf(fr[64], addr_e), o64 = shf(fr[64], addr_o);
         L[127] = p ? -o64 : e64;
       }
       zs = SrftScale<256>::value;
@@ -537,23 +536,22 @@ __global__ __launch_bounds__(64) void fwd_pair_kernel(const uint4* __restrict__ 
 }
 
 template <int G, int ROT>
-__global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ codes,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void inv_pair_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                      uint32_t n, SeedRule sr, int32_t per_wave) {
+                                                      uint32_t n, SeedRule sr, SignTable tb) {
   constexpr int CPR = 32, LROW = CPR + 1;
   __shared__ uint4 lds[32 * LROW];
   const int lane = threadIdx.x;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
   const float sigma = p ? -1.0f : 1.0f;
-  uint32_t t0, tiles;
-  wave_tile_range((n + 31u) / 32u, per_wave, t0, tiles);
-  ChunkSigns cs;
-  cs.valid = false;
-  for (uint32_t t = t0; t < tiles; ++t) {
-    const uint32_t row0 = t * 32u;
+  {
+    const uint32_t row0 = blockIdx.x * 32u;
     const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
-    const bool uniform = cs.prepare(sr, row0, rows, kpos);
+    const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+    const bool uniform = b0 == b1;
+    uint4 cm = make_uint4(0, 0, 0, 0);
+    if (uniform) cm = chunk_masks(tb, seed_offset(b0, sr), sr.seed, kpos);
     uint32_t cw[16], sb[128 / G];
     {
       const size_t row = (size_t)row0 + (v < rows ? v : 0);
@@ -645,7 +643,7 @@ __global__ __launch_bounds__(64) void inv_pair_kernel(const uint4* __restrict__ 
     if (uniform) {
       sfor<16>([&](auto J) {
         const int rl = 2 * RTQ_CI(J) + p;
-        if (rl < rows) stream_store(yt + ((uint32_t)(rl * CPR) + kpos), xor4(get(rl), cs.m));
+        if (rl < rows) stream_store(yt + ((uint32_t)(rl * CPR) + kpos), xor4(get(rl), cm));
       });
     } else {
 #pragma unroll 1
@@ -670,22 +668,46 @@ using KernelFn = const void*;
 // Rows per call: row indices are 32-bit on the device.
 constexpr int64_t kMaxRows = 0xffffff00ll;
 
-// Tiles per wave.  The grid is derived from the row count alone (no occupancy
-// query): each one-wave workgroup takes this many consecutive tiles and the
-// hardware dispatcher keeps every CU filled.  The one-lane kernels take one
-// tile per wave; the two-lane d = 256 kernels amortize their cached sign
-// masks over a few tiles.
-int32_t tiles_per_wave(bool fwd, int d, int64_t tiles) {
-  if (d != 256) return 1;
-  if (fwd) return 2;
-  return tiles < 16384 ? 1 : 4;
+// One wave per tile.  The grid is derived from the row count alone (no
+// occupancy query): the hardware dispatcher keeps every CU filled from a
+// grid far larger than the machine.
+rtq_status launch(KernelFn fn, int64_t tiles, void** kargs, hipStream_t stream) {
+  if (tiles <= 0 || tiles > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
+  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(64), kargs, 0, stream);
+  return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
 
-rtq_status launch(KernelFn fn, int64_t tiles, int32_t per_wave, void** kargs, hipStream_t stream) {
-  const int64_t grid = (tiles + per_wave - 1) / per_wave;
-  if (grid <= 0 || grid > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)grid), dim3(64), kargs, 0, stream);
-  return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
+// Sign words of the seeds a call uses (as many as the table holds).  The
+// table is a pure function of (seed, d, number of seeds); the last one built
+// on each host thread is kept to skip recomputing it for repeated calls.
+void fill_sign_table(SignTable& tb, const SeedRule& sr, int64_t n, int d) {
+  const uint32_t wps = (uint32_t)d / 64u;
+  uint64_t distinct = 1;
+  if (sr.rps) {
+    const uint64_t blocks = ((uint64_t)n + sr.rps - 1) / sr.rps;
+    distinct = sr.period && sr.period < blocks ? sr.period : blocks;
+  }
+  const uint32_t seeds = (uint32_t)(distinct < kSignTableWords / wps ? distinct : kSignTableWords / wps);
+  thread_local SignTable memo;
+  thread_local uint64_t memo_seed = 0;
+  thread_local bool memo_valid = false;
+  if (memo_valid && memo_seed == sr.seed && memo.words_per_seed == wps && memo.seeds >= seeds) {
+    tb = memo;
+    tb.seeds = seeds;
+    return;
+  }
+  tb.seeds = seeds;
+  tb.words_per_seed = wps;
+  for (uint32_t j = 0; j < kSignTableWords; ++j) tb.w[j] = 0;
+  for (uint32_t j = 0; j < seeds; ++j)
+    for (uint32_t q = 0; q < wps; ++q) {
+      uint64_t w = 0;
+      for (uint32_t e = 0; e < 64; ++e) w |= (uint64_t)sign_bit(sr.seed + j, 64u * q + e) << e;
+      tb.w[j * wps + q] = w;
+    }
+  memo = tb;
+  memo_seed = sr.seed;
+  memo_valid = true;
 }
 
 template <int D, int G, int ROT>
@@ -765,21 +787,22 @@ rtq_status run(bool fwd, int rot, const void* in0, const void* in1, void* out0, 
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   const int vpt = d == 256 ? 32 : 64;
   const int64_t tiles = (n + vpt - 1) / vpt;
-  int32_t per_wave = tiles_per_wave(fwd, d, tiles);
   uint32_t n32 = (uint32_t)n;
   SeedRule sr = make_seed_rule(seed, rps, period, n);
+  SignTable tb;
+  fill_sign_table(tb, sr, n, d);
   if (fwd) {
     const void* x = in0;
     void* codes = out0;
     void* scales = out1;
-    void* kargs[] = {&x, &codes, &scales, &n32, &sr, &per_wave};
-    return launch(fn, tiles, per_wave, kargs, stream);
+    void* kargs[] = {&x, &codes, &scales, &n32, &sr, &tb};
+    return launch(fn, tiles, kargs, stream);
   }
   const void* codes = in0;
   const void* scales = in1;
   void* y = out0;
-  void* kargs[] = {&codes, &scales, &y, &n32, &sr, &per_wave};
-  return launch(fn, tiles, per_wave, kargs, stream);
+  void* kargs[] = {&codes, &scales, &y, &n32, &sr, &tb};
+  return launch(fn, tiles, kargs, stream);
 }
 
 }  // namespace rtq

@@ -166,7 +166,7 @@ __device__ __forceinline__ uint32_t nibble_reverse(uint32_t x) {
 
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 
-__device__ __forceinline__ uint32_t sign_bit(uint64_t seed, uint32_t i) {
+__host__ __device__ __forceinline__ uint32_t sign_bit(uint64_t seed, uint32_t i) {
   uint64_t z = seed + (uint64_t)(i + 1u) * kGamma;
   z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
   z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;

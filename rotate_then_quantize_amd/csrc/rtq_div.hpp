@@ -53,9 +53,25 @@ __host__ __device__ inline uint32_t seed_block(uint32_t row, const SeedRule& s) 
   return s.rps ? div32(row, s.by_rps) : 0u;
 }
 
-__host__ __device__ inline uint64_t seed_of_block(uint32_t block, const SeedRule& s) {
-  const uint32_t b = s.period ? block - div32(block, s.by_period) * s.period : block;
-  return s.seed + b;
+// Offset of a block's seed from the base seed: (block mod period), or block.
+__host__ __device__ inline uint32_t seed_offset(uint32_t block, const SeedRule& s) {
+  return s.period ? block - div32(block, s.by_period) * s.period : block;
 }
+
+__host__ __device__ inline uint64_t seed_of_block(uint32_t block, const SeedRule& s) {
+  return s.seed + seed_offset(block, s);
+}
+
+// Sign words of the first seeds of a call, filled on the host and passed by
+// value in the kernel arguments: entry j holds the D/64 words of seed
+// (seed + j), word q bit e being the sign bit of element 64 q + e.  Seed
+// offsets at or beyond `seeds` are evaluated on the device.
+constexpr int kSignTableWords = 128;
+
+struct SignTable {
+  uint32_t seeds;
+  uint32_t words_per_seed;
+  uint64_t w[kSignTableWords];
+};
 
 }  // namespace rtq
