@@ -198,6 +198,45 @@ def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mi
         log(f"wrote {path}")
 
 
+def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warmup=3):
+    """The same step as four separate torch operations (rotate with torch.fft,
+    quantize, dequantize, inverse rotate) on the same buffers; signs are a
+    precomputed tensor.  Measurement only."""
+    import torch
+    from rotate_then_quantize_amd import eager
+    n_inv = w.n_rows
+    n_fwd = w.new_rows if w.new_tokens else w.n_rows
+    signs_inv = eager.sign_matrix(n_inv, w.d, w.sign_seed, w.rows_per_seed, w.seed_period)
+    signs_fwd = signs_inv[n_inv - n_fwd:] if w.new_tokens else signs_inv
+
+    def step(i):
+        x, codes, scales, _ = sets[i % replicas][2]
+        xin = x[n_inv - n_fwd:] if w.new_tokens else x
+        c, s = eager.quant_fwd(xin, w.group, 0, rot=rot, signs=signs_fwd)
+        _, codes2, scales2, _ = sets[(i + 1) % replicas][2]
+        return c, s, eager.dequant_inv(codes2, scales2, w.d, w.group, 0, rot=rot, signs=signs_inv)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    return {
+        "ms_per_step": ms,
+        "value": max(n_fwd, n_inv) / (ms * 1e-3),
+        "unit": "vectors/s",
+        "fused_speedup": ms / fused_ms_step,
+        "steps": steps,
+        "ops": "rotate (torch.fft.rfft or Hadamard matmul), quantize, dequantize, inverse rotate (irfft): "
+               "separate torch operations on the GPU, fp32 intermediates in HBM",
+    }
+
+
 def cpu_baseline(w, x_gpu, rot, seconds):
     """The oracle, as it is, on consecutive 65536-row chunks of the same
     workload until ``seconds`` of CPU time are spent (input copy excluded)."""
@@ -242,6 +281,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="buffer sets cycled per step (0 = enough to exceed 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-eager", action="store_true", help="skip the eager four-operation torch baseline")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -419,6 +459,8 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_eager:
+        result["eager_baseline"] = eager_baseline(w, sets, replicas, rot, ms_step, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x0, rot, args.cpu_seconds)
     print(json.dumps(result), flush=True)

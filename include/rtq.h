@@ -35,7 +35,10 @@
  *    Kernel Problem", "First, the 17%").
  *  Pointers: device pointers (or any pointers the GPU can address), each
  *    16-byte aligned.  The caller owns every buffer; the library allocates
- *    nothing, keeps no state between calls, and is thread-safe.  Outputs must
+ *    no device memory and is thread-safe.  The only state kept between calls
+ *    is a per-host-thread copy of the last sign table the host evaluated (a
+ *    pure function of seed, d and the seed count), reused by later calls
+ *    with the same seed.  Outputs must
  *    not overlap inputs.
  *  Stream: the work is enqueued asynchronously on `stream` (NULL = the
  *    default stream) and the call returns; results are visible after the
