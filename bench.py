@@ -396,7 +396,7 @@ def main():
     # before the forward, one between the two launches, one after the inverse.
     # An event marker costs a few microseconds of GPU idle time, so the other
     # steps run without markers.
-    SAMPLE = 4
+    SAMPLE = 10
     sampled = [i for i in range(args.steps) if i % SAMPLE == 0]
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
