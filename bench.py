@@ -198,6 +198,69 @@ def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mi
         log(f"wrote {path}")
 
 
+def graph_replay(w, sets, replicas, fwd_fn, inv_fn, steps, bpv, replays=5):
+    """The same steps captured once into a HIP graph and replayed: launch
+    overhead and event markers are gone, the kernels and their dispatch gaps
+    remain.  The outputs of the last replay are compared with a direct call."""
+    import torch
+    n_inv = w.n_rows
+    n_fwd = w.new_rows if w.new_tokens else w.n_rows
+
+    def args_on(stream_handle, i):
+        x, codes, scales, y = sets[i % replicas][2]
+        xin = x[n_inv - n_fwd:] if w.new_tokens else x
+        cin, sin = (codes[n_inv - n_fwd:], scales[n_inv - n_fwd:]) if w.new_tokens else (codes, scales)
+        fa = (ctypes.c_void_p(xin.data_ptr()), ctypes.c_void_p(cin.data_ptr()), ctypes.c_void_p(sin.data_ptr()),
+              n_fwd, w.d, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, stream_handle)
+        _, codes2, scales2, y2 = sets[(i + 1) % replicas][2]
+        ia = (ctypes.c_void_p(codes2.data_ptr()), ctypes.c_void_p(scales2.data_ptr()), ctypes.c_void_p(y2.data_ptr()),
+              n_inv, w.d, w.group, w.sign_seed, w.rows_per_seed, w.seed_period, stream_handle)
+        return fa, ia
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for i in range(steps):
+                fa, ia = args_on(h, i)
+                if fwd_fn(*fa) or inv_fn(*ia):
+                    raise RuntimeError("launch failed during capture")
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(replays):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / (replays * steps)
+    # replayed outputs equal a direct call on the same inputs
+    last = steps - 1
+    x, codes, scales, y = sets[last % replicas][2]
+    ref_c, ref_s = codes.clone(), scales.clone()
+    _, _, _, y_next = sets[(last + 1) % replicas][2]
+    ref_y = y_next.clone()
+    torch.cuda.synchronize()
+    fa, ia = args_on(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), last)
+    fwd_fn(*fa)
+    inv_fn(*ia)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(ref_c, codes) and torch.equal(ref_s, scales) and torch.equal(ref_y, y_next))
+    fwd_bytes, inv_bytes = n_fwd * bpv, n_inv * bpv
+    return {
+        "ms_per_step": ms,
+        "value": max(n_fwd, n_inv) / (ms * 1e-3),
+        "unit": "vectors/s",
+        "hbm_gbps_step": (fwd_bytes + inv_bytes) / (ms * 1e6),
+        "steps_per_graph": steps,
+        "replays": replays,
+        "outputs_match_direct_call": same,
+    }
+
+
 def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warmup=3):
     """The same step as four separate torch operations (rotate with torch.fft,
     quantize, dequantize, inverse rotate) on the same buffers; signs are a
@@ -275,13 +338,15 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--rot", choices=["srft", "srht"], default="srft")
     ap.add_argument("--replicas", type=int, default=0, help="buffer sets cycled per step (0 = enough to exceed 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager four-operation torch baseline")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the steps replayed from one HIP graph (on by default for workload 1)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -396,7 +461,7 @@ def main():
     # before the forward, one between the two launches, one after the inverse.
     # An event marker costs a few microseconds of GPU idle time, so the other
     # steps run without markers.
-    SAMPLE = 10
+    SAMPLE = 20
     sampled = [i for i in range(args.steps) if i % SAMPLE == 0]
     evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
     torch.cuda.synchronize()
@@ -459,6 +524,8 @@ def main():
             "traffic": traffic,
         },
     }
+    if args.graph or args.workload == 1:
+        result["graph_replay"] = graph_replay(w, sets, replicas, fwd_fn, inv_fn, args.steps, bpv)
     if not args.no_eager:
         result["eager_baseline"] = eager_baseline(w, sets, replicas, rot, ms_step, stream)
     if not args.no_cpu_baseline:
