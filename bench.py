@@ -345,8 +345,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-eager", action="store_true", help="skip the eager four-operation torch baseline")
-    ap.add_argument("--graph", action="store_true",
-                    help="also time the steps replayed from one HIP graph (on by default for workload 1)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the same steps replayed from one captured HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -524,7 +524,7 @@ def main():
             "traffic": traffic,
         },
     }
-    if args.graph or args.workload == 1:
+    if not args.no_graph:
         result["graph_replay"] = graph_replay(w, sets, replicas, fwd_fn, inv_fn, args.steps, bpv)
     if not args.no_eager:
         result["eager_baseline"] = eager_baseline(w, sets, replicas, rot, ms_step, stream)
