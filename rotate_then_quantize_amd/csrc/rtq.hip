@@ -307,6 +307,9 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
   else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, tb, 0, lane_seed(sr, row0, rows, lane), buf, lane);
 }
 
+// Output transpose passes of the inverse: d = 128 in two halves.
+template <int D> struct InvPhases { static constexpr int value = D == 128 ? 2 : 1; };
+
 // Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
 // row order): load instruction j of lane i fills slot 64j + i with chunk
 // 64j + i, a partial tile repeating its last row.
@@ -332,8 +335,6 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
                                               uint64_t s, uint4* lds, int lane) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
-  constexpr int LROW = CPR + 1;
-  const uint32_t kpos = lane % CPR;
   const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
   load_codes_to_lds<CW>(ct, rows, lds, lane);
   uint32_t sb[D / G];
@@ -362,28 +363,42 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   if constexpr (kUniform) sg.apply(h);
   else apply_lane_signs<D>(h, s);
-  // own row into LDS (the code block has been read), then coalesced chunks out
+  // Own row into LDS (the code block has been read), then coalesced chunks
+  // out.  d = 128 goes in two halves of 8 chunks per row, which halves the
+  // LDS tile (9 KB) so that LDS does not cap the resident waves.
   wait_lds_reads();
   lds_sync();
-  sfor<CPR>([&](auto C) {
-    constexpr int c = RTQ_CI(C);
-    lds[lane * LROW + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
-  });
-  lds_sync();
-  sfor<CPR>([&](auto J) {
-    const int rl = (RTQ_CI(J) * 64 + lane) / CPR;
-    if (rl < rows) stream_store(yt + (uint32_t)(RTQ_CI(J) * 64 + lane), lds[rl * LROW + kpos]);
+  constexpr int PH = InvPhases<D>::value;
+  constexpr int PC = CPR / PH, LR = PC + 1;
+  sfor<PH>([&](auto P) {
+    constexpr int ph = RTQ_CI(P);
+    if constexpr (ph > 0) {
+      wait_lds_reads();
+      lds_sync();
+    }
+    sfor<PC>([&](auto C) {
+      constexpr int c = ph * PC + RTQ_CI(C);
+      lds[lane * LR + RTQ_CI(C)] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
+    });
+    lds_sync();
+    sfor<PC>([&](auto J) {
+      const int idx = RTQ_CI(J) * 64 + lane;
+      const int rl = idx / PC, kk = idx % PC;
+      if (rl < rows) stream_store(yt + (uint32_t)(rl * CPR + ph * PC + kk), lds[rl * LR + kk]);
+    });
   });
 }
 
-// Inverse step, one 64-row tile per wave.
+// Inverse step, one 64-row tile per wave.  At most 168 VGPRs (3 waves per
+// SIMD): d = 128 then spills a little, and still runs 5% faster than at 2.
 template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void inv_lane_kernel(const uint4* __restrict__ codes,
-                                                      const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                      uint32_t n, SeedRule sr, SignTable tb) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_lane_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y, uint32_t n,
+    SeedRule sr, SignTable tb) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
-  __shared__ uint4 lds[64 * (CPR + 1)];
+  constexpr int LT = 64 * (CPR / InvPhases<D>::value + 1);  // output tile (uint4)
+  __shared__ uint4 lds[LT > 64 * CW ? LT : 64 * CW];
   const int lane = threadIdx.x;
   const uint32_t row0 = blockIdx.x * 64u;
   const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
