@@ -554,8 +554,8 @@ template <int G, int ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void inv_pair_kernel(const uint4* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales, uint4* __restrict__ y,
                                                       uint32_t n, SeedRule sr, SignTable tb) {
-  constexpr int CPR = 32, LROW = CPR + 1;
-  __shared__ uint4 lds[32 * LROW];
+  constexpr int CPR = 32;
+  __shared__ uint4 lds[32 * 17];
   const int lane = threadIdx.x;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
@@ -565,8 +565,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
     const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
     const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
     const bool uniform = b0 == b1;
-    uint4 cm = make_uint4(0, 0, 0, 0);
-    if (uniform) cm = chunk_masks(tb, seed_offset(b0, sr), sr.seed, kpos);
     uint32_t cw[16], sb[128 / G];
     {
       const size_t row = (size_t)row0 + (v < rows ? v : 0);
@@ -636,39 +634,65 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
         u[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
       });
     }
-    // fp16 samples into LDS (SRFT: lane p's samples are u_{2m+p}; they go to
-    // the p-th half of the row and are re-interleaved on the way out)
-    sfor<16>([&](auto C) {
-      constexpr int c = RTQ_CI(C);
-      lds[v * LROW + 16 * p + c] = make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
-                                              pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
-    });
-    lds_sync();
-    auto get = [&](int rl) -> uint4 {
-      if constexpr (ROT == kSRFT) {
-        const uint2* row = reinterpret_cast<const uint2*>(&lds[rl * LROW]);
-        const uint2 e = row[kpos], o = row[32 + kpos];
-        return make_uint4(__builtin_amdgcn_perm(o.x, e.x, 0x05040100u), __builtin_amdgcn_perm(o.x, e.x, 0x07060302u),
-                          __builtin_amdgcn_perm(o.y, e.y, 0x05040100u), __builtin_amdgcn_perm(o.y, e.y, 0x07060302u));
-      } else {
-        return lds[rl * LROW + kpos];
-      }
-    };
+    // fp16 samples out through LDS in two passes of 16 output chunks per row
+    // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
+    // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
+    // re-interleaves them on the way out.  SRHT: lane p holds output chunks
+    // 16 p .. 16 p + 15, written in pass p.
+    constexpr int LR2 = 17;
+    const int kk = lane & 15, rsub = lane >> 4;
     uint4* yt = y + (size_t)row0 * CPR;
-    if (uniform) {
-      sfor<16>([&](auto J) {
-        const int rl = 2 * RTQ_CI(J) + p;
-        if (rl < rows) stream_store(yt + ((uint32_t)(rl * CPR) + kpos), xor4(get(rl), cm));
-      });
-    } else {
-#pragma unroll 1
-      for (int j = 0; j < 16; ++j) {
-        const int rl = 2 * j + p;
-        if (rl < rows)
-          stream_store(yt + ((uint32_t)(rl * CPR) + kpos),
-                       xor4(get(rl), chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), kpos)));
+    sfor<2>([&](auto PH) {
+      constexpr int ph = RTQ_CI(PH);
+      if constexpr (ph > 0) {
+        wait_lds_reads();
+        lds_sync();
       }
-    }
+      if constexpr (ROT == kSRFT) {
+        sfor<8>([&](auto C) {
+          constexpr int c = 8 * ph + RTQ_CI(C);
+          lds[v * LR2 + 8 * p + RTQ_CI(C)] =
+              make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
+                         pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+        });
+      } else {
+        if (p == ph) {
+          sfor<16>([&](auto C) {
+            constexpr int c = RTQ_CI(C);
+            lds[v * LR2 + c] =
+                make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
+                           pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+          });
+        }
+      }
+      lds_sync();
+      const uint32_t k = 16u * ph + (uint32_t)kk;  // output chunk this lane stores
+      auto get = [&](int rl) -> uint4 {
+        if constexpr (ROT == kSRFT) {
+          const uint2* row = reinterpret_cast<const uint2*>(&lds[rl * LR2]);
+          const uint2 e = row[kk], o = row[16 + kk];
+          return make_uint4(__builtin_amdgcn_perm(o.x, e.x, 0x05040100u), __builtin_amdgcn_perm(o.x, e.x, 0x07060302u),
+                            __builtin_amdgcn_perm(o.y, e.y, 0x05040100u), __builtin_amdgcn_perm(o.y, e.y, 0x07060302u));
+        } else {
+          return lds[rl * LR2 + kk];
+        }
+      };
+      if (uniform) {
+        const uint4 m = chunk_masks(tb, seed_offset(b0, sr), sr.seed, k);
+        sfor<8>([&](auto J) {
+          const int rl = rsub + 4 * RTQ_CI(J);
+          if (rl < rows) stream_store(yt + ((uint32_t)(rl * CPR) + k), xor4(get(rl), m));
+        });
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+          const int rl = rsub + 4 * j;
+          if (rl < rows)
+            stream_store(yt + ((uint32_t)(rl * CPR) + k),
+                         xor4(get(rl), chunk_sign_masks(seed_of_block(seed_block(row0 + rl, sr), sr), k)));
+        }
+      }
+    });
     wait_lds_reads();
     lds_sync();
   }
