@@ -106,3 +106,11 @@ def test_python_binding_rejects_cpu_tensors():
         rtq.srft_quant_fwd(x, 32, 1)
     with pytest.raises(TypeError):
         rtq.srft_quant_fwd(x.float(), 32, 1)
+
+
+def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
+    """No fallback: with the shared library absent every entry point raises."""
+    monkeypatch.setattr(rtq, "_LIB_PATH", str(tmp_path / "missing" / "librtq.so"))
+    monkeypatch.setattr(rtq, "_lib", None)
+    with pytest.raises(rtq.RTQError):
+        rtq.library()
