@@ -599,20 +599,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
       sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
       float L[128];
-      dequant_unpack<128, G>(cw, sb, 1.0f, L);
+      dequant_unpack<128, G>(cw, sb, 0.5f, L);  // the halving of E and t folded in
       // P = lane v's slots (X_a), Q = lane v+32's slots (X_{128-a}, Re/Im swapped)
       const int src0 = v, src1 = v + 32;
       float yv[128];
       {
         const float p0 = __shfl(L[0], src0), q0 = __shfl(L[0], src1);
-        yv[0] = 0.5f * __builtin_fmaf(sigma, q0, p0);
+        yv[0] = __builtin_fmaf(sigma, q0, p0);
       }
       sfor<63>([&](auto A) {
         constexpr int a = RTQ_CI(A) + 1;
         const float pr = __shfl(L[2 * a - 1], src0), pi = __shfl(L[2 * a], src0);
         const float qr = __shfl(L[2 * a], src1), qi = __shfl(L[2 * a - 1], src1);
-        const float fr = 0.5f * __builtin_fmaf(sigma, qr, pr);  // E (lane 0) or t (lane 1)
-        const float fi = 0.5f * __builtin_fmaf(-sigma, qi, pi);
+        const float fr = __builtin_fmaf(sigma, qr, pr);  // E (lane 0) or t (lane 1)
+        const float fi = __builtin_fmaf(-sigma, qi, pi);
         // lane 1: O_a = w^-a t_a with w^-a = c + i s; lane 0 multiplies by 1
         constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);
         const float cc = p ? c : 1.0f, ss = p ? s : 0.0f;
@@ -621,8 +621,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
       });
       {
         const float p64 = __shfl(L[127], src0), q64 = __shfl(L[127], src1);
-        constexpr float r2 = 0.70710678118654752440f;
-        yv[127] = (p ? -q64 : p64) * r2;
+        constexpr float sq2 = 1.41421356237309504880f;  // 2 / sqrt(2): L is halved
+        yv[127] = (p ? -q64 : p64) * sq2;
       }
       srft_inv<128, Sqrt2>(yv, u);
     } else {
