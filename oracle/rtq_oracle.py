@@ -340,3 +340,47 @@ def int4_roundtrip_blocks(w: np.ndarray, block_rows: int, block_cols: int) -> np
     sb = s[:, None, :, None]
     q = quantize_with_scale(t, sb)
     return (q.astype(np.float64) * sb.astype(np.float64)).reshape(r, c)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the compressed cache (the consumer that dequantizes when it
+# reads the cache: [P1, "First, the 17%"]; "Dequantize in the attention
+# consumer" is the plain composition of dequant_inv and softmax attention).
+# ---------------------------------------------------------------------------
+
+
+def cache_rows(layer: int, kv: int, stream: int, streams: int, tokens_capacity: int,
+               tokens: int) -> np.ndarray:
+    """Row indices of one (layer, K/V, stream) in the layer-major cache
+    [layer][K, V][stream][token]: ((layer * 2 + kv) * streams + stream) *
+    tokens_capacity + t for t < tokens."""
+    base = ((layer * 2 + kv) * streams + stream) * tokens_capacity
+    return base + np.arange(tokens, dtype=np.int64)
+
+
+def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, layers: int, streams: int,
+                tokens_capacity: int, tokens: int, q_per_kv: int, d: int, group: int, seed: int,
+                rows_per_seed: int = 0, seed_period: int = 0, rot: str = "srft",
+                softmax_scale: float | None = None) -> np.ndarray:
+    """One decode step of attention for every (layer, stream): q[layer, stream,
+    g] attends over the first `tokens` cached keys and values of its stream,
+    each dequantized and rotated back exactly (fp64, no fp16 rounding).
+    Returns o [layers, streams, q_per_kv, d] in fp64."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    q = np.asarray(q_f16, dtype=np.float16).astype(np.float64).reshape(layers, streams, q_per_kv, d)
+    o = np.zeros_like(q)
+    for layer in range(layers):
+        for st in range(streams):
+            u = []
+            for kv in (0, 1):
+                rows = cache_rows(layer, kv, st, streams, tokens_capacity, tokens)
+                _, uu = dequant_inv(codes[rows], scales[rows], d, group, seed, rows_per_seed, seed_period, rot,
+                                    row0=int(rows[0]), return_fp64=True)
+                u.append(uu)
+            keys, values = u
+            for g in range(q_per_kv):
+                sc = keys @ q[layer, st, g] * softmax_scale
+                w = np.exp(sc - sc.max())
+                o[layer, st, g] = (w / w.sum()) @ values
+    return o

@@ -361,3 +361,104 @@ def check_group_scales(quantize_groups):
     q, s, _ = quantize_groups(z, 64)
     assert s.astype(np.float64).tolist() == [[2.0, 2.5]], s
     assert q[0, 5] == -4 and q[0, 100] == 1
+
+
+# ---------------------------------------------------------------------------
+# Attention over the compressed cache
+# ---------------------------------------------------------------------------
+
+
+def _attn_cache(m, rng, layers, streams, tcap, d, group, seed, rps, per, rot, scale=1.0):
+    n = layers * 2 * streams * tcap
+    x = (rng.standard_normal((n, d)) * scale).astype(np.float16)
+    codes, scales = m.quant_fwd(x, group, seed, rps, per, rot)
+    return codes, scales
+
+
+def _attn_values(m, codes, scales, rows, d, group, seed, rps, per, rot):
+    return m.dequant_inv(codes[rows], scales[rows], d, group, seed, rps, per, rot, row0=int(rows[0]),
+                              return_fp64=True)[1]
+
+
+def check_attn_single_token_returns_its_value(m):
+    rng = np.random.default_rng(1)
+    L, S, Tc, d, g = 2, 3, 4, 64, 32
+    rps, per = 2 * S * Tc, L
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 77, rps, per, "srft")
+    q = rng.standard_normal((L, S, 2, d)).astype(np.float16)
+    o = m.attn_decode(q, codes, scales, L, S, Tc, 1, 2, d, g, 77, rps, per, "srft")
+    for l in range(L):
+        for s in range(S):
+            v = _attn_values(m, codes, scales, m.cache_rows(l, 1, s, S, Tc, 1), d, g, 77, rps, per, "srft")[0]
+            assert np.allclose(o[l, s, 0], v, rtol=0, atol=1e-12)
+            assert np.allclose(o[l, s, 1], v, rtol=0, atol=1e-12)
+
+
+def check_attn_identical_keys_average_values(m):
+    rng = np.random.default_rng(2)
+    L, S, Tc, T, d, g = 1, 2, 8, 5, 128, 64
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 5, 0, 0, "srht")
+    for s in range(S):
+        rows = m.cache_rows(0, 0, s, S, Tc, T)
+        codes[rows] = codes[rows[0]]
+        scales[rows] = scales[rows[0]]
+    q = rng.standard_normal((L, S, 1, d)).astype(np.float16)
+    o = m.attn_decode(q, codes, scales, L, S, Tc, T, 1, d, g, 5, 0, 0, "srht")
+    for s in range(S):
+        v = _attn_values(m, codes, scales, m.cache_rows(0, 1, s, S, Tc, T), d, g, 5, 0, 0, "srht")
+        assert np.allclose(o[0, s, 0], v.mean(axis=0), rtol=0, atol=1e-12)
+
+
+def check_attn_dominant_key_selects_its_value(m):
+    rng = np.random.default_rng(3)
+    L, S, Tc, T, d, g = 1, 1, 6, 6, 64, 64
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 9, 0, 0, "srft", scale=0.01)
+    keys = _attn_values(m, codes, scales, m.cache_rows(0, 0, 0, S, Tc, T), d, g, 9, 0, 0, "srft")
+    # a query parallel to key 3, scaled so its score dominates by a wide margin
+    q = (keys[3] / np.linalg.norm(keys[3]) * 4e4).astype(np.float16).reshape(1, 1, 1, d)
+    o = m.attn_decode(q, codes, scales, L, S, Tc, T, 1, d, g, 9, 0, 0, "srft", softmax_scale=1.0)
+    v = _attn_values(m, codes, scales, m.cache_rows(0, 1, 0, S, Tc, T), d, g, 9, 0, 0, "srft")
+    assert np.allclose(o[0, 0, 0], v[3], rtol=0, atol=1e-9)
+
+
+def check_attn_token_permutation_invariance(m):
+    rng = np.random.default_rng(4)
+    L, S, Tc, T, d, g = 1, 1, 7, 7, 64, 32
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 11, 0, 0, "srft")
+    q = rng.standard_normal((1, 1, 3, d)).astype(np.float16)
+    o1 = m.attn_decode(q, codes, scales, L, S, Tc, T, 3, d, g, 11, 0, 0, "srft")
+    perm = rng.permutation(T)
+    c2, s2 = codes.copy(), scales.copy()
+    for kv in (0, 1):
+        rows = m.cache_rows(0, kv, 0, S, Tc, T)
+        c2[rows] = codes[rows[perm]]
+        s2[rows] = scales[rows[perm]]
+    o2 = m.attn_decode(q, c2, s2, L, S, Tc, T, 3, d, g, 11, 0, 0, "srft")
+    assert np.allclose(o1, o2, rtol=0, atol=1e-12)
+
+
+def check_attn_plain_softmax_attention_on_small_case(m):
+    """Against the textbook formula on explicit per-token values."""
+    rng = np.random.default_rng(5)
+    L, S, Tc, T, d, g = 1, 1, 3, 3, 64, 64
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 13, 0, 0, "srft")
+    k = _attn_values(m, codes, scales, m.cache_rows(0, 0, 0, S, Tc, T), d, g, 13, 0, 0, "srft")
+    v = _attn_values(m, codes, scales, m.cache_rows(0, 1, 0, S, Tc, T), d, g, 13, 0, 0, "srft")
+    q16 = rng.standard_normal(d).astype(np.float16)
+    qf = q16.astype(np.float64)
+    e = [math.exp(float(np.dot(qf, k[t])) / 8.0) for t in range(T)]
+    want = sum(e[t] * v[t] for t in range(T)) / sum(e)
+    o = m.attn_decode(q16.reshape(1, 1, 1, d), codes, scales, L, S, Tc, T, 1, d, g, 13)
+    assert np.allclose(o[0, 0, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def check_attn_cache_layout(m):
+    """The documented layer-major layout [layer][K, V][stream][token]: all K
+    rows of a layer precede its V rows, streams follow each other, tokens are
+    consecutive (a layout fixture, like the nibble layout)."""
+    S, Tc = 3, 5
+    assert list(m.cache_rows(0, 0, 0, S, Tc, 2)) == [0, 1]
+    assert int(m.cache_rows(0, 0, 1, S, Tc, 1)[0]) == Tc
+    assert int(m.cache_rows(0, 1, 0, S, Tc, 1)[0]) == S * Tc
+    assert int(m.cache_rows(1, 0, 0, S, Tc, 1)[0]) == 2 * S * Tc
+    assert int(m.cache_rows(1, 1, 2, S, Tc, 1)[0]) == (2 * S + S + 2) * Tc

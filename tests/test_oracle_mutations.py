@@ -40,6 +40,12 @@ def all_pins(m):
         "nibbles": lambda: P.check_nibbles(m.pack_nibbles, m.unpack_nibbles),
         "impulse": lambda: P.check_impulse_end_to_end(m),
         "roundtrip": lambda: P.check_roundtrip_energy(m),
+        "attn_single": lambda: P.check_attn_single_token_returns_its_value(m),
+        "attn_same_keys": lambda: P.check_attn_identical_keys_average_values(m),
+        "attn_dominant": lambda: P.check_attn_dominant_key_selects_its_value(m),
+        "attn_perm": lambda: P.check_attn_token_permutation_invariance(m),
+        "attn_textbook": lambda: P.check_attn_plain_softmax_attention_on_small_case(m),
+        "attn_layout": lambda: P.check_attn_cache_layout(m),
     }
     failed = []
     for name, fn in checks.items():
@@ -94,6 +100,15 @@ MUTATIONS = {
         "return D * (z @ rotation_matrix(rot, d))", "return D * (z @ rotation_matrix(rot, d).T)"),
     "inverse forgets the signs": (
         "return D * (z @ rotation_matrix(rot, d))", "return z @ rotation_matrix(rot, d)"),
+    "attention reads values from the key rows": (
+        "            for kv in (0, 1):\n                rows = cache_rows(layer, kv, st,",
+        "            for kv in (0, 0):\n                rows = cache_rows(layer, kv, st,"),
+    "attention drops the softmax scale": (
+        "                sc = keys @ q[layer, st, g] * softmax_scale",
+        "                sc = keys @ q[layer, st, g]"),
+    "cache rows interleave K/V inside the stream": (
+        "    base = ((layer * 2 + kv) * streams + stream) * tokens_capacity",
+        "    base = ((layer * streams + stream) * 2 + kv) * tokens_capacity"),
     "forward rotates before the sign flip": (
         "u = D * x\n    return u @ rotation_matrix(rot, d).T",
         "return D * (x @ rotation_matrix(rot, d).T)"),
