@@ -349,22 +349,37 @@ def int4_roundtrip_blocks(w: np.ndarray, block_rows: int, block_cols: int) -> np
 # ---------------------------------------------------------------------------
 
 
-def cache_rows(layer: int, kv: int, stream: int, streams: int, tokens_capacity: int,
-               tokens: int) -> np.ndarray:
-    """Row indices of one (layer, K/V, stream) in the layer-major cache
-    [layer][K, V][stream][token]: ((layer * 2 + kv) * streams + stream) *
-    tokens_capacity + t for t < tokens."""
-    base = ((layer * 2 + kv) * streams + stream) * tokens_capacity
-    return base + np.arange(tokens, dtype=np.int64)
+def cache_rows(layer: int, kv: int, stream: int, tokens: int, strides) -> np.ndarray:
+    """Row indices of tokens 0 .. tokens-1 of one (layer, K/V, stream) in a
+    cache whose row of (layer, kv, stream, t) is
+    layer*strides[0] + kv*strides[1] + stream*strides[2] + t*strides[3]
+    (kv = 0 for keys, 1 for values)."""
+    sl, skv, ss, st = (int(v) for v in strides)
+    return layer * sl + kv * skv + stream * ss + st * np.arange(tokens, dtype=np.int64)
 
 
-def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, layers: int, streams: int,
-                tokens_capacity: int, tokens: int, q_per_kv: int, d: int, group: int, seed: int,
-                rows_per_seed: int = 0, seed_period: int = 0, rot: str = "srft",
-                softmax_scale: float | None = None) -> np.ndarray:
-    """One decode step of attention for every (layer, stream): q[layer, stream,
-    g] attends over the first `tokens` cached keys and values of its stream,
-    each dequantized and rotated back exactly (fp64, no fp16 rounding).
+def dequant_rows(codes: np.ndarray, scales: np.ndarray, rows: np.ndarray, d: int, group: int, seed: int,
+                 rows_per_seed: int = 0, seed_period: int = 0, rot: str = "srft") -> np.ndarray:
+    """u = D(seed'(r)) (R^T z_hat) of each listed row r, in fp64: the steps of
+    dequant_inv (unpack, dequantize, inverse rotation, sign flip) before its
+    fp16 rounding, for rows that need not be consecutive."""
+    rows = np.asarray(rows, dtype=np.int64)
+    zhat = dequantize_groups(unpack_nibbles(codes[rows]), scales[rows], group)
+    u = zhat @ rotation_matrix(rot, d)
+    row_seeds = [row_seed(seed, int(r), rows_per_seed, seed_period) for r in rows]
+    for s in set(row_seeds):
+        idx = [i for i, v in enumerate(row_seeds) if v == s]
+        u[idx] *= sign_vector(s, d)
+    return u
+
+
+def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, strides, layers: int, streams: int,
+                tokens: int, q_per_kv: int, d: int, group: int, seed: int, rows_per_seed: int = 0,
+                seed_period: int = 0, rot: str = "srft", softmax_scale: float | None = None) -> np.ndarray:
+    """One decode step of attention for every (layer, stream): query g of
+    q[layer, stream] attends over the first `tokens` cached keys and values of
+    its stream (rows from cache_rows), each dequantized and rotated back
+    exactly (fp64, no fp16 rounding); softmax_scale defaults to 1/sqrt(d).
     Returns o [layers, streams, q_per_kv, d] in fp64."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
@@ -374,10 +389,8 @@ def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, layers
         for st in range(streams):
             u = []
             for kv in (0, 1):
-                rows = cache_rows(layer, kv, st, streams, tokens_capacity, tokens)
-                _, uu = dequant_inv(codes[rows], scales[rows], d, group, seed, rows_per_seed, seed_period, rot,
-                                    row0=int(rows[0]), return_fp64=True)
-                u.append(uu)
+                rows = cache_rows(layer, kv, st, tokens, strides)
+                u.append(dequant_rows(codes, scales, rows, d, group, seed, rows_per_seed, seed_period, rot))
             keys, values = u
             for g in range(q_per_kv):
                 sc = keys @ q[layer, st, g] * softmax_scale

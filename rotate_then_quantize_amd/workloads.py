@@ -43,6 +43,7 @@ class Workload:
     outlier_scale: float = 1.0
     fixed_channels: tuple = ()
     new_tokens: int = 0   # decode: rows quantized per step = new_tokens * layers * kv * streams
+    q_per_kv: int = 1     # query heads per K/V head of the model (grouped-query attention)
 
     @property
     def n_rows(self) -> int:
@@ -59,6 +60,14 @@ class Workload:
     @property
     def seed_period(self) -> int:
         return self.layers if self.layers > 1 else 0
+
+    @property
+    def cache_strides(self) -> tuple:
+        """Row of (layer, kv, stream, token) = layer*s0 + kv*s1 + stream*s2 +
+        token*s3 in this workload's layout."""
+        if self.layout == "layer_major":
+            return (self.kv * self.streams * self.tokens, self.streams * self.tokens, self.tokens, 1)
+        return (self.kv * self.streams, self.streams, 1, self.layers * self.kv * self.streams)
 
     @property
     def sign_seed(self) -> int:
@@ -84,15 +93,15 @@ WORKLOADS = {
                 fixed_channels=(3, 17)),
     2: Workload(2, "smollm2_360m_prefill_kv", d=64, group=32, rots=("srft",), layers=32, kv=2, streams=5,
                 tokens=4096, layout="layer_major", dist="normal", outlier="per_stream", outlier_count=2,
-                outlier_scale=15.0),
+                outlier_scale=15.0, q_per_kv=3),
     3: Workload(3, "qwen2.5_1.5b_decode_kv", d=128, group=32, rots=("srft",), layers=28, kv=2, streams=64 * 2,
-                tokens=2049, layout="time_major", dist="student_t3", outlier="none", new_tokens=1),
+                tokens=2049, layout="time_major", dist="student_t3", outlier="none", new_tokens=1, q_per_kv=6),
     4: Workload(4, "smollm2_1.7b_kv", d=64, group=64, rots=("srft", "srht"), layers=24, kv=2, streams=32,
                 tokens=2048, layout="layer_major", dist="normal", outlier="bernoulli", outlier_prob=0.01,
                 outlier_scale=20.0),
     5: Workload(5, "gemma3_1b_long_kv", d=256, group=32, rots=("srft",), layers=26, kv=2, streams=16,
                 tokens=32768, layout="layer_major", dist="normal", outlier="per_layer", outlier_count=4,
-                outlier_scale=25.0),
+                outlier_scale=25.0, q_per_kv=4),
 }
 
 

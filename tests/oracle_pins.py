@@ -368,6 +368,16 @@ def check_group_scales(quantize_groups):
 # ---------------------------------------------------------------------------
 
 
+def _lm(streams, tcap):
+    """Strides of the layer-major cache [layer][K, V][stream][token]."""
+    return (2 * streams * tcap, streams * tcap, tcap, 1)
+
+
+def _tm(layers, streams):
+    """Strides of the time-major cache [token][layer][K, V][stream]."""
+    return (2 * streams, streams, 1, 2 * layers * streams)
+
+
 def _attn_cache(m, rng, layers, streams, tcap, d, group, seed, rps, per, rot, scale=1.0):
     n = layers * 2 * streams * tcap
     x = (rng.standard_normal((n, d)) * scale).astype(np.float16)
@@ -376,36 +386,54 @@ def _attn_cache(m, rng, layers, streams, tcap, d, group, seed, rps, per, rot, sc
 
 
 def _attn_values(m, codes, scales, rows, d, group, seed, rps, per, rot):
-    return m.dequant_inv(codes[rows], scales[rows], d, group, seed, rps, per, rot, row0=int(rows[0]),
-                              return_fp64=True)[1]
+    """Rows dequantized one at a time through dequant_inv (row0 = the row)."""
+    return np.stack([m.dequant_inv(codes[r:r + 1], scales[r:r + 1], d, group, seed, rps, per, rot, row0=int(r),
+                                   return_fp64=True)[1][0] for r in rows])
+
+
+def check_attn_dequant_rows_match_rowwise_inverse(m):
+    """dequant_rows on scattered rows of different seeds equals dequant_inv
+    applied to each row on its own (before the fp16 rounding)."""
+    rng = np.random.default_rng(6)
+    n, d, g = 40, 64, 32
+    x = rng.standard_normal((n, d)).astype(np.float16)
+    codes, scales = m.quant_fwd(x, g, 21, 4, 3, "srft")
+    rows = np.array([37, 0, 5, 12, 13, 22, 9, 30])
+    got = m.dequant_rows(codes, scales, rows, d, g, 21, 4, 3, "srft")
+    want = _attn_values(m, codes, scales, rows, d, g, 21, 4, 3, "srft")
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
 
 
 def check_attn_single_token_returns_its_value(m):
+    """With one cached token the softmax weight is 1: o is that token's value
+    row, whatever the query (both layouts, per-layer seeds)."""
     rng = np.random.default_rng(1)
     L, S, Tc, d, g = 2, 3, 4, 64, 32
-    rps, per = 2 * S * Tc, L
-    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 77, rps, per, "srft")
-    q = rng.standard_normal((L, S, 2, d)).astype(np.float16)
-    o = m.attn_decode(q, codes, scales, L, S, Tc, 1, 2, d, g, 77, rps, per, "srft")
-    for l in range(L):
-        for s in range(S):
-            v = _attn_values(m, codes, scales, m.cache_rows(l, 1, s, S, Tc, 1), d, g, 77, rps, per, "srft")[0]
-            assert np.allclose(o[l, s, 0], v, rtol=0, atol=1e-12)
-            assert np.allclose(o[l, s, 1], v, rtol=0, atol=1e-12)
+    for strides, rps in ((_lm(S, Tc), 2 * S * Tc), (_tm(L, S), 2 * S)):
+        codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 77, rps, L, "srft")
+        q = rng.standard_normal((L, S, 2, d)).astype(np.float16)
+        o = m.attn_decode(q, codes, scales, strides, L, S, 1, 2, d, g, 77, rps, L, "srft")
+        for l in range(L):
+            for s in range(S):
+                row = l * strides[0] + strides[1] + s * strides[2]
+                v = _attn_values(m, codes, scales, [row], d, g, 77, rps, L, "srft")[0]
+                assert np.allclose(o[l, s, 0], v, rtol=0, atol=1e-12)
+                assert np.allclose(o[l, s, 1], v, rtol=0, atol=1e-12)
 
 
 def check_attn_identical_keys_average_values(m):
     rng = np.random.default_rng(2)
     L, S, Tc, T, d, g = 1, 2, 8, 5, 128, 64
+    st = _lm(S, Tc)
     codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 5, 0, 0, "srht")
     for s in range(S):
-        rows = m.cache_rows(0, 0, s, S, Tc, T)
+        rows = [s * Tc + t for t in range(T)]
         codes[rows] = codes[rows[0]]
         scales[rows] = scales[rows[0]]
     q = rng.standard_normal((L, S, 1, d)).astype(np.float16)
-    o = m.attn_decode(q, codes, scales, L, S, Tc, T, 1, d, g, 5, 0, 0, "srht")
+    o = m.attn_decode(q, codes, scales, st, L, S, T, 1, d, g, 5, 0, 0, "srht")
     for s in range(S):
-        v = _attn_values(m, codes, scales, m.cache_rows(0, 1, s, S, Tc, T), d, g, 5, 0, 0, "srht")
+        v = _attn_values(m, codes, scales, [S * Tc + s * Tc + t for t in range(T)], d, g, 5, 0, 0, "srht")
         assert np.allclose(o[0, s, 0], v.mean(axis=0), rtol=0, atol=1e-12)
 
 
@@ -413,11 +441,11 @@ def check_attn_dominant_key_selects_its_value(m):
     rng = np.random.default_rng(3)
     L, S, Tc, T, d, g = 1, 1, 6, 6, 64, 64
     codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 9, 0, 0, "srft", scale=0.01)
-    keys = _attn_values(m, codes, scales, m.cache_rows(0, 0, 0, S, Tc, T), d, g, 9, 0, 0, "srft")
+    keys = _attn_values(m, codes, scales, range(T), d, g, 9, 0, 0, "srft")
     # a query parallel to key 3, scaled so its score dominates by a wide margin
     q = (keys[3] / np.linalg.norm(keys[3]) * 4e4).astype(np.float16).reshape(1, 1, 1, d)
-    o = m.attn_decode(q, codes, scales, L, S, Tc, T, 1, d, g, 9, 0, 0, "srft", softmax_scale=1.0)
-    v = _attn_values(m, codes, scales, m.cache_rows(0, 1, 0, S, Tc, T), d, g, 9, 0, 0, "srft")
+    o = m.attn_decode(q, codes, scales, _lm(S, Tc), L, S, T, 1, d, g, 9, 0, 0, "srft", softmax_scale=1.0)
+    v = _attn_values(m, codes, scales, range(Tc, Tc + T), d, g, 9, 0, 0, "srft")
     assert np.allclose(o[0, 0, 0], v[3], rtol=0, atol=1e-9)
 
 
@@ -426,14 +454,14 @@ def check_attn_token_permutation_invariance(m):
     L, S, Tc, T, d, g = 1, 1, 7, 7, 64, 32
     codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 11, 0, 0, "srft")
     q = rng.standard_normal((1, 1, 3, d)).astype(np.float16)
-    o1 = m.attn_decode(q, codes, scales, L, S, Tc, T, 3, d, g, 11, 0, 0, "srft")
+    o1 = m.attn_decode(q, codes, scales, _lm(S, Tc), L, S, T, 3, d, g, 11, 0, 0, "srft")
     perm = rng.permutation(T)
     c2, s2 = codes.copy(), scales.copy()
-    for kv in (0, 1):
-        rows = m.cache_rows(0, kv, 0, S, Tc, T)
+    for base in (0, Tc):
+        rows = np.arange(base, base + T)
         c2[rows] = codes[rows[perm]]
         s2[rows] = scales[rows[perm]]
-    o2 = m.attn_decode(q, c2, s2, L, S, Tc, T, 3, d, g, 11, 0, 0, "srft")
+    o2 = m.attn_decode(q, c2, s2, _lm(S, Tc), L, S, T, 3, d, g, 11, 0, 0, "srft")
     assert np.allclose(o1, o2, rtol=0, atol=1e-12)
 
 
@@ -442,23 +470,27 @@ def check_attn_plain_softmax_attention_on_small_case(m):
     rng = np.random.default_rng(5)
     L, S, Tc, T, d, g = 1, 1, 3, 3, 64, 64
     codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 13, 0, 0, "srft")
-    k = _attn_values(m, codes, scales, m.cache_rows(0, 0, 0, S, Tc, T), d, g, 13, 0, 0, "srft")
-    v = _attn_values(m, codes, scales, m.cache_rows(0, 1, 0, S, Tc, T), d, g, 13, 0, 0, "srft")
+    k = _attn_values(m, codes, scales, range(T), d, g, 13, 0, 0, "srft")
+    v = _attn_values(m, codes, scales, range(Tc, Tc + T), d, g, 13, 0, 0, "srft")
     q16 = rng.standard_normal(d).astype(np.float16)
     qf = q16.astype(np.float64)
     e = [math.exp(float(np.dot(qf, k[t])) / 8.0) for t in range(T)]
     want = sum(e[t] * v[t] for t in range(T)) / sum(e)
-    o = m.attn_decode(q16.reshape(1, 1, 1, d), codes, scales, L, S, Tc, T, 1, d, g, 13)
+    o = m.attn_decode(q16.reshape(1, 1, 1, d), codes, scales, _lm(S, Tc), L, S, T, 1, d, g, 13)
     assert np.allclose(o[0, 0, 0], want, rtol=1e-12, atol=1e-12)
 
 
 def check_attn_cache_layout(m):
-    """The documented layer-major layout [layer][K, V][stream][token]: all K
-    rows of a layer precede its V rows, streams follow each other, tokens are
-    consecutive (a layout fixture, like the nibble layout)."""
-    S, Tc = 3, 5
-    assert list(m.cache_rows(0, 0, 0, S, Tc, 2)) == [0, 1]
-    assert int(m.cache_rows(0, 0, 1, S, Tc, 1)[0]) == Tc
-    assert int(m.cache_rows(0, 1, 0, S, Tc, 1)[0]) == S * Tc
-    assert int(m.cache_rows(1, 0, 0, S, Tc, 1)[0]) == 2 * S * Tc
-    assert int(m.cache_rows(1, 1, 2, S, Tc, 1)[0]) == (2 * S + S + 2) * Tc
+    """Enumerating (layer, kv, stream, token) through cache_rows visits every
+    row once, in the order [layer][kv][stream][token] for the layer-major
+    strides and [token][layer][kv][stream] for the time-major ones."""
+    L, S, T = 2, 3, 4
+    lm = [int(r) for l in range(L) for kv in (0, 1) for s in range(S) for r in m.cache_rows(l, kv, s, T, _lm(S, T))]
+    assert lm == list(range(L * 2 * S * T))
+    tm = {}
+    for l in range(L):
+        for kv in (0, 1):
+            for s in range(S):
+                for t, r in enumerate(m.cache_rows(l, kv, s, T, _tm(L, S))):
+                    tm[(t, l, kv, s)] = int(r)
+    assert [tm[k] for k in sorted(tm)] == list(range(L * 2 * S * T))

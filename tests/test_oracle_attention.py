@@ -30,3 +30,7 @@ def test_plain_softmax_attention_on_small_case():
 
 def test_cache_layout():
     P.check_attn_cache_layout(oracle)
+
+
+def test_dequant_rows_match_rowwise_inverse():
+    P.check_attn_dequant_rows_match_rowwise_inverse(oracle)

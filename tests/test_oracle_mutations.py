@@ -46,6 +46,7 @@ def all_pins(m):
         "attn_perm": lambda: P.check_attn_token_permutation_invariance(m),
         "attn_textbook": lambda: P.check_attn_plain_softmax_attention_on_small_case(m),
         "attn_layout": lambda: P.check_attn_cache_layout(m),
+        "attn_rows": lambda: P.check_attn_dequant_rows_match_rowwise_inverse(m),
     }
     failed = []
     for name, fn in checks.items():
@@ -103,12 +104,16 @@ MUTATIONS = {
     "attention reads values from the key rows": (
         "            for kv in (0, 1):\n                rows = cache_rows(layer, kv, st,",
         "            for kv in (0, 0):\n                rows = cache_rows(layer, kv, st,"),
+    "attention rows use one seed for every row": (
+        "    row_seeds = [row_seed(seed, int(r), rows_per_seed, seed_period) for r in rows]",
+        "    row_seeds = [row_seed(seed, int(rows[0]), rows_per_seed, seed_period) for r in rows]"),
+    "attention rows skip the sign flip": ("        u[idx] *= sign_vector(s, d)", "        u[idx] *= 1.0"),
     "attention drops the softmax scale": (
         "                sc = keys @ q[layer, st, g] * softmax_scale",
         "                sc = keys @ q[layer, st, g]"),
-    "cache rows interleave K/V inside the stream": (
-        "    base = ((layer * 2 + kv) * streams + stream) * tokens_capacity",
-        "    base = ((layer * streams + stream) * 2 + kv) * tokens_capacity"),
+    "cache rows swap the kv and stream strides": (
+        "    return layer * sl + kv * skv + stream * ss + st * np.arange(tokens, dtype=np.int64)",
+        "    return layer * sl + kv * ss + stream * skv + st * np.arange(tokens, dtype=np.int64)"),
     "forward rotates before the sign flip": (
         "u = D * x\n    return u @ rotation_matrix(rot, d).T",
         "return D * (x @ rotation_matrix(rot, d).T)"),
