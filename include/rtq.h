@@ -126,6 +126,59 @@ rtq_status srht_dequant_inv(const void* codes_u8, const void* scales_f16, void* 
                             int64_t rows_per_seed, int32_t seed_period,
                             hipStream_t stream);
 
+/*
+ * srft_attn_decode / srht_attn_decode -- one decode step of softmax attention
+ * that reads the int4 cache written by srft_quant_fwd / srht_quant_fwd
+ * directly: the cache is dequantized and rotated back when attention reads
+ * it ("Quantization Speed Is Often a Kernel Problem", "First, the 17%"), here
+ * inside the attention kernel, so no fp16 K/V is written to memory.
+ *
+ * For every layer l < layers, stream s < streams (a batch entry times a K/V
+ * head) and query g < q_per_kv, with keys k_t and values v_t the dequantized,
+ * inverse-rotated, sign-flipped rows (what *_dequant_inv returns before its
+ * fp16 rounding) of tokens t < tokens:
+ *   out[l][s][g] = fp16( sum_t w_t v_t ),
+ *   w_t = exp(c_t - max c) / sum_t' exp(c_t' - max c),
+ *   c_t = softmax_scale * (q[l][s][g] . k_t).
+ * The kernel uses R's orthogonality: it rotates each query with the keys'
+ * sign vector (q . k_t = (R D q) . z_t) and rotates the weighted sum of the
+ * rotated values back once per query.
+ *
+ *   q_f16      in : [layers][streams][q_per_kv][d] fp16
+ *   codes_u8   in : the cache codes, rows of d/2 bytes (layout as above)
+ *   scales_f16 in : the cache scales, rows of d/group fp16
+ *   out_f16    out: [layers][streams][q_per_kv][d] fp16
+ *   Row of (layer l, kv, stream s, token t), kv = 0 for keys and 1 for values:
+ *     l*stride_layer + kv*stride_kv + s*stride_stream + t*stride_token
+ *   (a layer-major cache [layer][K,V][stream][token] of capacity C has
+ *   strides (2*streams*C, streams*C, C, 1); a time-major one
+ *   [token][layer][K,V][stream] has (2*streams, streams, 1, 2*layers*streams)).
+ *   seed, rows_per_seed, seed_period: the rule the cache was written with.
+ *   Every key row of one (layer, stream) must have the same seed, and every
+ *   value row likewise (true for one seed per layer, or per layer and K/V);
+ *   otherwise RTQ_ERR_INVALID_ARG.
+ *
+ * Supported: (d, group) in {(64,32), (64,64), (128,32), (128,64), (128,128)}
+ * and 1 <= q_per_kv <= 8, else RTQ_ERR_UNSUPPORTED.  tokens >= 1, strides >= 0,
+ * layers <= 65535, softmax_scale finite, else RTQ_ERR_INVALID_ARG; layers == 0
+ * or streams == 0 returns RTQ_OK and touches nothing.  The caller guarantees
+ * that the cache holds every row the strides reach; out must not overlap the
+ * inputs.  Pointers, streams and error behaviour as in the common conventions.
+ * Numerics: scores keep about 22 bits (fp16 hi/lo query, exact int4 keys,
+ * fp32 scaling); values and softmax weights enter the weighted sum as fp16.
+ */
+rtq_status srft_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
+                            int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
+                            int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
+                            int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                            float softmax_scale, hipStream_t stream);
+
+rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
+                            int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
+                            int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
+                            int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                            float softmax_scale, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtq_status_string(rtq_status status);
 

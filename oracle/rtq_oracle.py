@@ -375,25 +375,27 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray, rows: np.ndarray, d: int
 
 def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, strides, layers: int, streams: int,
                 tokens: int, q_per_kv: int, d: int, group: int, seed: int, rows_per_seed: int = 0,
-                seed_period: int = 0, rot: str = "srft", softmax_scale: float | None = None) -> np.ndarray:
+                seed_period: int = 0, rot: str = "srft", softmax_scale: float | None = None,
+                pairs=None) -> np.ndarray:
     """One decode step of attention for every (layer, stream): query g of
     q[layer, stream] attends over the first `tokens` cached keys and values of
     its stream (rows from cache_rows), each dequantized and rotated back
     exactly (fp64, no fp16 rounding); softmax_scale defaults to 1/sqrt(d).
-    Returns o [layers, streams, q_per_kv, d] in fp64."""
+    Returns o [layers, streams, q_per_kv, d] in fp64 (entries of (layer,
+    stream) pairs outside `pairs`, when a list is given, stay zero)."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     q = np.asarray(q_f16, dtype=np.float16).astype(np.float64).reshape(layers, streams, q_per_kv, d)
     o = np.zeros_like(q)
-    for layer in range(layers):
-        for st in range(streams):
-            u = []
-            for kv in (0, 1):
-                rows = cache_rows(layer, kv, st, tokens, strides)
-                u.append(dequant_rows(codes, scales, rows, d, group, seed, rows_per_seed, seed_period, rot))
-            keys, values = u
-            for g in range(q_per_kv):
-                sc = keys @ q[layer, st, g] * softmax_scale
-                w = np.exp(sc - sc.max())
-                o[layer, st, g] = (w / w.sum()) @ values
+    todo = [(l, s) for l in range(layers) for s in range(streams)] if pairs is None else list(pairs)
+    for layer, st in todo:
+        u = []
+        for kv in (0, 1):
+            rows = cache_rows(layer, kv, st, tokens, strides)
+            u.append(dequant_rows(codes, scales, rows, d, group, seed, rows_per_seed, seed_period, rot))
+        keys, values = u
+        for g in range(q_per_kv):
+            sc = keys @ q[layer, st, g] * softmax_scale
+            w = np.exp(sc - sc.max())
+            o[layer, st, g] = (w / w.sum()) @ values
     return o

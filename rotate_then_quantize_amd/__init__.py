@@ -20,7 +20,8 @@ import os
 
 __all__ = [
     "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
-    "RTQError", "library", "library_path", "SUPPORTED",
+    "srft_attn_decode", "srht_attn_decode",
+    "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -30,6 +31,9 @@ _lib = None
 RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_HIP = 0, 1, 2, 3
 # (d, group) pairs the library is built for
 SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+# (d, group) pairs of the decode-attention kernels; at most 8 query heads per K/V head
+ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
+ATTN_MAX_Q_PER_KV = 8
 
 
 class RTQError(RuntimeError):
@@ -55,6 +59,14 @@ def library():
         for name in ("srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv"):
             fn = getattr(lib, name)
             fn.argtypes = fwd_args
+            fn.restype = ctypes.c_int
+        attn_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                     ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                     ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+        for name in ("srft_attn_decode", "srht_attn_decode"):
+            fn = getattr(lib, name)
+            fn.argtypes = attn_args
             fn.restype = ctypes.c_int
         lib.rtq_status_string.argtypes = [ctypes.c_int]
         lib.rtq_status_string.restype = ctypes.c_char_p
@@ -145,6 +157,62 @@ def srht_quant_fwd(x, group, seed, rows_per_seed=0, seed_period=0, codes=None, s
 def srht_dequant_inv(codes, scales, d, group, seed, rows_per_seed=0, seed_period=0, out=None, stream=None):
     """Inverse step with the SRHT (Walsh-Hadamard) control rotation."""
     return _inv("srht_dequant_inv", codes, scales, d, group, seed, rows_per_seed, seed_period, out, stream)
+
+
+def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period, softmax_scale,
+          out, stream):
+    import math
+    import torch
+    _need(q, torch.float16, "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [layers, streams, q_per_kv, d]")
+    layers, streams, q_per_kv, d = q.shape
+    _need(codes, torch.uint8, "codes")
+    if codes.dim() != 2 or codes.shape[1] * 2 != d:
+        raise ValueError("codes must be [n, d/2]")
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    _need(scales, torch.float16, "scales", (codes.shape[0], d // group))
+    strides = tuple(int(v) for v in strides)
+    if len(strides) != 4 or min(strides) < 0:
+        raise ValueError("strides must be four non-negative row counts (layer, kv, stream, token)")
+    if tokens < 1:
+        raise ValueError("tokens must be at least 1")
+    if layers and streams:
+        max_row = (layers - 1) * strides[0] + strides[1] + (streams - 1) * strides[2] + (tokens - 1) * strides[3]
+        if max_row >= codes.shape[0]:
+            raise ValueError(f"the cache has {codes.shape[0]} rows; the strides reach row {max_row}")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, torch.float16, "out", tuple(q.shape))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), layers, streams, tokens, q_per_kv, d, group, *strides,
+        seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale), _stream_handle(q, stream)))
+    return out
+
+
+def srft_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
+                     softmax_scale=None, out=None, stream=None):
+    """One decode step of attention over an SRFT int4 cache: q [layers, streams, q_per_kv, d] fp16
+    attends over tokens 0..tokens-1 of its stream, whose key / value row is
+    layer*strides[0] + kv*strides[1] + stream*strides[2] + token*strides[3] (kv 0 = K, 1 = V).
+    Returns o like q (fp16); softmax_scale defaults to 1/sqrt(d)."""
+    return _attn("srft_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
+                 softmax_scale, out, stream)
+
+
+def srht_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
+                     softmax_scale=None, out=None, stream=None):
+    """srft_attn_decode over an SRHT (Walsh-Hadamard) int4 cache."""
+    return _attn("srht_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
+                 softmax_scale, out, stream)
+
+
+def attn_decode(rot, *args, **kw):
+    return (srft_attn_decode if rot == "srft" else srht_attn_decode)(*args, **kw)
 
 
 def quant_fwd(rot, *args, **kw):

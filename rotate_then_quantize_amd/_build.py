@@ -8,8 +8,9 @@ import subprocess
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 LIB_PATH = os.path.join(PKG_DIR, "librtq.so")
-SOURCES = [os.path.join(PKG_DIR, "csrc", "rtq.hip")]
-HEADERS = [os.path.join(PKG_DIR, "csrc", "rtq_device.hpp"), os.path.join(PKG_DIR, "csrc", "rtq_div.hpp"), os.path.join(ROOT, "include", "rtq.h")]
+SOURCES = [os.path.join(PKG_DIR, "csrc", "rtq.hip"), os.path.join(PKG_DIR, "csrc", "rtq_attn.hip")]
+HEADERS = [os.path.join(PKG_DIR, "csrc", "rtq_device.hpp"), os.path.join(PKG_DIR, "csrc", "rtq_div.hpp"),
+           os.path.join(PKG_DIR, "csrc", "rtq_mem.hpp"), os.path.join(ROOT, "include", "rtq.h")]
 
 
 def hipcc_command(out: str = LIB_PATH, extra: list[str] | None = None) -> list[str]:

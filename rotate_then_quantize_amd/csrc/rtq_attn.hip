@@ -1,0 +1,627 @@
+// rtq_attn.hip -- one decode step of attention that reads the int4 rotated
+// K/V cache directly (MI355X, gfx950), and its C ABI entry points.
+//
+// The method stores every K/V vector rotated and int4-quantized and
+// dequantizes and rotates it back when attention reads it ("Quantization
+// Speed Is Often a Kernel Problem", "First, the 17%").  Here the dequantize
+// happens in registers inside the attention kernel, so no fp16 K/V ever
+// lands in HBM (the fusion of dequantization into the consumer, "Chapter
+// 25 - Quantization: The Hardware View", section "Kernels: Marlin, CUTLASS,
+// and Why INT4 Packing Needs Special Code").
+//
+// R is orthogonal and each stream's keys share one sign vector D_K (values
+// one D_V), so with y = R D_K q and z_t = the dequantized rotated key,
+//   q . k_t = y . z_t   and   sum_t p_t v_t = D_V R^T (sum_t p_t z^V_t).
+// The kernel rotates each query once, runs softmax attention in the rotated
+// domain, and rotates one output vector back per query, instead of
+// inverse-rotating every cached vector.
+//
+// Mapping to CDNA4 (d = 64 / 128; q_per_kv <= 8):
+//   * One workgroup of 4 waves per (layer, stream); the waves split the
+//     tokens into 32-token chunks and merge their softmax partials in LDS.
+//   * Each chunk's code and scale rows arrive by direct-to-LDS loads
+//     (global_load_lds), three chunks in flight per wave.  Rows may sit
+//     anywhere (the cache layout is given by strides).
+//   * q.k is a [16 tokens x 32 dims] x [32 dims x 16 columns] MFMA
+//     (v_mfma_f32_16x16x32_f16) per group of 32 dims.  The A operand is the
+//     exact int4 code value as fp16 (no scale), so each group's partial dot
+//     product is scaled by its fp16 scale in fp32 afterwards.  The query
+//     operand carries the rotated query split into an fp16 high part
+//     (columns 0..7) and low part (columns 8..15); one DPP add merges them,
+//     so scores keep about 22 bits.
+//   * p.v runs as O^T = V^T P^T per 16 output dims (v_mfma_f32_16x16x32_f16
+//     over 32 tokens), with V decoded as fp16 (q * s / 16: the 1/16 keeps
+//     every value finite for any fp16 scale) and P in fp16.  The P operand
+//     is the q.k result layout itself, and O^T columns are queries, so the
+//     online-softmax rescale stays in the lane that owns the query.
+//   * int4 -> fp16 takes one v_bitop3 per pair of codes (mask, bias and
+//     fp16 exponent at once) and one packed fp16 add or fma.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "rtq.h"
+#include "rtq_device.hpp"
+#include "rtq_mem.hpp"
+
+namespace rtq {
+namespace attn {
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;      // waves per workgroup; they split the tokens
+constexpr int kChunk = 32;     // tokens per chunk (one p.v k-step)
+constexpr int kBufs = 3;       // chunk buffers per wave
+constexpr int kMaxQ = 8;       // query heads per K/V head
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, below any score
+constexpr float kVShift = 0.0625f;   // V is decoded as q * s / 16
+
+struct Params {
+  const uint4* q;        // [layers][streams][q_per_kv][d] fp16
+  const uint8_t* codes;  // rows of d/2 bytes
+  const uint8_t* scales; // rows of 2*d/group bytes
+  uint4* out;            // like q
+  int64_t stride_layer, stride_kv, stride_stream, stride_token;  // in rows
+  uint64_t seed;
+  int64_t rows_per_seed;
+  int32_t seed_period;
+  int32_t tokens, q_per_kv;
+  float qscale;  // softmax_scale * log2(e): scores come out in base-2 units
+};
+
+template <int D, int GR>
+struct Cfg {
+  static constexpr int KS = D / 32;       // q.k k-steps = 16-byte pieces per code row
+  static constexpr int NT = D / 16;       // p.v output tiles of 16 dims
+  static constexpr int RB = D / 2;        // code bytes per row
+  static constexpr int SPR = D / GR;      // scales per row
+  static constexpr int SLOT = SPR == 4 ? 8 : 4;  // LDS bytes per token of scales
+  static constexpr int CODE_BYTES = kChunk * RB;
+  static constexpr int SCALE_BYTES = kChunk * SLOT;
+  static constexpr int BUF = 2 * CODE_BYTES + 2 * SCALE_BYTES;  // K codes, V codes, K scales, V scales
+  static constexpr int CODE_DMA = CODE_BYTES / 1024;             // 16-byte loads per chunk per K or V
+  static constexpr int NDMA = 2 * CODE_DMA + (SPR == 4 ? 2 : 1);
+  static constexpr int QROW = D + 4;  // fp32 row stride of the query / output staging
+  static constexpr int SLOT_ARRAY = kWaves * BUF;  // one ring slot of every wave
+  static constexpr int COMBINE = kWaves * kMaxQ * QROW * 4 + 2 * kWaves * kMaxQ * 4;
+  static_assert(COMBINE <= SLOT_ARRAY, "the merge area fits in ring slot 0");
+  static_assert(GR >= 32 && D % GR == 0, "groups of at least 32 values");
+};
+
+// Token row r of a chunk sits in LDS row lrow(r) (an involution), and 16-byte
+// piece k of LDS row L in slot k ^ swz(L).  For d = 128 this makes both the
+// q.k reads (16 rows x 4 lanes) and the p.v reads (4 rows x 16 lanes) hit 64
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int lrow(int r) {
+  return D == 128 ? (r ^ ((r >> 2) & 3)) : r;
+}
+template <int D>
+__device__ __forceinline__ int swz(int lr) {
+  return D == 128 ? ((lr >> 2) & 3) : ((lr >> 3) & 1);
+}
+
+__device__ __forceinline__ f16x2_t as_h2(uint32_t w) { return __builtin_bit_cast(f16x2_t, w); }
+__device__ __forceinline__ uint32_t as_u32(f16x2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+// Codes K and K+4 of a code word (low and high half of the result) as exact
+// fp16 integers in [-8, 7].  K even: mask bits 4K'..4K'+3 of each half into
+// the fp16 mantissa under the exponent of 1024 with the sign bit of the code
+// flipped (one v_bitop3), giving 1032 + q; subtract 1032.  K odd: the code
+// sits 4 bits higher, giving 1152 + 16 q; scale by 1/16 and subtract 72.
+template <int K>
+__device__ __forceinline__ f16x2_t code_pair(uint32_t w) {
+  const uint32_t x = K >= 2 ? w >> 8 : w;
+  if constexpr ((K & 1) == 0) {
+    return as_h2((x & 0x000f000fu) ^ 0x64086408u) + (f16x2_t){(_Float16)-1032.0f, (_Float16)-1032.0f};
+  } else {
+    return __builtin_elementwise_fma(as_h2((x & 0x00f000f0u) ^ 0x64806480u),
+                                     (f16x2_t){(_Float16)0.0625f, (_Float16)0.0625f},
+                                     (f16x2_t){(_Float16)-72.0f, (_Float16)-72.0f});
+  }
+}
+
+__device__ __forceinline__ f16x8_t pack8(f16x2_t a, f16x2_t b, f16x2_t c, f16x2_t d) {
+  const u32x4v_t w = {as_u32(a), as_u32(b), as_u32(c), as_u32(d)};
+  return __builtin_bit_cast(f16x8_t, w);
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+__device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// x + (x of the lane 8 places further in the same row of 16 lanes).
+__device__ __forceinline__ float add_ror8(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false);
+  return x + __int_as_float(y);
+}
+
+__device__ __forceinline__ uint64_t seed_of_row(const Params& p, int64_t row) {
+  return row_seed(p.seed, row, p.rows_per_seed, p.seed_period);
+}
+
+// Sign masks of one seed for the D/2 packed pairs, the same in every lane.
+template <int D>
+__device__ __forceinline__ void wave_sign_masks(uint64_t s, int lane, uint32_t (&m)[D / 2]) {
+  sfor<D / 64>([&](auto Q) {
+    constexpr int q = RTQ_CI(Q);
+    const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
+    sfor<32>([&](auto M) {
+      const uint32_t v = (uint32_t)(bits >> (2 * RTQ_CI(M))) & 3u;
+      m[32 * q + RTQ_CI(M)] = (v * 0x40008000u) & 0x80008000u;
+    });
+  });
+}
+
+// One direct-to-LDS load (nt): lane i's BYTES bytes from g land at LDS byte
+// lds + BYTES * i.  Written as inline asm so that the compiler, which cannot
+// tell the ring slots apart, does not add a full vmcnt wait before every LDS
+// read; the kernel waits for each chunk itself (wait_vmcnt).  The asm has no
+// register outputs.
+// A 2-byte load fills the whole 4-byte slot of its lane (zero-extended).
+template <int BYTES>
+__device__ __forceinline__ void dma_to_lds(const void* g, const void* lds) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds);  // wave-uniform
+  if constexpr (BYTES == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
+  else if constexpr (BYTES == 4)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
+}
+
+// Direct-to-LDS loads of chunk tokens tok0 .. tok0+31 (tokens past the end
+// reload the last token; their scores are masked).
+template <int D, int GR>
+__device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int64_t row_v, int tok0, uint8_t* buf,
+                                            int lane) {
+  using C = Cfg<D, GR>;
+  constexpr int PPR = C::RB / 16;  // pieces per row
+  constexpr int RPI = 64 / PPR;    // LDS rows per load instruction
+  const int last = p.tokens - 1;
+  sfor<C::CODE_DMA>([&](auto I) {
+    const int lr = RTQ_CI(I) * RPI + lane / PPR;
+    const int r = lrow<D>(lr);
+    const int piece = (lane % PPR) ^ swz<D>(lr);
+    const int t = tok0 + r < last ? tok0 + r : last;
+    const int64_t off = (int64_t)t * p.stride_token;
+    const uint8_t* gk = p.codes + (row_k + off) * C::RB + 16 * piece;
+    const uint8_t* gv = p.codes + (row_v + off) * C::RB + 16 * piece;
+    dma_to_lds<16>(gk, buf + RTQ_CI(I) * 1024);
+    dma_to_lds<16>(gv, buf + C::CODE_BYTES + RTQ_CI(I) * 1024);
+  });
+  uint8_t* sb = buf + 2 * C::CODE_BYTES;
+  if constexpr (C::SPR == 4) {
+    // 8 bytes per token: lane l loads word l & 1 of token l / 2
+    const int t = tok0 + lane / 2 < last ? tok0 + lane / 2 : last;
+    const int64_t off = (int64_t)t * p.stride_token;
+    dma_to_lds<4>(p.scales + (row_k + off) * 8 + 4 * (lane & 1), sb);
+    dma_to_lds<4>(p.scales + (row_v + off) * 8 + 4 * (lane & 1), sb + C::SCALE_BYTES);
+  } else {
+    // one 4-byte slot per token (2 or 4 bytes of scales): lanes 0..31 keys, 32..63 values
+    const int r = lane & 31;
+    const int t = tok0 + r < last ? tok0 + r : last;
+    const int64_t row = (lane < 32 ? row_k : row_v) + (int64_t)t * p.stride_token;
+    dma_to_lds<2 * C::SPR>(p.scales + row * (2 * C::SPR), sb);
+  }
+}
+
+template <int D, int GR, int ROT>
+__global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
+  using C = Cfg<D, GR>;
+  // Three ring slots as three LDS arrays: the compiler then tells the
+  // direct-to-LDS loads of one slot from the reads of another and waits only
+  // for the chunk being read.
+  __shared__ __attribute__((aligned(16))) uint8_t slot0[C::SLOT_ARRAY];
+  __shared__ __attribute__((aligned(16))) uint8_t slot1[C::SLOT_ARRAY];
+  __shared__ __attribute__((aligned(16))) uint8_t slot2[C::SLOT_ARRAY];
+  __shared__ __attribute__((aligned(16))) float stage[kMaxQ * C::QROW];  // query in, output out (fp32)
+  __shared__ int qexp[kMaxQ];
+
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, h = lane >> 4;
+  const int G = p.q_per_kv, T = p.tokens;
+  const int stream = blockIdx.x, layer = blockIdx.y;
+  const int64_t row_k = (int64_t)layer * p.stride_layer + (int64_t)stream * p.stride_stream;
+  const int64_t row_v = row_k + p.stride_kv;
+  const int64_t qrow = ((int64_t)layer * gridDim.x + stream) * G;  // first query row of this stream
+
+  const int nchunks = (T + kChunk - 1) / kChunk;
+  const int c_begin = w * nchunks / kWaves, c_end = (w + 1) * nchunks / kWaves;
+
+  // ---- prologue: queries (wave 0) and the first two chunks (every wave) ----
+  uint4 qv[D / 8];
+  if (w == 0 && lane < G) {
+    const uint4* src = p.q + (qrow + lane) * (D / 8);
+    sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
+  }
+  if (c_begin < c_end) issue_chunk<D, GR>(p, row_k, row_v, c_begin * kChunk, slot0 + w * C::BUF, lane);
+  if (c_begin + 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c_begin + 1) * kChunk, slot1 + w * C::BUF, lane);
+  if (w == 0) {
+    uint32_t mk[D / 2];
+    wave_sign_masks<D>(seed_of_row(p, row_k), lane, mk);
+    if (lane < G) {
+      uint32_t hq[D / 2];
+      sfor<D / 8>([&](auto I) {
+        constexpr int i = RTQ_CI(I);
+        hq[4 * i] = qv[i].x ^ mk[4 * i];
+        hq[4 * i + 1] = qv[i].y ^ mk[4 * i + 1];
+        hq[4 * i + 2] = qv[i].z ^ mk[4 * i + 2];
+        hq[4 * i + 3] = qv[i].w ^ mk[4 * i + 3];
+      });
+      float y[D];
+      float sc;
+      if constexpr (ROT == 0) {
+        srft_fwd_unscaled<D>(hq, y);
+        sc = SrftScale<D>::value * p.qscale;
+      } else {
+        fwht_from_f16<D>(hq, y);
+        sc = InvSqrt<D>::value * p.qscale;
+      }
+      float amax = 0.0f;
+      sfor<D>([&](auto I) {
+        y[RTQ_CI(I)] *= sc;
+        amax = fmaxf(amax, fabsf(y[RTQ_CI(I)]));
+      });
+      // scale the query by 2^-e so that its largest entry lies in [2^13, 2^14):
+      // the fp16 high part cannot overflow and the low part keeps its bits
+      const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+      float* dst = stage + lane * C::QROW;
+      sfor<D / 4>([&](auto I) {
+        constexpr int i = RTQ_CI(I);
+        *reinterpret_cast<float4*>(dst + 4 * i) =
+            make_float4(__builtin_ldexpf(y[4 * i], -e), __builtin_ldexpf(y[4 * i + 1], -e),
+                        __builtin_ldexpf(y[4 * i + 2], -e), __builtin_ldexpf(y[4 * i + 3], -e));
+      });
+      qexp[lane] = e;
+    }
+  }
+  __syncthreads();
+
+  // q.k B operand, k-step j: column n < 8 holds the fp16 high part of query
+  // n, column n + 8 its low part; lane group h supplies dims
+  // 32j + 8h + {v, v + 4} as pair v (the order code_pair produces).
+  f16x8_t bq[C::KS];
+  {
+    const int g = n & 7;
+    const bool valid = g < G;
+    const float* src = stage + g * C::QROW;
+    sfor<C::KS>([&](auto J) {
+      constexpr int j = RTQ_CI(J);
+      uint32_t wds[4];
+      sfor<4>([&](auto V) {
+        constexpr int v = RTQ_CI(V);
+        const float a = valid ? src[32 * j + 8 * h + v] : 0.0f;
+        const float b = valid ? src[32 * j + 8 * h + v + 4] : 0.0f;
+        const _Float16 ah = (_Float16)a, bh = (_Float16)b;
+        const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
+        wds[v] = n < 8 ? as_u32((f16x2_t){ah, bh}) : as_u32((f16x2_t){al, bl});
+      });
+      bq[j] = pack8(as_h2(wds[0]), as_h2(wds[1]), as_h2(wds[2]), as_h2(wds[3]));
+    });
+  }
+  const int my_e = n < G ? qexp[n & 7] : 0;
+  const bool q_lane = n < G;  // lanes whose scores / outputs belong to a query
+
+  f32x4_t acc[C::NT];
+  sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f}; });
+  float m_run = kNegBig, l_run = 0.0f;
+
+  // p.v A operand: lane n reads code word dw of each token row; for d = 128
+  // dims 8n + i for tile i, for d = 64 dims 8(n & 7) + 4(n >> 3) + i.
+  const int dw = D == 128 ? n : (n & 7);
+  const int vgi = (8 * dw) / GR;  // the scale group of those dims
+  const uint32_t vsel = (D == 64 && n >= 8) ? 0x07060302u : 0x05040100u;
+
+  // one chunk in ring slot B (chunk c - c_begin lives in slot (c - c_begin) % 3)
+  auto chunk = [&](auto B, int c) {
+    constexpr int b = RTQ_CI(B);
+    uint8_t* const buf = b == 0 ? slot0 + w * C::BUF : b == 1 ? slot1 + w * C::BUF : slot2 + w * C::BUF;
+    uint8_t* const next = b == 0 ? slot2 + w * C::BUF : b == 1 ? slot0 + w * C::BUF : slot1 + w * C::BUF;
+    if (c + 1 < c_end) wait_vmcnt<C::NDMA>();
+    else wait_vmcnt<0>();
+    lds_sync();
+    if (c + 2 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + 2) * kChunk, next, lane);
+    const uint8_t* kc = buf;
+    const uint8_t* vc = buf + C::CODE_BYTES;
+    const uint8_t* ks = buf + 2 * C::CODE_BYTES;
+    const uint8_t* vs = ks + C::SCALE_BYTES;
+    const int tok0 = c * kChunk;
+
+    // ---- scores of tokens 16 tau + 4h + r (column n) ----
+    float sc[2][4];
+    sfor<2>([&](auto TAU) {
+      constexpr int tau = RTQ_CI(TAU);
+      const int lr = lrow<D>(16 * tau + n);
+      const uint8_t* rowp = kc + lr * C::RB + 4 * h;
+      const int sw = swz<D>(lr);
+      uint32_t kw[C::KS];
+      sfor<C::KS>([&](auto J) { kw[RTQ_CI(J)] = *reinterpret_cast<const uint32_t*>(rowp + 16 * (RTQ_CI(J) ^ sw)); });
+      uint32_t sk[2 * C::SLOT / 2];  // scale words of tokens 16 tau + 4h + 0..3
+      if constexpr (C::SLOT == 8) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + 8 * (16 * tau + 4 * h));
+        const uint4 b = *reinterpret_cast<const uint4*>(ks + 8 * (16 * tau + 4 * h) + 16);
+        sk[0] = a.x; sk[1] = a.y; sk[2] = a.z; sk[3] = a.w; sk[4] = b.x; sk[5] = b.y; sk[6] = b.z; sk[7] = b.w;
+      } else {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + 4 * (16 * tau + 4 * h));
+        sk[0] = a.x; sk[1] = a.y; sk[2] = a.z; sk[3] = a.w;
+      }
+      f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+      sfor<C::SPR>([&](auto GI) {
+        constexpr int gi = RTQ_CI(GI);
+        f32x4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+        sfor<GR / 32>([&](auto JJ) {
+          constexpr int j = gi * (GR / 32) + RTQ_CI(JJ);
+          const uint32_t x = kw[j];
+          part = mfma(pack8(code_pair<0>(x), code_pair<1>(x), code_pair<2>(x), code_pair<3>(x)), bq[j], part);
+        });
+        sfor<4>([&](auto R) {
+          constexpr int r = RTQ_CI(R);
+          if constexpr (C::SPR == 4) {
+            s[r] = mix_fma<gi & 1>(sk[2 * r + (gi >> 1)], part[r], s[r]);
+          } else {
+            s[r] = mix_fma<gi>(sk[r], part[r], s[r]);
+          }
+        });
+      });
+      sfor<4>([&](auto R) {
+        constexpr int r = RTQ_CI(R);
+        const float v = __builtin_ldexpf(add_ror8(s[r]), my_e);
+        const bool ok = q_lane && (tok0 + 16 * tau + 4 * h + r < T);
+        sc[tau][r] = ok ? v : -__builtin_inff();
+      });
+    });
+
+    // ---- online softmax (base 2) over the chunk, per query column ----
+    float cmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    float pr[2][4];
+    float psum = 0.0f;
+    sfor<2>([&](auto TAU) {
+      sfor<4>([&](auto R) {
+        const float e = __builtin_amdgcn_exp2f(sc[RTQ_CI(TAU)][RTQ_CI(R)] - m_new);
+        pr[RTQ_CI(TAU)][RTQ_CI(R)] = e;
+        psum += e;
+      });
+    });
+    l_run = __builtin_fmaf(l_run, alpha, psum);
+    m_run = m_new;
+    if (__ballot(alpha != 1.0f)) {
+      sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] *= alpha; });
+    }
+    // P^T operand: element 4 tau + r = token 16 tau + 4h + r of query n
+    const f16x8_t pb = pack8((f16x2_t){(_Float16)pr[0][0], (_Float16)pr[0][1]},
+                             (f16x2_t){(_Float16)pr[0][2], (_Float16)pr[0][3]},
+                             (f16x2_t){(_Float16)pr[1][0], (_Float16)pr[1][1]},
+                             (f16x2_t){(_Float16)pr[1][2], (_Float16)pr[1][3]});
+
+    // ---- values: V^T operand of tokens (a, b) = pair v of lane group h ----
+    uint32_t ylo[4], yhi[4], s2[4];
+    sfor<4>([&](auto V) {
+      constexpr int v = RTQ_CI(V);
+      const int ta = 16 * (v >> 1) + 4 * h + 2 * (v & 1), tb = ta + 1;
+      const int la = lrow<D>(ta), lb = lrow<D>(tb);
+      const uint32_t xa = *reinterpret_cast<const uint32_t*>(vc + la * C::RB + 16 * ((dw >> 2) ^ swz<D>(la)) + 4 * (dw & 3));
+      const uint32_t xb = *reinterpret_cast<const uint32_t*>(vc + lb * C::RB + 16 * ((dw >> 2) ^ swz<D>(lb)) + 4 * (dw & 3));
+      if constexpr (D == 128) {
+        ylo[v] = __builtin_amdgcn_perm(xb, xa, 0x05040100u);
+        yhi[v] = __builtin_amdgcn_perm(xb, xa, 0x07060302u);
+      } else {
+        ylo[v] = __builtin_amdgcn_perm(xb, xa, vsel);
+        yhi[v] = ylo[v];
+      }
+      const uint16_t sa = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * ta + 2 * vgi);
+      const uint16_t sb2 = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * tb + 2 * vgi);
+      const f16x2_t sp = as_h2((uint32_t)sa | ((uint32_t)sb2 << 16)) * (f16x2_t){(_Float16)kVShift, (_Float16)kVShift};
+      s2[v] = as_u32(sp);
+    });
+    sfor<C::NT>([&](auto I) {
+      constexpr int i = RTQ_CI(I);
+      constexpr int k = i & 3;
+      f16x2_t a[4];
+      sfor<4>([&](auto V) {
+        constexpr int v = RTQ_CI(V);
+        const uint32_t y = (D == 128 && i >= 4) ? yhi[v] : ylo[v];
+        a[v] = code_pair<k>(y) * as_h2(s2[v]);
+      });
+      acc[i] = mfma(pack8(a[0], a[1], a[2], a[3]), pb, acc[i]);
+    });
+  };
+#pragma unroll 1
+  for (int c = c_begin; c < c_end; c += kBufs) {
+    chunk(ic<0>{}, c);
+    if (c + 1 >= c_end) break;
+    chunk(ic<1>{}, c + 1);
+    if (c + 2 >= c_end) break;
+    chunk(ic<2>{}, c + 2);
+  }
+
+  // ---- merge the waves' partials ----
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  __syncthreads();  // every wave is done with its ring; the merge area aliases it
+  float* ow = reinterpret_cast<float*>(slot0);                  // [kWaves][kMaxQ][QROW]
+  float* mw = ow + kWaves * kMaxQ * C::QROW;                    // [kWaves][kMaxQ]
+  float* lw = mw + kWaves * kMaxQ;                              // [kWaves][kMaxQ]
+  if (q_lane) {
+    if (h == 0) {
+      mw[w * kMaxQ + n] = m_run;
+      lw[w * kMaxQ + n] = l_run;
+    }
+    float* dst = ow + (w * kMaxQ + n) * C::QROW;
+    sfor<C::NT>([&](auto I) {
+      constexpr int i = RTQ_CI(I);
+      sfor<4>([&](auto R) {
+        constexpr int r = RTQ_CI(R);
+        const int mrow = 4 * h + r;  // output row of the O^T tile = dim lane index
+        const int dim = D == 128 ? 8 * mrow + i : 8 * (mrow & 7) + 4 * (mrow >> 3) + i;
+        dst[dim] = acc[i][r];
+      });
+    });
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+    const int g = idx / D, dim = idx % D;
+    float mx = kNegBig;
+    for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
+    float num = 0.0f, den = 0.0f;
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = __builtin_amdgcn_exp2f(mw[ww * kMaxQ + g] - mx);
+      den = __builtin_fmaf(f, lw[ww * kMaxQ + g], den);
+      num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
+    }
+    stage[g * C::QROW + dim] = num / (den * kVShift);
+  }
+  __syncthreads();
+
+  // ---- rotate the outputs back: o = D_V R^T o_rot ----
+  if (w == 0) {
+    uint32_t mvs[D / 2];
+    wave_sign_masks<D>(seed_of_row(p, row_v), lane, mvs);
+    if (lane < G) {
+      float z[D], u[D];
+      const float* src = stage + lane * C::QROW;
+      sfor<D / 4>([&](auto I) {
+        constexpr int i = RTQ_CI(I);
+        const float4 f = *reinterpret_cast<const float4*>(src + 4 * i);
+        z[4 * i] = f.x; z[4 * i + 1] = f.y; z[4 * i + 2] = f.z; z[4 * i + 3] = f.w;
+      });
+      if constexpr (ROT == 0) {
+        srft_inv<D, One>(z, u);
+      } else {
+        fwht_f32<D>(z);
+        sfor<D>([&](auto I) { u[RTQ_CI(I)] = z[RTQ_CI(I)] * InvSqrt<D>::value; });
+      }
+      uint4* dst = p.out + (qrow + lane) * (D / 8);
+      sfor<D / 8>([&](auto I) {
+        constexpr int i = RTQ_CI(I);
+        dst[i] = make_uint4(pack_f16x2(u[8 * i], u[8 * i + 1]) ^ mvs[4 * i],
+                            pack_f16x2(u[8 * i + 2], u[8 * i + 3]) ^ mvs[4 * i + 1],
+                            pack_f16x2(u[8 * i + 4], u[8 * i + 5]) ^ mvs[4 * i + 2],
+                            pack_f16x2(u[8 * i + 6], u[8 * i + 7]) ^ mvs[4 * i + 3]);
+      });
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+using KernelFn = const void*;
+
+template <int ROT>
+KernelFn find_kernel(int d, int g) {
+#define RTQ_ATTN_CASE(DD, GG) \
+  if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT>);
+  RTQ_ATTN_CASE(64, 32) RTQ_ATTN_CASE(64, 64)
+  RTQ_ATTN_CASE(128, 32) RTQ_ATTN_CASE(128, 64) RTQ_ATTN_CASE(128, 128)
+#undef RTQ_ATTN_CASE
+  return nullptr;
+}
+
+// Block index of a row under the seed rule, before the modulo.
+inline int64_t block_of(int64_t row, int64_t rps) { return rps ? row / rps : 0; }
+
+// True when every token of every (layer, kv, stream) has the seed of its
+// token 0, so one sign vector serves the whole key (or value) sequence.
+bool seeds_constant(int64_t layers, int64_t streams, int64_t tokens, const int64_t (&st)[4], int64_t rps,
+                    int32_t period) {
+  if (rps == 0 || period == 1 || tokens == 1) return true;
+  // each token step moves a whole number of seed periods
+  if (st[3] % rps == 0 && period != 0 && (st[3] / rps) % period == 0) return true;
+  for (int64_t l = 0; l < layers; ++l)
+    for (int64_t kv = 0; kv < 2; ++kv)
+      for (int64_t s = 0; s < streams; ++s) {
+        const int64_t r0 = l * st[0] + kv * st[1] + s * st[2];
+        if (block_of(r0, rps) != block_of(r0 + (tokens - 1) * st[3], rps)) return false;
+      }
+  return true;
+}
+
+bool overlaps(const void* a, __int128 na, const void* b, __int128 nb) {
+  const __int128 a0 = (__int128)(uintptr_t)a, b0 = (__int128)(uintptr_t)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+rtq_status run(int rot, const void* q, const void* codes, const void* scales, void* out, int32_t layers,
+               int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d, int32_t group, const int64_t (&st)[4],
+               uint64_t seed, int64_t rps, int32_t period, float softmax_scale, hipStream_t stream) {
+  if (layers < 0 || streams < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+    return RTQ_ERR_INVALID_ARG;
+  const KernelFn fn = rot == 0 ? find_kernel<0>(d, group) : find_kernel<1>(d, group);
+  if (!fn) return RTQ_ERR_UNSUPPORTED;
+  if (q_per_kv < 1) return RTQ_ERR_INVALID_ARG;
+  if (q_per_kv > kMaxQ) return RTQ_ERR_UNSUPPORTED;
+  if (layers == 0 || streams == 0) return RTQ_OK;
+  if (tokens < 1 || tokens > 0x7fffff00) return RTQ_ERR_INVALID_ARG;
+  if (layers > 65535) return RTQ_ERR_INVALID_ARG;
+  if (!q || !codes || !scales || !out) return RTQ_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return RTQ_ERR_INVALID_ARG;
+  // largest row the kernel reads, in 128-bit arithmetic
+  const __int128 max_row = (__int128)(layers - 1) * st[0] + st[1] + (__int128)(streams - 1) * st[2] +
+                           (__int128)(tokens - 1) * st[3];
+  if (max_row >= ((__int128)1 << 56)) return RTQ_ERR_INVALID_ARG;
+  if (!seeds_constant(layers, streams, tokens, st, rps, period)) return RTQ_ERR_INVALID_ARG;
+  const __int128 qo_bytes = (__int128)layers * streams * q_per_kv * d * 2;
+  const __int128 code_bytes = (max_row + 1) * (d / 2), scale_bytes = (max_row + 1) * 2 * (d / group);
+  if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, codes, code_bytes) ||
+      overlaps(out, qo_bytes, scales, scale_bytes))
+    return RTQ_ERR_INVALID_ARG;
+  Params p;
+  p.q = static_cast<const uint4*>(q);
+  p.codes = static_cast<const uint8_t*>(codes);
+  p.scales = static_cast<const uint8_t*>(scales);
+  p.out = static_cast<uint4*>(out);
+  p.stride_layer = st[0];
+  p.stride_kv = st[1];
+  p.stride_stream = st[2];
+  p.stride_token = st[3];
+  p.seed = seed;
+  p.rows_per_seed = rps;
+  p.seed_period = period;
+  p.tokens = tokens;
+  p.q_per_kv = q_per_kv;
+  p.qscale = (float)((double)softmax_scale * 1.4426950408889634074);
+  void* kargs[] = {&p};
+  const hipError_t e =
+      hipLaunchKernel(fn, dim3((unsigned)streams, (unsigned)layers), dim3(64 * kWaves), kargs, 0, stream);
+  return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
+}
+
+}  // namespace attn
+}  // namespace rtq
+
+#define RTQ_API extern "C" __attribute__((visibility("default")))
+
+RTQ_API rtq_status srft_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
+                                    int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
+                                    int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
+                                    int64_t stride_token, uint64_t seed, int64_t rows_per_seed,
+                                    int32_t seed_period, float softmax_scale, hipStream_t stream) {
+  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
+  return rtq::attn::run(0, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
+                        seed, rows_per_seed, seed_period, softmax_scale, stream);
+}
+
+RTQ_API rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
+                                    int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
+                                    int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
+                                    int64_t stride_token, uint64_t seed, int64_t rows_per_seed,
+                                    int32_t seed_period, float softmax_scale, hipStream_t stream) {
+  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
+  return rtq::attn::run(1, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
+                        seed, rows_per_seed, seed_period, softmax_scale, stream);
+}

@@ -108,3 +108,30 @@ def check_inverse(codes, scales, y_gpu, d, group, seed, rps=0, period=0, rot="sr
     exact = float(np.mean(y_gpu.view(np.uint16) == y_orc.view(np.uint16))) if y_orc.size else 1.0
     rel = np.where(s_row > 0, err / np.where(s_row > 0, s_row, 1.0), 0.0)
     return {"max_err_over_s": float(np.max(rel, initial=0.0)), "exact_frac": exact}
+
+
+def check_attention(o_gpu, o_orc, scales, strides, tokens, group, pairs=None):
+    """Assert decode-attention outputs agree: for every (layer, stream, query,
+    dim), |o_gpu - o_oracle| <= 2e-3 * s_v + 1 ulp of fp16 at o_oracle, where
+    s_v is the largest value scale of that stream's cached tokens.  The output
+    is a convex combination of the stream's dequantized value rows, so the
+    per-row inverse bound (2e-3 times the row's scale) carries over with the
+    stream's largest scale; the ulp term covers the final fp16 rounding.
+    Returns the largest error in units of 2e-3 * s_v."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    layers, streams = o_orc.shape[:2]
+    todo = [(l, s) for l in range(layers) for s in range(streams)] if pairs is None else pairs
+    worst = 0.0
+    for l, s in todo:
+        rows = oracle.cache_rows(l, 1, s, tokens, strides)
+        sv = float(np.max(np.asarray(scales[rows], dtype=np.float64)))
+        err = np.abs(o_gpu[l, s] - o_orc[l, s])
+        bound = 2e-3 * sv + fp16_ulp(o_orc[l, s])
+        if not np.all(np.isfinite(o_gpu[l, s])) or np.any(err > bound):
+            g, i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+            raise AssertionError(f"attention mismatch at layer {l} stream {s} query {g} dim {i}: gpu "
+                                 f"{o_gpu[l, s, g, i]!r} oracle {o_orc[l, s, g, i]!r} (bound {bound[g, i]:.3g}, "
+                                 f"s_v {sv:.3g})")
+        if sv > 0:
+            worst = max(worst, float(np.max(err / (2e-3 * sv))))
+    return worst

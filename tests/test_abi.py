@@ -24,8 +24,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["rtq_status_string", "srft_dequant_inv", "srft_quant_fwd",
-                                    "srht_dequant_inv", "srht_quant_fwd"]
+    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv", "srft_quant_fwd",
+                                    "srht_attn_decode", "srht_dequant_inv", "srht_quant_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -97,6 +97,67 @@ def test_inverse_rejects_overlapping_buffers(name):
     assert call(name, A + 1024, B, A, n, d, g) == rtq.RTQ_ERR_INVALID_ARG   # codes inside y
     assert call(name, A, B, A + 3000, n, d, g) == rtq.RTQ_ERR_INVALID_ARG        # y overlaps codes
     assert call(name, A, B, B - 16, n, d, g) == rtq.RTQ_ERR_INVALID_ARG         # y overlaps scales
+
+
+ATTN = ["srft_attn_decode", "srht_attn_decode"]
+Q, K, S_, O = 0x10000, 0x2000000, 0x6000000, 0x8000000  # q, codes, scales, out (never dereferenced)
+
+
+def attn_call(name, q=Q, codes=K, scales=S_, out=O, layers=2, streams=3, tokens=50, qpk=4, d=128, g=32,
+              strides=(300, 150, 50, 1), seed=1, rps=0, per=0, softmax_scale=0.125):
+    fn = getattr(rtq.library(), name)
+    return fn(ctypes.c_void_p(q), ctypes.c_void_p(codes), ctypes.c_void_p(scales), ctypes.c_void_p(out),
+              layers, streams, tokens, qpk, d, g, *strides, seed, rps, per, ctypes.c_float(softmax_scale), None)
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_rejects_bad_arguments_without_launching(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    assert attn_call(name, layers=-1) == bad
+    assert attn_call(name, streams=-1) == bad
+    assert attn_call(name, tokens=0) == bad
+    assert attn_call(name, qpk=0) == bad
+    assert attn_call(name, rps=-1) == bad
+    assert attn_call(name, per=-1) == bad
+    assert attn_call(name, strides=(300, 150, 50, -1)) == bad
+    assert attn_call(name, softmax_scale=float("nan")) == bad
+    assert attn_call(name, softmax_scale=float("inf")) == bad
+    assert attn_call(name, layers=70000, strides=(0, 150, 50, 1)) == bad
+    for kw in ({"q": 0}, {"codes": 0}, {"scales": 0}, {"out": 0}, {"q": Q + 8}, {"codes": K + 4},
+               {"scales": S_ + 2}, {"out": O + 8}):
+        assert attn_call(name, **kw) == bad, kw
+    # rows past 2^56
+    assert attn_call(name, strides=(1 << 60, 150, 50, 1)) == bad
+    # unsupported shapes and head ratios
+    for d, g in [(256, 32), (64, 128), (128, 16), (96, 32)]:
+        assert attn_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
+    assert attn_call(name, qpk=9) == rtq.RTQ_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_requires_one_seed_per_key_and_value_sequence(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    L, S, T = 2, 3, 50
+    lm = (2 * S * T, S * T, T, 1)
+    tm = (2 * S, S, 1, 2 * L * S)
+    assert attn_call(name, strides=lm, rps=1) == bad              # a seed per row
+    assert attn_call(name, strides=lm, rps=T + 1) == bad          # blocks cut through the token sequences
+    assert attn_call(name, strides=tm, rps=2 * S, per=2 * L) == bad   # time-major, period of two layers
+    assert attn_call(name, strides=tm, rps=1, per=0) == bad
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_empty_grid_is_a_no_op(name):
+    assert attn_call(name, q=0, codes=0, scales=0, out=0, layers=0) == rtq.RTQ_OK
+    assert attn_call(name, q=0, codes=0, scales=0, out=0, streams=0) == rtq.RTQ_OK
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_rejects_overlapping_output(name):
+    # q and out: 2*3*4*128*2 = 6144 B; codes reach row 299 (19200 B); scales 2400 B
+    assert attn_call(name, out=Q + 4096) == rtq.RTQ_ERR_INVALID_ARG
+    assert attn_call(name, out=K + 16384) == rtq.RTQ_ERR_INVALID_ARG
+    assert attn_call(name, out=S_ - 4096) == rtq.RTQ_ERR_INVALID_ARG
 
 
 def test_python_binding_rejects_cpu_tensors():

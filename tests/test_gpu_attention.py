@@ -1,0 +1,180 @@
+"""Decode attention over the int4 rotated cache, HIP path against the oracle
+(needs an MI355X).
+
+The cache is built on the CPU by the oracle's forward (or, at full size, drawn
+as seeded random codes and scales on the device), the kernel runs through the
+C ABI (ctypes binding), and every output element is compared with
+oracle.attn_decode under the bound of tests/parity.py (check_attention).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.conftest import gpu_available
+from tests.parity import check_attention
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+torch = pytest.importorskip("torch")
+import rotate_then_quantize_amd as rtq  # noqa: E402
+from rotate_then_quantize_amd import workloads as W  # noqa: E402
+
+DEV = "cuda"
+ATTN = sorted(rtq.ATTN_SUPPORTED)
+
+
+def lm(streams, tcap):
+    return (2 * streams * tcap, streams * tcap, tcap, 1)
+
+
+def tm(layers, streams):
+    return (2 * streams, streams, 1, 2 * layers * streams)
+
+
+def make_cache(rng, n, d, g, seed, rps, per, rot, scale=1.0, outliers=0):
+    x = rng.standard_normal((n, d)) * scale
+    if outliers:
+        x[:, rng.choice(d, outliers, replace=False)] *= 15.0
+    return oracle.quant_fwd(x.astype(np.float16), g, seed, rps, per, rot)
+
+
+def gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale=None):
+    q = torch.from_numpy(np.ascontiguousarray(q16)).to(DEV)
+    c = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
+    o = rtq.attn_decode(rot, q, c, s, strides, tokens, g, seed, rps, per, softmax_scale)
+    torch.cuda.synchronize()
+    return o.cpu().numpy()
+
+
+def run_case(rot, d, g, layers, streams, tokens, qpk, strides, n, seed=7, rps=0, per=0, softmax_scale=None,
+             q_scale=1.0, v_scale=1.0, rng_seed=0, outliers=0):
+    rng = np.random.default_rng(rng_seed)
+    codes, scales = make_cache(rng, n, d, g, seed, rps, per, rot, v_scale, outliers)
+    q16 = (rng.standard_normal((layers, streams, qpk, d)) * q_scale).astype(np.float16)
+    print(f"case rot={rot} d={d} g={g} L={layers} S={streams} T={tokens} G={qpk} strides={strides}", flush=True)
+    o_gpu = gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale)
+    o_orc = oracle.attn_decode(q16, codes, scales, strides, layers, streams, tokens, qpk, d, g, seed, rps, per,
+                               rot, softmax_scale)
+    worst = check_attention(o_gpu, o_orc, scales, strides, tokens, g)
+    print(f"  worst error / (2e-3 s_v) = {worst:.3f}", flush=True)
+    return worst
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,g", ATTN)
+@pytest.mark.parametrize("qpk", [1, 3, 8])
+def test_layer_major_per_layer_seeds(rot, d, g, qpk):
+    L, S, T = 2, 3, 100  # four 32-token chunks, the last one ragged
+    run_case(rot, d, g, L, S, T, qpk, lm(S, T), L * 2 * S * T, seed=11, rps=2 * S * T, per=L, outliers=2)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("tokens", [1, 2, 31, 32, 33, 64, 65, 127, 128, 129, 200, 385])
+def test_token_counts(rot, tokens):
+    S = 2
+    run_case(rot, 128, 32, 1, S, tokens, 6, lm(S, tokens), 2 * S * tokens, seed=5)
+
+
+@pytest.mark.parametrize("d,g,qpk", [(128, 32, 6), (64, 32, 3), (64, 64, 1)])
+def test_time_major_decode_layout(d, g, qpk):
+    L, S, T = 3, 4, 70
+    run_case("srft", d, g, L, S, T, qpk, tm(L, S), L * 2 * S * T, seed=0x5EED * 3, rps=2 * S, per=L)
+
+
+@pytest.mark.parametrize("d,g", [(128, 32), (64, 64)])
+def test_many_chunks_per_wave(d, g):
+    S, T = 2, 1000  # 32 chunks: eight per wave, the three-slot ring wraps
+    run_case("srft", d, g, 1, S, T, 4, lm(S, T), 2 * S * T, seed=3)
+
+
+@pytest.mark.parametrize("q_scale", [1e-3, 30.0, 600.0])
+def test_query_magnitudes(q_scale):
+    S, T = 2, 90
+    run_case("srft", 128, 32, 1, S, T, 5, lm(S, T), 2 * S * T, seed=9, q_scale=q_scale)
+
+
+@pytest.mark.parametrize("v_scale", [1e-2, 300.0])
+def test_cache_magnitudes(v_scale):
+    S, T = 2, 90
+    run_case("srft", 128, 64, 1, S, T, 2, lm(S, T), 2 * S * T, seed=9, v_scale=v_scale, q_scale=1.0 / v_scale)
+
+
+@pytest.mark.parametrize("softmax_scale", [0.0, 1.0, -0.2])
+def test_softmax_scales(softmax_scale):
+    S, T = 2, 77
+    run_case("srht", 64, 32, 1, S, T, 3, lm(S, T), 2 * S * T, seed=4, softmax_scale=softmax_scale)
+
+
+def test_strided_cache_with_gaps():
+    """Rows of a stream need not be adjacent: a token stride of 3 and unused rows between streams."""
+    L, S, T = 2, 2, 50
+    strides = (2 * S * 160, S * 160, 160, 3)
+    run_case("srft", 128, 32, L, S, T, 2, strides, L * 2 * S * 160, seed=1)
+
+
+def test_empty_grid_is_a_no_op():
+    q = torch.zeros((0, 3, 2, 128), dtype=torch.float16, device=DEV)
+    c = torch.zeros((10, 64), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((10, 4), dtype=torch.float16, device=DEV)
+    o = rtq.srft_attn_decode(q, c, s, (0, 0, 0, 1), 1, 32, 1)
+    assert o.shape == q.shape
+
+
+def test_argument_errors():
+    q = torch.zeros((1, 1, 2, 128), dtype=torch.float16, device=DEV)
+    c = torch.zeros((64, 64), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((64, 4), dtype=torch.float16, device=DEV)
+    with pytest.raises(ValueError):
+        rtq.srft_attn_decode(q, c, s, (0, 32, 0, 1), 0, 32, 1)          # no tokens
+    with pytest.raises(ValueError):
+        rtq.srft_attn_decode(q, c, s, (0, 32, 0, 1), 40, 32, 1)         # rows past the cache
+    with pytest.raises(rtq.RTQError):
+        rtq.srft_attn_decode(q, c, s, (0, 32, 0, 1), 8, 32, 1, 1, 0)    # a seed per row
+    q9 = torch.zeros((1, 1, 9, 128), dtype=torch.float16, device=DEV)
+    with pytest.raises(rtq.RTQError):
+        rtq.srft_attn_decode(q9, c, s, (0, 32, 0, 1), 8, 32, 1)         # 9 query heads per K/V head
+    q256 = torch.zeros((1, 1, 1, 256), dtype=torch.float16, device=DEV)
+    c256 = torch.zeros((64, 128), dtype=torch.uint8, device=DEV)
+    s256 = torch.zeros((64, 8), dtype=torch.float16, device=DEV)
+    with pytest.raises(rtq.RTQError):
+        rtq.srft_attn_decode(q256, c256, s256, (0, 32, 0, 1), 8, 32, 1)  # d = 256 not built
+
+
+# ---------------------------------------------------------------------------
+# Full-size caches in the launch configuration the bench times, checked on
+# sampled (layer, stream) pairs.  Codes are uniform over [-8, 7] and scales
+# |N(0, 1)| * 0.3 in fp16 (the magnitude absmax/8 takes for unit-variance K/V).
+# ---------------------------------------------------------------------------
+
+
+def random_cache(n, d, g, seed):
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed)
+    codes = torch.randint(0, 256, (n, d // 2), generator=gen, device=DEV, dtype=torch.int32).to(torch.uint8)
+    scales = (torch.randn((n, d // g), generator=gen, device=DEV).abs() * 0.3).to(torch.float16)
+    return codes, scales
+
+
+@pytest.mark.parametrize("wid", [3, 2])
+def test_workload_full_size_sampled(wid):
+    w = W.WORKLOADS[wid]
+    L, S, T, G, d, g = w.layers, w.streams, w.tokens, w.q_per_kv, w.d, w.group
+    codes, scales = random_cache(w.n_rows, d, g, 100 + wid)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(200 + wid)
+    q = torch.randn((L, S, G, d), generator=gen, device=DEV).to(torch.float16)
+    print(f"full size {w.name}: L={L} S={S} T={T} G={G} rows={w.n_rows}", flush=True)
+    o = rtq.srft_attn_decode(q, codes, scales, w.cache_strides, T, g, w.sign_seed, w.rows_per_seed, w.seed_period)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wid)
+    pairs = [(0, 0), (L - 1, S - 1)] + [(int(rng.integers(L)), int(rng.integers(S))) for _ in range(4)]
+    qh, ch, sh, oh = q.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy(), o.cpu().numpy()
+    o_orc = oracle.attn_decode(qh, ch, sh, w.cache_strides, L, S, T, G, d, g, w.sign_seed, w.rows_per_seed,
+                               w.seed_period, "srft", pairs=pairs)
+    worst = check_attention(oh, o_orc, sh, w.cache_strides, T, g, pairs=pairs)
+    print(f"  sampled pairs {pairs}: worst error / (2e-3 s_v) = {worst:.3f}", flush=True)
+    del codes, scales, q, o
+    torch.cuda.empty_cache()

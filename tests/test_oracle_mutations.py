@@ -102,15 +102,15 @@ MUTATIONS = {
     "inverse forgets the signs": (
         "return D * (z @ rotation_matrix(rot, d))", "return z @ rotation_matrix(rot, d)"),
     "attention reads values from the key rows": (
-        "            for kv in (0, 1):\n                rows = cache_rows(layer, kv, st,",
-        "            for kv in (0, 0):\n                rows = cache_rows(layer, kv, st,"),
+        "        for kv in (0, 1):\n            rows = cache_rows(layer, kv, st,",
+        "        for kv in (0, 0):\n            rows = cache_rows(layer, kv, st,"),
     "attention rows use one seed for every row": (
         "    row_seeds = [row_seed(seed, int(r), rows_per_seed, seed_period) for r in rows]",
         "    row_seeds = [row_seed(seed, int(rows[0]), rows_per_seed, seed_period) for r in rows]"),
     "attention rows skip the sign flip": ("        u[idx] *= sign_vector(s, d)", "        u[idx] *= 1.0"),
     "attention drops the softmax scale": (
-        "                sc = keys @ q[layer, st, g] * softmax_scale",
-        "                sc = keys @ q[layer, st, g]"),
+        "            sc = keys @ q[layer, st, g] * softmax_scale",
+        "            sc = keys @ q[layer, st, g]"),
     "cache rows swap the kv and stream strides": (
         "    return layer * sl + kv * skv + stream * ss + st * np.arange(tokens, dtype=np.int64)",
         "    return layer * sl + kv * ss + stream * skv + st * np.arange(tokens, dtype=np.int64)"),
