@@ -13,6 +13,13 @@ buffers are cycled so the 256 MB last-level cache cannot hold a step's data.
 Prints one JSON line on stdout (human-readable notes go to stderr).
 
   python bench.py [--steps K] [--warmup W] [--workload 1..5] [--rot srft|srht]
+
+With --attn it measures instead one decode step of attention that reads the
+int4 cache directly (srft_attn_decode): every query head of every (layer,
+stream) attends over all cached tokens (default: the Qwen2.5-1.5B decode
+cache, 28 layers x 128 streams x 2049 tokens, 6 query heads per K/V head),
+beside the unfused path (inverse kernel to an fp16 cache, then attention as
+torch batched matmuls and softmax).
 """
 from __future__ import annotations
 
@@ -31,7 +38,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, public figure
 METRIC = "K/V vectors/s and HBM GB/s (% of peak), fused SRFT-int4 quant+dequant, 1 GPU"
-KERNEL_SOURCES = [os.path.join(ROOT, "rotate_then_quantize_amd", "csrc", f) for f in ("rtq.hip", "rtq_device.hpp", "rtq_div.hpp")]
+ATTN_METRIC = "decode-attention steps/s over the int4 rotated K/V cache (dequantized in registers), 1 GPU"
+_CSRC = os.path.join(ROOT, "rotate_then_quantize_amd", "csrc")
+# sources each kernel family is compiled from (a profile is current while their code is unchanged)
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq.hip", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp")]
+ATTN_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq_attn.hip", "rtq_device.hpp", "rtq_mem.hpp")]
 
 
 def log(*a):
@@ -45,10 +56,10 @@ def code_text(src: str) -> str:
     return " ".join(src.split())
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     """Hash of the kernel sources' code (comments ignored)."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(p, encoding="utf-8") as f:
             h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
@@ -66,7 +77,8 @@ def read_traffic(workload_name: str, rot: str, kernel: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha") != kernel_source_hash():
+    sources = ATTN_SOURCES if kernel == "attn_decode" else KERNEL_SOURCES
+    if vals.get("kernel_source_sha") != kernel_source_hash(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -74,7 +86,26 @@ def read_traffic(workload_name: str, rot: str, kernel: str):
         return None
 
 
-KERNEL_ROLES = (("fwd_", "quant_fwd"), ("inv_", "dequant_inv"))
+KERNEL_ROLES = (("fwd_", "quant_fwd"), ("inv_", "dequant_inv"), ("attn::", "attn_decode"))
+
+
+def attn_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode-attention launch over workload w:
+    every K and V row's codes and scales once, plus the queries and outputs."""
+    rows = w.layers * 2 * w.streams * w.tokens
+    qo = 2 * w.layers * w.streams * w.q_per_kv * w.d * 2
+    return rows * (w.d // 2 + 2 * (w.d // w.group)) + qo
+
+
+def role_bytes(w, role: str) -> int:
+    if role == "attn_decode":
+        return attn_bytes(w)
+    rows = w.new_rows if (w.new_tokens and role == "quant_fwd") else w.n_rows
+    return rows * w.bytes_per_vector()
+
+
+def role_sources(role: str):
+    return ATTN_SOURCES if role == "attn_decode" else KERNEL_SOURCES
 
 
 def short_kernel_name(name: str) -> str:
@@ -113,13 +144,14 @@ def find_csv(directory: str, suffix: str) -> str:
     return hits[0]
 
 
-def summarize_trace(trace_dir: str, w, rot: str, command: str) -> None:
+def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = False) -> None:
     """Write the rocprofv3 --kernel-trace --stats summary of a bench run."""
     import csv
     rows = list(csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv"))))
-    lines = [f"# rocprofv3 kernel trace, workload {w.name} (d={w.d}, group={w.group}, {rot})",
+    what = "decode attention" if attn else "forward + inverse"
+    lines = [f"# rocprofv3 kernel trace, {what}, workload {w.name} (d={w.d}, group={w.group}, {rot})",
              f"# command: {command}",
-             f"# kernel_source_sha: {kernel_source_hash()}",
+             f"# kernel_source_sha: {kernel_source_hash(ATTN_SOURCES if attn else KERNEL_SOURCES)}",
              "# kernel | calls | average us | min us | max us | share of GPU time",
              ]
     for r in rows:
@@ -127,11 +159,11 @@ def summarize_trace(trace_dir: str, w, rot: str, command: str) -> None:
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}%")
     for r in rows:
         role = kernel_role(r["Name"])
-        if role:
-            bytes_launch = (w.new_rows if (w.new_tokens and role == "quant_fwd") else w.n_rows) * w.bytes_per_vector()
+        if role and (role == "attn_decode") == attn:
+            bytes_launch = role_bytes(w, role)
             lines.append(f"{role}_average_us: {float(r['AverageNs']) / 1e3:.3f}")
             lines.append(f"{role}_algorithmic_GBps: {bytes_launch / float(r['AverageNs']):.1f}")
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{rot}_{w.name}.txt")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{'attn_' if attn else ''}{rot}_{w.name}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     log(f"wrote {path}")
@@ -167,15 +199,14 @@ def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mi
         role = kernel_role(kname)
         if not role:
             continue
-        rows = w.new_rows if (w.new_tokens and role == "quant_fwd") else w.n_rows
-        algo = rows * w.bytes_per_vector()
+        algo = role_bytes(w, role)
         fb = fetch[kname] * cal["FETCH_SIZE"][0] * 1024.0
         wb = write[kname] * cal["WRITE_SIZE"][0] * 1024.0
         lines = [f"# HBM traffic of {kname}, workload {w.name} (d={w.d}, group={w.group}, {rot})"]
         lines += [f"# command ({c}): {cmd}" for c, cmd in commands]
         lines += [
             f"kernel: {kname}",
-            f"kernel_source_sha: {kernel_source_hash()}",
+            f"kernel_source_sha: {kernel_source_hash(role_sources(role))}",
             f"dispatches_fetch: {nf[kname]}",
             f"dispatches_write: {nw[kname]}",
             f"fetch_kib_per_dispatch_raw: {fetch[kname]:.1f}",
@@ -334,12 +365,198 @@ def cpu_baseline(w, x_gpu, rot, seconds):
     }
 
 
+def attn_unfused_baseline(w, rot, fused_ms, dev, steps=10, warmup=2):
+    """The unfused consumer: the inverse kernel dequantizes the whole cache to
+    fp16 (kv-major, so K and V are contiguous [layers*streams, tokens, d]
+    blocks), then attention runs as torch.bmm, softmax in fp32, torch.bmm.
+    Measurement only."""
+    import torch
+    import rotate_then_quantize_amd as rtq
+    L, S, T, G, d, g = w.layers, w.streams, w.tokens, w.q_per_kv, w.d, w.group
+    n = L * 2 * S * T
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4321)
+    codes = torch.randint(0, 256, (n, d // 2), generator=gen, device=dev, dtype=torch.uint8)
+    scales = (torch.randn((n, d // g), generator=gen, device=dev).abs_() * 0.3).to(torch.float16)
+    y = torch.empty((n, d), dtype=torch.float16, device=dev)
+    q = torch.randn((L * S, G, d), generator=gen, device=dev).to(torch.float16)
+    qt = q.transpose(1, 2).contiguous()
+    scale = 1.0 / math.sqrt(d)
+
+    def step():
+        rtq.dequant_inv(rot, codes, scales, d, g, w.sign_seed, S * T, L, out=y)
+        k = y[: n // 2].view(L * S, T, d)
+        v = y[n // 2:].view(L * S, T, d)
+        sc = torch.bmm(k, qt)                                   # [L*S, T, G]
+        p = torch.softmax(sc.float() * scale, dim=1).to(torch.float16)
+        return torch.bmm(p.transpose(1, 2).contiguous(), v)     # [L*S, G, d]
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        step()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    del codes, scales, y
+    torch.cuda.empty_cache()
+    return {
+        "ms_per_step": ms,
+        "value": 1e3 / ms,
+        "unit": "steps/s",
+        "fused_speedup": ms / fused_ms,
+        "steps": steps,
+        "ops": f"{rot}_dequant_inv of every K/V row to fp16 (this library), then torch.bmm (K q^T), "
+               "fp32 softmax, torch.bmm (P V) on the GPU",
+    }
+
+
+def attn_cpu_baseline(w, codes_gpu, scales_gpu, q_gpu, rot, seconds, strides, rps, per):
+    """oracle.attn_decode, as it is, on consecutive (layer, stream) pairs of
+    the same cache until ``seconds`` of CPU time are spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    codes, scales, q = codes_gpu.cpu().numpy(), scales_gpu.cpu().numpy(), q_gpu.cpu().numpy()
+    L, S = w.layers, w.streams
+    done, spent = 0, 0.0
+    while spent < seconds and done < L * S:
+        pair = (done // S, done % S)
+        t0 = time.perf_counter()
+        oracle.attn_decode(q, codes, scales, strides, L, S, w.tokens, w.q_per_kv, w.d, w.group,
+                           w.sign_seed, rps, per, rot, pairs=[pair])
+        spent += time.perf_counter() - t0
+        done += 1
+    return {
+        "value": done / spent / (L * S),
+        "unit": "steps/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} of the {L * S} (layer, stream) pairs ({w.tokens} tokens, {w.q_per_kv} queries each), "
+                  f"fp64 numpy oracle, {spent:.1f} s of oracle time; steps/s = pairs/s / {L * S}",
+    }
+
+
+def attn_main(args, w, dev):
+    import torch
+    import rotate_then_quantize_amd as rtq
+    rot = args.rot
+    lib = rtq.library()
+    fn = lib.srft_attn_decode if rot == "srft" else lib.srht_attn_decode
+    L, S, T, G, d, g = w.layers, w.streams, w.tokens, w.q_per_kv, w.d, w.group
+    n = w.n_rows
+    if args.attn_layout == "heads":
+        strides = (2 * S * T, S * T, T, 1)
+        rps, per = (2 * S * T, L) if L > 1 else (0, 0)   # one sign seed per layer
+    else:
+        strides, rps, per = w.cache_strides, w.rows_per_seed, w.seed_period
+    cache_bytes = n * (d // 2 + 2 * (d // g))
+    replicas = args.replicas or max(1, math.ceil((1 << 30) / cache_bytes))
+    log(f"decode attention, workload {w.name}: L={L} S={S} T={T} G={G} d={d} group={g} rot={rot}, "
+        f"{replicas} cache replica(s) of {cache_bytes / 1e6:.1f} MB")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    scale = ctypes.c_float(1.0 / math.sqrt(d))
+    sets = []
+    for _ in range(replicas):
+        codes = torch.randint(0, 256, (n, d // 2), generator=gen, device=dev, dtype=torch.uint8)
+        scales = (torch.randn((n, d // g), generator=gen, device=dev).abs_() * 0.3).to(torch.float16)
+        q = torch.randn((L, S, G, d), generator=gen, device=dev).to(torch.float16)
+        out = torch.empty_like(q)
+        a = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+             ctypes.c_void_p(out.data_ptr()), L, S, T, G, d, g, *strides, w.sign_seed, rps, per, scale, sh)
+        sets.append((a, (codes, scales, q, out)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        st = fn(*sets[i % replicas][0])
+        if st:
+            raise RuntimeError(lib.rtq_status_string(st).decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    SAMPLE = 20
+    sampled = [i for i in range(args.steps) if i % SAMPLE == 0]
+    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev = evs.get(i)
+        if ev:
+            ev[0].record(stream)
+        step(args.warmup + i)
+        if ev:
+            ev[1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    k_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in sampled) / len(sampled)
+    nbytes = attn_bytes(w)
+    achieved = nbytes / k_ms / 1e6
+    log(f"step {ms_step * 1e3:.1f} us | kernel {k_ms * 1e3:.1f} us {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
+    result = {
+        "metric": ATTN_METRIC,
+        "value": args.steps / (t1 - t0),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 mfma, f32 accumulate",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "layers": L, "streams": S, "tokens": T, "q_per_kv": G, "d": d, "group": g,
+            "rotation": rot, "layout": "[layer][K,V][stream][token]" if args.attn_layout == "heads" else w.layout,
+            "cache_strides": list(strides),
+            "cache_replicas": replicas, "cache": "uniform int4 codes, |N(0,1)|*0.3 fp16 scales",
+        },
+        "kernel_us": {"attn_decode": k_ms * 1e3,
+                      "timing": f"hipEvents on the launch stream, every {SAMPLE}th timed step "
+                                f"({len(sampled)} of {args.steps})"},
+        "roofline": {
+            "kernel": f"{rot}_attn_decode d={d} g={g} q_per_kv={G}",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS,
+            "traffic": read_traffic(w.name, rot, "attn_decode"),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_eager:
+        result["unfused_baseline"] = attn_unfused_baseline(w, rot, ms_step, dev)
+    if not args.no_cpu_baseline:
+        codes, scales, q, _ = sets[0][1]
+        result["cpu_baseline"] = attn_cpu_baseline(w, codes, scales, q, rot, args.cpu_seconds, strides, rps, per)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
+                    help="workload id (default 2; 3 with --attn)")
+    ap.add_argument("--attn", action="store_true",
+                    help="measure decode attention over the int4 cache instead of forward + inverse")
+    ap.add_argument("--attn-layout", choices=["heads", "workload"], default="heads",
+                    help="attention cache layout: 'heads' = [layer][K,V][stream][token] (each head's tokens "
+                         "contiguous, as a per-layer [batch, heads, tokens, d] cache), 'workload' = the "
+                         "workload's own row order")
     ap.add_argument("--rot", choices=["srft", "srht"], default="srft")
     ap.add_argument("--replicas", type=int, default=0, help="buffer sets cycled per step (0 = enough to exceed 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -356,12 +573,14 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
+    if args.workload is None:
+        args.workload = 3 if args.attn else 2
 
     if args.summarize_trace or args.summarize_traffic:
         from rotate_then_quantize_amd import workloads as W
         w = W.WORKLOADS[args.workload]
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command))
+            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn)
         if args.summarize_traffic:
             names = ("FETCH_SIZE", "WRITE_SIZE", "copy FETCH_SIZE", "copy WRITE_SIZE")
             cmds = list(zip(names, args.command[-4:])) if len(args.command) >= 4 else []
@@ -395,6 +614,9 @@ def main():
         return
 
     w = W.WORKLOADS[args.workload]
+    if args.attn:
+        attn_main(args, w, dev)
+        return
     rot = args.rot
     if rot not in w.rots:
         log(f"note: workload {w.name} is specified with {w.rots}; running {rot} anyway")

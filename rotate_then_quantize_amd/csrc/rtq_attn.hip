@@ -17,8 +17,10 @@
 // inverse-rotating every cached vector.
 //
 // Mapping to CDNA4 (d = 64 / 128; q_per_kv <= 8):
-//   * One workgroup of 4 waves per (layer, stream); the waves split the
-//     tokens into 32-token chunks and merge their softmax partials in LDS.
+//   * One workgroup of 8 waves per two adjacent streams of a layer (the two
+//     K/V heads of a sequence share each 128-byte line of a time-major
+//     cache); four waves split each stream's tokens into 32-token chunks and
+//     merge their softmax partials in LDS.
 //   * Each chunk's code and scale rows arrive by direct-to-LDS loads
 //     (global_load_lds), three chunks in flight per wave.  Rows may sit
 //     anywhere (the cache layout is given by strides).
@@ -52,12 +54,18 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;      // waves per workgroup; they split the tokens
+constexpr int kWavesPerStream = 4; // a stream's tokens are split over 4 waves
 constexpr int kChunk = 32;     // tokens per chunk (one p.v k-step)
-constexpr int kBufs = 3;       // chunk buffers per wave
+constexpr int kBufs = 3;       // chunk buffers per wave (kBufs - 1 chunks in flight)
+// Waves per SIMD the register allocation targets.  The LDS ring (about 60 KB
+// per workgroup at d = 128) allows two workgroups per CU; a two-slot ring at
+// three waves per SIMD measured no faster (423 vs 417 us on the Qwen2.5-1.5B
+// decode cache).
+constexpr int kWavesPerEU = 2;
 constexpr int kMaxQ = 8;       // query heads per K/V head
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, below any score
 constexpr float kVShift = 0.0625f;   // V is decoded as q * s / 16
+constexpr float kRescaleSlack = 8.0f;  // base-2 headroom of the running softmax max
 
 struct Params {
   const uint4* q;        // [layers][streams][q_per_kv][d] fp16
@@ -68,12 +76,13 @@ struct Params {
   uint64_t seed;
   int64_t rows_per_seed;
   int32_t seed_period;
-  int32_t tokens, q_per_kv;
+  int32_t streams, tokens, q_per_kv;
   float qscale;  // softmax_scale * log2(e): scores come out in base-2 units
 };
 
-template <int D, int GR>
+template <int D, int GR, int SPW = 1>
 struct Cfg {
+  static constexpr int WAVES = SPW * kWavesPerStream;
   static constexpr int KS = D / 32;       // q.k k-steps = 16-byte pieces per code row
   static constexpr int NT = D / 16;       // p.v output tiles of 16 dims
   static constexpr int RB = D / 2;        // code bytes per row
@@ -85,8 +94,8 @@ struct Cfg {
   static constexpr int CODE_DMA = CODE_BYTES / 1024;             // 16-byte loads per chunk per K or V
   static constexpr int NDMA = 2 * CODE_DMA + (SPR == 4 ? 2 : 1);
   static constexpr int QROW = D + 4;  // fp32 row stride of the query / output staging
-  static constexpr int SLOT_ARRAY = kWaves * BUF;  // one ring slot of every wave
-  static constexpr int COMBINE = kWaves * kMaxQ * QROW * 4 + 2 * kWaves * kMaxQ * 4;
+  static constexpr int SLOT_ARRAY = WAVES * BUF;  // one ring slot of every wave
+  static constexpr int COMBINE = WAVES * kMaxQ * QROW * 4 + 2 * WAVES * kMaxQ * 4;
   static_assert(COMBINE <= SLOT_ARRAY, "the merge area fits in ring slot 0");
   static_assert(GR >= 32 && D % GR == 0, "groups of at least 32 values");
 };
@@ -124,6 +133,15 @@ __device__ __forceinline__ f16x2_t code_pair(uint32_t w) {
   }
 }
 
+// half SEL of w (fp16) times b plus c, in fp32 (one v_fma_mix_f32).  Plain
+// code, not inline asm: b is an MFMA result, and the compiler inserts the wait
+// states between an MFMA and a VALU read of its result only for instructions
+// it can see.
+template <int SEL>
+__device__ __forceinline__ float half_fma(uint32_t w, float b, float c) {
+  return __builtin_fmaf((float)as_h2(w)[SEL], b, c);
+}
+
 __device__ __forceinline__ f16x8_t pack8(f16x2_t a, f16x2_t b, f16x2_t c, f16x2_t d) {
   const u32x4v_t w = {as_u32(a), as_u32(b), as_u32(c), as_u32(d)};
   return __builtin_bit_cast(f16x8_t, w);
@@ -139,6 +157,16 @@ __device__ __forceinline__ f32x4_t mfma(f16x8_t a, f16x8_t b, f32x4_t c) {
 __device__ __forceinline__ float add_ror8(float x) {
   const int y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false);
   return x + __int_as_float(y);
+}
+
+// Max of x over lanes n, n + 16, n + 32, n + 48 (the four lane groups that
+// hold one query column), with the gfx950 lane-swap instructions: swapping
+// x with itself across 16-lane rows and then across 32-lane halves.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ uint64_t seed_of_row(const Params& p, int64_t row) {
@@ -211,38 +239,55 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int6
   }
 }
 
-template <int D, int GR, int ROT>
-__global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
-  using C = Cfg<D, GR>;
+template <int D, int GR, int ROT, int SPW>
+__global__ void __launch_bounds__(64 * SPW * kWavesPerStream) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
+attn_decode_kernel(Params p) {
+  using C = Cfg<D, GR, SPW>;
+  constexpr int kWaves = C::WAVES, kStreams = SPW;
   // Three ring slots as three LDS arrays: the compiler then tells the
   // direct-to-LDS loads of one slot from the reads of another and waits only
   // for the chunk being read.
   __shared__ __attribute__((aligned(16))) uint8_t slot0[C::SLOT_ARRAY];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[C::SLOT_ARRAY];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[C::SLOT_ARRAY];
-  __shared__ __attribute__((aligned(16))) float stage[kMaxQ * C::QROW];  // query in, output out (fp32)
-  __shared__ int qexp[kMaxQ];
+  __shared__ __attribute__((aligned(16))) uint8_t slot2[kBufs > 2 ? C::SLOT_ARRAY : 16];
+  __shared__ __attribute__((aligned(16))) float stage_all[kStreams * kMaxQ * C::QROW];  // query in, output out
+  __shared__ int qexp_all[kStreams * kMaxQ];
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;
   const int G = p.q_per_kv, T = p.tokens;
-  const int stream = blockIdx.x, layer = blockIdx.y;
+  // Workgroups go to the 8 XCDs round-robin (id b to XCD b % 8).  Give XCD x
+  // one contiguous range of work items (a layer's stream pairs in order), so
+  // the workgroups running together on an XCD read neighbouring streams, whose
+  // scale rows share 128-byte lines in a time-major cache, through one L2.
+  const int nwg = gridDim.x, b = blockIdx.x;
+  const int per = nwg >> 3, extra = nwg & 7, x = b & 7;
+  const int item = x * per + (x < extra ? x : extra) + (b >> 3);
+  const int pairs_per_layer = (p.streams + kStreams - 1) / kStreams;
+  const int layer = item / pairs_per_layer;
+  const int sw = w / kWavesPerStream, part_w = w % kWavesPerStream;  // stream of the wave, token part
+  const int stream = (item - layer * pairs_per_layer) * kStreams + sw;
+  const bool active = stream < p.streams;
   const int64_t row_k = (int64_t)layer * p.stride_layer + (int64_t)stream * p.stride_stream;
   const int64_t row_v = row_k + p.stride_kv;
-  const int64_t qrow = ((int64_t)layer * gridDim.x + stream) * G;  // first query row of this stream
+  const int64_t qrow = ((int64_t)layer * p.streams + stream) * G;  // first query row of this stream
+  float* const stage = stage_all + sw * kMaxQ * C::QROW;
+  int* const qexp = qexp_all + sw * kMaxQ;
 
-  const int nchunks = (T + kChunk - 1) / kChunk;
-  const int c_begin = w * nchunks / kWaves, c_end = (w + 1) * nchunks / kWaves;
+  const int nchunks = active ? (T + kChunk - 1) / kChunk : 0;
+  const int c_begin = part_w * nchunks / kWavesPerStream, c_end = (part_w + 1) * nchunks / kWavesPerStream;
+  const bool lead = active && part_w == 0;  // rotates the stream's queries and outputs
 
-  // ---- prologue: queries (wave 0) and the first two chunks (every wave) ----
+  // ---- prologue: queries (lead waves) and the first two chunks (every wave) ----
   uint4 qv[D / 8];
-  if (w == 0 && lane < G) {
+  if (lead && lane < G) {
     const uint4* src = p.q + (qrow + lane) * (D / 8);
     sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
   }
   if (c_begin < c_end) issue_chunk<D, GR>(p, row_k, row_v, c_begin * kChunk, slot0 + w * C::BUF, lane);
-  if (c_begin + 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c_begin + 1) * kChunk, slot1 + w * C::BUF, lane);
-  if (w == 0) {
+  if (kBufs > 2 && c_begin + 1 < c_end)
+    issue_chunk<D, GR>(p, row_k, row_v, (c_begin + 1) * kChunk, slot1 + w * C::BUF, lane);
+  if (lead) {
     uint32_t mk[D / 2];
     wave_sign_masks<D>(seed_of_row(p, row_k), lane, mk);
     if (lane < G) {
@@ -318,15 +363,17 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
   const int vgi = (8 * dw) / GR;  // the scale group of those dims
   const uint32_t vsel = (D == 64 && n >= 8) ? 0x07060302u : 0x05040100u;
 
-  // one chunk in ring slot B (chunk c - c_begin lives in slot (c - c_begin) % 3)
+  // one chunk in ring slot B (chunk c - c_begin lives in slot (c - c_begin) % kBufs);
+  // kBufs - 1 chunks are in flight while one is computed
   auto chunk = [&](auto B, int c) {
     constexpr int b = RTQ_CI(B);
+    constexpr int nb = (b + kBufs - 1) % kBufs;  // slot of chunk c + kBufs - 1
     uint8_t* const buf = b == 0 ? slot0 + w * C::BUF : b == 1 ? slot1 + w * C::BUF : slot2 + w * C::BUF;
-    uint8_t* const next = b == 0 ? slot2 + w * C::BUF : b == 1 ? slot0 + w * C::BUF : slot1 + w * C::BUF;
-    if (c + 1 < c_end) wait_vmcnt<C::NDMA>();
+    uint8_t* const next = nb == 0 ? slot0 + w * C::BUF : nb == 1 ? slot1 + w * C::BUF : slot2 + w * C::BUF;
+    if (kBufs > 2 && c + 1 < c_end) wait_vmcnt<C::NDMA>();
     else wait_vmcnt<0>();
     lds_sync();
-    if (c + 2 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + 2) * kChunk, next, lane);
+    if (c + kBufs - 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + kBufs - 1) * kChunk, next, lane);
     const uint8_t* kc = buf;
     const uint8_t* vc = buf + C::CODE_BYTES;
     const uint8_t* ks = buf + 2 * C::CODE_BYTES;
@@ -363,9 +410,9 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
         sfor<4>([&](auto R) {
           constexpr int r = RTQ_CI(R);
           if constexpr (C::SPR == 4) {
-            s[r] = mix_fma<gi & 1>(sk[2 * r + (gi >> 1)], part[r], s[r]);
+            s[r] = half_fma<gi & 1>(sk[2 * r + (gi >> 1)], part[r], s[r]);
           } else {
-            s[r] = mix_fma<gi>(sk[r], part[r], s[r]);
+            s[r] = half_fma<gi>(sk[r], part[r], s[r]);
           }
         });
       });
@@ -378,26 +425,30 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
     });
 
     // ---- online softmax (base 2) over the chunk, per query column ----
+    // The running max moves only when a score passes it by more than 8
+    // (weights stay <= 2^8, well inside fp16), so the accumulators are
+    // rescaled a handful of times per stream instead of on most chunks.
     float cmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                        fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    cmax = max_over_row_groups(cmax);
+    const bool grow = cmax > m_run + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float m_new = grow ? cmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+      sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] *= alpha; });
+      m_run = m_new;
+    }
     float pr[2][4];
     float psum = 0.0f;
     sfor<2>([&](auto TAU) {
       sfor<4>([&](auto R) {
-        const float e = __builtin_amdgcn_exp2f(sc[RTQ_CI(TAU)][RTQ_CI(R)] - m_new);
+        const float e = __builtin_amdgcn_exp2f(sc[RTQ_CI(TAU)][RTQ_CI(R)] - m_run);
         pr[RTQ_CI(TAU)][RTQ_CI(R)] = e;
         psum += e;
       });
     });
-    l_run = __builtin_fmaf(l_run, alpha, psum);
-    m_run = m_new;
-    if (__ballot(alpha != 1.0f)) {
-      sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] *= alpha; });
-    }
+    l_run += psum;
     // P^T operand: element 4 tau + r = token 16 tau + 4h + r of query n
     const f16x8_t pb = pack8((f16x2_t){(_Float16)pr[0][0], (_Float16)pr[0][1]},
                              (f16x2_t){(_Float16)pr[0][2], (_Float16)pr[0][3]},
@@ -441,11 +492,13 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
     chunk(ic<0>{}, c);
     if (c + 1 >= c_end) break;
     chunk(ic<1>{}, c + 1);
-    if (c + 2 >= c_end) break;
-    chunk(ic<2>{}, c + 2);
+    if constexpr (kBufs > 2) {
+      if (c + 2 >= c_end) break;
+      chunk(ic<2>{}, c + 2);
+    }
   }
 
-  // ---- merge the waves' partials ----
+  // ---- merge the partials of each stream's waves ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   __syncthreads();  // every wave is done with its ring; the merge area aliases it
@@ -469,22 +522,24 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
     });
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
-    const int g = idx / D, dim = idx % D;
+  for (int idx = threadIdx.x; idx < kStreams * G * D; idx += 64 * kWaves) {
+    const int s2 = idx / (G * D), g = (idx / D) % G, dim = idx % D;
+    const int w0 = s2 * kWavesPerStream;
     float mx = kNegBig;
-    for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
+    for (int ww = w0; ww < w0 + kWavesPerStream; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
     float num = 0.0f, den = 0.0f;
-    for (int ww = 0; ww < kWaves; ++ww) {
+    for (int ww = w0; ww < w0 + kWavesPerStream; ++ww) {
       const float f = __builtin_amdgcn_exp2f(mw[ww * kMaxQ + g] - mx);
       den = __builtin_fmaf(f, lw[ww * kMaxQ + g], den);
       num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
     }
-    stage[g * C::QROW + dim] = num / (den * kVShift);
+    // a stream past the end has no partials (den = 0); nothing reads its row
+    stage_all[(s2 * kMaxQ + g) * C::QROW + dim] = den > 0.0f ? num / (den * kVShift) : 0.0f;
   }
   __syncthreads();
 
   // ---- rotate the outputs back: o = D_V R^T o_rot ----
-  if (w == 0) {
+  if (lead) {
     uint32_t mvs[D / 2];
     wave_sign_masks<D>(seed_of_row(p, row_v), lane, mvs);
     if (lane < G) {
@@ -519,10 +574,11 @@ __global__ void __launch_bounds__(64 * kWaves) attn_decode_kernel(Params p) {
 
 using KernelFn = const void*;
 
-template <int ROT>
+
+template <int ROT, int SPW>
 KernelFn find_kernel(int d, int g) {
 #define RTQ_ATTN_CASE(DD, GG) \
-  if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT>);
+  if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT, SPW>);
   RTQ_ATTN_CASE(64, 32) RTQ_ATTN_CASE(64, 64)
   RTQ_ATTN_CASE(128, 32) RTQ_ATTN_CASE(128, 64) RTQ_ATTN_CASE(128, 128)
 #undef RTQ_ATTN_CASE
@@ -561,13 +617,17 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
     if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return RTQ_ERR_INVALID_ARG;
-  const KernelFn fn = rot == 0 ? find_kernel<0>(d, group) : find_kernel<1>(d, group);
+  // One stream per workgroup (measured faster than two adjacent streams per
+  // 8-wave workgroup on the time-major decode cache: 414 vs 537 us).
+  const int spw = 1;
+  const KernelFn fn = rot == 0 ? find_kernel<0, 1>(d, group) : find_kernel<1, 1>(d, group);
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   if (q_per_kv < 1) return RTQ_ERR_INVALID_ARG;
   if (q_per_kv > kMaxQ) return RTQ_ERR_UNSUPPORTED;
   if (layers == 0 || streams == 0) return RTQ_OK;
   if (tokens < 1 || tokens > 0x7fffff00) return RTQ_ERR_INVALID_ARG;
-  if (layers > 65535) return RTQ_ERR_INVALID_ARG;
+  const int64_t wgs = (int64_t)layers * ((streams + spw - 1) / spw);
+  if (wgs > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
   if (!q || !codes || !scales || !out) return RTQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return RTQ_ERR_INVALID_ARG;
   // largest row the kernel reads, in 128-bit arithmetic
@@ -592,12 +652,13 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   p.seed = seed;
   p.rows_per_seed = rps;
   p.seed_period = period;
+  p.streams = streams;
   p.tokens = tokens;
   p.q_per_kv = q_per_kv;
   p.qscale = (float)((double)softmax_scale * 1.4426950408889634074);
   void* kargs[] = {&p};
   const hipError_t e =
-      hipLaunchKernel(fn, dim3((unsigned)streams, (unsigned)layers), dim3(64 * kWaves), kargs, 0, stream);
+      hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * kWavesPerStream * spw), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
 

@@ -122,7 +122,7 @@ def test_attention_rejects_bad_arguments_without_launching(name):
     assert attn_call(name, strides=(300, 150, 50, -1)) == bad
     assert attn_call(name, softmax_scale=float("nan")) == bad
     assert attn_call(name, softmax_scale=float("inf")) == bad
-    assert attn_call(name, layers=70000, strides=(0, 150, 50, 1)) == bad
+    assert attn_call(name, layers=70000, streams=40000, strides=(0, 150, 50, 1)) == bad
     for kw in ({"q": 0}, {"codes": 0}, {"scales": 0}, {"out": 0}, {"q": Q + 8}, {"codes": K + 4},
                {"scales": S_ + 2}, {"out": O + 8}):
         assert attn_call(name, **kw) == bad, kw
