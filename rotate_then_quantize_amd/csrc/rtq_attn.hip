@@ -5,9 +5,14 @@
 // dequantizes and rotates it back when attention reads it ("Quantization
 // Speed Is Often a Kernel Problem", "First, the 17%").  Here the dequantize
 // happens in registers inside the attention kernel, so no fp16 K/V ever
-// lands in HBM (the fusion of dequantization into the consumer, "Chapter
-// 25 - Quantization: The Hardware View", section "Kernels: Marlin, CUTLASS,
-// and Why INT4 Packing Needs Special Code").
+// lands in HBM: a separate dequantize pass would write and re-read the fp16
+// cache and give back the bandwidth the int4 codes save ("Day 9 -
+// Quantization: Shrink the Bytes Themselves", "Dequantization Must Fuse into
+// the Kernel"; "Chapter 25 - Quantization: The Hardware View", "The
+// Dequant/Requant Tax").  Per-group scales split each dot product into
+// blocks that are scaled one by one and summed in higher precision (same
+// chapter, "Granularity: Per-Tensor vs Per-Channel vs Per-Group"): here one
+// fp32 scaling per 32-dim group of q.k.
 //
 // R is orthogonal and each stream's keys share one sign vector D_K (values
 // one D_V), so with y = R D_K q and z_t = the dequantized rotated key,
@@ -17,13 +22,14 @@
 // inverse-rotating every cached vector.
 //
 // Mapping to CDNA4 (d = 64 / 128; q_per_kv <= 8):
-//   * One workgroup of 8 waves per two adjacent streams of a layer (the two
-//     K/V heads of a sequence share each 128-byte line of a time-major
-//     cache); four waves split each stream's tokens into 32-token chunks and
-//     merge their softmax partials in LDS.
+//   * One workgroup of 4 waves per (layer, stream); the waves split the
+//     stream's tokens into 32-token chunks and merge their softmax partials
+//     in LDS.  Workgroup ids are remapped so that each XCD works through one
+//     contiguous range of (layer, stream) pairs.
 //   * Each chunk's code and scale rows arrive by direct-to-LDS loads
-//     (global_load_lds), three chunks in flight per wave.  Rows may sit
-//     anywhere (the cache layout is given by strides).
+//     (global_load_lds) into a three-slot ring, two chunks ahead of the one
+//     being computed.  Rows may sit anywhere (the cache layout is given by
+//     strides).
 //   * q.k is a [16 tokens x 32 dims] x [32 dims x 16 columns] MFMA
 //     (v_mfma_f32_16x16x32_f16) per group of 32 dims.  The A operand is the
 //     exact int4 code value as fp16 (no scale), so each group's partial dot
@@ -80,9 +86,9 @@ struct Params {
   float qscale;  // softmax_scale * log2(e): scores come out in base-2 units
 };
 
-template <int D, int GR, int SPW = 1>
+template <int D, int GR>
 struct Cfg {
-  static constexpr int WAVES = SPW * kWavesPerStream;
+  static constexpr int WAVES = kWavesPerStream;
   static constexpr int KS = D / 32;       // q.k k-steps = 16-byte pieces per code row
   static constexpr int NT = D / 16;       // p.v output tiles of 16 dims
   static constexpr int RB = D / 2;        // code bytes per row
@@ -239,11 +245,11 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int6
   }
 }
 
-template <int D, int GR, int ROT, int SPW>
-__global__ void __launch_bounds__(64 * SPW * kWavesPerStream) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
+template <int D, int GR, int ROT>
+__global__ void __launch_bounds__(64 * kWavesPerStream) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
 attn_decode_kernel(Params p) {
-  using C = Cfg<D, GR, SPW>;
-  constexpr int kWaves = C::WAVES, kStreams = SPW;
+  using C = Cfg<D, GR>;
+  constexpr int kWaves = C::WAVES, kStreams = 1;
   // Three ring slots as three LDS arrays: the compiler then tells the
   // direct-to-LDS loads of one slot from the reads of another and waits only
   // for the chunk being read.
@@ -575,10 +581,10 @@ attn_decode_kernel(Params p) {
 using KernelFn = const void*;
 
 
-template <int ROT, int SPW>
+template <int ROT>
 KernelFn find_kernel(int d, int g) {
 #define RTQ_ATTN_CASE(DD, GG) \
-  if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT, SPW>);
+  if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT>);
   RTQ_ATTN_CASE(64, 32) RTQ_ATTN_CASE(64, 64)
   RTQ_ATTN_CASE(128, 32) RTQ_ATTN_CASE(128, 64) RTQ_ATTN_CASE(128, 128)
 #undef RTQ_ATTN_CASE
@@ -617,16 +623,17 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
     if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
     return RTQ_ERR_INVALID_ARG;
-  // One stream per workgroup (measured faster than two adjacent streams per
-  // 8-wave workgroup on the time-major decode cache: 414 vs 537 us).
-  const int spw = 1;
-  const KernelFn fn = rot == 0 ? find_kernel<0, 1>(d, group) : find_kernel<1, 1>(d, group);
+  // One stream per workgroup.  (Two adjacent streams per 8-wave workgroup,
+  // to share the 128-byte lines of a time-major cache, measured slower: 537
+  // vs 414 us on the Qwen2.5-1.5B decode cache, as the whole CU then waits
+  // at the workgroup's barriers.)
+  const KernelFn fn = rot == 0 ? find_kernel<0>(d, group) : find_kernel<1>(d, group);
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   if (q_per_kv < 1) return RTQ_ERR_INVALID_ARG;
   if (q_per_kv > kMaxQ) return RTQ_ERR_UNSUPPORTED;
   if (layers == 0 || streams == 0) return RTQ_OK;
   if (tokens < 1 || tokens > 0x7fffff00) return RTQ_ERR_INVALID_ARG;
-  const int64_t wgs = (int64_t)layers * ((streams + spw - 1) / spw);
+  const int64_t wgs = (int64_t)layers * streams;
   if (wgs > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
   if (!q || !codes || !scales || !out) return RTQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return RTQ_ERR_INVALID_ARG;
@@ -658,7 +665,7 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   p.qscale = (float)((double)softmax_scale * 1.4426950408889634074);
   void* kargs[] = {&p};
   const hipError_t e =
-      hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * kWavesPerStream * spw), kargs, 0, stream);
+      hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * kWavesPerStream), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
 
