@@ -544,6 +544,97 @@ def attn_main(args, w, dev):
     print(json.dumps(result), flush=True)
 
 
+def decode_cache_main(args, w, dev):
+    """Per-step cost of keeping a dequantized fp16 prefix with a 16-token fp16
+    window (append each token to the window; every 16th step quantize the
+    window in place and dequantize just those rows), against dequantizing
+    the whole cache every step."""
+    import torch
+    import rotate_then_quantize_amd as rtq
+    from rotate_then_quantize_amd.decode_cache import DecodeCache
+    rot, W = args.rot, 16
+    L, S, T, d, g = w.layers, w.streams, w.tokens - 1, w.d, w.group  # prefix tokens; one more per step
+    steps = max(W, (args.steps // W) * W)
+    cap = T + steps
+    log(f"decode cache, workload {w.name}: L={L} S={S} prefix {T} tokens, window {W}, {steps} steps, d={d} g={g}")
+    cache = DecodeCache(L, S, cap, d, g, w.sign_seed, rot, W, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    cache.prefill(torch.randn((L, 2, S, T, d), generator=gen, device=dev).to(torch.float16))
+    new = torch.randn((steps + args.warmup, L, 2, S, d), generator=gen, device=dev).to(torch.float16)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    # the window policy: `steps` appends (steps / 16 window flushes)
+    ev[0].record(stream)
+    for i in range(steps):
+        cache.append(new[i])
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    window_ms = ev[0].elapsed_time(ev[1]) / steps
+    # one flush alone: quantize 16 tokens in place + refresh their dequantized rows
+    t0 = cache.quantized - W
+    blk = torch.randn((L, 2, S, W, d), generator=gen, device=dev).to(torch.float16)
+    flush_ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    for _ in range(2):
+        rtq.quant_append(rot, blk, cache.codes, cache.scales, cache.strides, t0, g, cache.seed,
+                         cache.rows_per_seed, cache.seed_period)
+        rtq.dequant_rows(rot, cache.codes, cache.scales, cache.prefix, L, S, t0, W, cache.strides, g, cache.seed,
+                         cache.rows_per_seed, cache.seed_period)
+    flush_ev[0].record(stream)
+    rtq.quant_append(rot, blk, cache.codes, cache.scales, cache.strides, t0, g, cache.seed, cache.rows_per_seed,
+                     cache.seed_period)
+    flush_ev[1].record(stream)
+    rtq.dequant_rows(rot, cache.codes, cache.scales, cache.prefix, L, S, t0, W, cache.strides, g, cache.seed,
+                     cache.rows_per_seed, cache.seed_period)
+    flush_ev[2].record(stream)
+    torch.cuda.synchronize()
+    append_ms, rows_ms = flush_ev[0].elapsed_time(flush_ev[1]), flush_ev[1].elapsed_time(flush_ev[2])
+    # without the dequantized prefix: quantize the new token, dequantize every cached row, each step
+    n_all = cache.codes.shape[0]
+    y = torch.empty((n_all, d), dtype=torch.float16, device=dev)
+    for _ in range(args.warmup):
+        rtq.dequant_inv(rot, cache.codes, cache.scales, d, g, cache.seed, cache.rows_per_seed, cache.seed_period,
+                        out=y)
+    tok = new[0].reshape(L, 2, S, 1, d).contiguous()
+    full_steps = 20
+    ev[0].record(stream)
+    for i in range(full_steps):
+        rtq.quant_append(rot, tok, cache.codes, cache.scales, cache.strides, cap - 1, g, cache.seed,
+                         cache.rows_per_seed, cache.seed_period)
+        rtq.dequant_inv(rot, cache.codes, cache.scales, d, g, cache.seed, cache.rows_per_seed, cache.seed_period,
+                        out=y)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    full_ms = ev[0].elapsed_time(ev[1]) / full_steps
+    rows_flush = L * 2 * S * W
+    bpv = w.bytes_per_vector()
+    log(f"window policy {window_ms * 1e3:.1f} us/step | flush: append {append_ms * 1e3:.1f} us + refresh "
+        f"{rows_ms * 1e3:.1f} us ({rows_flush} rows) | full re-dequantize {full_ms * 1e3:.1f} us/step")
+    result = {
+        "metric": "decode-step cache maintenance time, dequantized prefix + 16-token fp16 window, 1 GPU",
+        "value": window_ms * 1e3,
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": window_ms,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": L, "streams": S, "prefix_tokens": T, "window": W, "d": d,
+                   "group": g, "rotation": rot, "layout": "[layer][K,V][stream][token]", "capacity": cap},
+        "flush": {"append_us": append_ms * 1e3, "refresh_us": rows_ms * 1e3, "rows": rows_flush,
+                  "append_GBps": rows_flush * bpv / append_ms / 1e6, "refresh_GBps": rows_flush * bpv / rows_ms / 1e6},
+        "full_redequantize": {"us_per_step": full_ms * 1e3, "rows": n_all,
+                              "ops": "append of the new token + dequant_inv of every cache row, each step"},
+        "speedup_vs_full_redequantize": full_ms / window_ms,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -553,6 +644,8 @@ def main():
                     help="workload id (default 2; 3 with --attn)")
     ap.add_argument("--attn", action="store_true",
                     help="measure decode attention over the int4 cache instead of forward + inverse")
+    ap.add_argument("--decode-cache", action="store_true",
+                    help="measure the dequantized-prefix cache with a 16-token fp16 window (workload 3 by default)")
     ap.add_argument("--attn-layout", choices=["heads", "workload"], default="heads",
                     help="attention cache layout: 'heads' = [layer][K,V][stream][token] (each head's tokens "
                          "contiguous, as a per-layer [batch, heads, tokens, d] cache), 'workload' = the "
@@ -574,7 +667,7 @@ def main():
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
     if args.workload is None:
-        args.workload = 3 if args.attn else 2
+        args.workload = 3 if (args.attn or args.decode_cache) else 2
 
     if args.summarize_trace or args.summarize_traffic:
         from rotate_then_quantize_amd import workloads as W
@@ -616,6 +709,9 @@ def main():
     w = W.WORKLOADS[args.workload]
     if args.attn:
         attn_main(args, w, dev)
+        return
+    if args.decode_cache:
+        decode_cache_main(args, w, dev)
         return
     rot = args.rot
     if rot not in w.rots:

@@ -127,6 +127,61 @@ rtq_status srht_dequant_inv(const void* codes_u8, const void* scales_f16, void* 
                             hipStream_t stream);
 
 /*
+ * srft_quant_append / srht_quant_append -- the forward step written in place
+ * into a cache whose rows are addressed by strides: the new tokens of every
+ * layer, K/V and stream go straight to their cache rows.  With
+ * srft_dequant_rows it maintains a dequantized fp16 copy of the cache prefix
+ * between decode steps while the newest tokens stay in fp16 and are quantized
+ * when that window fills ("Quantization Speed Is Often a Kernel Problem",
+ * "First, the 17%").
+ *
+ *   x_f16       in : [layers][2][streams][n_tokens][d] fp16, contiguous
+ *                    (index 0 / 1 of the second axis = keys / values)
+ *   codes_u8    out: cache codes, rows of d/2 bytes
+ *   scales_f16  out: cache scales, rows of d/group fp16
+ * x[l][kv][s][j] goes to cache row
+ *   l*stride_layer + kv*stride_kv + s*stride_stream + (t0 + j)*stride_token
+ * and is rotated, quantized and packed exactly as srft_quant_fwd would do for
+ * that row (its seed is the seed rule applied to that cache row).  Other rows
+ * are not touched.  The strides must map distinct (layer, kv, stream, token)
+ * to distinct rows.
+ *
+ * Supported: d in {64, 128} with the groups of the common conventions, else
+ * RTQ_ERR_UNSUPPORTED.  layers, streams, t0, n_tokens, strides >= 0,
+ * layers*2*streams*n_tokens <= 0xFFFFFF00, else RTQ_ERR_INVALID_ARG; an empty
+ * block returns RTQ_OK.  The caller guarantees that the cache holds every row
+ * the strides reach.  Pointers, streams and errors as in the common
+ * conventions.
+ */
+rtq_status srft_quant_append(const void* x_f16, void* codes_u8, void* scales_f16, int32_t layers, int32_t streams,
+                             int32_t t0, int32_t n_tokens, int32_t d, int32_t group, int64_t stride_layer,
+                             int64_t stride_kv, int64_t stride_stream, int64_t stride_token, uint64_t seed,
+                             int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+rtq_status srht_quant_append(const void* x_f16, void* codes_u8, void* scales_f16, int32_t layers, int32_t streams,
+                             int32_t t0, int32_t n_tokens, int32_t d, int32_t group, int64_t stride_layer,
+                             int64_t stride_kv, int64_t stride_stream, int64_t stride_token, uint64_t seed,
+                             int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+/*
+ * srft_dequant_rows / srht_dequant_rows -- the inverse step on the cache rows
+ * of tokens t0 .. t0+n_tokens-1 of every (layer, K/V, stream), addressed as in
+ * srft_quant_append, written to the same rows of y_f16 (an fp16 copy of the
+ * cache with rows of d fp16): y[row] is what srft_dequant_inv gives for that
+ * row.  Other rows of y are not touched.  Arguments, support and errors as
+ * for srft_quant_append; y must not overlap the cache.
+ */
+rtq_status srft_dequant_rows(const void* codes_u8, const void* scales_f16, void* y_f16, int32_t layers,
+                             int32_t streams, int32_t t0, int32_t n_tokens, int32_t d, int32_t group,
+                             int64_t stride_layer, int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                             uint64_t seed, int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+rtq_status srht_dequant_rows(const void* codes_u8, const void* scales_f16, void* y_f16, int32_t layers,
+                             int32_t streams, int32_t t0, int32_t n_tokens, int32_t d, int32_t group,
+                             int64_t stride_layer, int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                             uint64_t seed, int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+/*
  * srft_attn_decode / srht_attn_decode -- one decode step of softmax attention
  * that reads the int4 cache written by srft_quant_fwd / srht_quant_fwd
  * directly: the cache is dequantized and rotated back when attention reads

@@ -8,6 +8,6 @@ from .rtq_oracle import (  # noqa: F401
     attn_decode, cache_rows, dequant_inv, dequant_rows, dequantize_groups, forward_detail, fp16_scale_from_absmax,
     int4_roundtrip_blocks, pack_nibbles, quant_fwd, quantize_groups,
     quantize_with_scale, rotate_fwd, rotate_inv, rotation_matrix, row_seed,
-    sign_matrix, sign_vector, splitmix64_stream, srft_matrix, srht_matrix,
+    sign_matrix, sign_vector, splitmix64_stream, srft_matrix, srht_matrix, window_schedule,
     unpack_nibbles,
 )

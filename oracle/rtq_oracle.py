@@ -100,12 +100,13 @@ def row_seed(seed: int, row: int, rows_per_seed: int, seed_period: int) -> int:
 
 
 def sign_matrix(n: int, d: int, seed: int, rows_per_seed: int = 0,
-                seed_period: int = 0, row0: int = 0) -> np.ndarray:
-    """[n, d] matrix of per-row sign vectors for rows row0 .. row0+n-1."""
+                seed_period: int = 0, row0: int = 0, rows=None) -> np.ndarray:
+    """[n, d] matrix of per-row sign vectors for rows row0 .. row0+n-1, or for
+    the listed row indices when ``rows`` is given."""
     cache: dict[int, np.ndarray] = {}
     out = np.empty((n, d), dtype=np.float64)
     for i in range(n):
-        s = row_seed(seed, row0 + i, rows_per_seed, seed_period)
+        s = row_seed(seed, row0 + i if rows is None else int(rows[i]), rows_per_seed, seed_period)
         if s not in cache:
             cache[s] = sign_vector(s, d)
         out[i] = cache[s]
@@ -268,53 +269,54 @@ def unpack_nibbles(b: np.ndarray) -> np.ndarray:
 
 
 def rotate_fwd(x_f16: np.ndarray, seed: int, rows_per_seed: int = 0,
-               seed_period: int = 0, rot: str = "srft", row0: int = 0) -> np.ndarray:
-    """z = R (D (.) x) per row, fp64.  Sign first, then the transform."""
+               seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None) -> np.ndarray:
+    """z = R (D (.) x) per row, fp64.  Sign first, then the transform.  Row i
+    is cache row row0 + i, or rows[i] when ``rows`` is given."""
     x = np.asarray(x_f16, dtype=np.float16).astype(np.float64)
     n, d = x.shape
-    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0)
+    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0, rows)
     u = D * x
     return u @ rotation_matrix(rot, d).T
 
 
 def rotate_inv(z: np.ndarray, seed: int, rows_per_seed: int = 0,
-               seed_period: int = 0, rot: str = "srft", row0: int = 0) -> np.ndarray:
+               seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None) -> np.ndarray:
     """u = D (.) (R^T z) per row, fp64 (before the fp16 rounding of y)."""
     z = np.asarray(z, dtype=np.float64)
     n, d = z.shape
-    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0)
+    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0, rows)
     return D * (z @ rotation_matrix(rot, d))
 
 
 def quant_fwd(x_f16: np.ndarray, group: int, seed: int, rows_per_seed: int = 0,
-              seed_period: int = 0, rot: str = "srft", row0: int = 0):
+              seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None):
     """Forward: sign, rotate, per-group absmax int4, pack.
 
     Returns (codes uint8 [n, d/2], scales float16 [n, d/group]).
     """
-    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0)
+    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0, rows)
     q, s, _ = quantize_groups(z, group)
     return pack_nibbles(q), s
 
 
 def dequant_inv(codes: np.ndarray, scales: np.ndarray, d: int, group: int,
                 seed: int, rows_per_seed: int = 0, seed_period: int = 0,
-                rot: str = "srft", row0: int = 0, return_fp64: bool = False):
+                rot: str = "srft", row0: int = 0, return_fp64: bool = False, rows=None):
     """Inverse: unpack, dequantize, inverse-rotate, sign, round to fp16."""
     q = unpack_nibbles(codes)
     if q.shape[-1] != d:
         raise ValueError("codes do not match d")
     zhat = dequantize_groups(q, scales, group)
-    u = rotate_inv(zhat, seed, rows_per_seed, seed_period, rot, row0)
+    u = rotate_inv(zhat, seed, rows_per_seed, seed_period, rot, row0, rows)
     with np.errstate(over="ignore"):
         y = u.astype(np.float16)
     return (y, u) if return_fp64 else y
 
 
 def forward_detail(x_f16: np.ndarray, group: int, seed: int, rows_per_seed: int = 0,
-                   seed_period: int = 0, rot: str = "srft", row0: int = 0) -> dict:
+                   seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None) -> dict:
     """All intermediate values of the forward step, for tolerance checks."""
-    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0)
+    z = rotate_fwd(x_f16, seed, rows_per_seed, seed_period, rot, row0, rows)
     q, s, a = quantize_groups(z, group)
     return {"z": z, "q": q, "s": s, "a": a, "codes": pack_nibbles(q)}
 
@@ -347,6 +349,20 @@ def int4_roundtrip_blocks(w: np.ndarray, block_rows: int, block_cols: int) -> np
 # reads the cache: [P1, "First, the 17%"]; "Dequantize in the attention
 # consumer" is the plain composition of dequant_inv and softmax attention).
 # ---------------------------------------------------------------------------
+
+
+def window_schedule(prefill_tokens: int, appended: int, window: int) -> tuple[int, int]:
+    """(tokens in the int4 cache, tokens in the fp16 window) after a prefill
+    of ``prefill_tokens`` (all quantized) and ``appended`` single-token
+    appends, when the newest tokens stay in an fp16 window of ``window``
+    tokens that is quantized as a whole, and the dequantized prefix refreshed,
+    when it fills ([P1] "First, the 17%")."""
+    quantized, held = prefill_tokens, 0
+    for _ in range(appended):
+        held += 1
+        if held == window:
+            quantized, held = quantized + window, 0
+    return quantized, held
 
 
 def cache_rows(layer: int, kv: int, stream: int, tokens: int, strides) -> np.ndarray:

@@ -21,6 +21,7 @@ import os
 __all__ = [
     "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
     "srft_attn_decode", "srht_attn_decode",
+    "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
     "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED",
 ]
 
@@ -67,6 +68,14 @@ def library():
         for name in ("srft_attn_decode", "srht_attn_decode"):
             fn = getattr(lib, name)
             fn.argtypes = attn_args
+            fn.restype = ctypes.c_int
+        mapped_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                       ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+        for name in ("srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"):
+            fn = getattr(lib, name)
+            fn.argtypes = mapped_args
             fn.restype = ctypes.c_int
         lib.rtq_status_string.argtypes = [ctypes.c_int]
         lib.rtq_status_string.restype = ctypes.c_char_p
@@ -213,6 +222,86 @@ def srht_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_se
 
 def attn_decode(rot, *args, **kw):
     return (srft_attn_decode if rot == "srft" else srht_attn_decode)(*args, **kw)
+
+
+def _check_block(codes, scales, d, group, strides, layers, streams, t0, n_tokens):
+    import torch
+    _need(codes, torch.uint8, "codes")
+    if codes.dim() != 2 or codes.shape[1] * 2 != d:
+        raise ValueError("codes must be [rows, d/2]")
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    _need(scales, torch.float16, "scales", (codes.shape[0], d // group))
+    strides = tuple(int(v) for v in strides)
+    if len(strides) != 4 or min(strides) < 0:
+        raise ValueError("strides must be four non-negative row counts (layer, kv, stream, token)")
+    if t0 < 0 or n_tokens < 0:
+        raise ValueError("t0 and n_tokens must be non-negative")
+    if layers and streams and n_tokens:
+        max_row = (layers - 1) * strides[0] + strides[1] + (streams - 1) * strides[2] + (t0 + n_tokens - 1) * strides[3]
+        if max_row >= codes.shape[0]:
+            raise ValueError(f"the cache has {codes.shape[0]} rows; the strides reach row {max_row}")
+    return strides
+
+
+def _append(cname, x, codes, scales, strides, t0, group, seed, rows_per_seed, seed_period, stream):
+    import torch
+    _need(x, torch.float16, "x")
+    if x.dim() != 5 or x.shape[1] != 2:
+        raise ValueError("x must be [layers, 2, streams, n_tokens, d]")
+    layers, _, streams, n_tokens, d = x.shape
+    strides = _check_block(codes, scales, d, group, strides, layers, streams, t0, n_tokens)
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+        layers, streams, t0, n_tokens, d, group, *strides, seed & ((1 << 64) - 1), rows_per_seed, seed_period,
+        _stream_handle(x, stream)))
+
+
+def _rows(cname, codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed, rows_per_seed,
+          seed_period, stream):
+    import torch
+    d = codes.shape[1] * 2 if codes.dim() == 2 else 0
+    strides = _check_block(codes, scales, d, group, strides, layers, streams, t0, n_tokens)
+    _need(y, torch.float16, "y", (codes.shape[0], d))
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+        layers, streams, t0, n_tokens, d, group, *strides, seed & ((1 << 64) - 1), rows_per_seed, seed_period,
+        _stream_handle(codes, stream)))
+    return y
+
+
+def srft_quant_append(x, codes, scales, strides, t0, group, seed, rows_per_seed=0, seed_period=0, stream=None):
+    """Quantize x [layers, 2, streams, n_tokens, d] (fp16; axis 1 = K, V) into the cache rows of tokens
+    t0 .. t0+n_tokens-1 (row = layer*s0 + kv*s1 + stream*s2 + token*s3), in place."""
+    _append("srft_quant_append", x, codes, scales, strides, t0, group, seed, rows_per_seed, seed_period, stream)
+
+
+def srht_quant_append(x, codes, scales, strides, t0, group, seed, rows_per_seed=0, seed_period=0, stream=None):
+    """srft_quant_append with the SRHT rotation."""
+    _append("srht_quant_append", x, codes, scales, strides, t0, group, seed, rows_per_seed, seed_period, stream)
+
+
+def srft_dequant_rows(codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed, rows_per_seed=0,
+                      seed_period=0, stream=None):
+    """Dequantize the cache rows of tokens t0 .. t0+n_tokens-1 of every (layer, kv, stream) into the same
+    rows of y (an fp16 [rows, d] copy of the cache); other rows of y are left as they are."""
+    return _rows("srft_dequant_rows", codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed,
+                 rows_per_seed, seed_period, stream)
+
+
+def srht_dequant_rows(codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed, rows_per_seed=0,
+                      seed_period=0, stream=None):
+    """srft_dequant_rows with the SRHT rotation."""
+    return _rows("srht_dequant_rows", codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed,
+                 rows_per_seed, seed_period, stream)
+
+
+def quant_append(rot, *args, **kw):
+    return (srft_quant_append if rot == "srft" else srht_quant_append)(*args, **kw)
+
+
+def dequant_rows(rot, *args, **kw):
+    return (srft_dequant_rows if rot == "srft" else srht_dequant_rows)(*args, **kw)
 
 
 def quant_fwd(rot, *args, **kw):

@@ -494,3 +494,33 @@ def check_attn_cache_layout(m):
                 for t, r in enumerate(m.cache_rows(l, kv, s, T, _tm(L, S))):
                     tm[(t, l, kv, s)] = int(r)
     assert [tm[k] for k in sorted(tm)] == list(range(L * 2 * S * T))
+
+
+
+# ---------------------------------------------------------------------------
+# Row lists and the decode-cache window
+# ---------------------------------------------------------------------------
+
+
+def check_row_list_matches_single_rows(m):
+    """quant_fwd / dequant_inv with an explicit row list give, row by row,
+    what a one-row call at that row index gives (the seed follows the row)."""
+    rng = np.random.default_rng(7)
+    d, g = 64, 32
+    rows = np.array([5, 40, 41, 7, 130, 2])
+    x = rng.standard_normal((len(rows), d)).astype(np.float16)
+    codes, scales = m.quant_fwd(x, g, 99, 8, 5, "srft", rows=rows)
+    y = m.dequant_inv(codes, scales, d, g, 99, 8, 5, "srft", rows=rows)
+    for i, r in enumerate(rows):
+        c1, s1 = m.quant_fwd(x[i:i + 1], g, 99, 8, 5, "srft", row0=int(r))
+        assert np.array_equal(codes[i:i + 1], c1) and np.array_equal(scales[i:i + 1], s1)
+        y1 = m.dequant_inv(c1, s1, d, g, 99, 8, 5, "srft", row0=int(r))
+        assert np.array_equal(y[i:i + 1], y1)
+
+
+def check_window_schedule_closed_form(m):
+    """After a prefill of T0 tokens and k appends with a window of W tokens,
+    T0 + W*floor(k/W) tokens are quantized and k mod W stay in fp16."""
+    for t0, w in ((0, 16), (20, 16), (5, 4), (3, 1)):
+        for k in range(0, 3 * w + 3):
+            assert m.window_schedule(t0, k, w) == (t0 + w * (k // w), k % w), (t0, k, w)

@@ -44,11 +44,11 @@ def near_fp16_midpoint(v, rel=1e-6):
 
 
 def check_forward(x16, codes_gpu, scales_gpu, group, seed, rps=0, period=0, rot="srft", row0=0,
-                  allow_ties=False, detail=None):
+                  allow_ties=False, detail=None, rows=None):
     """Assert the GPU forward output matches the oracle; return mismatch stats."""
     x16 = np.asarray(x16, dtype=np.float16)
     n, d = x16.shape
-    det = detail or oracle.forward_detail(x16, group, seed, rps, period, rot, row0)
+    det = detail or oracle.forward_detail(x16, group, seed, rps, period, rot, row0, rows)
     s_orc = det["s"]
     s_gpu = np.asarray(scales_gpu, dtype=np.float16).reshape(s_orc.shape)
     diff = s_gpu.view(np.uint16) != s_orc.view(np.uint16)
@@ -86,11 +86,13 @@ def check_forward(x16, codes_gpu, scales_gpu, group, seed, rps=0, period=0, rot=
     return {"scale_1ulp": int(diff.sum()), "code_ties": nm, "elements": int(q_ref.size)}
 
 
-def check_inverse(codes, scales, y_gpu, d, group, seed, rps=0, period=0, rot="srft", row0=0):
-    """Assert the GPU inverse of (codes, scales) matches the oracle's inverse of the same input."""
+def check_inverse(codes, scales, y_gpu, d, group, seed, rps=0, period=0, rot="srft", row0=0, rows=None):
+    """Assert the GPU inverse of (codes, scales) matches the oracle's inverse of the same input
+    (row i is cache row row0 + i, or rows[i] when a row list is given)."""
     codes = np.asarray(codes, dtype=np.uint8)
     scales = np.asarray(scales, dtype=np.float16)
-    y_orc, u = oracle.dequant_inv(codes, scales, d, group, seed, rps, period, rot, row0, return_fp64=True)
+    y_orc, u = oracle.dequant_inv(codes, scales, d, group, seed, rps, period, rot, row0, return_fp64=True,
+                                  rows=rows)
     y_gpu = np.asarray(y_gpu, dtype=np.float16)
     s_row = np.max(scales.astype(np.float64), axis=1, keepdims=True)
     tol = np.maximum(2e-3 * s_row, fp16_ulp(u)) * (1 + 1e-9)

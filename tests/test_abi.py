@@ -24,8 +24,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv", "srft_quant_fwd",
-                                    "srht_attn_decode", "srht_dequant_inv", "srht_quant_fwd"]
+    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv", "srft_dequant_rows",
+                                    "srft_quant_append", "srft_quant_fwd", "srht_attn_decode", "srht_dequant_inv",
+                                    "srht_dequant_rows", "srht_quant_append", "srht_quant_fwd"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -158,6 +159,40 @@ def test_attention_rejects_overlapping_output(name):
     assert attn_call(name, out=Q + 4096) == rtq.RTQ_ERR_INVALID_ARG
     assert attn_call(name, out=K + 16384) == rtq.RTQ_ERR_INVALID_ARG
     assert attn_call(name, out=S_ - 4096) == rtq.RTQ_ERR_INVALID_ARG
+
+
+MAPPED = ["srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"]
+
+
+def mapped_call(name, a=A, b=B, c=C, layers=2, streams=3, t0=5, n=4, d=128, g=32, strides=(300, 150, 50, 1),
+                seed=1, rps=0, per=0):
+    fn = getattr(rtq.library(), name)
+    return fn(ctypes.c_void_p(a), ctypes.c_void_p(b), ctypes.c_void_p(c), layers, streams, t0, n, d, g, *strides,
+              seed, rps, per, None)
+
+
+@pytest.mark.parametrize("name", MAPPED)
+def test_mapped_rejects_bad_arguments_without_launching(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    for kw in ({"layers": -1}, {"streams": -1}, {"t0": -1}, {"n": -1}, {"rps": -1}, {"per": -1},
+               {"strides": (300, 150, -50, 1)}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
+               {"c": C + 2}, {"strides": (1 << 60, 150, 50, 1)}, {"layers": 1 << 20, "streams": 1 << 10, "n": 1 << 10}):
+        assert mapped_call(name, **kw) == bad, kw
+    for d, g in [(256, 32), (96, 32), (64, 128), (128, 16)]:
+        assert mapped_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
+
+
+@pytest.mark.parametrize("name", MAPPED)
+def test_mapped_empty_block_is_a_no_op(name):
+    assert mapped_call(name, a=0, b=0, c=0, n=0) == rtq.RTQ_OK
+    assert mapped_call(name, a=0, b=0, c=0, layers=0) == rtq.RTQ_OK
+
+
+def test_mapped_rejects_overlapping_buffers():
+    # block rows reach row 299 + 5 + 3 = ... ; codes 64 B/row, scales 8 B/row, x 256 B/row
+    assert mapped_call("srft_quant_append", a=A, b=A + 1024) == rtq.RTQ_ERR_INVALID_ARG       # codes inside x
+    assert mapped_call("srft_dequant_rows", a=A, b=B, c=A + 4096) == rtq.RTQ_ERR_INVALID_ARG  # y overlaps codes
+    assert mapped_call("srft_dequant_rows", a=A, b=B, c=B - 64) == rtq.RTQ_ERR_INVALID_ARG    # y overlaps scales
 
 
 def test_python_binding_rejects_cpu_tensors():

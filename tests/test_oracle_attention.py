@@ -34,3 +34,11 @@ def test_cache_layout():
 
 def test_dequant_rows_match_rowwise_inverse():
     P.check_attn_dequant_rows_match_rowwise_inverse(oracle)
+
+
+def test_row_list_matches_single_rows():
+    P.check_row_list_matches_single_rows(oracle)
+
+
+def test_window_schedule_closed_form():
+    P.check_window_schedule_closed_form(oracle)

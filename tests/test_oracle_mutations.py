@@ -47,6 +47,8 @@ def all_pins(m):
         "attn_textbook": lambda: P.check_attn_plain_softmax_attention_on_small_case(m),
         "attn_layout": lambda: P.check_attn_cache_layout(m),
         "attn_rows": lambda: P.check_attn_dequant_rows_match_rowwise_inverse(m),
+        "row_list": lambda: P.check_row_list_matches_single_rows(m),
+        "window": lambda: P.check_window_schedule_closed_form(m),
     }
     failed = []
     for name, fn in checks.items():
@@ -108,6 +110,9 @@ MUTATIONS = {
         "    row_seeds = [row_seed(seed, int(r), rows_per_seed, seed_period) for r in rows]",
         "    row_seeds = [row_seed(seed, int(rows[0]), rows_per_seed, seed_period) for r in rows]"),
     "attention rows skip the sign flip": ("        u[idx] *= sign_vector(s, d)", "        u[idx] *= 1.0"),
+    "row list ignored by the sign matrix": (
+        "row0 + i if rows is None else int(rows[i])", "row0 + i"),
+    "window flushed one token late": ("        if held == window:", "        if held == window + 1:"),
     "attention drops the softmax scale": (
         "            sc = keys @ q[layer, st, g] * softmax_scale",
         "            sc = keys @ q[layer, st, g]"),
