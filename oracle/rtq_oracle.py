@@ -322,6 +322,110 @@ def forward_detail(x_f16: np.ndarray, group: int, seed: int, rows_per_seed: int 
 
 
 # ---------------------------------------------------------------------------
+# Other code widths and a per-channel lambda ([P1, "First, the 17%": the
+# fused recipe adds one scale per channel to the per-group absmax, and the
+# quality study runs 3-, 4-, 6- and 8-bit codes)
+#
+# Readings (the page gives neither formula): b-bit codes use the int4 rule
+# with 2^(b-1) in place of 8: s = fp16(absmax / 2^(b-1)), q = clamp(rne(z/s),
+# -2^(b-1), 2^(b-1)-1).  A row's codes form one little-endian bit stream:
+# code i fills stream bits [i*b, (i+1)*b), stream bit k is bit (k mod 8) of
+# byte k div 8, each field two's complement (b = 4 is the nibble layout
+# above).  lambda is a caller-given fp16 vector, one value per channel,
+# multiplied into x before the sign flip and divided out after the inverse
+# rotation.
+# ---------------------------------------------------------------------------
+
+CODE_BITS = (3, 4, 6, 8)
+
+
+def fp16_scale_bits(a: np.ndarray, bits: int) -> np.ndarray:
+    """s = fp16(absmax / 2^(bits-1)), round-to-nearest-even, saturated at 65504."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = (a / float(1 << (bits - 1))).astype(np.float16)
+    return np.where(np.isinf(s), np.float16(FP16_MAX), s).astype(np.float16)
+
+
+def quantize_groups_bits(z: np.ndarray, group: int, bits: int):
+    """Per-group absmax b-bit quantization of the last axis: (q, s, a)."""
+    z = np.asarray(z, dtype=np.float64)
+    d = z.shape[-1]
+    zg = z.reshape(z.shape[:-1] + (d // group, group))
+    a = np.max(np.abs(zg), axis=-1)
+    s = fp16_scale_bits(a, bits)
+    s64 = s.astype(np.float64)[..., None]
+    r = np.where(s64 > 0, zg / np.where(s64 > 0, s64, 1.0), 0.0)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    q = np.clip(np.rint(r), lo, hi).astype(np.int16)
+    return q.reshape(z.shape), s, a
+
+
+def pack_bits(q: np.ndarray, bits: int) -> np.ndarray:
+    """Rows of b-bit two's-complement codes -> bytes [..., d*bits/8], one
+    little-endian bit stream per row."""
+    q = np.asarray(q, dtype=np.int64)
+    d = q.shape[-1]
+    flat = q.reshape(-1, d) & ((1 << bits) - 1)
+    out = np.zeros((flat.shape[0], d * bits // 8), dtype=np.uint8)
+    for i in range(d):
+        for k in range(bits):
+            bit = (flat[:, i] >> k) & 1
+            pos = i * bits + k
+            out[:, pos // 8] |= (bit << (pos % 8)).astype(np.uint8)
+    return out.reshape(q.shape[:-1] + (d * bits // 8,))
+
+
+def unpack_bits(b: np.ndarray, bits: int, d: int) -> np.ndarray:
+    """Inverse of pack_bits: bytes -> sign-extended b-bit codes [..., d]."""
+    b = np.asarray(b, dtype=np.int64)
+    flat = b.reshape(-1, b.shape[-1])
+    q = np.zeros((flat.shape[0], d), dtype=np.int64)
+    for i in range(d):
+        for k in range(bits):
+            pos = i * bits + k
+            q[:, i] |= ((flat[:, pos // 8] >> (pos % 8)) & 1) << k
+    q = np.where(q >= (1 << (bits - 1)), q - (1 << bits), q)
+    return q.astype(np.int16).reshape(b.shape[:-1] + (d,))
+
+
+def forward_detail_ext(x_f16: np.ndarray, group: int, bits: int, lam_f16, seed: int, rows_per_seed: int = 0,
+                       seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None) -> dict:
+    """Forward with b-bit codes and an optional per-channel lambda: u = D (.)
+    (lambda (.) x), z = R u, per-group absmax b-bit quantization, packing."""
+    x = np.asarray(x_f16, dtype=np.float16).astype(np.float64)
+    n, d = x.shape
+    if lam_f16 is not None:
+        x = x * np.asarray(lam_f16, dtype=np.float16).astype(np.float64)[None, :]
+    D = sign_matrix(n, d, seed, rows_per_seed, seed_period, row0, rows)
+    z = (D * x) @ rotation_matrix(rot, d).T
+    q, s, a = quantize_groups_bits(z, group, bits)
+    return {"z": z, "q": q, "s": s, "a": a, "codes": pack_bits(q, bits)}
+
+
+def quant_fwd_ext(x_f16: np.ndarray, group: int, bits: int, lam_f16, seed: int, rows_per_seed: int = 0,
+                  seed_period: int = 0, rot: str = "srft", row0: int = 0, rows=None):
+    """(codes uint8 [n, d*bits/8], scales float16 [n, d/group])."""
+    det = forward_detail_ext(x_f16, group, bits, lam_f16, seed, rows_per_seed, seed_period, rot, row0, rows)
+    return det["codes"], det["s"]
+
+
+def dequant_inv_ext(codes: np.ndarray, scales: np.ndarray, d: int, group: int, bits: int, lam_f16, seed: int,
+                    rows_per_seed: int = 0, seed_period: int = 0, rot: str = "srft", row0: int = 0,
+                    return_fp64: bool = False, rows=None):
+    """Unpack b-bit codes, dequantize, inverse-rotate, flip signs, divide by
+    lambda, round to fp16."""
+    q = unpack_bits(codes, bits, d)
+    zhat = dequantize_groups(q, scales, group)
+    u = rotate_inv(zhat, seed, rows_per_seed, seed_period, rot, row0, rows)
+    if lam_f16 is not None:
+        u = u / np.asarray(lam_f16, dtype=np.float16).astype(np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        y = u.astype(np.float16)
+    return (y, u) if return_fp64 else y
+
+
+# ---------------------------------------------------------------------------
 # Generic granularity helper for the MSE-ordering check of [P4]
 # ---------------------------------------------------------------------------
 

@@ -524,3 +524,120 @@ def check_window_schedule_closed_form(m):
     for t0, w in ((0, 16), (20, 16), (5, 4), (3, 1)):
         for k in range(0, 3 * w + 3):
             assert m.window_schedule(t0, k, w) == (t0 + w * (k // w), k % w), (t0, k, w)
+
+
+
+# ---------------------------------------------------------------------------
+# Other code widths and the per-channel lambda
+# ---------------------------------------------------------------------------
+
+
+def check_ext_bits4_without_lambda_is_the_int4_path(m):
+    """b = 4 with no lambda gives exactly the int4 forward and inverse."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((12, 128)) * 3).astype(np.float16)
+    for rot in ("srft", "srht"):
+        c1, s1 = m.quant_fwd_ext(x, 32, 4, None, 5, 4, 3, rot)
+        c2, s2 = m.quant_fwd(x, 32, 5, 4, 3, rot)
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+        assert np.array_equal(m.dequant_inv_ext(c1, s1, 128, 32, 4, None, 5, 4, 3, rot),
+                              m.dequant_inv(c2, s2, 128, 32, 5, 4, 3, rot))
+
+
+def check_pack_bits_layout_fixtures(m):
+    """Hand-packed streams: code i in stream bits [i*b, (i+1)*b), least
+    significant bit first, stream bit k = bit k%8 of byte k//8."""
+    cases = [
+        (3, [1, -1, 2, -4, 3, 0, -2, 1], [185, 56, 56]),
+        (6, [5, -32, 31, -1], [5, 248, 253]),
+        (8, [-128, 127, -1, 0], [128, 127, 255, 0]),
+        (4, [3, -2], [0xE3]),
+    ]
+    for bits, codes, want in cases:
+        got = m.pack_bits(np.array([codes]), bits)[0]
+        assert got.tolist() == want, (bits, got.tolist(), want)
+        assert m.unpack_bits(got[None], bits, len(codes))[0].tolist() == codes
+
+
+def check_pack_bits_exhaustive_round_trip(m):
+    for bits in m.CODE_BITS:
+        vals = np.arange(-(1 << (bits - 1)), 1 << (bits - 1))
+        d = ((len(vals) + 7) // 8) * 8 * 2
+        row = np.resize(vals, d)[None, :]
+        assert np.array_equal(m.unpack_bits(m.pack_bits(row, bits), bits, d), row), bits
+
+
+def check_ext_quantizer_brute_force(m):
+    """Each code is the argmin of |z - s q| over the b-bit range, ties to even."""
+    rng = np.random.default_rng(22)
+    for bits in m.CODE_BITS:
+        z = rng.standard_normal((4, 64)) * 2.0
+        z[0, 5] = 0.0
+        q, s, _ = m.quantize_groups_bits(z, 32, bits)
+        lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+        cand = np.arange(lo, hi + 1, dtype=np.float64)
+        for r in range(z.shape[0]):
+            for i in range(64):
+                sc = float(s[r, i // 32])
+                err = np.abs(z[r, i] - sc * cand)
+                best = cand[err <= err.min() + 1e-12 * max(1.0, abs(z[r, i]))]
+                want = best[0] if len(best) == 1 else [c for c in best if c % 2 == 0][0]
+                assert q[r, i] == want, (bits, r, i, q[r, i], want)
+
+
+def check_ext_absmax_maps_to_extreme_codes(m):
+    """s = absmax / 2^(b-1) per group: the group's -absmax lands on the lowest
+    code, +absmax clips to the highest; a huge absmax saturates at 65504."""
+    for bits in m.CODE_BITS:
+        z = np.zeros((1, 64))
+        z[0, 3], z[0, 9], z[0, 40] = 3.0, -3.0, 0.5
+        q, s, _ = m.quantize_groups_bits(z, 32, bits)
+        assert float(s[0, 0]) == float(np.float16(3.0 / (1 << (bits - 1))))
+        assert float(s[0, 1]) == float(np.float16(0.5 / (1 << (bits - 1))))
+        assert q[0, 9] == -(1 << (bits - 1)) and q[0, 3] == (1 << (bits - 1)) - 1
+        assert float(m.fp16_scale_bits(np.array([1e9]), bits)[0]) == 65504.0
+
+
+def check_lambda_power_of_two_is_exact_input_scaling(m):
+    """With lambda a power of two per channel, the forward equals the plain
+    forward of the scaled fp16 input and the inverse equals the plain inverse
+    divided by lambda, exactly."""
+    rng = np.random.default_rng(23)
+    d = 64
+    lam = (2.0 ** rng.integers(-2, 3, size=d)).astype(np.float16)
+    x = rng.standard_normal((10, d)).astype(np.float16)
+    for bits in (3, 4, 8):
+        c1, s1 = m.quant_fwd_ext(x, 32, bits, lam, 9, 0, 0, "srft")
+        c2, s2 = m.quant_fwd_ext((x.astype(np.float64) * lam).astype(np.float16), 32, bits, None, 9, 0, 0, "srft")
+        assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+        _, u1 = m.dequant_inv_ext(c1, s1, d, 32, bits, lam, 9, return_fp64=True)
+        _, u2 = m.dequant_inv_ext(c1, s1, d, 32, bits, None, 9, return_fp64=True)
+        assert np.array_equal(u1, u2 / lam.astype(np.float64))
+
+
+def check_lambda_energy_identity(m):
+    """||lambda (.) (u - x)|| = ||z_hat - z|| per row: lambda multiplies before
+    the orthogonal rotation and divides after the inverse."""
+    rng = np.random.default_rng(24)
+    d = 128
+    lam = rng.uniform(0.25, 4.0, size=d).astype(np.float16)
+    x = rng.standard_normal((6, d)).astype(np.float16)
+    det = m.forward_detail_ext(x, 32, 3, lam, 3, 0, 0, "srft")
+    zhat = m.dequantize_groups(det["q"], det["s"], 32)
+    _, u = m.dequant_inv_ext(det["codes"], det["s"], d, 32, 3, lam, 3, return_fp64=True)
+    lhs = np.linalg.norm(lam.astype(np.float64) * (u - x.astype(np.float64)), axis=1)
+    rhs = np.linalg.norm(zhat - det["z"], axis=1)
+    assert np.allclose(lhs, rhs, rtol=1e-9, atol=1e-12)
+
+
+def check_error_falls_with_code_width(m):
+    """Round-trip RMS error falls with the code width (3 > 4 > 6 > 8 bits),
+    roughly by 2x per bit."""
+    rng = np.random.default_rng(25)
+    x = rng.standard_normal((64, 64)).astype(np.float16)
+    err = {}
+    for bits in m.CODE_BITS:
+        c, s = m.quant_fwd_ext(x, 32, bits, None, 1)
+        y = m.dequant_inv_ext(c, s, 64, 32, bits, None, 1).astype(np.float64)
+        err[bits] = float(np.sqrt(np.mean((y - x.astype(np.float64)) ** 2)))
+    assert err[3] > 1.5 * err[4] > 0 and err[4] > 3.0 * err[6] and err[6] > 3.0 * err[8], err

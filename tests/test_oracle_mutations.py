@@ -49,6 +49,14 @@ def all_pins(m):
         "attn_rows": lambda: P.check_attn_dequant_rows_match_rowwise_inverse(m),
         "row_list": lambda: P.check_row_list_matches_single_rows(m),
         "window": lambda: P.check_window_schedule_closed_form(m),
+        "ext_bits4": lambda: P.check_ext_bits4_without_lambda_is_the_int4_path(m),
+        "ext_layout": lambda: P.check_pack_bits_layout_fixtures(m),
+        "ext_roundtrip": lambda: P.check_pack_bits_exhaustive_round_trip(m),
+        "ext_brute": lambda: P.check_ext_quantizer_brute_force(m),
+        "ext_absmax": lambda: P.check_ext_absmax_maps_to_extreme_codes(m),
+        "ext_lam_pow2": lambda: P.check_lambda_power_of_two_is_exact_input_scaling(m),
+        "ext_lam_energy": lambda: P.check_lambda_energy_identity(m),
+        "ext_order": lambda: P.check_error_falls_with_code_width(m),
     }
     failed = []
     for name, fn in checks.items():
@@ -80,8 +88,12 @@ MUTATIONS = {
     "scale rounds through fp32": (
         "s = (a / 8.0).astype(np.float16)", "s = (a / 8.0).astype(np.float32).astype(np.float16)"),
     "scale not saturated": (
-        "return np.where(np.isinf(s), np.float16(FP16_MAX), s).astype(np.float16)",
-        "return s.astype(np.float16)"),
+        "(a / 8.0).astype(np.float16)\n    return np.where(np.isinf(s), np.float16(FP16_MAX), s).astype(np.float16)",
+        "(a / 8.0).astype(np.float16)\n    return s.astype(np.float16)"),
+    "b-bit scale not saturated": (
+        "(a / float(1 << (bits - 1))).astype(np.float16)\n    return np.where(np.isinf(s), np.float16(FP16_MAX), s)"
+        ".astype(np.float16)",
+        "(a / float(1 << (bits - 1))).astype(np.float16)\n    return s.astype(np.float16)"),
     "clamp to [-7, 7]": ("INT4_MIN = -8", "INT4_MIN = -7"),
     "round half away from zero": (
         "return np.clip(np.rint(r), INT4_MIN, INT4_MAX).astype(np.int8)",
@@ -92,8 +104,13 @@ MUTATIONS = {
     "zero scale divides by zero": (
         "r = np.where(s64 > 0, z / safe, 0.0)", "r = z / s64"),
     "absmax over the whole row": (
-        "a = np.max(np.abs(zg), axis=-1)",
-        "a = np.repeat(np.max(np.abs(zg), axis=(-1, -2))[..., None], zg.shape[-2], axis=-1)"),
+        "a = np.max(np.abs(zg), axis=-1)\n    s = fp16_scale_from_absmax(a)",
+        "a = np.repeat(np.max(np.abs(zg), axis=(-1, -2))[..., None], zg.shape[-2], axis=-1)\n"
+        "    s = fp16_scale_from_absmax(a)"),
+    "b-bit absmax over the whole row": (
+        "a = np.max(np.abs(zg), axis=-1)\n    s = fp16_scale_bits(a, bits)",
+        "a = np.repeat(np.max(np.abs(zg), axis=(-1, -2))[..., None], zg.shape[-2], axis=-1)\n"
+        "    s = fp16_scale_bits(a, bits)"),
     "nibbles swapped": ("return (lo | (hi << 4)).astype(np.uint8)", "return (hi | (lo << 4)).astype(np.uint8)"),
     "unpack without sign extension": ("lo = np.where(lo >= 8, lo - 16, lo)", "lo = lo"),
     "splitmix wrong multiplier": ("0xBF58476D1CE4E5B9", "0xBF58476D1CE4E5B8"),
@@ -113,6 +130,21 @@ MUTATIONS = {
     "row list ignored by the sign matrix": (
         "row0 + i if rows is None else int(rows[i])", "row0 + i"),
     "window flushed one token late": ("        if held == window:", "        if held == window + 1:"),
+    "b-bit stream packed most significant bit first": (
+        "            bit = (flat[:, i] >> k) & 1", "            bit = (flat[:, i] >> (bits - 1 - k)) & 1"),
+    "b-bit scale divides by 2^b": (
+        "        s = (a / float(1 << (bits - 1))).astype(np.float16)", "        s = (a / float(1 << bits)).astype(np.float16)"),
+    "lambda applied after the rotation": (
+        "    z = (D * x) @ rotation_matrix(rot, d).T\n    q, s, a = quantize_groups_bits(z, group, bits)",
+        "    z = (D * np.asarray(x_f16, dtype=np.float16).astype(np.float64)) @ rotation_matrix(rot, d).T\n"
+        "    z = z * (1.0 if lam_f16 is None else np.asarray(lam_f16, dtype=np.float16).astype(np.float64))\n"
+        "    q, s, a = quantize_groups_bits(z, group, bits)"),
+    "inverse multiplies by lambda": (
+        "        u = u / np.asarray(lam_f16, dtype=np.float16).astype(np.float64)[None, :]",
+        "        u = u * np.asarray(lam_f16, dtype=np.float16).astype(np.float64)[None, :]"),
+    "b-bit clamp one code short": (
+        "    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1\n    q = np.clip",
+        "    lo, hi = -(1 << (bits - 1)) + 1, (1 << (bits - 1)) - 1\n    q = np.clip"),
     "attention drops the softmax scale": (
         "            sc = keys @ q[layer, st, g] * softmax_scale",
         "            sc = keys @ q[layer, st, g]"),
