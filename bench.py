@@ -41,7 +41,8 @@ METRIC = "K/V vectors/s and HBM GB/s (% of peak), fused SRFT-int4 quant+dequant,
 ATTN_METRIC = "decode-attention steps/s over the int4 rotated K/V cache (dequantized in registers), 1 GPU"
 _CSRC = os.path.join(ROOT, "rotate_then_quantize_amd", "csrc")
 # sources each kernel family is compiled from (a profile is current while their code is unchanged)
-KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq.hip", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp")]
+KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in (
+    "rtq.hip", "rtq_lane.hpp", "rtq_host.hpp", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp")]
 ATTN_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq_attn.hip", "rtq_device.hpp", "rtq_mem.hpp")]
 
 
@@ -635,6 +636,106 @@ def decode_cache_main(args, w, dev):
     print(json.dumps(result), flush=True)
 
 
+def ext_main(args, w, dev):
+    """Forward + inverse with each code width (3, 4, 6, 8 bits) and a
+    per-channel lambda, on the workload's rows: the same step as the default
+    bench (forward over every row, then inverse over every row of another
+    replica), one line with every width."""
+    import torch
+    import rotate_then_quantize_amd as rtq
+    rot = args.rot
+    lib = rtq.library()
+    fwd_fn = lib.srft_quant_fwd_ext if rot == "srft" else lib.srht_quant_fwd_ext
+    inv_fn = lib.srft_dequant_inv_ext if rot == "srft" else lib.srht_dequant_inv_ext
+    n, d, g = w.n_rows, w.d, w.group
+    x0 = W_generate(w, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    lam = (torch.rand((d,), generator=gen, device=dev) * 3.75 + 0.25).to(torch.float16)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    lp = ctypes.c_void_p(lam.data_ptr())
+    out = {}
+    for bits in rtq.CODE_BITS:
+        footprint = n * (2 * d + d * bits // 8 + 2 * (d // g) + 2 * d)
+        replicas = args.replicas or max(1, math.ceil((1 << 30) / footprint))
+        sets = []
+        for r in range(replicas):
+            x = x0 if r == 0 else x0.clone()
+            codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=dev)
+            scales = torch.empty((n, d // g), dtype=torch.float16, device=dev)
+            y = torch.empty((n, d), dtype=torch.float16, device=dev)
+            fa = (ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                  n, d, g, bits, lp, w.sign_seed, w.rows_per_seed, w.seed_period, sh)
+            ia = (ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(y.data_ptr()),
+                  n, d, g, bits, lp, w.sign_seed, w.rows_per_seed, w.seed_period, sh)
+            sets.append((fa, ia, (x, codes, scales, y)))
+        for fa, _, _ in sets:
+            assert fwd_fn(*fa) == 0
+        torch.cuda.synchronize()
+        steps = max(20, args.steps // 4)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(args.warmup):
+            fwd_fn(*sets[i % replicas][0])
+            inv_fn(*sets[(i + 1) % replicas][1])
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            ev = evs[i] if i % 5 == 0 else None
+            if ev:
+                ev[0].record(stream)
+            s1 = fwd_fn(*sets[i % replicas][0])
+            if ev:
+                ev[1].record(stream)
+            s2 = inv_fn(*sets[(i + 1) % replicas][1])
+            if ev:
+                ev[2].record(stream)
+            if s1 or s2:
+                raise RuntimeError(lib.rtq_status_string(s1 or s2).decode())
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        sampled = [evs[i] for i in range(steps) if i % 5 == 0]
+        f_ms = sum(e[0].elapsed_time(e[1]) for e in sampled) / len(sampled)
+        i_ms = sum(e[1].elapsed_time(e[2]) for e in sampled) / len(sampled)
+        bpv = 2 * d + d * bits // 8 + 2 * (d // g)
+        out[bits] = {"step_us": (t1 - t0) * 1e6 / steps, "forward_us": f_ms * 1e3, "inverse_us": i_ms * 1e3,
+                     "forward_GBps": n * bpv / f_ms / 1e6, "inverse_GBps": n * bpv / i_ms / 1e6,
+                     "bytes_per_vector": bpv, "vectors_per_s": n * steps / (t1 - t0), "buffer_replicas": replicas}
+        log(f"bits {bits}: step {out[bits]['step_us']:.1f} us | fwd {f_ms * 1e3:.1f} us "
+            f"{out[bits]['forward_GBps']:.0f} GB/s | inv {i_ms * 1e3:.1f} us {out[bits]['inverse_GBps']:.0f} GB/s")
+        del sets
+        torch.cuda.empty_cache()
+    head = out[4]
+    dom = "inverse" if head["inverse_us"] >= head["forward_us"] else "forward"
+    achieved = head[f"{dom}_GBps"]
+    result = {
+        "metric": "K/V vectors/s, fused forward + inverse with per-channel lambda, 4-bit codes (3/6/8-bit beside), 1 GPU",
+        "value": head["vectors_per_s"],
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": max(20, args.steps // 4),
+        "warmup": args.warmup,
+        "ms_per_step": head["step_us"] / 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": n, "d": d, "group": g, "rotation": rot,
+                   "lambda": "uniform(0.25, 4) fp16 per channel"},
+        "by_bits": {str(b): v for b, v in out.items()},
+        "roofline": {"kernel": f"{rot}_{'dequant_inv' if dom == 'inverse' else 'quant_fwd'}_ext bits=4 lambda",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+    }
+    print(json.dumps(result), flush=True)
+
+
+def W_generate(w, dev):
+    from rotate_then_quantize_amd import workloads as W
+    return W.generate(w, dev)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -644,6 +745,8 @@ def main():
                     help="workload id (default 2; 3 with --attn)")
     ap.add_argument("--attn", action="store_true",
                     help="measure decode attention over the int4 cache instead of forward + inverse")
+    ap.add_argument("--ext", action="store_true",
+                    help="measure forward + inverse with 3/4/6/8-bit codes and a per-channel lambda")
     ap.add_argument("--decode-cache", action="store_true",
                     help="measure the dequantized-prefix cache with a 16-token fp16 window (workload 3 by default)")
     ap.add_argument("--attn-layout", choices=["heads", "workload"], default="heads",
@@ -712,6 +815,9 @@ def main():
         return
     if args.decode_cache:
         decode_cache_main(args, w, dev)
+        return
+    if args.ext:
+        ext_main(args, w, dev)
         return
     rot = args.rot
     if rot not in w.rots:

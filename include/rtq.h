@@ -127,6 +127,49 @@ rtq_status srht_dequant_inv(const void* codes_u8, const void* scales_f16, void* 
                             hipStream_t stream);
 
 /*
+ * srft_quant_fwd_ext / srht_quant_fwd_ext / srft_dequant_inv_ext /
+ * srht_dequant_inv_ext -- the forward and inverse steps with other code widths
+ * and an optional per-channel lambda.  The method page's fused recipe adds one
+ * scale per channel to the per-group absmax, and its quality study runs 3-,
+ * 4-, 6- and 8-bit codes ("Quantization Speed Is Often a Kernel Problem",
+ * "First, the 17%"); the formulas below are this library's reading.
+ *
+ *   bits        : 3, 4, 6 or 8.  Group scale s_j = fp16_rne(absmax / 2^(bits-1))
+ *                 (saturated at 65504), q = clamp(round_half_even(z / s_j),
+ *                 -2^(bits-1), 2^(bits-1) - 1).
+ *   codes_u8    : [n][d*bits/8] bytes.  The codes of a row form one bit
+ *                 stream: code i fills stream bits [i*bits, (i+1)*bits), least
+ *                 significant bit first, stream bit k being bit k%8 of byte
+ *                 k/8; each field is two's complement.  bits = 4 gives the
+ *                 nibble layout of the common conventions (and the same codes
+ *                 as srft_quant_fwd when lambda_f16 is NULL).
+ *   lambda_f16  : NULL, or d fp16 values (16-byte aligned), one per channel.
+ *                 The forward rotates D * (lambda .* x) (the products are exact
+ *                 in fp32); the inverse returns fp16(D * (R^T z_hat) ./ lambda).
+ *                 Entries must be finite and nonzero.
+ *   x_f16, y_f16, scales_f16, n, d, group, seed rule, stream: as for
+ *                 srft_quant_fwd / srft_dequant_inv.
+ * Supported: d in {64, 128} with the groups of the common conventions; other
+ * bits or d = 256 return RTQ_ERR_UNSUPPORTED.  Errors otherwise as in the
+ * common conventions.
+ */
+rtq_status srft_quant_fwd_ext(const void* x_f16, void* codes_u8, void* scales_f16, int64_t n, int32_t d,
+                              int32_t group, int32_t bits, const void* lambda_f16, uint64_t seed,
+                              int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+rtq_status srht_quant_fwd_ext(const void* x_f16, void* codes_u8, void* scales_f16, int64_t n, int32_t d,
+                              int32_t group, int32_t bits, const void* lambda_f16, uint64_t seed,
+                              int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+rtq_status srft_dequant_inv_ext(const void* codes_u8, const void* scales_f16, void* y_f16, int64_t n, int32_t d,
+                                int32_t group, int32_t bits, const void* lambda_f16, uint64_t seed,
+                                int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+rtq_status srht_dequant_inv_ext(const void* codes_u8, const void* scales_f16, void* y_f16, int64_t n, int32_t d,
+                                int32_t group, int32_t bits, const void* lambda_f16, uint64_t seed,
+                                int64_t rows_per_seed, int32_t seed_period, hipStream_t stream);
+
+/*
  * srft_quant_append / srht_quant_append -- the forward step written in place
  * into a cache whose rows are addressed by strides: the new tokens of every
  * layer, K/V and stream go straight to their cache rows.  With

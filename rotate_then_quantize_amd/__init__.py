@@ -22,6 +22,7 @@ __all__ = [
     "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
     "srft_attn_decode", "srht_attn_decode",
     "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
+    "srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext", "CODE_BITS",
     "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED",
 ]
 
@@ -35,6 +36,8 @@ SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (2
 # (d, group) pairs of the decode-attention kernels; at most 8 query heads per K/V head
 ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
 ATTN_MAX_Q_PER_KV = 8
+# code widths of the *_ext entry points (d = 64 or 128)
+CODE_BITS = (3, 4, 6, 8)
 
 
 class RTQError(RuntimeError):
@@ -76,6 +79,13 @@ def library():
         for name in ("srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"):
             fn = getattr(lib, name)
             fn.argtypes = mapped_args
+            fn.restype = ctypes.c_int
+        ext_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                    ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32,
+                    ctypes.c_void_p]
+        for name in ("srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext"):
+            fn = getattr(lib, name)
+            fn.argtypes = ext_args
             fn.restype = ctypes.c_int
         lib.rtq_status_string.argtypes = [ctypes.c_int]
         lib.rtq_status_string.restype = ctypes.c_char_p
@@ -294,6 +304,97 @@ def srht_dequant_rows(codes, scales, y, layers, streams, t0, n_tokens, strides, 
     """srft_dequant_rows with the SRHT rotation."""
     return _rows("srht_dequant_rows", codes, scales, y, layers, streams, t0, n_tokens, strides, group, seed,
                  rows_per_seed, seed_period, stream)
+
+
+def _lambda_ptr(lam, d, device):
+    import torch
+    if lam is None:
+        return ctypes.c_void_p(0)
+    _need(lam, torch.float16, "lam", (d,))
+    if lam.device != device:
+        raise ValueError("lam must be on the same device as the data")
+    return ctypes.c_void_p(lam.data_ptr())
+
+
+def _fwd_ext(cname, x, group, bits, lam, seed, rows_per_seed, seed_period, codes, scales, stream):
+    import torch
+    _need(x, torch.float16, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [n, d]")
+    n, d = x.shape
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    if bits not in CODE_BITS:
+        raise ValueError(f"bits must be one of {CODE_BITS}")
+    if codes is None:
+        codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, d // group), dtype=torch.float16, device=x.device)
+    _need(codes, torch.uint8, "codes", (n, d * bits // 8))
+    _need(scales, torch.float16, "scales", (n, d // group))
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+        n, d, group, bits, _lambda_ptr(lam, d, x.device), seed & ((1 << 64) - 1), rows_per_seed, seed_period,
+        _stream_handle(x, stream)))
+    return codes, scales
+
+
+def _inv_ext(cname, codes, scales, d, group, bits, lam, seed, rows_per_seed, seed_period, out, stream):
+    import torch
+    if bits not in CODE_BITS:
+        raise ValueError(f"bits must be one of {CODE_BITS}")
+    _need(codes, torch.uint8, "codes")
+    if codes.dim() != 2 or codes.shape[1] * 8 != d * bits:
+        raise ValueError("codes must be [n, d*bits/8]")
+    n = codes.shape[0]
+    if d % group or group <= 0:
+        raise ValueError("group must divide d")
+    _need(scales, torch.float16, "scales", (n, d // group))
+    if out is None:
+        out = torch.empty((n, d), dtype=torch.float16, device=codes.device)
+    _need(out, torch.float16, "out", (n, d))
+    _check(getattr(library(), cname)(
+        ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+        n, d, group, bits, _lambda_ptr(lam, d, codes.device), seed & ((1 << 64) - 1), rows_per_seed, seed_period,
+        _stream_handle(codes, stream)))
+    return out
+
+
+def srft_quant_fwd_ext(x, group, bits, seed, lam=None, rows_per_seed=0, seed_period=0, codes=None, scales=None,
+                       stream=None):
+    """Forward step with `bits`-bit codes (3, 4, 6, 8) and an optional per-channel fp16 lambda [d]:
+    returns (codes [n, d*bits/8] uint8, scales [n, d/group] fp16)."""
+    return _fwd_ext("srft_quant_fwd_ext", x, group, bits, lam, seed, rows_per_seed, seed_period, codes, scales,
+                    stream)
+
+
+def srht_quant_fwd_ext(x, group, bits, seed, lam=None, rows_per_seed=0, seed_period=0, codes=None, scales=None,
+                       stream=None):
+    """srft_quant_fwd_ext with the SRHT rotation."""
+    return _fwd_ext("srht_quant_fwd_ext", x, group, bits, lam, seed, rows_per_seed, seed_period, codes, scales,
+                    stream)
+
+
+def srft_dequant_inv_ext(codes, scales, d, group, bits, seed, lam=None, rows_per_seed=0, seed_period=0, out=None,
+                         stream=None):
+    """Inverse step for `bits`-bit codes and an optional lambda: returns y [n, d] fp16."""
+    return _inv_ext("srft_dequant_inv_ext", codes, scales, d, group, bits, lam, seed, rows_per_seed, seed_period,
+                    out, stream)
+
+
+def srht_dequant_inv_ext(codes, scales, d, group, bits, seed, lam=None, rows_per_seed=0, seed_period=0, out=None,
+                         stream=None):
+    """srft_dequant_inv_ext with the SRHT rotation."""
+    return _inv_ext("srht_dequant_inv_ext", codes, scales, d, group, bits, lam, seed, rows_per_seed, seed_period,
+                    out, stream)
+
+
+def quant_fwd_ext(rot, *args, **kw):
+    return (srft_quant_fwd_ext if rot == "srft" else srht_quant_fwd_ext)(*args, **kw)
+
+
+def dequant_inv_ext(rot, *args, **kw):
+    return (srft_dequant_inv_ext if rot == "srft" else srht_dequant_inv_ext)(*args, **kw)
 
 
 def quant_append(rot, *args, **kw):

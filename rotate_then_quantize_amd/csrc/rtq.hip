@@ -35,174 +35,15 @@
 #include "rtq.h"
 #include "rtq_device.hpp"
 #include "rtq_div.hpp"
+#include "rtq_host.hpp"
+#include "rtq_lane.hpp"
 #include "rtq_mem.hpp"
 
 namespace rtq {
 
-enum Rot : int { kSRFT = 0, kSRHT = 1 };
-
-// ---------------------------------------------------------------------------
-// Sign masks
-// ---------------------------------------------------------------------------
-
-// XOR mask of packed pair m (elements 2m, 2m+1) from a word of 64 sign bits
-// (bit e = element e): bit 2m goes to bit 15 (low fp16), bit 2m+1 to bit 31.
-__device__ __forceinline__ uint32_t pair_mask(uint64_t bits, int m) {
-  const uint32_t v = (uint32_t)(bits >> (2 * m)) & 3u;
-  return (v * 0x40008000u) & 0x80008000u;
-}
-
-// h ^ m for a wave-uniform mask m kept in an SGPR: one VALU instruction.
-__device__ __forceinline__ uint32_t xor_uniform(uint32_t h, uint32_t m) {
-  uint32_t r;
-  asm("v_xor_b32 %0, %1, %2" : "=v"(r) : "s"(m), "v"(h));
-  return r;
-}
-
-// Sign masks of one seed for the D/2 packed pairs of a row, wave-uniform:
-// lane l evaluates the sign bits of elements l, l + 64, ... and a ballot
-// gathers them into scalar registers.
-template <int D>
-struct UniformSigns {
-  uint32_t m[D / 2];
-
-  // Seed offset j (wave-uniform) of base seed s0: the sign words come from
-  // the host-filled table when it holds j, otherwise from a ballot.
-  __device__ __forceinline__ void setup(const SignTable& tb, uint32_t j, uint64_t s0, int lane) {
-    if (j < tb.seeds) {
-      sfor<D / 64>([&](auto Q) {
-        constexpr int q = RTQ_CI(Q);
-        const uint64_t bits = tb.w[j * (D / 64) + q];
-        sfor<32>([&](auto M) { m[32 * q + RTQ_CI(M)] = pair_mask(bits, RTQ_CI(M)); });
-      });
-      return;
-    }
-    const uint64_t s = s0 + j;
-    sfor<D / 64>([&](auto Q) {
-      constexpr int q = RTQ_CI(Q);
-      const uint64_t bits = __ballot(sign_bit(s, (uint32_t)(64 * q + lane)));
-      sfor<32>([&](auto M) { m[32 * q + RTQ_CI(M)] = pair_mask(bits, RTQ_CI(M)); });
-    });
-  }
-
-  __device__ __forceinline__ void apply(uint32_t (&h)[D / 2]) const {
-    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = xor_uniform(h[RTQ_CI(M)], m[RTQ_CI(M)]); });
-  }
-};
-
-// Signs of a lane's own seed s, evaluated element by element; used only for
-// the few tiles whose rows straddle a seed boundary.
-template <int D>
-__device__ __forceinline__ void apply_lane_signs(uint32_t (&h)[D / 2], uint64_t s) {
-  sfor<D / 64>([&](auto Q) {
-    uint64_t bits = 0;
-#pragma unroll 1
-    for (uint32_t e = 0; e < 64; ++e) bits |= (uint64_t)sign_bit(s, 64u * RTQ_CI(Q) + e) << e;
-    sfor<32>([&](auto M) { h[32 * RTQ_CI(Q) + RTQ_CI(M)] ^= pair_mask(bits, RTQ_CI(M)); });
-  });
-}
-
-// Seed of the row a lane owns in a tile (rows past the end reuse the last).
-__device__ __forceinline__ uint64_t lane_seed(const SeedRule& sr, uint32_t row0, int rows, int lane) {
-  return seed_of_block(seed_block(row0 + (uint32_t)(lane < rows ? lane : rows - 1), sr), sr);
-}
-
-// XOR masks flipping the fp16 sign bits of chunk k (elements 8k .. 8k+7) for
-// seed offset j (wave-uniform) of base seed s0, from the host-filled table
-// when it holds j (D = 256: four words per seed), otherwise evaluated here.
-__device__ __forceinline__ uint4 chunk_masks(const SignTable& tb, uint32_t j, uint64_t s0, uint32_t k) {
-  if (j < tb.seeds) {
-    const uint64_t w0 = tb.w[4 * j], w1 = tb.w[4 * j + 1], w2 = tb.w[4 * j + 2], w3 = tb.w[4 * j + 3];
-    const uint32_t q = k >> 3;
-    const uint64_t w = q == 0 ? w0 : q == 1 ? w1 : q == 2 ? w2 : w3;
-    const uint64_t byte = (w >> (8 * (k & 7))) & 0xffu;
-    return make_uint4(pair_mask(byte, 0), pair_mask(byte, 1), pair_mask(byte, 2), pair_mask(byte, 3));
-  }
-  return chunk_sign_masks(s0 + j, k);
-}
-
 // ---------------------------------------------------------------------------
 // d = 64 / 128: one lane per vector, 64 vectors per tile.
 // ---------------------------------------------------------------------------
-
-// Direct-to-LDS staging of one tile.  Load instruction j of lane i fills LDS
-// slot 64j + i (hardware layout); slot s holds row r = s / CPR, chunk
-// k = (s % CPR) ^ (r & 7).  The xor swizzle makes the owning lane's
-// ds_read_b128 of its row conflict free while every row's chunks still come
-// from one contiguous row in HBM.  A partial tile reloads its last row.
-template <int CPR>
-__device__ __forceinline__ void load_tile_to_lds(const uint4* __restrict__ xt, int rows, uint4* buf, int lane) {
-  auto issue = [&](auto J, int rmax) {
-    const int slot = RTQ_CI(J) * 64 + lane;
-    const int r = slot / CPR;
-    const int k = (slot % CPR) ^ (r & 7);
-    const int rr = r < rmax ? r : rmax - 1;
-    const uint32_t off = (uint32_t)(rr * CPR + k) * 16u;
-    __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)xt + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16, 0,
-                                     kCachePolicyNT);
-  };
-  if (rows == 64) {
-    sfor<CPR>([&](auto J) { issue(J, 64); });
-  } else {
-    sfor<CPR>([&](auto J) { issue(J, rows); });
-  }
-}
-
-template <int CPR>
-__device__ __forceinline__ void read_own_row(const uint4* buf, int lane, uint32_t (&h)[CPR * 4]) {
-  const int sw = lane & 7;
-  sfor<CPR>([&](auto C) {
-    const uint4 q = buf[lane * CPR + (RTQ_CI(C) ^ sw)];
-    h[4 * RTQ_CI(C) + 0] = q.x;
-    h[4 * RTQ_CI(C) + 1] = q.y;
-    h[4 * RTQ_CI(C) + 2] = q.z;
-    h[4 * RTQ_CI(C) + 3] = q.w;
-  });
-}
-
-template <int D, int G, int ROT>
-__device__ __forceinline__ void quantize_row(const uint32_t (&h)[D / 2], uint32_t (&cw)[D / 8],
-                                             uint32_t (&sb)[D / G]) {
-  float z[D];
-  float zs;
-  if constexpr (ROT == kSRFT) {
-    srft_fwd_unscaled<D>(h, z);
-    zs = SrftScale<D>::value;
-  } else {
-    fwht_from_f16<D>(h, z);
-    zs = InvSqrt<D>::value;
-  }
-  quantize_pack<D, G>(z, zs, cw, sb);
-}
-
-// scales of one row, packed as written to memory (fp16 pairs, low half first)
-template <int D, int G>
-__device__ __forceinline__ void store_row_scales(uint8_t* __restrict__ st, uint32_t r, const uint32_t (&sb)[D / G]) {
-  if constexpr (D / G == 1) {
-    stream_store(reinterpret_cast<uint16_t*>(st) + r, (uint16_t)sb[0]);
-  } else if constexpr (D / G == 2) {
-    stream_store(reinterpret_cast<uint32_t*>(st) + r, sb[0] | (sb[1] << 16));
-  } else {
-    stream_store(reinterpret_cast<uint2*>(st) + r, make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)));
-  }
-}
-
-template <int D, int G>
-__device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, uint32_t r, uint32_t (&sb)[D / G]) {
-  if constexpr (D / G == 1) {
-    sb[0] = stream_load(reinterpret_cast<const uint16_t*>(st) + r);
-  } else if constexpr (D / G == 2) {
-    const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(st) + r);
-    sb[0] = w & 0xffffu;
-    sb[1] = w >> 16;
-  } else {
-    const uint2 w = stream_load(reinterpret_cast<const uint2*>(st) + r);
-    sb[0] = w.x & 0xffffu;
-    sb[1] = w.x >> 16;
-    sb[2] = w.y & 0xffffu;
-    sb[3] = w.y >> 16;
-  }
-}
 
 // One forward tile: rows row0 .. row0 + rows - 1, lane l owning row row0 + l.
 // kUniform: every row has seed s (masks are scalar); otherwise s is the
@@ -255,9 +96,6 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
   if (b0 == b1) fwd_lane_tile<D, G, ROT, true>(xt, ct, st, rows, tb, seed_offset(b0, sr), sr.seed, buf, lane);
   else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, tb, 0, lane_seed(sr, row0, rows, lane), buf, lane);
 }
-
-// Output transpose passes of the inverse: d = 128 in two halves.
-template <int D> struct InvPhases { static constexpr int value = D == 128 ? 2 : 1; };
 
 // Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
 // row order): load instruction j of lane i fills slot 64j + i with chunk
@@ -357,137 +195,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
   if (b0 == b1) inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, tb, seed_offset(b0, sr), sr.seed, lds, lane);
   else inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, tb, 0, lane_seed(sr, row0, rows, lane), lds, lane);
-}
-
-// ---------------------------------------------------------------------------
-// Cache blocks addressed by strides (d = 64 / 128): the in-place append of new
-// tokens and the row-mapped inverse that refreshes a dequantized fp16 mirror
-// of the cache ("Quantization Speed Is Often a Kernel Problem", "First, the
-// 17%": the dequantized prefix is kept between steps, the newest tokens stay
-// in fp16, and the prefix is refreshed when that window fills).  One lane per
-// row, 64 rows per wave; each lane reads or writes its own cache row.
-// ---------------------------------------------------------------------------
-
-// Row i of a block [layers][2][streams][n] lives at cache row
-// l*sl + kv*skv + s*ss + (t0 + j)*st.
-struct RowMap {
-  int64_t sl, skv, ss, st;
-  uint32_t t0, n, streams;
-  Div32 by_n, by_streams;
-};
-
-__device__ __forceinline__ int64_t map_row(const RowMap& m, uint32_t i) {
-  const uint32_t q1 = div32(i, m.by_n), j = i - q1 * m.n;
-  const uint32_t q2 = div32(q1, m.by_streams), s = q1 - q2 * m.streams;
-  return (int64_t)(q2 >> 1) * m.sl + (int64_t)(q2 & 1u) * m.skv + (int64_t)s * m.ss + (int64_t)(m.t0 + j) * m.st;
-}
-
-// The cache's seed rule on 64-bit row indices.
-struct RowSeeds {
-  uint64_t seed;
-  int64_t rps;
-  int32_t period;
-};
-
-// Flip the sign bits of h by the lane's seed s: one ballot per 64 elements
-// when every lane of the wave has the same seed, element by element otherwise.
-template <int D>
-__device__ __forceinline__ void flip_signs(uint32_t (&h)[D / 2], uint64_t s, int lane) {
-  const uint64_t s0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(s >> 32)) << 32) |
-                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s);
-  if (__all(s == s0)) {
-    sfor<D / 64>([&](auto Q) {
-      constexpr int q = RTQ_CI(Q);
-      const uint64_t bits = __ballot(sign_bit(s0, (uint32_t)(64 * q + lane)));
-      sfor<32>([&](auto M) { h[32 * q + RTQ_CI(M)] ^= pair_mask(bits, RTQ_CI(M)); });
-    });
-  } else {
-    apply_lane_signs<D>(h, s);
-  }
-}
-
-// Quantize rows 0 .. n-1 of x (a contiguous [layers][2][streams][n_tokens][d]
-// block) into the cache rows map_row(i).
-template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void fwd_mapped_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                                        uint8_t* __restrict__ scales, uint32_t n, RowMap m,
-                                                        RowSeeds rs) {
-  constexpr int CPR = D / 8;
-  constexpr int CW = D / 32;
-  __shared__ uint4 buf[64 * CPR];
-  const int lane = threadIdx.x;
-  const uint32_t row0 = blockIdx.x * 64u;
-  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
-  load_tile_to_lds<CPR>(x + (size_t)row0 * CPR, rows, buf, lane);
-  const int64_t dst = map_row(m, row0 + (uint32_t)(lane < rows ? lane : rows - 1));
-  const uint64_t s = row_seed(rs.seed, dst, rs.rps, rs.period);
-  wait_vmcnt<0>();
-  lds_sync();
-  uint32_t h[D / 2];
-  read_own_row<CPR>(buf, lane, h);
-  flip_signs<D>(h, s, lane);
-  uint32_t cw[D / 8], sb[D / G];
-  quantize_row<D, G, ROT>(h, cw, sb);
-  if (lane < rows) {
-    // ordinary (cached) stores: each lane writes its own row in pieces, and
-    // L2 merges the pieces of a line before it goes to HBM
-    uint4* c = codes + dst * CW;
-    sfor<CW>([&](auto C) {
-      constexpr int k = RTQ_CI(C);
-      c[k] = make_uint4(cw[4 * k], cw[4 * k + 1], cw[4 * k + 2], cw[4 * k + 3]);
-    });
-    uint8_t* srow = scales + dst * (2 * D / G);
-    if constexpr (D / G == 1) {
-      *reinterpret_cast<uint16_t*>(srow) = (uint16_t)sb[0];
-    } else if constexpr (D / G == 2) {
-      *reinterpret_cast<uint32_t*>(srow) = sb[0] | (sb[1] << 16);
-    } else {
-      *reinterpret_cast<uint2*>(srow) = make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16));
-    }
-  }
-}
-
-// Dequantize the cache rows map_row(i), i < n, into the same rows of y (an
-// fp16 mirror of the cache).
-template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void inv_mapped_kernel(const uint4* __restrict__ codes,
-                                                        const uint8_t* __restrict__ scales, uint4* __restrict__ y,
-                                                        uint32_t n, RowMap m, RowSeeds rs) {
-  constexpr int CPR = D / 8;
-  constexpr int CW = D / 32;
-  const int lane = threadIdx.x;
-  const uint32_t row0 = blockIdx.x * 64u;
-  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
-  const int64_t src = map_row(m, row0 + (uint32_t)(lane < rows ? lane : rows - 1));
-  uint32_t cw[D / 8], sb[D / G];
-  sfor<CW>([&](auto C) {
-    constexpr int k = RTQ_CI(C);
-    const uint4 q = codes[src * CW + k];
-    cw[4 * k] = q.x;
-    cw[4 * k + 1] = q.y;
-    cw[4 * k + 2] = q.z;
-    cw[4 * k + 3] = q.w;
-  });
-  load_row_scales<D, G>(scales + src * (2 * D / G), 0u, sb);
-  const uint64_t s = row_seed(rs.seed, src, rs.rps, rs.period);
-  float z[D], u[D];
-  if constexpr (ROT == kSRFT) {
-    dequant_unpack<D, G>(cw, sb, 1.0f, z);
-    srft_inv<D, One>(z, u);
-  } else {
-    dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
-    fwht_f32<D>(u);
-  }
-  uint32_t h[D / 2];
-  sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
-  flip_signs<D>(h, s, lane);
-  if (lane < rows) {
-    uint4* out = y + src * CPR;  // ordinary stores, merged per line in L2
-    sfor<CPR>([&](auto C) {
-      constexpr int k = RTQ_CI(C);
-      out[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
-    });
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -779,22 +486,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
 }
 
 // ---------------------------------------------------------------------------
-// Host side: validation, launch configuration, dispatch.
+// Host side
 // ---------------------------------------------------------------------------
-
-using KernelFn = const void*;
-
-// Rows per call: row indices are 32-bit on the device.
-constexpr int64_t kMaxRows = 0xffffff00ll;
-
-// One wave per tile.  The grid is derived from the row count alone (no
-// occupancy query): the hardware dispatcher keeps every CU filled from a
-// grid far larger than the machine.
-rtq_status launch(KernelFn fn, int64_t tiles, void** kargs, hipStream_t stream) {
-  if (tiles <= 0 || tiles > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
-  const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(64), kargs, 0, stream);
-  return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
-}
 
 // Sign words of the seeds a call uses (as many as the table holds).  The
 // table is a pure function of (seed, d, number of seeds); the last one built
@@ -851,35 +544,6 @@ KernelFn find_kernel(bool fwd, int d, int g) {
   return nullptr;
 }
 
-bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb) {
-  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
-  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
-}
-
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// Supported (d, group): d in {64,128,256}; group in {32,64,128,256}, group <= d.
-// (d = 256, group = 256) is a per-token scale over two lanes and is not built.
-rtq_status check_shape(int32_t d, int32_t g) {
-  if (d != 64 && d != 128 && d != 256) return RTQ_ERR_UNSUPPORTED;
-  if (g != 32 && g != 64 && g != 128 && g != 256) return RTQ_ERR_UNSUPPORTED;
-  if (g > d) return RTQ_ERR_UNSUPPORTED;
-  if (d == 256 && g == 256) return RTQ_ERR_UNSUPPORTED;
-  return RTQ_OK;
-}
-
-// The row seed rule as the kernels apply it: rows_per_seed >= n selects one
-// seed for all rows, exactly as rows_per_seed == 0 does.
-SeedRule make_seed_rule(uint64_t seed, int64_t rps, int32_t period, int64_t n) {
-  SeedRule s;
-  s.seed = seed;
-  s.rps = (rps == 0 || rps >= n) ? 0u : (uint32_t)rps;
-  s.period = (uint32_t)period;
-  s.by_rps = make_div32(s.rps ? s.rps : 1u);
-  s.by_period = make_div32(s.period ? s.period : 1u);
-  return s;
-}
-
 rtq_status run(bool fwd, int rot, const void* in0, const void* in1, void* out0, void* out1, int64_t n, int32_t d,
                int32_t g, uint64_t seed, int64_t rps, int32_t period, hipStream_t stream) {
   if (n < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
@@ -924,87 +588,6 @@ rtq_status run(bool fwd, int rot, const void* in0, const void* in1, void* out0, 
   return launch(fn, tiles, kargs, stream);
 }
 
-template <int ROT>
-KernelFn find_mapped(bool fwd, int d, int g) {
-#define RTQ_MAPPED_CASE(DD, GG)                                                        \
-  if (d == DD && g == GG)                                                              \
-    return fwd ? reinterpret_cast<KernelFn>(&fwd_mapped_kernel<DD, GG, ROT>)           \
-               : reinterpret_cast<KernelFn>(&inv_mapped_kernel<DD, GG, ROT>);
-  RTQ_MAPPED_CASE(64, 32) RTQ_MAPPED_CASE(64, 64)
-  RTQ_MAPPED_CASE(128, 32) RTQ_MAPPED_CASE(128, 64) RTQ_MAPPED_CASE(128, 128)
-#undef RTQ_MAPPED_CASE
-  return nullptr;
-}
-
-bool overlaps128(const void* a, __int128 na, const void* b, __int128 nb) {
-  const __int128 a0 = (__int128)(uintptr_t)a, b0 = (__int128)(uintptr_t)b;
-  return a0 < b0 + nb && b0 < a0 + na;
-}
-
-// Append (fwd: in0 = x, out0 = codes, out1 = scales) or row-mapped inverse
-// (in0 = codes, in1 = scales, out0 = y) over tokens t0 .. t0+ntok-1 of every
-// (layer, kv, stream).
-rtq_status run_mapped(bool fwd, int rot, const void* in0, const void* in1, void* out0, void* out1, int32_t layers,
-                      int32_t streams, int32_t t0, int32_t ntok, int32_t d, int32_t g, const int64_t (&st)[4],
-                      uint64_t seed, int64_t rps, int32_t period, hipStream_t stream) {
-  if (layers < 0 || streams < 0 || t0 < 0 || ntok < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
-    if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
-  const rtq_status shape = check_shape(d, g);
-  if (shape != RTQ_OK) return shape;
-  const KernelFn fn = rot == kSRFT ? find_mapped<kSRFT>(fwd, d, g) : find_mapped<kSRHT>(fwd, d, g);
-  if (!fn) return RTQ_ERR_UNSUPPORTED;
-  const int64_t n = (int64_t)layers * 2 * streams * ntok;
-  if (n == 0) return RTQ_OK;
-  if (n > kMaxRows || (int64_t)t0 + ntok > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
-  const void* a = in0;
-  const void* b = fwd ? out0 : in1;
-  const void* c = fwd ? out1 : out0;
-  if (!a || !b || !c || !aligned16(a) || !aligned16(b) || !aligned16(c)) return RTQ_ERR_INVALID_ARG;
-  const __int128 max_row = (__int128)(layers - 1) * st[0] + st[1] + (__int128)(streams - 1) * st[2] +
-                           ((__int128)t0 + ntok - 1) * st[3];
-  if (max_row >= ((__int128)1 << 56)) return RTQ_ERR_INVALID_ARG;
-  const __int128 code_bytes = (max_row + 1) * (d / 2), scale_bytes = (max_row + 1) * 2 * (d / g);
-  if (fwd) {
-    const __int128 x_bytes = (__int128)n * 2 * d;
-    if (overlaps128(in0, x_bytes, out0, code_bytes) || overlaps128(in0, x_bytes, out1, scale_bytes) ||
-        overlaps128(out0, code_bytes, out1, scale_bytes))
-      return RTQ_ERR_INVALID_ARG;
-  } else {
-    const __int128 y_bytes = (max_row + 1) * 2 * d;
-    if (overlaps128(out0, y_bytes, in0, code_bytes) || overlaps128(out0, y_bytes, in1, scale_bytes))
-      return RTQ_ERR_INVALID_ARG;
-  }
-  RowMap m;
-  m.sl = st[0];
-  m.skv = st[1];
-  m.ss = st[2];
-  m.st = st[3];
-  m.t0 = (uint32_t)t0;
-  m.n = (uint32_t)ntok;
-  m.streams = (uint32_t)streams;
-  m.by_n = make_div32((uint32_t)ntok);
-  m.by_streams = make_div32((uint32_t)streams);
-  RowSeeds rs;
-  rs.seed = seed;
-  rs.rps = rps;
-  rs.period = period;
-  uint32_t n32 = (uint32_t)n;
-  const int64_t tiles = (n + 63) / 64;
-  if (fwd) {
-    const void* x = in0;
-    void* codes = out0;
-    void* scales = out1;
-    void* kargs[] = {&x, &codes, &scales, &n32, &m, &rs};
-    return launch(fn, tiles, kargs, stream);
-  }
-  const void* codes = in0;
-  const void* scales = in1;
-  void* y = out0;
-  void* kargs[] = {&codes, &scales, &y, &n32, &m, &rs};
-  return launch(fn, tiles, kargs, stream);
-}
-
 }  // namespace rtq
 
 #define RTQ_API extern "C" __attribute__((visibility("default")))
@@ -1037,38 +620,6 @@ RTQ_API rtq_status srht_dequant_inv(const void* codes_u8, const void* scales_f16
                   seed_period, stream);
 }
 
-#define RTQ_MAPPED_API(NAME, A0, A1, A2)                                                          \
-  RTQ_API rtq_status NAME(A0, A1, A2, int32_t layers, int32_t streams, int32_t t0, int32_t n_tokens, int32_t d,  \
-                          int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,          \
-                          int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,        \
-                          hipStream_t stream)
-
-RTQ_MAPPED_API(srft_quant_append, const void* x_f16, void* codes_u8, void* scales_f16) {
-  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
-  return rtq::run_mapped(true, rtq::kSRFT, x_f16, nullptr, codes_u8, scales_f16, layers, streams, t0, n_tokens, d,
-                         group, st, seed, rows_per_seed, seed_period, stream);
-}
-
-RTQ_MAPPED_API(srht_quant_append, const void* x_f16, void* codes_u8, void* scales_f16) {
-  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
-  return rtq::run_mapped(true, rtq::kSRHT, x_f16, nullptr, codes_u8, scales_f16, layers, streams, t0, n_tokens, d,
-                         group, st, seed, rows_per_seed, seed_period, stream);
-}
-
-RTQ_MAPPED_API(srft_dequant_rows, const void* codes_u8, const void* scales_f16, void* y_f16) {
-  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
-  return rtq::run_mapped(false, rtq::kSRFT, codes_u8, scales_f16, y_f16, nullptr, layers, streams, t0, n_tokens, d,
-                         group, st, seed, rows_per_seed, seed_period, stream);
-}
-
-RTQ_MAPPED_API(srht_dequant_rows, const void* codes_u8, const void* scales_f16, void* y_f16) {
-  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
-  return rtq::run_mapped(false, rtq::kSRHT, codes_u8, scales_f16, y_f16, nullptr, layers, streams, t0, n_tokens, d,
-                         group, st, seed, rows_per_seed, seed_period, stream);
-}
-
-#undef RTQ_MAPPED_API
-
 RTQ_API const char* rtq_status_string(rtq_status status) {
   switch (status) {
     case RTQ_OK: return "RTQ_OK: success";
@@ -1079,3 +630,4 @@ RTQ_API const char* rtq_status_string(rtq_status status) {
   }
   return "rtq: unknown status";
 }
+

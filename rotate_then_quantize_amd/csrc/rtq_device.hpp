@@ -245,23 +245,8 @@ __device__ __forceinline__ void fft_stages_from4(float (&re)[M], float (&im)[M])
   });
 }
 
-// W = DFT_M(w), w_m = lo(h[m]) + i hi(h[m]) (packed fp16 pairs).  Natural order
-// in and out; the bit reversal is register renaming only.
-template <int M>
-__device__ __forceinline__ void cfft_from_f16(const uint32_t (&h)[M], float (&re)[M], float (&im)[M]) {
-  constexpr int LOG = ilog2(M);
-  sfor<M / 2>([&](auto I) {
-    constexpr int i = RTQ_CI(I);
-    constexpr int e = bitrev(2 * i, LOG);  // pair (e, e + M/2)
-    re[2 * i] = mix_add<0, 0>(h[e], h[e + M / 2]);
-    im[2 * i] = mix_add<1, 1>(h[e], h[e + M / 2]);
-    re[2 * i + 1] = mix_sub<0, 0>(h[e], h[e + M / 2]);
-    im[2 * i + 1] = mix_sub<1, 1>(h[e], h[e + M / 2]);
-  });
-  fft_stages_from4<M>(re, im);
-}
-
-// Same for fp32 input arrays (natural order).
+// W = DFT_M(x), x_m = xr[m] + i xi[m] (fp32, natural order in and out; the
+// bit reversal is register renaming only).
 template <int M>
 __device__ __forceinline__ void cfft_f32(const float (&xr)[M], const float (&xi)[M], float (&re)[M],
                                          float (&im)[M]) {
@@ -360,16 +345,22 @@ struct OrthoPacked {  // the packed orthonormal rfft: z[0]=X0, ..., sqrt2 on int
   static constexpr double si = csqrt(2.0 / (double)D);
 };
 
-// Bins U_k (k = 0..M) of the real sequence u, u_{2m} = lo(h[m]),
-// u_{2m+1} = hi(h[m]):  U_k = sum_n u_n exp(-2 pi i k n / D), scaled per SC.
-// With W = DFT_M(u_{2m} + i u_{2m+1}):
+// Bins U_k (k = 0..M) of the real fp32 sequence u:
+// U_k = sum_n u_n exp(-2 pi i k n / D), scaled per SC.  With
+// W = DFT_M(u_{2m} + i u_{2m+1}):
 //   U_k = (W_k + conj W_{M-k})/2 - (i/2) exp(-2 pi i k / D) (W_k - conj W_{M-k}).
+// (The fp16-input path of the fused kernels is rdft above; this one serves
+// inputs already in fp32, such as lambda-weighted vectors.)
 template <int D, class SC>
-__device__ __forceinline__ void rfft_bins(const uint32_t (&h)[D / 2], float (&ur)[D / 2 + 1],
-                                          float (&ui)[D / 2 + 1]) {
+__device__ __forceinline__ void rfft_bins(const float (&u)[D], float (&ur)[D / 2 + 1], float (&ui)[D / 2 + 1]) {
   constexpr int M = D / 2;
+  float xr[M], xi[M];
+  sfor<M>([&](auto I) {
+    xr[RTQ_CI(I)] = u[2 * RTQ_CI(I)];
+    xi[RTQ_CI(I)] = u[2 * RTQ_CI(I) + 1];
+  });
   float re[M], im[M];
-  cfft_from_f16<M>(h, re, im);
+  cfft_f32<M>(xr, xi, re, im);
   constexpr float s0 = (float)SC::s0, sm = (float)SC::sm, si = (float)SC::si;
   ur[0] = s0 * (re[0] + im[0]);
   ui[0] = 0.0f;
@@ -393,12 +384,13 @@ __device__ __forceinline__ void rfft_bins(const uint32_t (&h)[D / 2], float (&ur
   });
 }
 
-// z = R u for the packed orthonormal SRFT of length D (D <= 128, one lane).
+// z = R u for the packed orthonormal SRFT of length D (D <= 128, one lane),
+// u in fp32.
 template <int D>
-__device__ __forceinline__ void srft_fwd(const uint32_t (&h)[D / 2], float (&z)[D]) {
+__device__ __forceinline__ void srft_fwd(const float (&u)[D], float (&z)[D]) {
   constexpr int M = D / 2;
   float ur[M + 1], ui[M + 1];
-  rfft_bins<D, OrthoPacked<D>>(h, ur, ui);
+  rfft_bins<D, OrthoPacked<D>>(u, ur, ui);
   z[0] = ur[0];
   sfor<M - 1>([&](auto K) {
     constexpr int k = RTQ_CI(K) + 1;
@@ -571,6 +563,62 @@ __device__ __forceinline__ void dequant_unpack(const uint32_t (&cw)[D / 8], cons
         z[base + j] = mix_fma<0>(pr, s, c);
         z[base + j + 4] = mix_fma<1>(pr, s, c);
       });
+    });
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Other code widths: B-bit codes in a little-endian bit stream.
+// ---------------------------------------------------------------------------
+
+// Per group of G values of (zs * z): s = fp16_rne(absmax / 2^(B-1)) saturated
+// at 65504, q = clamp(rne(zs * z / s), -2^(B-1), 2^(B-1) - 1) (q = 0 when
+// s == 0).  Code i fills stream bits [i*B, (i+1)*B); word k of cw holds stream
+// bits 32k .. 32k+31.  The rounding is quantize_pack's: the fma lands in
+// [2^23, 2^24), where the low bits of the fp32 pattern are q mod 2^B.
+template <int D, int G, int B>
+__device__ __forceinline__ void quantize_pack_bits(const float (&z)[D], float zs, uint32_t (&cw)[D * B / 32],
+                                                   uint32_t (&sb)[D / G]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  constexpr float kLo = -(float)(1 << (B - 1)), kHi = (float)((1 << (B - 1)) - 1);
+  constexpr float kInvRange = 1.0f / (float)(1 << (B - 1));
+  constexpr uint32_t kMask = (1u << B) - 1u;
+  sfor<D * B / 32>([&](auto K) { cw[RTQ_CI(K)] = 0u; });
+  sfor<D / G>([&](auto GI) {
+    constexpr int g0 = RTQ_CI(GI) * G;
+    float a = 0.0f;
+    sfor<G>([&](auto I) { a = fmaxf(a, fabsf(z[g0 + RTQ_CI(I)])); });
+    a *= zs;
+    uint32_t bits = __half_as_ushort(__float2half_rn(a * kInvRange));
+    bits = bits < 0x7bffu ? bits : 0x7bffu;
+    sb[RTQ_CI(GI)] = bits;
+    const float s = __half2float(__ushort_as_half((unsigned short)bits));
+    const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
+    sfor<G>([&](auto I) {
+      constexpr int i = g0 + RTQ_CI(I);
+      constexpr int pos = i * B, w = pos / 32, sh = pos % 32;
+      const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(z[i], inv, kMagic), kMagic + kLo, kMagic + kHi);
+      const uint32_t f = __float_as_uint(t) & kMask;
+      cw[w] |= f << sh;
+      if constexpr (sh + B > 32) cw[w + 1] |= f >> (32 - sh);
+    });
+  });
+}
+
+// z = s' * q for every value, s' = zs * s (inverse of quantize_pack_bits).
+template <int D, int G, int B>
+__device__ __forceinline__ void dequant_unpack_bits(const uint32_t (&cw)[D * B / 32], const uint32_t (&sb)[D / G],
+                                                    float zs, float (&z)[D]) {
+  sfor<D / G>([&](auto GI) {
+    constexpr int g0 = RTQ_CI(GI) * G;
+    const float s = __half2float(__ushort_as_half((unsigned short)sb[RTQ_CI(GI)])) * zs;
+    sfor<G>([&](auto I) {
+      constexpr int i = g0 + RTQ_CI(I);
+      constexpr int pos = i * B, w = pos / 32, sh = pos % 32;
+      uint32_t v = cw[w] >> sh;
+      if constexpr (sh + B > 32) v |= cw[w + 1] << (32 - sh);
+      const int q = (int)(v << (32 - B)) >> (32 - B);  // sign-extend the B-bit field
+      z[i] = (float)q * s;
     });
   });
 }

@@ -137,3 +137,58 @@ def check_attention(o_gpu, o_orc, scales, strides, tokens, group, pairs=None):
         if sv > 0:
             worst = max(worst, float(np.max(err / (2e-3 * sv))))
     return worst
+
+
+def check_forward_ext(x16, codes_gpu, scales_gpu, group, bits, lam, seed, rps=0, period=0, rot="srft"):
+    """check_forward for b-bit codes and an optional lambda: scales exact (or
+    one fp16 ulp apart at an fp16 rounding midpoint of absmax/2^(b-1)); codes
+    exact except +-1 at elements within 1e-4 of a rounding tie.  Returns the
+    number of tie mismatches."""
+    x16 = np.asarray(x16, dtype=np.float16)
+    n, d = x16.shape
+    det = oracle.forward_detail_ext(x16, group, bits, lam, seed, rps, period, rot)
+    s_orc = det["s"]
+    s_gpu = np.asarray(scales_gpu, dtype=np.float16).reshape(s_orc.shape)
+    diff = s_gpu.view(np.uint16) != s_orc.view(np.uint16)
+    ulp_apart = np.abs(s_gpu.astype(np.float64) - s_orc.astype(np.float64)) <= fp16_ulp(s_orc) * (1 + 1e-9)
+    amb = near_fp16_midpoint(det["a"] / float(1 << (bits - 1)))
+    bad = diff & ~(amb & ulp_apart)
+    if bad.any():
+        r, j = np.argwhere(bad)[0]
+        raise AssertionError(f"scale mismatch row {r} group {j}: gpu {s_gpu[r, j]!r} oracle {s_orc[r, j]!r}")
+    z = det["z"].reshape(n, d // group, group)
+    s_used = np.where(diff, s_gpu, s_orc).astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        t = np.where(s_used > 0, z / np.where(s_used > 0, s_used, 1.0), 0.0)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    q_ref = np.clip(np.rint(t), lo, hi)
+    q_gpu = oracle.unpack_bits(np.asarray(codes_gpu, dtype=np.uint8), bits, d).reshape(q_ref.shape)
+    mism = q_gpu != q_ref
+    if mism.any():
+        tie = np.abs((t - np.floor(t)) - 0.5) < 1e-4
+        ok = tie & (np.abs(q_gpu.astype(int) - q_ref.astype(int)) == 1)
+        if not ok[mism].all():
+            idx = np.argwhere(mism & ~ok)[0]
+            raise AssertionError(f"code mismatch row {idx[0]} coord {idx[1] * group + idx[2]}: gpu "
+                                 f"{q_gpu[tuple(idx)]} oracle {q_ref[tuple(idx)]} z/s={t[tuple(idx)]!r}")
+        assert int(mism.sum()) <= 1e-5 * q_ref.size + 2, f"{int(mism.sum())} tie mismatches"
+    return int(mism.sum())
+
+
+def check_inverse_ext(codes, scales, y_gpu, d, group, bits, lam, seed, rps=0, period=0, rot="srft"):
+    """check_inverse for b-bit codes and an optional lambda: |y_gpu - y_oracle|
+    <= max(2e-3 * s_row / |lambda_c|, 1 fp16 ulp of y_oracle) (lambda divides
+    the output channel by channel)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float16)
+    y_orc, u = oracle.dequant_inv_ext(codes, scales, d, group, bits, lam, seed, rps, period, rot, return_fp64=True)
+    s_row = np.max(scales.astype(np.float64), axis=1, keepdims=True)
+    lam64 = np.ones(d) if lam is None else np.abs(np.asarray(lam, dtype=np.float16).astype(np.float64))
+    tol = np.maximum(2e-3 * s_row / lam64[None, :], fp16_ulp(u)) * (1 + 1e-9)
+    err = np.abs(np.asarray(y_gpu, dtype=np.float16).astype(np.float64) - y_orc.astype(np.float64))
+    bad = ~(err <= tol)
+    if bad.any():
+        r, c = np.argwhere(bad)[0]
+        raise AssertionError(f"output mismatch row {r} col {c}: gpu {y_gpu[r, c]!r} oracle {y_orc[r, c]!r} "
+                             f"(tol {tol[r, c]!r}); {int(bad.sum())} bad")
+    return float(np.max(err / tol, initial=0.0))

@@ -24,9 +24,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv", "srft_dequant_rows",
-                                    "srft_quant_append", "srft_quant_fwd", "srht_attn_decode", "srht_dequant_inv",
-                                    "srht_dequant_rows", "srht_quant_append", "srht_quant_fwd"]
+    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv",
+                                    "srft_dequant_inv_ext", "srft_dequant_rows", "srft_quant_append", "srft_quant_fwd",
+                                    "srft_quant_fwd_ext", "srht_attn_decode", "srht_dequant_inv",
+                                    "srht_dequant_inv_ext", "srht_dequant_rows", "srht_quant_append", "srht_quant_fwd",
+                                    "srht_quant_fwd_ext"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -193,6 +195,38 @@ def test_mapped_rejects_overlapping_buffers():
     assert mapped_call("srft_quant_append", a=A, b=A + 1024) == rtq.RTQ_ERR_INVALID_ARG       # codes inside x
     assert mapped_call("srft_dequant_rows", a=A, b=B, c=A + 4096) == rtq.RTQ_ERR_INVALID_ARG  # y overlaps codes
     assert mapped_call("srft_dequant_rows", a=A, b=B, c=B - 64) == rtq.RTQ_ERR_INVALID_ARG    # y overlaps scales
+
+
+EXT = ["srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext"]
+LAM = 0x9000000
+
+
+def ext_call(name, a=A, b=B, c=C, n=10, d=64, g=32, bits=3, lam=0, seed=1, rps=0, per=0):
+    fn = getattr(rtq.library(), name)
+    return fn(ctypes.c_void_p(a), ctypes.c_void_p(b), ctypes.c_void_p(c), n, d, g, bits, ctypes.c_void_p(lam), seed,
+              rps, per, None)
+
+
+@pytest.mark.parametrize("name", EXT)
+def test_ext_rejects_bad_arguments_without_launching(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    for kw in ({"n": -1}, {"rps": -1}, {"per": -1}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
+               {"c": C + 2}, {"lam": LAM + 2}, {"n": 0xFFFFFF01}):
+        assert ext_call(name, **kw) == bad, kw
+    for kw in ({"bits": 2}, {"bits": 5}, {"bits": 16}, {"d": 256}, {"d": 96}, {"g": 16}):
+        assert ext_call(name, **kw) == rtq.RTQ_ERR_UNSUPPORTED, kw
+
+
+@pytest.mark.parametrize("name", EXT)
+def test_ext_zero_rows_is_a_no_op(name):
+    assert ext_call(name, a=0, b=0, c=0, n=0) == rtq.RTQ_OK
+
+
+def test_ext_rejects_overlapping_buffers():
+    # n = 100, d = 64, 6 bits: x 12800 B, codes 4800 B, scales 400 B
+    assert ext_call("srft_quant_fwd_ext", n=100, bits=6, b=A + 1024) == rtq.RTQ_ERR_INVALID_ARG    # codes in x
+    assert ext_call("srft_quant_fwd_ext", n=100, bits=6, lam=B + 4784) == rtq.RTQ_ERR_INVALID_ARG   # lambda on codes
+    assert ext_call("srft_dequant_inv_ext", n=100, bits=6, c=A + 4096) == rtq.RTQ_ERR_INVALID_ARG  # y on codes
 
 
 def test_python_binding_rejects_cpu_tensors():
