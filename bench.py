@@ -466,6 +466,10 @@ def attn_main(args, w, dev):
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
     scale = ctypes.c_float(1.0 / math.sqrt(d))
+    # token-split workspace (zero-filled once; every call leaves it zeroed)
+    ws_bytes = rtq.attn_workspace_bytes(L, S, T, G, d)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    ws_ptr = ctypes.c_void_p(ws.data_ptr() if ws_bytes else None)
     sets = []
     for _ in range(replicas):
         codes = torch.randint(0, 256, (n, d // 2), generator=gen, device=dev, dtype=torch.uint8)
@@ -473,7 +477,8 @@ def attn_main(args, w, dev):
         q = torch.randn((L, S, G, d), generator=gen, device=dev).to(torch.float16)
         out = torch.empty_like(q)
         a = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
-             ctypes.c_void_p(out.data_ptr()), L, S, T, G, d, g, *strides, w.sign_seed, rps, per, scale, sh)
+             ctypes.c_void_p(out.data_ptr()), L, S, T, G, d, g, *strides, w.sign_seed, rps, per, scale,
+             ws_ptr, ws_bytes, sh)
         sets.append((a, (codes, scales, q, out)))
     torch.cuda.synchronize()
 
@@ -522,6 +527,7 @@ def attn_main(args, w, dev):
             "rotation": rot, "layout": "[layer][K,V][stream][token]" if args.attn_layout == "heads" else w.layout,
             "cache_strides": list(strides),
             "cache_replicas": replicas, "cache": "uniform int4 codes, |N(0,1)|*0.3 fp16 scales",
+            "token_split_workspace_bytes": ws_bytes,
         },
         "kernel_us": {"attn_decode": k_ms * 1e3,
                       "timing": f"hipEvents on the launch stream, every {SAMPLE}th timed step "

@@ -51,6 +51,7 @@
 #ifndef RTQ_H
 #define RTQ_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -264,18 +265,38 @@ rtq_status srht_dequant_rows(const void* codes_u8, const void* scales_f16, void*
  * inputs.  Pointers, streams and error behaviour as in the common conventions.
  * Numerics: scores keep about 22 bits (fp16 hi/lo query, exact int4 keys,
  * fp32 scaling); values and softmax weights enter the weighted sum as fp16.
+ *
+ * Token splits (optional): with fewer (layer, stream) pairs than the GPU has
+ * room for, the call can spread each stream's tokens over several
+ * workgroups, which merge their softmax partials (running max, denominator,
+ * unnormalized sum; the usual online-softmax merge) through a workspace:
+ *   workspace       inout: caller-owned device memory, 16-byte aligned, of
+ *                   workspace_bytes bytes; or NULL with workspace_bytes == 0
+ *                   (then every stream runs in one workgroup).  It must be
+ *                   zero-filled before its first use; every call that
+ *                   completes leaves it ready for the next one.  Calls that
+ *                   may run at the same time (other streams) need workspaces
+ *                   of their own.  It must not overlap the other buffers.
+ *   rtq_attn_workspace_bytes(layers, streams, tokens, q_per_kv, d) gives the
+ *   size that allows every split the call would make (0: it would not split;
+ *   0 also for invalid sizes).  A smaller workspace gives fewer splits.  The
+ *   result does not depend on the split count beyond fp32 rounding.
+ * workspace == NULL with workspace_bytes != 0 (or the reverse), or a
+ * misaligned workspace: RTQ_ERR_INVALID_ARG.
  */
 rtq_status srft_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
                             int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
                             int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
                             int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
-                            float softmax_scale, hipStream_t stream);
+                            float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
                             int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
                             int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
                             int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
-                            float softmax_scale, hipStream_t stream);
+                            float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtq_status_string(rtq_status status);

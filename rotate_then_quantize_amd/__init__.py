@@ -20,7 +20,7 @@ import os
 
 __all__ = [
     "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
-    "srft_attn_decode", "srht_attn_decode",
+    "srft_attn_decode", "srht_attn_decode", "attn_workspace_bytes",
     "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
     "srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext", "CODE_BITS",
     "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED",
@@ -67,11 +67,14 @@ def library():
         attn_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                     ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p]
+                     ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p,
+                     ctypes.c_size_t, ctypes.c_void_p]
         for name in ("srft_attn_decode", "srht_attn_decode"):
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = ctypes.c_int
+        lib.rtq_attn_workspace_bytes.argtypes = [ctypes.c_int32] * 5
+        lib.rtq_attn_workspace_bytes.restype = ctypes.c_size_t
         mapped_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
@@ -178,8 +181,32 @@ def srht_dequant_inv(codes, scales, d, group, seed, rows_per_seed=0, seed_period
     return _inv("srht_dequant_inv", codes, scales, d, group, seed, rows_per_seed, seed_period, out, stream)
 
 
+def attn_workspace_bytes(layers: int, streams: int, tokens: int, q_per_kv: int, d: int) -> int:
+    """Bytes of workspace that let *_attn_decode split every stream's tokens as far as it would (0: no split)."""
+    return int(library().rtq_attn_workspace_bytes(layers, streams, tokens, q_per_kv, d))
+
+
+# Zero-filled attention workspaces kept per (device, stream): every completed
+# call leaves its workspace zeroed again, and calls on one stream never overlap.
+_workspaces = {}
+
+
+def _attn_workspace(q, tokens, stream_handle):
+    import torch
+    layers, streams, q_per_kv, d = q.shape
+    need = attn_workspace_bytes(layers, streams, tokens, q_per_kv, d)
+    if need == 0:
+        return None
+    key = (q.device.index, stream_handle.value)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        _workspaces[key] = ws
+    return ws
+
+
 def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period, softmax_scale,
-          out, stream):
+          out, stream, workspace=None):
     import math
     import torch
     _need(q, torch.float16, "q")
@@ -206,28 +233,39 @@ def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, 
     _need(out, torch.float16, "out", tuple(q.shape))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
+    sh = _stream_handle(q, stream)
+    if workspace is None:
+        workspace = _attn_workspace(q, tokens, sh)
+    if workspace is None or workspace.numel() == 0:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _need(workspace, torch.uint8, "workspace")
+        ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel()
     _check(getattr(library(), cname)(
         ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
         ctypes.c_void_p(out.data_ptr()), layers, streams, tokens, q_per_kv, d, group, *strides,
-        seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale), _stream_handle(q, stream)))
+        seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale), ws_ptr, ws_bytes, sh))
     return out
 
 
 def srft_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
-                     softmax_scale=None, out=None, stream=None):
+                     softmax_scale=None, out=None, stream=None, workspace=None):
     """One decode step of attention over an SRFT int4 cache: q [layers, streams, q_per_kv, d] fp16
     attends over tokens 0..tokens-1 of its stream, whose key / value row is
     layer*strides[0] + kv*strides[1] + stream*strides[2] + token*strides[3] (kv 0 = K, 1 = V).
-    Returns o like q (fp16); softmax_scale defaults to 1/sqrt(d)."""
+    Returns o like q (fp16); softmax_scale defaults to 1/sqrt(d).
+    workspace: None = a zero-filled workspace kept per (device, stream), which lets the kernel split each
+    stream's tokens over several workgroups when there are few streams; a uint8 tensor = that memory
+    (zero-filled before its first use, see attn_workspace_bytes); an empty tensor = no split."""
     return _attn("srft_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
-                 softmax_scale, out, stream)
+                 softmax_scale, out, stream, workspace)
 
 
 def srht_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
-                     softmax_scale=None, out=None, stream=None):
+                     softmax_scale=None, out=None, stream=None, workspace=None):
     """srft_attn_decode over an SRHT (Walsh-Hadamard) int4 cache."""
     return _attn("srht_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
-                 softmax_scale, out, stream)
+                 softmax_scale, out, stream, workspace)
 
 
 def attn_decode(rot, *args, **kw):

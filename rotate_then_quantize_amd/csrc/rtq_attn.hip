@@ -25,7 +25,10 @@
 //   * One workgroup of 4 waves per (layer, stream); the waves split the
 //     stream's tokens into 32-token chunks and merge their softmax partials
 //     in LDS.  Workgroup ids are remapped so that each XCD works through one
-//     contiguous range of (layer, stream) pairs.
+//     contiguous range of (layer, stream) pairs.  With few pairs and a
+//     caller workspace, a stream's chunks are spread over several workgroups
+//     whose partials the last one to finish merges (the online-softmax merge
+//     again).
 //   * Each chunk's code and scale rows arrive by direct-to-LDS loads
 //     (global_load_lds) into a three-slot ring, two chunks ahead of the one
 //     being computed.  Rows may sit anywhere (the cache layout is given by
@@ -84,7 +87,17 @@ struct Params {
   int32_t seed_period;
   int32_t streams, tokens, q_per_kv;
   float qscale;  // softmax_scale * log2(e): scores come out in base-2 units
+  // Token splits per (layer, stream): splits > 1 spreads a stream's chunks
+  // over that many workgroups, which leave unnormalized partials in part and
+  // count in count; the last one to finish merges them.
+  int32_t splits;
+  float* part;      // [pairs][splits][PartFloats]
+  uint32_t* count;  // [pairs], zero between calls
 };
+
+// Floats of one split's partial: the unnormalized output sum of each query
+// (q_per_kv rows of d), then its running max and its softmax denominator.
+__host__ __device__ constexpr int64_t part_floats(int g, int d) { return ((int64_t)g * (d + 2) + 3) & ~(int64_t)3; }
 
 template <int D, int GR>
 struct Cfg {
@@ -173,6 +186,14 @@ __device__ __forceinline__ float max_over_row_groups(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Device-scope (all XCDs) store and load of one float of a split partial.
+__device__ __forceinline__ void publish(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float collect(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ uint64_t seed_of_row(const Params& p, int64_t row) {
@@ -269,10 +290,11 @@ attn_decode_kernel(Params p) {
   const int nwg = gridDim.x, b = blockIdx.x;
   const int per = nwg >> 3, extra = nwg & 7, x = b & 7;
   const int item = x * per + (x < extra ? x : extra) + (b >> 3);
+  const int pair = item / p.splits, split = item - pair * p.splits;  // a pair's splits are neighbours
   const int pairs_per_layer = (p.streams + kStreams - 1) / kStreams;
-  const int layer = item / pairs_per_layer;
+  const int layer = pair / pairs_per_layer;
   const int sw = w / kWavesPerStream, part_w = w % kWavesPerStream;  // stream of the wave, token part
-  const int stream = (item - layer * pairs_per_layer) * kStreams + sw;
+  const int stream = (pair - layer * pairs_per_layer) * kStreams + sw;
   const bool active = stream < p.streams;
   const int64_t row_k = (int64_t)layer * p.stride_layer + (int64_t)stream * p.stride_stream;
   const int64_t row_v = row_k + p.stride_kv;
@@ -280,8 +302,11 @@ attn_decode_kernel(Params p) {
   float* const stage = stage_all + sw * kMaxQ * C::QROW;
   int* const qexp = qexp_all + sw * kMaxQ;
 
-  const int nchunks = active ? (T + kChunk - 1) / kChunk : 0;
-  const int c_begin = part_w * nchunks / kWavesPerStream, c_end = (part_w + 1) * nchunks / kWavesPerStream;
+  // this workgroup's chunks (its split of the stream), then this wave's part of them
+  const int64_t nchunks = active ? (T + kChunk - 1) / kChunk : 0;
+  const int s_begin = (int)(split * nchunks / p.splits), s_len = (int)((split + 1) * nchunks / p.splits) - s_begin;
+  const int c_begin = s_begin + part_w * s_len / kWavesPerStream;
+  const int c_end = s_begin + (part_w + 1) * s_len / kWavesPerStream;
   const bool lead = active && part_w == 0;  // rotates the stream's queries and outputs
 
   // ---- prologue: queries (lead waves) and the first two chunks (every wave) ----
@@ -528,19 +553,58 @@ attn_decode_kernel(Params p) {
     });
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kStreams * G * D; idx += 64 * kWaves) {
-    const int s2 = idx / (G * D), g = (idx / D) % G, dim = idx % D;
-    const int w0 = s2 * kWavesPerStream;
+  static_assert(kStreams == 1, "the split partials assume one stream per workgroup");
+  float* const mine = p.splits > 1 ? p.part + ((int64_t)pair * p.splits + split) * part_floats(G, D) : nullptr;
+  for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+    const int g = idx / D, dim = idx % D;
     float mx = kNegBig;
-    for (int ww = w0; ww < w0 + kWavesPerStream; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
+    for (int ww = 0; ww < kWavesPerStream; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
     float num = 0.0f, den = 0.0f;
-    for (int ww = w0; ww < w0 + kWavesPerStream; ++ww) {
+    for (int ww = 0; ww < kWavesPerStream; ++ww) {
       const float f = __builtin_amdgcn_exp2f(mw[ww * kMaxQ + g] - mx);
       den = __builtin_fmaf(f, lw[ww * kMaxQ + g], den);
       num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
     }
-    // a stream past the end has no partials (den = 0); nothing reads its row
-    stage_all[(s2 * kMaxQ + g) * C::QROW + dim] = den > 0.0f ? num / (den * kVShift) : 0.0f;
+    if (p.splits == 1) {
+      stage_all[g * C::QROW + dim] = num / (den * kVShift);  // den >= 1: the max score has weight 1
+    } else {
+      publish(mine + idx, num);
+      if (dim == 0) {
+        publish(mine + G * D + g, mx);
+        publish(mine + G * D + G + g, den);
+      }
+    }
+  }
+  if (p.splits > 1) {
+    // Publish this split's partial; the workgroup that completes the count
+    // merges all of them (no workgroup ever waits for another).
+    // The partials are written and read with device-scope accesses, which
+    // the L2 of each XCD does not keep to itself, so no L2 writeback or
+    // invalidate (an agent-scope fence, which costs far more than the merge)
+    // is needed: waiting for the stores before the count moves is enough.
+    __shared__ int is_last;
+    wait_vmcnt<0>();  // this lane's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0)
+      is_last = __hip_atomic_fetch_add(p.count + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                (uint32_t)(p.splits - 1);
+    __syncthreads();
+    if (!is_last) return;
+    const float* first = p.part + (int64_t)pair * p.splits * part_floats(G, D);
+    for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
+      const int g = idx / D, dim = idx % D;
+      float mx = kNegBig;
+      for (int sp = 0; sp < p.splits; ++sp) mx = fmaxf(mx, collect(first + sp * part_floats(G, D) + G * D + g));
+      float num = 0.0f, den = 0.0f;
+      for (int sp = 0; sp < p.splits; ++sp) {
+        const float* ps = first + sp * part_floats(G, D);
+        const float f = __builtin_amdgcn_exp2f(collect(ps + G * D + g) - mx);
+        den = __builtin_fmaf(f, collect(ps + G * D + G + g), den);
+        num = __builtin_fmaf(f, collect(ps + idx), num);
+      }
+      stage_all[g * C::QROW + dim] = num / (den * kVShift);
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(p.count + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 
@@ -610,6 +674,32 @@ bool seeds_constant(int64_t layers, int64_t streams, int64_t tokens, const int64
   return true;
 }
 
+// Token splits.  The kernel's LDS ring and registers allow two resident
+// workgroups per CU, 512 on MI355X's 256 CUs.  Fewer (layer, stream) pairs
+// leave CUs idle, so each stream's chunks are spread over as many workgroups
+// as still fit in that one round (at least kMinChunksPerSplit chunks each).
+// More splits than that measured slower: a second round of shorter
+// workgroups, each with its own query rotation and merge.
+constexpr int64_t kResidentWorkgroups = 512;
+constexpr int64_t kMinChunksPerSplit = 8;
+constexpr int64_t kMaxSplits = 64;
+
+int choose_splits(int64_t pairs, int64_t tokens) {
+  if (pairs <= 0 || 2 * pairs > kResidentWorkgroups) return 1;
+  int64_t s = kResidentWorkgroups / pairs;
+  const int64_t by_tokens = (tokens + kChunk - 1) / kChunk / kMinChunksPerSplit;
+  if (s > by_tokens) s = by_tokens;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 2 ? 1 : (int)s;
+}
+
+// Workspace of a launch with `splits` splits: the per-pair counters (padded
+// to 256 bytes), then the partials.
+uint64_t workspace_bytes(int64_t pairs, int splits, int g, int d) {
+  if (splits < 2) return 0;
+  return (uint64_t)((pairs * 4 + 255) & ~(int64_t)255) + (uint64_t)pairs * splits * part_floats(g, d) * 4;
+}
+
 bool overlaps(const void* a, __int128 na, const void* b, __int128 nb) {
   const __int128 a0 = (__int128)(uintptr_t)a, b0 = (__int128)(uintptr_t)b;
   return a0 < b0 + nb && b0 < a0 + na;
@@ -617,7 +707,8 @@ bool overlaps(const void* a, __int128 na, const void* b, __int128 nb) {
 
 rtq_status run(int rot, const void* q, const void* codes, const void* scales, void* out, int32_t layers,
                int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d, int32_t group, const int64_t (&st)[4],
-               uint64_t seed, int64_t rps, int32_t period, float softmax_scale, hipStream_t stream) {
+               uint64_t seed, int64_t rps, int32_t period, float softmax_scale, void* workspace,
+               size_t workspace_size, hipStream_t stream) {
   if (layers < 0 || streams < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
@@ -637,6 +728,7 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   if (wgs > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
   if (!q || !codes || !scales || !out) return RTQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return RTQ_ERR_INVALID_ARG;
+  if ((workspace == nullptr) != (workspace_size == 0) || !aligned16(workspace)) return RTQ_ERR_INVALID_ARG;
   // largest row the kernel reads, in 128-bit arithmetic
   const __int128 max_row = (__int128)(layers - 1) * st[0] + st[1] + (__int128)(streams - 1) * st[2] +
                            (__int128)(tokens - 1) * st[3];
@@ -647,6 +739,14 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, codes, code_bytes) ||
       overlaps(out, qo_bytes, scales, scale_bytes))
     return RTQ_ERR_INVALID_ARG;
+  if (workspace && (overlaps(workspace, workspace_size, q, qo_bytes) || overlaps(workspace, workspace_size, out, qo_bytes) ||
+                    overlaps(workspace, workspace_size, codes, code_bytes) ||
+                    overlaps(workspace, workspace_size, scales, scale_bytes)))
+    return RTQ_ERR_INVALID_ARG;
+  // as many splits as the policy asks for and the workspace holds
+  int splits = workspace ? choose_splits(wgs, tokens) : 1;
+  while (splits > 1 && (workspace_bytes(wgs, splits, q_per_kv, d) > workspace_size || wgs * splits > 0x7fffffff))
+    --splits;
   Params p;
   p.q = static_cast<const uint4*>(q);
   p.codes = static_cast<const uint8_t*>(codes);
@@ -663,9 +763,13 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   p.tokens = tokens;
   p.q_per_kv = q_per_kv;
   p.qscale = (float)((double)softmax_scale * 1.4426950408889634074);
+  p.splits = splits;
+  p.count = splits > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
+  p.part = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ((wgs * 4 + 255) & ~(int64_t)255))
+                      : nullptr;
   void* kargs[] = {&p};
   const hipError_t e =
-      hipLaunchKernel(fn, dim3((unsigned)wgs), dim3(64 * kWavesPerStream), kargs, 0, stream);
+      hipLaunchKernel(fn, dim3((unsigned)(wgs * splits)), dim3(64 * kWavesPerStream), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
 
@@ -678,18 +782,31 @@ RTQ_API rtq_status srft_attn_decode(const void* q_f16, const void* codes_u8, con
                                     int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
                                     int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
                                     int64_t stride_token, uint64_t seed, int64_t rows_per_seed,
-                                    int32_t seed_period, float softmax_scale, hipStream_t stream) {
+                                    int32_t seed_period, float softmax_scale, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
   return rtq::attn::run(0, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
-                        seed, rows_per_seed, seed_period, softmax_scale, stream);
+                        seed, rows_per_seed, seed_period, softmax_scale, workspace, workspace_bytes, stream);
 }
 
 RTQ_API rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
                                     int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
                                     int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
                                     int64_t stride_token, uint64_t seed, int64_t rows_per_seed,
-                                    int32_t seed_period, float softmax_scale, hipStream_t stream) {
+                                    int32_t seed_period, float softmax_scale, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
   return rtq::attn::run(1, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
-                        seed, rows_per_seed, seed_period, softmax_scale, stream);
+                        seed, rows_per_seed, seed_period, softmax_scale, workspace, workspace_bytes, stream);
+}
+
+RTQ_API size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv,
+                                        int32_t d) {
+  if (layers <= 0 || streams <= 0 || tokens < 1 || q_per_kv < 1 || q_per_kv > rtq::attn::kMaxQ || d <= 0)
+    return 0;
+  const int64_t pairs = (int64_t)layers * streams;
+  if (pairs > 0x7fffffff) return 0;
+  int splits = rtq::attn::choose_splits(pairs, tokens);
+  while (splits > 1 && pairs * splits > 0x7fffffff) --splits;
+  return (size_t)rtq::attn::workspace_bytes(pairs, splits, q_per_kv, d);
 }

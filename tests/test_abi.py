@@ -24,7 +24,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["rtq_status_string", "srft_attn_decode", "srft_dequant_inv",
+    assert declared_functions() == ["rtq_attn_workspace_bytes", "rtq_status_string", "srft_attn_decode", "srft_dequant_inv",
                                     "srft_dequant_inv_ext", "srft_dequant_rows", "srft_quant_append", "srft_quant_fwd",
                                     "srft_quant_fwd_ext", "srht_attn_decode", "srht_dequant_inv",
                                     "srht_dequant_inv_ext", "srht_dequant_rows", "srht_quant_append", "srht_quant_fwd",
@@ -106,11 +106,15 @@ ATTN = ["srft_attn_decode", "srht_attn_decode"]
 Q, K, S_, O = 0x10000, 0x2000000, 0x6000000, 0x8000000  # q, codes, scales, out (never dereferenced)
 
 
+WS = 0xA000000  # workspace (never dereferenced)
+
+
 def attn_call(name, q=Q, codes=K, scales=S_, out=O, layers=2, streams=3, tokens=50, qpk=4, d=128, g=32,
-              strides=(300, 150, 50, 1), seed=1, rps=0, per=0, softmax_scale=0.125):
+              strides=(300, 150, 50, 1), seed=1, rps=0, per=0, softmax_scale=0.125, ws=0, ws_bytes=0):
     fn = getattr(rtq.library(), name)
     return fn(ctypes.c_void_p(q), ctypes.c_void_p(codes), ctypes.c_void_p(scales), ctypes.c_void_p(out),
-              layers, streams, tokens, qpk, d, g, *strides, seed, rps, per, ctypes.c_float(softmax_scale), None)
+              layers, streams, tokens, qpk, d, g, *strides, seed, rps, per, ctypes.c_float(softmax_scale),
+              ctypes.c_void_p(ws), ws_bytes, None)
 
 
 @pytest.mark.parametrize("name", ATTN)
@@ -161,6 +165,39 @@ def test_attention_rejects_overlapping_output(name):
     assert attn_call(name, out=Q + 4096) == rtq.RTQ_ERR_INVALID_ARG
     assert attn_call(name, out=K + 16384) == rtq.RTQ_ERR_INVALID_ARG
     assert attn_call(name, out=S_ - 4096) == rtq.RTQ_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_rejects_bad_workspaces(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    assert attn_call(name, ws=WS, ws_bytes=0) == bad          # pointer without a size
+    assert attn_call(name, ws=0, ws_bytes=4096) == bad        # size without a pointer
+    assert attn_call(name, ws=WS + 8, ws_bytes=4096) == bad   # misaligned
+    assert attn_call(name, ws=Q - 1024, ws_bytes=4096) == bad   # overlaps q
+    assert attn_call(name, ws=O + 16, ws_bytes=4096) == bad     # overlaps out
+    assert attn_call(name, ws=K + 4096, ws_bytes=4096) == bad   # overlaps the codes
+    assert attn_call(name, ws=S_ - 16, ws_bytes=64) == bad      # overlaps the scales
+    assert attn_call(name, q=0, codes=0, scales=0, out=0, layers=0, ws=WS, ws_bytes=4096) == rtq.RTQ_OK
+
+
+def test_attention_workspace_size_query():
+    f = rtq.attn_workspace_bytes
+    # many (layer, stream) pairs or short streams: no split, no workspace
+    assert f(28, 64, 2048, 6, 128) == 0
+    assert f(1, 1, 255, 1, 64) == 0
+    # invalid sizes
+    for args in [(0, 1, 4096, 1, 64), (1, 0, 4096, 1, 64), (1, 1, 0, 1, 64), (1, 1, 4096, 0, 64),
+                 (1, 1, 4096, 9, 64), (1, 1, 4096, 1, 0), (-1, 1, 4096, 1, 64)]:
+        assert f(*args) == 0, args
+    # few pairs, long streams: counters (256-byte block) + pairs * splits partials
+    # of q_per_kv * (d + 2) floats rounded up to 4
+    pairs, qpk, d = 160, 3, 64
+    splits = 3  # 512 // 160 resident workgroups, below 4096 tokens / (32 * 8)
+    assert f(32, 5, 4096, qpk, d) == 768 + pairs * splits * 200 * 4
+    assert f(1, 1, 1 << 20, 8, 128) == 256 + 64 * (8 * 130) * 4  # capped at 64 splits
+    assert f(1, 1, 2048, 8, 128) == 256 + 8 * (8 * 130) * 4       # 2048 tokens / (32 * 8)
+    assert f(16, 16, 4096, 1, 64) == 1024 + 256 * 2 * 68 * 4     # 256 pairs: two per CU
+    assert f(16, 17, 4096, 1, 64) == 0                            # 272 pairs: splitting needs a second round
 
 
 MAPPED = ["srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"]

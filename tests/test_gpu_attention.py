@@ -40,22 +40,24 @@ def make_cache(rng, n, d, g, seed, rps, per, rot, scale=1.0, outliers=0):
     return oracle.quant_fwd(x.astype(np.float16), g, seed, rps, per, rot)
 
 
-def gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale=None):
+def gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale=None, workspace=None):
     q = torch.from_numpy(np.ascontiguousarray(q16)).to(DEV)
     c = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
     s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
-    o = rtq.attn_decode(rot, q, c, s, strides, tokens, g, seed, rps, per, softmax_scale)
+    o = rtq.attn_decode(rot, q, c, s, strides, tokens, g, seed, rps, per, softmax_scale, workspace=workspace)
     torch.cuda.synchronize()
     return o.cpu().numpy()
 
 
 def run_case(rot, d, g, layers, streams, tokens, qpk, strides, n, seed=7, rps=0, per=0, softmax_scale=None,
-             q_scale=1.0, v_scale=1.0, rng_seed=0, outliers=0):
+             q_scale=1.0, v_scale=1.0, rng_seed=0, outliers=0, workspace=None):
     rng = np.random.default_rng(rng_seed)
     codes, scales = make_cache(rng, n, d, g, seed, rps, per, rot, v_scale, outliers)
     q16 = (rng.standard_normal((layers, streams, qpk, d)) * q_scale).astype(np.float16)
-    print(f"case rot={rot} d={d} g={g} L={layers} S={streams} T={tokens} G={qpk} strides={strides}", flush=True)
-    o_gpu = gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale)
+    ws = "auto" if workspace is None else f"{workspace.numel()} bytes"
+    print(f"case rot={rot} d={d} g={g} L={layers} S={streams} T={tokens} G={qpk} strides={strides} workspace={ws}",
+          flush=True)
+    o_gpu = gpu_attn(rot, q16, codes, scales, strides, tokens, g, seed, rps, per, softmax_scale, workspace)
     o_orc = oracle.attn_decode(q16, codes, scales, strides, layers, streams, tokens, qpk, d, g, seed, rps, per,
                                rot, softmax_scale)
     worst = check_attention(o_gpu, o_orc, scales, strides, tokens, g)
@@ -113,6 +115,73 @@ def test_strided_cache_with_gaps():
     L, S, T = 2, 2, 50
     strides = (2 * S * 160, S * 160, 160, 3)
     run_case("srft", 128, 32, L, S, T, 2, strides, L * 2 * S * 160, seed=1)
+
+
+# ---------------------------------------------------------------------------
+# Token splits: few (layer, stream) pairs and long streams, so the call spreads
+# each stream over several workgroups that merge through the workspace.
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,g", ATTN)
+def test_split_streams(rot, d, g):
+    L, S, T, G = 1, 2, 1500, 3  # 47 chunks, the last one ragged
+    assert rtq.attn_workspace_bytes(L, S, T, G, d) > 0, "this shape is meant to split"
+    run_case(rot, d, g, L, S, T, G, lm(S, T), L * 2 * S * T, seed=21, outliers=2)
+
+
+@pytest.mark.parametrize("T", [512, 513, 2047, 4100])
+def test_split_token_counts(T):
+    L, S, G = 2, 1, 8
+    run_case("srft", 128, 32, L, S, T, G, lm(S, T), L * 2 * S * T, seed=23, rps=2 * S * T, per=L)
+
+
+def test_split_workspace_sizes_and_reuse():
+    """The same call with no workspace, a workspace for two splits, and the full
+    workspace (twice, then again with fewer tokens: every call leaves the
+    counters at zero) agrees with the oracle each time."""
+    L, S, T, G, d, g = 1, 3, 1200, 4, 64, 32
+    full = rtq.attn_workspace_bytes(L, S, T, G, d)
+    assert full > 0
+    pairs = L * S
+    two = ((pairs * 4 + 255) // 256) * 256 + pairs * 2 * (((G * (d + 2)) + 3) // 4 * 4) * 4
+    assert two < full
+    ws_full = torch.zeros(full, dtype=torch.uint8, device=DEV)
+    for ws in (torch.empty(0, dtype=torch.uint8, device=DEV), torch.zeros(two, dtype=torch.uint8, device=DEV),
+               ws_full, ws_full):
+        run_case("srft", d, g, L, S, T, G, lm(S, T), L * 2 * S * T, seed=31, workspace=ws)
+    run_case("srft", d, g, L, S, 700, G, lm(S, T), L * 2 * S * T, seed=31, workspace=ws_full)
+    assert int(ws_full[:256].sum()) == 0, "the counters are back at zero"
+
+
+def test_split_matches_unsplit_closely():
+    """Split and unsplit runs differ only by fp32 rounding of the merge."""
+    rng = np.random.default_rng(5)
+    L, S, T, G, d, g = 1, 2, 3000, 6, 128, 32
+    codes, scales = make_cache(rng, L * 2 * S * T, d, g, 3, 0, 0, "srft")
+    q16 = rng.standard_normal((L, S, G, d)).astype(np.float16)
+    a = gpu_attn("srft", q16, codes, scales, lm(S, T), T, g, 3, 0, 0,
+                 workspace=torch.empty(0, dtype=torch.uint8, device=DEV)).astype(np.float64)
+    b = gpu_attn("srft", q16, codes, scales, lm(S, T), T, g, 3, 0, 0).astype(np.float64)
+    scale = np.abs(a).max()
+    assert np.abs(a - b).max() <= 2e-3 * scale, np.abs(a - b).max() / scale
+
+
+def test_workspace_errors():
+    q = torch.zeros((1, 1, 2, 128), dtype=torch.float16, device=DEV)
+    c = torch.zeros((4096, 64), dtype=torch.uint8, device=DEV)
+    s = torch.zeros((4096, 4), dtype=torch.float16, device=DEV)
+    ws = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(rtq.RTQError):
+        rtq.srft_attn_decode(q, c, s, (0, 2048, 0, 1), 2048, 32, 1, workspace=ws[1:])   # misaligned
+    with pytest.raises(rtq.RTQError):
+        rtq.srft_attn_decode(q, c, s, (0, 2048, 0, 1), 2048, 32, 1, workspace=c.view(-1))  # overlaps the codes
+    lib = rtq.library()
+    st = lib.srft_attn_decode(q.data_ptr(), c.data_ptr(), s.data_ptr(), ws.data_ptr() + 4096, 1, 1, 2048, 2, 128, 32,
+                              0, 2048, 0, 1, 1, 0, 0, 0.1, None, 64, None)  # size without a pointer
+    assert st == rtq.RTQ_ERR_INVALID_ARG
+    torch.cuda.synchronize()
 
 
 def test_empty_grid_is_a_no_op():
