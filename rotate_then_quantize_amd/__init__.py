@@ -34,7 +34,7 @@ RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_HIP = 0, 1, 2, 3
 # (d, group) pairs the library is built for
 SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 # (d, group) pairs of the decode-attention kernels; at most 8 query heads per K/V head
-ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
+ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 ATTN_MAX_Q_PER_KV = 8
 # code widths of the *_ext entry points (d = 64 or 128)
 CODE_BITS = (3, 4, 6, 8)

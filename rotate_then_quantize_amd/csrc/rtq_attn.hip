@@ -21,7 +21,7 @@
 // domain, and rotates one output vector back per query, instead of
 // inverse-rotating every cached vector.
 //
-// Mapping to CDNA4 (d = 64 / 128; q_per_kv <= 8):
+// Mapping to CDNA4 (d = 64 / 128 / 256; q_per_kv <= 8):
 //   * One workgroup of 4 waves per (layer, stream); the waves split the
 //     stream's tokens into 32-token chunks and merge their softmax partials
 //     in LDS.  Workgroup ids are remapped so that each XCD works through one
@@ -102,34 +102,51 @@ __host__ __device__ constexpr int64_t part_floats(int g, int d) { return ((int64
 template <int D, int GR>
 struct Cfg {
   static constexpr int WAVES = kWavesPerStream;
+  // Ring slots per wave: three (two chunks in flight) up to d = 128; two at
+  // d = 256, where three would leave room for one workgroup per CU only.
+  static constexpr int BUFS = D == 256 ? 2 : kBufs;
   static constexpr int KS = D / 32;       // q.k k-steps = 16-byte pieces per code row
   static constexpr int NT = D / 16;       // p.v output tiles of 16 dims
   static constexpr int RB = D / 2;        // code bytes per row
   static constexpr int SPR = D / GR;      // scales per row
-  static constexpr int SLOT = SPR == 4 ? 8 : 4;  // LDS bytes per token of scales
+  static constexpr int SLOT = 2 * SPR > 4 ? 2 * SPR : 4;  // LDS bytes per token of scales
   static constexpr int CODE_BYTES = kChunk * RB;
   static constexpr int SCALE_BYTES = kChunk * SLOT;
   static constexpr int BUF = 2 * CODE_BYTES + 2 * SCALE_BYTES;  // K codes, V codes, K scales, V scales
   static constexpr int CODE_DMA = CODE_BYTES / 1024;             // 16-byte loads per chunk per K or V
-  static constexpr int NDMA = 2 * CODE_DMA + (SPR == 4 ? 2 : 1);
+  static constexpr int NDMA = 2 * CODE_DMA + (SLOT == 8 ? 2 : 1);
   static constexpr int QROW = D + 4;  // fp32 row stride of the query / output staging
   static constexpr int SLOT_ARRAY = WAVES * BUF;  // one ring slot of every wave
   static constexpr int COMBINE = WAVES * kMaxQ * QROW * 4 + 2 * WAVES * kMaxQ * 4;
   static_assert(COMBINE <= SLOT_ARRAY, "the merge area fits in ring slot 0");
   static_assert(GR >= 32 && D % GR == 0, "groups of at least 32 values");
+  // d = 256: the whole workgroup rotates the queries and outputs (one
+  // coordinate per thread), in a work area that aliases ring slot 1, which
+  // is free before the first chunk and after the last one: the query stage
+  // [kMaxQ][QROW], the transposed vectors [D][kMaxQ] and the twiddles [D].
+  static constexpr bool DENSE_ROT = D == 256;
+  static constexpr int ROT_AREA = kMaxQ * QROW * 4 + D * kMaxQ * 4 + D * 8;
+  static_assert(!DENSE_ROT || (BUFS == 2 && ROT_AREA <= SLOT_ARRAY && D == 64 * WAVES),
+                "the rotation area needs a free ring slot and one thread per coordinate");
 };
 
 // Token row r of a chunk sits in LDS row lrow(r) (an involution), and 16-byte
-// piece k of LDS row L in slot k ^ swz(L).  For d = 128 this makes both the
-// q.k reads (16 rows x 4 lanes) and the p.v reads (4 rows x 16 lanes) hit 64
-// distinct banks.
+// piece k of LDS row L in slot k ^ swz(L).  For d = 128 and d = 256 this
+// makes both the q.k reads (16 rows x 4 lanes) and the p.v reads (4 rows x
+// 16 lanes) hit 64 distinct banks.  At d = 256 (128-byte rows, two rows per
+// 64 banks) the p.v rows 4h + c get alternating parity from lrow, and the
+// two rows of one parity get slot ranges 4 apart from swz.
 template <int D>
 __device__ __forceinline__ int lrow(int r) {
-  return D == 128 ? (r ^ ((r >> 2) & 3)) : r;
+  if constexpr (D == 256) return r ^ ((r >> 2) & 1);
+  else if constexpr (D == 128) return r ^ ((r >> 2) & 3);
+  else return r;
 }
 template <int D>
 __device__ __forceinline__ int swz(int lr) {
-  return D == 128 ? ((lr >> 2) & 3) : ((lr >> 3) & 1);
+  if constexpr (D == 256) return (lr >> 1) & 7;
+  else if constexpr (D == 128) return (lr >> 2) & 3;
+  else return (lr >> 3) & 1;
 }
 
 __device__ __forceinline__ f16x2_t as_h2(uint32_t w) { return __builtin_bit_cast(f16x2_t, w); }
@@ -213,6 +230,105 @@ __device__ __forceinline__ void wave_sign_masks(uint64_t s, int lane, uint32_t (
   });
 }
 
+// ---------------------------------------------------------------------------
+// d = 256: the queries are rotated and the outputs rotated back by the whole
+// workgroup, thread t computing coordinate t of every query as a direct sum
+// over the 256 inputs.  This runs once per stream and step, about 2k
+// instructions per thread, where one lane per vector would need 256 fp32
+// registers.  Vectors sit transposed in LDS, v[n * kMaxQ + g], so each term's
+// reads are one broadcast.
+// ---------------------------------------------------------------------------
+
+struct Twiddle256 {
+  float c[256], s[256];  // cos(2 pi m / 256), sin(2 pi m / 256)
+};
+consteval Twiddle256 make_twiddle256() {
+  Twiddle256 t{};
+  for (int m = 0; m < 256; ++m) {
+    t.c[m] = (float)cos2pi(m, 256);
+    t.s[m] = (float)sin2pi(m, 256);
+  }
+  return t;
+}
+__constant__ Twiddle256 kTwiddle256 = make_twiddle256();
+
+template <int NQ>
+__device__ __forceinline__ void load_column(const float* v, int n, float (&a)[NQ]) {
+  const float4 x = *reinterpret_cast<const float4*>(v + n * kMaxQ);
+  a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+  if constexpr (NQ == 8) {
+    const float4 y = *reinterpret_cast<const float4*>(v + n * kMaxQ + 4);
+    a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+  }
+}
+
+// z[g] = coordinate t of R v_g for NQ vectors: the packed orthonormal real
+// DFT (z_0 = X_0 / 16, z_{2k-1} = sqrt2 Re X_k / 16, z_{2k} = sqrt2 Im X_k / 16,
+// z_255 = X_128 / 16) for SRFT, H v / 16 for SRHT.
+template <int ROT, int NQ>
+__device__ __forceinline__ void dense_forward(const float* v, const float2* tw, int t, float (&z)[NQ]) {
+  float acc[NQ];
+  sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = 0.0f; });
+  if constexpr (ROT == 0) {
+    const int k = (t + 1) >> 1;
+    const bool im = t > 0 && t < 255 && (t & 1) == 0;  // X_k = sum v_n (cos - i sin)(2 pi k n / 256)
+    int idx = 0;
+#pragma unroll 4
+    for (int n = 0; n < 256; ++n) {
+      const float2 w = tw[idx];
+      const float c = im ? -w.y : w.x;
+      float a[NQ];
+      load_column<NQ>(v, n, a);
+      sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = __builtin_fmaf(c, a[RTQ_CI(G)], acc[RTQ_CI(G)]); });
+      idx = (idx + k) & 255;
+    }
+    const float norm = (t == 0 || t == 255) ? 0.0625f : (float)(csqrt(2.0) / 16.0);
+    sfor<NQ>([&](auto G) { z[RTQ_CI(G)] = acc[RTQ_CI(G)] * norm; });
+  } else {
+#pragma unroll 4
+    for (int n = 0; n < 256; ++n) {
+      const float c = (__builtin_popcount(t & n) & 1) ? -1.0f : 1.0f;  // H[t][n]
+      float a[NQ];
+      load_column<NQ>(v, n, a);
+      sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = __builtin_fmaf(c, a[RTQ_CI(G)], acc[RTQ_CI(G)]); });
+    }
+    sfor<NQ>([&](auto G) { z[RTQ_CI(G)] = acc[RTQ_CI(G)] * 0.0625f; });
+  }
+}
+
+// u[g] = element t of R^T z_g: the orthonormal inverse real DFT of the
+// unpacked bins for SRFT, H z / 16 for SRHT.
+template <int ROT, int NQ>
+__device__ __forceinline__ void dense_inverse(const float* z, const float2* tw, int t, float (&u)[NQ]) {
+  if constexpr (ROT == 0) {
+    float a0[NQ], a1[NQ], acc[NQ];
+    load_column<NQ>(z, 0, a0);
+    load_column<NQ>(z, 255, a1);
+    const float alt = (t & 1) ? -1.0f : 1.0f;  // cos(pi t)
+    sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = 0.0f; });
+    int idx = t;
+#pragma unroll 4
+    for (int k = 1; k < 128; ++k) {
+      const float2 w = tw[idx];
+      float re[NQ], im[NQ];
+      load_column<NQ>(z, 2 * k - 1, re);
+      load_column<NQ>(z, 2 * k, im);
+      sfor<NQ>([&](auto G) {
+        constexpr int g = RTQ_CI(G);
+        acc[g] = __builtin_fmaf(w.x, re[g], __builtin_fmaf(-w.y, im[g], acc[g]));
+      });
+      idx = (idx + t) & 255;
+    }
+    constexpr float r2 = (float)csqrt(2.0);
+    sfor<NQ>([&](auto G) {
+      constexpr int g = RTQ_CI(G);
+      u[g] = __builtin_fmaf(r2, acc[g], __builtin_fmaf(alt, a1[g], a0[g])) * 0.0625f;
+    });
+  } else {
+    dense_forward<1, NQ>(z, tw, t, u);  // H / 16 is its own inverse
+  }
+}
+
 // One direct-to-LDS load (nt): lane i's BYTES bytes from g land at LDS byte
 // lds + BYTES * i.  Written as inline asm so that the compiler, which cannot
 // tell the ring slots apart, does not add a full vmcnt wait before every LDS
@@ -228,6 +344,55 @@ __device__ __forceinline__ void dma_to_lds(const void* g, const void* lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
   else
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
+}
+
+// d = 256 prologue, every thread: the stream's G queries, sign-flipped with
+// the key signs (element t by thread t), go transposed into the work area;
+// thread t computes coordinate t of each rotated query, scaled by qscale;
+// then each query is scaled by the power of two 2^-e that puts its largest
+// entry in [2^13, 2^14) and stored to the stage [kMaxQ][D + 4].
+template <int D, int ROT>
+__device__ __forceinline__ void dense_queries(const Params& p, int64_t qrow, uint64_t seed_k, int G, uint8_t* area,
+                                              float* stage, int* qexp) {
+  __shared__ uint32_t amax_bits[kMaxQ];
+  const int t = threadIdx.x;
+  float* vt = reinterpret_cast<float*>(area + kMaxQ * (D + 4) * 4);
+  float2* tw = reinterpret_cast<float2*>(vt + D * kMaxQ);
+  const _Float16* q16 = reinterpret_cast<const _Float16*>(p.q);
+  const float sg = sign_bit(seed_k, (uint32_t)t) ? -1.0f : 1.0f;
+  float col[kMaxQ];
+  sfor<kMaxQ>([&](auto Gi) {
+    constexpr int g = RTQ_CI(Gi);
+    col[g] = g < G ? sg * (float)q16[(qrow + g) * D + t] : 0.0f;
+  });
+  *reinterpret_cast<float4*>(vt + t * kMaxQ) = make_float4(col[0], col[1], col[2], col[3]);
+  *reinterpret_cast<float4*>(vt + t * kMaxQ + 4) = make_float4(col[4], col[5], col[6], col[7]);
+  if constexpr (ROT == 0) tw[t] = make_float2(kTwiddle256.c[t], kTwiddle256.s[t]);
+  if (t < kMaxQ) amax_bits[t] = 0u;
+  __syncthreads();
+  float z[kMaxQ];
+  if (G <= 4) {
+    float z4[4];
+    dense_forward<ROT, 4>(vt, tw, t, z4);
+    sfor<kMaxQ>([&](auto Gi) { z[RTQ_CI(Gi)] = RTQ_CI(Gi) < 4 ? z4[RTQ_CI(Gi) & 3] : 0.0f; });
+  } else {
+    dense_forward<ROT, 8>(vt, tw, t, z);
+  }
+  sfor<kMaxQ>([&](auto Gi) {
+    constexpr int g = RTQ_CI(Gi);
+    z[g] *= p.qscale;
+    if (g < G)
+      __hip_atomic_fetch_max(&amax_bits[g], __float_as_uint(fabsf(z[g])), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
+  });
+  __syncthreads();
+  sfor<kMaxQ>([&](auto Gi) {
+    constexpr int g = RTQ_CI(Gi);
+    const float amax = __uint_as_float(amax_bits[g]);
+    const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+    stage[g * (D + 4) + t] = __builtin_ldexpf(z[g], -e);
+    if (t == g) qexp[g] = e;
+  });
 }
 
 // Direct-to-LDS loads of chunk tokens tok0 .. tok0+31 (tokens past the end
@@ -251,7 +416,13 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int6
     dma_to_lds<16>(gv, buf + C::CODE_BYTES + RTQ_CI(I) * 1024);
   });
   uint8_t* sb = buf + 2 * C::CODE_BYTES;
-  if constexpr (C::SPR == 4) {
+  if constexpr (C::SLOT == 16) {
+    // 16 bytes per token: lanes 0..31 keys, 32..63 values, one load each
+    const int r = lane & 31;
+    const int t = tok0 + r < last ? tok0 + r : last;
+    const int64_t row = (lane < 32 ? row_k : row_v) + (int64_t)t * p.stride_token;
+    dma_to_lds<16>(p.scales + row * 16, sb);
+  } else if constexpr (C::SLOT == 8) {
     // 8 bytes per token: lane l loads word l & 1 of token l / 2
     const int t = tok0 + lane / 2 < last ? tok0 + lane / 2 : last;
     const int64_t off = (int64_t)t * p.stride_token;
@@ -276,9 +447,12 @@ attn_decode_kernel(Params p) {
   // for the chunk being read.
   __shared__ __attribute__((aligned(16))) uint8_t slot0[C::SLOT_ARRAY];
   __shared__ __attribute__((aligned(16))) uint8_t slot1[C::SLOT_ARRAY];
-  __shared__ __attribute__((aligned(16))) uint8_t slot2[kBufs > 2 ? C::SLOT_ARRAY : 16];
-  __shared__ __attribute__((aligned(16))) float stage_all[kStreams * kMaxQ * C::QROW];  // query in, output out
+  __shared__ __attribute__((aligned(16))) uint8_t slot2[C::BUFS > 2 ? C::SLOT_ARRAY : 16];
+  // query in, output out (d = 256: in the work area of ring slot 1)
+  __shared__ __attribute__((aligned(16))) float stage_arr[C::DENSE_ROT ? 4 : kStreams * kMaxQ * C::QROW];
   __shared__ int qexp_all[kStreams * kMaxQ];
+  float* const stage_all = C::DENSE_ROT ? reinterpret_cast<float*>(slot1) : stage_arr;
+  float* const vt_all = reinterpret_cast<float*>(slot1 + kMaxQ * C::QROW * 4);  // d = 256: [D][kMaxQ]
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;
@@ -310,15 +484,17 @@ attn_decode_kernel(Params p) {
   const bool lead = active && part_w == 0;  // rotates the stream's queries and outputs
 
   // ---- prologue: queries (lead waves) and the first two chunks (every wave) ----
-  uint4 qv[D / 8];
-  if (lead && lane < G) {
+  uint4 qv[C::DENSE_ROT ? 1 : D / 8];
+  if (!C::DENSE_ROT && lead && lane < G) {
     const uint4* src = p.q + (qrow + lane) * (D / 8);
     sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
   }
   if (c_begin < c_end) issue_chunk<D, GR>(p, row_k, row_v, c_begin * kChunk, slot0 + w * C::BUF, lane);
-  if (kBufs > 2 && c_begin + 1 < c_end)
+  if (C::BUFS > 2 && c_begin + 1 < c_end)
     issue_chunk<D, GR>(p, row_k, row_v, (c_begin + 1) * kChunk, slot1 + w * C::BUF, lane);
-  if (lead) {
+  if constexpr (C::DENSE_ROT) {
+    dense_queries<D, ROT>(p, qrow, seed_of_row(p, row_k), G, slot1, stage, qexp);
+  } else if (lead) {
     uint32_t mk[D / 2];
     wave_sign_masks<D>(seed_of_row(p, row_k), lane, mk);
     if (lane < G) {
@@ -383,28 +559,31 @@ attn_decode_kernel(Params p) {
   }
   const int my_e = n < G ? qexp[n & 7] : 0;
   const bool q_lane = n < G;  // lanes whose scores / outputs belong to a query
+  if constexpr (C::DENSE_ROT) __syncthreads();  // the stage in ring slot 1 is read; the ring may refill it
 
   f32x4_t acc[C::NT];
   sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f}; });
   float m_run = kNegBig, l_run = 0.0f;
 
-  // p.v A operand: lane n reads code word dw of each token row; for d = 128
-  // dims 8n + i for tile i, for d = 64 dims 8(n & 7) + 4(n >> 3) + i.
-  const int dw = D == 128 ? n : (n & 7);
-  const int vgi = (8 * dw) / GR;  // the scale group of those dims
+  // p.v A operand: lane n reads code word dw of each token row (and word
+  // dw + 16 at d = 256); tile i covers dims 8n + i (d = 128), 128 (i / 8) +
+  // 8n + i % 8 (d = 256), or 8(n & 7) + 4(n >> 3) + i (d = 64).
+  constexpr int WH = D == 256 ? 2 : 1;  // code words per lane and token row
+  const int dw = D == 64 ? (n & 7) : n;
   const uint32_t vsel = (D == 64 && n >= 8) ? 0x07060302u : 0x05040100u;
 
-  // one chunk in ring slot B (chunk c - c_begin lives in slot (c - c_begin) % kBufs);
-  // kBufs - 1 chunks are in flight while one is computed
+  // one chunk in ring slot B (chunk c - c_begin lives in slot (c - c_begin) % BUFS);
+  // BUFS - 1 chunks are in flight while one is computed
   auto chunk = [&](auto B, int c) {
+    constexpr int NB = C::BUFS;
     constexpr int b = RTQ_CI(B);
-    constexpr int nb = (b + kBufs - 1) % kBufs;  // slot of chunk c + kBufs - 1
+    constexpr int nb = (b + NB - 1) % NB;  // slot of chunk c + NB - 1
     uint8_t* const buf = b == 0 ? slot0 + w * C::BUF : b == 1 ? slot1 + w * C::BUF : slot2 + w * C::BUF;
     uint8_t* const next = nb == 0 ? slot0 + w * C::BUF : nb == 1 ? slot1 + w * C::BUF : slot2 + w * C::BUF;
-    if (kBufs > 2 && c + 1 < c_end) wait_vmcnt<C::NDMA>();
+    if (NB > 2 && c + 1 < c_end) wait_vmcnt<C::NDMA>();
     else wait_vmcnt<0>();
     lds_sync();
-    if (c + kBufs - 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + kBufs - 1) * kChunk, next, lane);
+    if (c + NB - 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + NB - 1) * kChunk, next, lane);
     const uint8_t* kc = buf;
     const uint8_t* vc = buf + C::CODE_BYTES;
     const uint8_t* ks = buf + 2 * C::CODE_BYTES;
@@ -420,15 +599,12 @@ attn_decode_kernel(Params p) {
       const int sw = swz<D>(lr);
       uint32_t kw[C::KS];
       sfor<C::KS>([&](auto J) { kw[RTQ_CI(J)] = *reinterpret_cast<const uint32_t*>(rowp + 16 * (RTQ_CI(J) ^ sw)); });
-      uint32_t sk[2 * C::SLOT / 2];  // scale words of tokens 16 tau + 4h + 0..3
-      if constexpr (C::SLOT == 8) {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + 8 * (16 * tau + 4 * h));
-        const uint4 b = *reinterpret_cast<const uint4*>(ks + 8 * (16 * tau + 4 * h) + 16);
-        sk[0] = a.x; sk[1] = a.y; sk[2] = a.z; sk[3] = a.w; sk[4] = b.x; sk[5] = b.y; sk[6] = b.z; sk[7] = b.w;
-      } else {
-        const uint4 a = *reinterpret_cast<const uint4*>(ks + 4 * (16 * tau + 4 * h));
-        sk[0] = a.x; sk[1] = a.y; sk[2] = a.z; sk[3] = a.w;
-      }
+      constexpr int SW = C::SLOT / 4;  // scale words per token
+      uint32_t sk[4 * SW];             // tokens 16 tau + 4h + r: words SW r .. SW r + SW - 1
+      sfor<SW>([&](auto Q) {
+        const uint4 a = *reinterpret_cast<const uint4*>(ks + C::SLOT * (16 * tau + 4 * h) + 16 * RTQ_CI(Q));
+        sk[4 * RTQ_CI(Q)] = a.x; sk[4 * RTQ_CI(Q) + 1] = a.y; sk[4 * RTQ_CI(Q) + 2] = a.z; sk[4 * RTQ_CI(Q) + 3] = a.w;
+      });
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
       sfor<C::SPR>([&](auto GI) {
         constexpr int gi = RTQ_CI(GI);
@@ -440,11 +616,7 @@ attn_decode_kernel(Params p) {
         });
         sfor<4>([&](auto R) {
           constexpr int r = RTQ_CI(R);
-          if constexpr (C::SPR == 4) {
-            s[r] = half_fma<gi & 1>(sk[2 * r + (gi >> 1)], part[r], s[r]);
-          } else {
-            s[r] = half_fma<gi>(sk[r], part[r], s[r]);
-          }
+          s[r] = half_fma<gi & 1>(sk[SW * r + (gi >> 1)], part[r], s[r]);
         });
       });
       sfor<4>([&](auto R) {
@@ -487,43 +659,48 @@ attn_decode_kernel(Params p) {
                              (f16x2_t){(_Float16)pr[1][2], (_Float16)pr[1][3]});
 
     // ---- values: V^T operand of tokens (a, b) = pair v of lane group h ----
-    uint32_t ylo[4], yhi[4], s2[4];
+    uint32_t ylo[WH][4], yhi[WH][4], s2[WH][4];
     sfor<4>([&](auto V) {
       constexpr int v = RTQ_CI(V);
       const int ta = 16 * (v >> 1) + 4 * h + 2 * (v & 1), tb = ta + 1;
       const int la = lrow<D>(ta), lb = lrow<D>(tb);
-      const uint32_t xa = *reinterpret_cast<const uint32_t*>(vc + la * C::RB + 16 * ((dw >> 2) ^ swz<D>(la)) + 4 * (dw & 3));
-      const uint32_t xb = *reinterpret_cast<const uint32_t*>(vc + lb * C::RB + 16 * ((dw >> 2) ^ swz<D>(lb)) + 4 * (dw & 3));
-      if constexpr (D == 128) {
-        ylo[v] = __builtin_amdgcn_perm(xb, xa, 0x05040100u);
-        yhi[v] = __builtin_amdgcn_perm(xb, xa, 0x07060302u);
-      } else {
-        ylo[v] = __builtin_amdgcn_perm(xb, xa, vsel);
-        yhi[v] = ylo[v];
-      }
-      const uint16_t sa = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * ta + 2 * vgi);
-      const uint16_t sb2 = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * tb + 2 * vgi);
-      const f16x2_t sp = as_h2((uint32_t)sa | ((uint32_t)sb2 << 16)) * (f16x2_t){(_Float16)kVShift, (_Float16)kVShift};
-      s2[v] = as_u32(sp);
+      sfor<WH>([&](auto HH) {
+        constexpr int hh = RTQ_CI(HH);
+        const int wd = dw + 16 * hh;
+        const uint32_t xa = *reinterpret_cast<const uint32_t*>(vc + la * C::RB + 16 * ((wd >> 2) ^ swz<D>(la)) + 4 * (wd & 3));
+        const uint32_t xb = *reinterpret_cast<const uint32_t*>(vc + lb * C::RB + 16 * ((wd >> 2) ^ swz<D>(lb)) + 4 * (wd & 3));
+        if constexpr (D >= 128) {
+          ylo[hh][v] = __builtin_amdgcn_perm(xb, xa, 0x05040100u);
+          yhi[hh][v] = __builtin_amdgcn_perm(xb, xa, 0x07060302u);
+        } else {
+          ylo[hh][v] = __builtin_amdgcn_perm(xb, xa, vsel);
+          yhi[hh][v] = ylo[hh][v];
+        }
+        const int vgi = (8 * wd) / GR;  // the scale group of those dims
+        const uint16_t sa = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * ta + 2 * vgi);
+        const uint16_t sb2 = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * tb + 2 * vgi);
+        const f16x2_t sp = as_h2((uint32_t)sa | ((uint32_t)sb2 << 16)) * (f16x2_t){(_Float16)kVShift, (_Float16)kVShift};
+        s2[hh][v] = as_u32(sp);
+      });
     });
     sfor<C::NT>([&](auto I) {
       constexpr int i = RTQ_CI(I);
-      constexpr int k = i & 3;
+      constexpr int k = i & 3, hh = i / 8;
       f16x2_t a[4];
       sfor<4>([&](auto V) {
         constexpr int v = RTQ_CI(V);
-        const uint32_t y = (D == 128 && i >= 4) ? yhi[v] : ylo[v];
-        a[v] = code_pair<k>(y) * as_h2(s2[v]);
+        const uint32_t y = (D >= 128 && (i & 4)) ? yhi[hh][v] : ylo[hh][v];
+        a[v] = code_pair<k>(y) * as_h2(s2[hh][v]);
       });
       acc[i] = mfma(pack8(a[0], a[1], a[2], a[3]), pb, acc[i]);
     });
   };
 #pragma unroll 1
-  for (int c = c_begin; c < c_end; c += kBufs) {
+  for (int c = c_begin; c < c_end; c += C::BUFS) {
     chunk(ic<0>{}, c);
     if (c + 1 >= c_end) break;
     chunk(ic<1>{}, c + 1);
-    if constexpr (kBufs > 2) {
+    if constexpr (C::BUFS > 2) {
       if (c + 2 >= c_end) break;
       chunk(ic<2>{}, c + 2);
     }
@@ -547,13 +724,19 @@ attn_decode_kernel(Params p) {
       sfor<4>([&](auto R) {
         constexpr int r = RTQ_CI(R);
         const int mrow = 4 * h + r;  // output row of the O^T tile = dim lane index
-        const int dim = D == 128 ? 8 * mrow + i : 8 * (mrow & 7) + 4 * (mrow >> 3) + i;
+        const int dim = D == 64 ? 8 * (mrow & 7) + 4 * (mrow >> 3) + i : 128 * (i / 8) + 8 * mrow + i % 8;
         dst[dim] = acc[i][r];
       });
     });
   }
   __syncthreads();
   static_assert(kStreams == 1, "the split partials assume one stream per workgroup");
+  // the merged output of query g, dim: the stage row (one lane per query
+  // rotates it back), or at d = 256 the transposed work area
+  auto put_out = [&](int g, int dim, float val) {
+    if constexpr (C::DENSE_ROT) vt_all[dim * kMaxQ + g] = val;
+    else stage_all[g * C::QROW + dim] = val;
+  };
   float* const mine = p.splits > 1 ? p.part + ((int64_t)pair * p.splits + split) * part_floats(G, D) : nullptr;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int g = idx / D, dim = idx % D;
@@ -566,7 +749,7 @@ attn_decode_kernel(Params p) {
       num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
     }
     if (p.splits == 1) {
-      stage_all[g * C::QROW + dim] = num / (den * kVShift);  // den >= 1: the max score has weight 1
+      put_out(g, dim, num / (den * kVShift));  // den >= 1: the max score has weight 1
     } else {
       publish(mine + idx, num);
       if (dim == 0) {
@@ -602,14 +785,34 @@ attn_decode_kernel(Params p) {
         den = __builtin_fmaf(f, collect(ps + G * D + G + g), den);
         num = __builtin_fmaf(f, collect(ps + idx), num);
       }
-      stage_all[g * C::QROW + dim] = num / (den * kVShift);
+      put_out(g, dim, num / (den * kVShift));
     }
     if (threadIdx.x == 0) __hip_atomic_store(p.count + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
 
   // ---- rotate the outputs back: o = D_V R^T o_rot ----
-  if (lead) {
+  if constexpr (C::DENSE_ROT) {
+    const int t = threadIdx.x;
+    float2* tw = reinterpret_cast<float2*>(vt_all + D * kMaxQ);
+    if constexpr (ROT == 0) tw[t] = make_float2(kTwiddle256.c[t], kTwiddle256.s[t]);
+    __syncthreads();
+    const float sv = sign_bit(seed_of_row(p, row_v), (uint32_t)t) ? -1.0f : 1.0f;
+    _Float16* o16 = reinterpret_cast<_Float16*>(p.out);
+    if (G <= 4) {
+      float u[4];
+      dense_inverse<ROT, 4>(vt_all, tw, t, u);
+      sfor<4>([&](auto Gi) {
+        if (RTQ_CI(Gi) < G) o16[(qrow + RTQ_CI(Gi)) * D + t] = (_Float16)(sv * u[RTQ_CI(Gi)]);
+      });
+    } else {
+      float u[kMaxQ];
+      dense_inverse<ROT, kMaxQ>(vt_all, tw, t, u);
+      sfor<kMaxQ>([&](auto Gi) {
+        if (RTQ_CI(Gi) < G) o16[(qrow + RTQ_CI(Gi)) * D + t] = (_Float16)(sv * u[RTQ_CI(Gi)]);
+      });
+    }
+  } else if (lead) {
     uint32_t mvs[D / 2];
     wave_sign_masks<D>(seed_of_row(p, row_v), lane, mvs);
     if (lane < G) {
@@ -651,6 +854,7 @@ KernelFn find_kernel(int d, int g) {
   if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT>);
   RTQ_ATTN_CASE(64, 32) RTQ_ATTN_CASE(64, 64)
   RTQ_ATTN_CASE(128, 32) RTQ_ATTN_CASE(128, 64) RTQ_ATTN_CASE(128, 128)
+  RTQ_ATTN_CASE(256, 32) RTQ_ATTN_CASE(256, 64) RTQ_ATTN_CASE(256, 128)
 #undef RTQ_ATTN_CASE
   return nullptr;
 }

@@ -136,7 +136,7 @@ def test_attention_rejects_bad_arguments_without_launching(name):
     # rows past 2^56
     assert attn_call(name, strides=(1 << 60, 150, 50, 1)) == bad
     # unsupported shapes and head ratios
-    for d, g in [(256, 32), (64, 128), (128, 16), (96, 32)]:
+    for d, g in [(256, 256), (64, 128), (128, 16), (96, 32), (512, 32)]:
         assert attn_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
     assert attn_call(name, qpk=9) == rtq.RTQ_ERR_UNSUPPORTED
 
