@@ -23,7 +23,7 @@ __all__ = [
     "srft_attn_decode", "srht_attn_decode", "attn_workspace_bytes",
     "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
     "srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext", "CODE_BITS",
-    "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED",
+    "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED", "CACHE_SUPPORTED", "EXT_SUPPORTED",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +35,10 @@ RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_HIP = 0, 1, 2, 3
 SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 # (d, group) pairs of the decode-attention kernels; at most 8 query heads per K/V head
 ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+# (d, group) pairs of the cache-layout entry points (*_quant_append, *_dequant_rows) and of the
+# code-width / lambda entry points (*_ext)
+CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
+EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
 ATTN_MAX_Q_PER_KV = 8
 # code widths of the *_ext entry points (d = 64 or 128)
 CODE_BITS = (3, 4, 6, 8)

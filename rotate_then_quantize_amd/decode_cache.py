@@ -31,7 +31,7 @@ class DecodeCache:
         import torch
         if min(layers, streams, capacity, window) < 1:
             raise ValueError("layers, streams, capacity and window must be positive")
-        if (d, group) not in rtq.ATTN_SUPPORTED:
+        if (d, group) not in rtq.CACHE_SUPPORTED:
             raise ValueError(f"(d, group) = ({d}, {group}) is not supported for the decode cache")
         self.layers, self.streams, self.capacity, self.d, self.group = layers, streams, capacity, d, group
         self.seed, self.rot, self.window = seed, rot, window

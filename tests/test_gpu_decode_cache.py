@@ -20,7 +20,7 @@ import rotate_then_quantize_amd as rtq  # noqa: E402
 from rotate_then_quantize_amd.decode_cache import DecodeCache  # noqa: E402
 
 DEV = "cuda"
-SHAPES = sorted(rtq.ATTN_SUPPORTED)
+SHAPES = sorted(rtq.CACHE_SUPPORTED)
 SENTINEL = 0xA5
 
 

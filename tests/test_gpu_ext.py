@@ -19,7 +19,7 @@ torch = pytest.importorskip("torch")
 import rotate_then_quantize_amd as rtq  # noqa: E402
 
 DEV = "cuda"
-SHAPES = sorted(rtq.ATTN_SUPPORTED)
+SHAPES = sorted(rtq.EXT_SUPPORTED)
 
 
 def rows(n, d, seed, outliers=2):
