@@ -42,7 +42,7 @@ ATTN_METRIC = "decode-attention steps/s over the int4 rotated K/V cache (dequant
 _CSRC = os.path.join(ROOT, "rotate_then_quantize_amd", "csrc")
 # sources each kernel family is compiled from (a profile is current while their code is unchanged)
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in (
-    "rtq.hip", "rtq_lane.hpp", "rtq_host.hpp", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp")]
+    "rtq.hip", "rtq_lane.hpp", "rtq_host.hpp", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp", "rtq_pair.hpp")]
 ATTN_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq_attn.hip", "rtq_device.hpp", "rtq_mem.hpp")]
 
 

@@ -190,7 +190,7 @@ rtq_status srht_dequant_inv_ext(const void* codes_u8, const void* scales_f16, vo
  * are not touched.  The strides must map distinct (layer, kv, stream, token)
  * to distinct rows.
  *
- * Supported: d in {64, 128} with the groups of the common conventions, else
+ * Supported: every (d, group) of the common conventions, else
  * RTQ_ERR_UNSUPPORTED.  layers, streams, t0, n_tokens, strides >= 0,
  * layers*2*streams*n_tokens <= 0xFFFFFF00, else RTQ_ERR_INVALID_ARG; an empty
  * block returns RTQ_OK.  The caller guarantees that the cache holds every row

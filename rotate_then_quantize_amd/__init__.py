@@ -37,7 +37,7 @@ SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (2
 ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 # (d, group) pairs of the cache-layout entry points (*_quant_append, *_dequant_rows) and of the
 # code-width / lambda entry points (*_ext)
-CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
+CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
 ATTN_MAX_Q_PER_KV = 8
 # code widths of the *_ext entry points (d = 64 or 128)

@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(PKG_DIR, "librtq.so")
 CSRC = os.path.join(PKG_DIR, "csrc")
 SOURCES = [os.path.join(CSRC, f) for f in ("rtq.hip", "rtq_attn.hip", "rtq_cache.hip", "rtq_ext.hip")]
 HEADERS = [os.path.join(CSRC, f) for f in ("rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp", "rtq_lane.hpp",
-                                           "rtq_host.hpp")] + [os.path.join(ROOT, "include", "rtq.h")]
+                                           "rtq_host.hpp", "rtq_pair.hpp")] + [os.path.join(ROOT, "include", "rtq.h")]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-fvisibility=hidden",

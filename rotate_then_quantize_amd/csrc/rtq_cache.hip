@@ -1,6 +1,6 @@
 // rtq_cache.hip -- the in-place append of new tokens into a strided cache and
 // the row-mapped inverse that refreshes a dequantized fp16 copy of the
-// cache (d = 64 / 128), and their C ABI entry points (include/rtq.h).
+// cache (d = 64 / 128 / 256), and their C ABI entry points (include/rtq.h).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -11,6 +11,7 @@
 #include "rtq_host.hpp"
 #include "rtq_lane.hpp"
 #include "rtq_mem.hpp"
+#include "rtq_pair.hpp"
 
 namespace rtq {
 
@@ -128,6 +129,52 @@ __global__ __launch_bounds__(64) void inv_mapped_kernel(const uint4* __restrict_
   }
 }
 
+// d = 256 (two lanes per vector, rtq_pair.hpp): tile row rl is row row0 + rl
+// of the block, at cache row map_row(row0 + rl) with that row's own seed.
+// The tile counts as uniform when every row's seed is the first row's.
+struct MappedTileRows {
+  uint32_t row0;
+  int rows;
+  bool uniform;
+  uint64_t seed0;  // seed of the tile's first row
+  const RowMap& m;
+  const RowSeeds& rs;
+  static constexpr bool kStreamStores = false;  // scattered rows: let L2 merge the pieces
+  __device__ uint4 uniform_masks(uint32_t k) const { return chunk_sign_masks(seed0, k); }
+  __device__ uint4 row_masks(int rl, uint32_t k) const {
+    return chunk_sign_masks(row_seed(rs.seed, (int64_t)cache_row(rl), rs.rps, rs.period), k);
+  }
+  __device__ size_t cache_row(int rl) const { return (size_t)map_row(m, row0 + (uint32_t)rl); }
+  __device__ uint4* y_chunk(uint4* y, int rl, uint32_t k) const { return y + cache_row(rl) * 32 + k; }
+};
+
+__device__ __forceinline__ MappedTileRows mapped_tile_rows(uint32_t n, const RowMap& m, const RowSeeds& rs) {
+  const uint32_t row0 = blockIdx.x * 32u;
+  const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
+  const int lane = threadIdx.x & 31;
+  const uint64_t s = row_seed(rs.seed, map_row(m, row0 + (uint32_t)(lane < rows ? lane : rows - 1)), rs.rps, rs.period);
+  const uint64_t s0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(s >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)s);
+  const bool uniform = __ballot(s != s0) == 0;
+  return MappedTileRows{row0, rows, uniform, s0, m, rs};
+}
+
+template <int G, int ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_mapped_pair_kernel(
+    const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, RowMap m,
+    RowSeeds rs) {
+  __shared__ uint4 lds[32 * 33];
+  fwd_pair_tile<G, ROT>(x, codes, scales, mapped_tile_rows(n, m, rs), lds, threadIdx.x);
+}
+
+template <int G, int ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void inv_mapped_pair_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y, uint32_t n, RowMap m,
+    RowSeeds rs) {
+  __shared__ uint4 lds[32 * 17];
+  inv_pair_tile<G, ROT>(codes, scales, y, mapped_tile_rows(n, m, rs), lds, threadIdx.x);
+}
+
 template <int ROT>
 KernelFn find_mapped(bool fwd, int d, int g) {
 #define RTQ_MAPPED_CASE(DD, GG)                                                        \
@@ -137,6 +184,12 @@ KernelFn find_mapped(bool fwd, int d, int g) {
   RTQ_MAPPED_CASE(64, 32) RTQ_MAPPED_CASE(64, 64)
   RTQ_MAPPED_CASE(128, 32) RTQ_MAPPED_CASE(128, 64) RTQ_MAPPED_CASE(128, 128)
 #undef RTQ_MAPPED_CASE
+#define RTQ_MAPPED_PAIR_CASE(GG)                                                       \
+  if (d == 256 && g == GG)                                                             \
+    return fwd ? reinterpret_cast<KernelFn>(&fwd_mapped_pair_kernel<GG, ROT>)          \
+               : reinterpret_cast<KernelFn>(&inv_mapped_pair_kernel<GG, ROT>);
+  RTQ_MAPPED_PAIR_CASE(32) RTQ_MAPPED_PAIR_CASE(64) RTQ_MAPPED_PAIR_CASE(128)
+#undef RTQ_MAPPED_PAIR_CASE
   return nullptr;
 }
 
@@ -194,7 +247,8 @@ rtq_status run_mapped(bool fwd, int rot, const void* in0, const void* in1, void*
   rs.rps = rps;
   rs.period = period;
   uint32_t n32 = (uint32_t)n;
-  const int64_t tiles = (n + 63) / 64;
+  const int vpt = d == 256 ? 32 : 64;  // rows per tile
+  const int64_t tiles = (n + vpt - 1) / vpt;
   if (fwd) {
     const void* x = in0;
     void* codes = out0;

@@ -1,0 +1,321 @@
+// rtq_pair.hpp -- d = 256 tiles of the fused rotate-then-quantize kernels
+// (MI355X, gfx950): two lanes per vector (lane v and lane v + 32), 32
+// vectors per tile.  The tiles are written once and used by the plain
+// entry points (rows of a contiguous [n, 256] tensor) and by the cache-layout
+// entry points (rows placed by strides), through a row policy:
+//
+//   struct Rows {
+//     uint32_t row0;  // first row of the tile in the input numbering
+//     int rows;       // rows in the tile (1 .. 32)
+//     bool uniform;   // every row of the tile has the same sign seed
+//     static constexpr bool kStreamStores;  // non-temporal stores (streaming tiles)
+//     uint4 uniform_masks(uint32_t k) const;      // sign masks of chunk k, the tile's seed
+//     uint4 row_masks(int rl, uint32_t k) const;  // sign masks of chunk k, row rl's seed
+//     size_t cache_row(int rl) const;             // codes / scales row of tile row rl
+//     uint4* y_chunk(uint4* y, int rl, uint32_t k) const;  // 16-byte chunk k of row rl of y
+//   };
+//
+//   SRFT: lane p holds the samples u_{2m+p} (m = 0..127), computes their real
+//     DFT of length 128 (E for p = 0, O for p = 1), both lanes exchange E and O
+//     (ds_bpermute), and combine X_a = E_a + w^a O_a (lane 0, bins 0..64) and
+//     X_{128-a} = conj(E_a - w^a O_a) (lane 1, bins 64..128).  Lane 1 keeps its
+//     coordinates mirrored (local index 127 - i) with Re/Im swapped, which
+//     makes its register layout identical to lane 0's; the mirror is undone
+//     on the packed codes and scales.
+//   SRHT: lane p holds the contiguous half p; H_256 = H_2 (x) H_128, so each
+//     lane applies H_128 and the halves combine as F0 + F1 / F0 - F1.
+//
+// Method: "Quantization Speed Is Often a Kernel Problem", "First, the 17%"
+// and "Fusing four steps into two kernels is not enough" (rotate + quantize
+// in one kernel, dequantize + inverse-rotate in the other).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "rtq_device.hpp"
+#include "rtq_lane.hpp"
+#include "rtq_mem.hpp"
+
+namespace rtq {
+
+// Non-temporal store for streaming tiles, ordinary (L2-merged) store for rows
+// scattered by a cache layout.
+template <bool NT, class T>
+__device__ __forceinline__ void put_store(T* p, T v) {
+  if constexpr (NT) stream_store(p, v);
+  else *p = v;
+}
+
+// Forward tile: rows R.row0 .. R.row0 + R.rows - 1 of x (contiguous, 32
+// 16-byte chunks per row) into the codes / scales rows R.cache_row(.).  lds
+// holds 32 x 33 uint4.
+template <int G, int ROT, class Rows>
+__device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                              uint8_t* __restrict__ scales, const Rows& R, uint4* lds, int lane) {
+  constexpr int D = 256, CPR = 32, LROW = CPR + 1;
+  const int p = lane >> 5, v = lane & 31;
+  const uint32_t kpos = lane & 31;
+  const float sigma = p ? -1.0f : 1.0f;
+  {
+    const uint32_t row0 = R.row0;
+    const int rows = R.rows;
+    const bool uniform = R.uniform;
+    uint4 cm = make_uint4(0, 0, 0, 0);
+    if (uniform) cm = R.uniform_masks(kpos);
+    auto put = [&](int rl, uint4 q) {
+      if constexpr (ROT == kSRFT) {
+        // de-interleave: evens to the first half of the LDS row, odds to the second
+        uint2* row = reinterpret_cast<uint2*>(&lds[rl * LROW]);
+        row[kpos] = make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x05040100u), __builtin_amdgcn_perm(q.w, q.z, 0x05040100u));
+        row[32 + kpos] = make_uint2(__builtin_amdgcn_perm(q.y, q.x, 0x07060302u), __builtin_amdgcn_perm(q.w, q.z, 0x07060302u));
+      } else {
+        lds[rl * LROW + kpos] = q;
+      }
+    };
+    if (uniform) {
+      const uint4* xt = x + (size_t)row0 * CPR;
+      uint4 in[16];
+      sfor<16>([&](auto J) {
+        const int rl = 2 * RTQ_CI(J) + p;
+        in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
+      });
+      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cm)); });
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < 16; ++j) {
+        const int rl = 2 * j + p;
+        const uint4 q = rl < rows ? stream_load(x + ((size_t)(row0 + rl) * CPR + kpos)) : make_uint4(0, 0, 0, 0);
+        put(rl, xor4(q, R.row_masks(rl, kpos)));
+      }
+    }
+    lds_sync();
+    uint32_t h[64];
+    sfor<16>([&](auto C) {
+      const uint4 q = lds[v * LROW + 16 * p + RTQ_CI(C)];
+      h[4 * RTQ_CI(C) + 0] = q.x;
+      h[4 * RTQ_CI(C) + 1] = q.y;
+      h[4 * RTQ_CI(C) + 2] = q.z;
+      h[4 * RTQ_CI(C) + 3] = q.w;
+    });
+    wait_lds_reads();
+    lds_sync();
+    float L[128];
+    float zs;
+    if constexpr (ROT == kSRFT) {
+      float fr[65], fi[65];
+      rdft<128, 1, 0, 64>(h, fr, fi);  // unnormalized; sqrt(2/256) is applied by the quantizer
+      // Partner exchange by ds_bpermute.  Every 4 bins the next addresses are
+      // tied to the last result, so each group of shuffles issues only once
+      // the previous group has been consumed; this keeps the exchange from
+      // holding all 260 shuffled values at once (register pressure).
+      int addr_e = v * 4, addr_o = (v + 32) * 4;
+      auto shf = [](float x, int addr) { return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x))); };
+      // slot 0: E_0 + sigma * O_0 (real)
+      {
+        const float e0 = shf(fr[0], addr_e), o0 = shf(fr[0], addr_o);
+        constexpr float r2 = 0.70710678118654752440f;  // real end bins: 1/16 = sqrt(2/256) / sqrt(2)
+        L[0] = __builtin_fmaf(sigma, o0, e0) * r2;
+      }
+      sfor<63>([&](auto A) {
+        constexpr int a = RTQ_CI(A) + 1;
+        const float er = shf(fr[a], addr_e), ei = shf(fi[a], addr_e);
+        const float orr = shf(fr[a], addr_o), oi = shf(fi[a], addr_o);
+        constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);  // w^a = c - i s
+        const float tr = __builtin_fmaf(c, orr, s * oi);
+        const float ti = __builtin_fmaf(c, oi, -s * orr);
+        const float rr = __builtin_fmaf(sigma, tr, er);
+        const float ri = __builtin_fmaf(sigma, ei, ti);
+        L[2 * a - 1] = p ? ri : rr;
+        L[2 * a] = p ? rr : ri;
+        if constexpr (a % 4 == 0) asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(L[2 * a]));
+      });
+      {  // slot 64: X_64 = E_64 - i O_64; lane 0 keeps Re, lane 1 keeps Im
+        const float e64 = shf(fr[64], addr_e), o64 = shf(fr[64], addr_o);
+        L[127] = p ? -o64 : e64;
+      }
+      zs = SrftScale<256>::value;
+    } else {
+      float f[128];
+      fwht_from_f16<128>(h, f);
+      sfor<128>([&](auto K) {
+        const float r = __shfl_xor(f[RTQ_CI(K)], 32);
+        L[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
+      });
+      zs = 1.0f / 16.0f;
+    }
+    uint32_t cw[16], sb[128 / G];
+    quantize_pack<128, G>(L, zs, cw, sb);
+    if constexpr (ROT == kSRFT) {
+      // lane 1: codes and scales are in mirrored order -> reverse them
+      uint32_t rev[16];
+      sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
+      sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
+      uint32_t sr[128 / G];
+      sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
+      sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
+    }
+    if (v < rows) {
+      const size_t row = R.cache_row(v);
+      constexpr bool nt = Rows::kStreamStores;
+      sfor<4>([&](auto C) {
+        put_store<nt>(codes + (row * 8 + 4 * p + RTQ_CI(C)),
+                     make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]));
+      });
+      // this lane's half of the row's scales: 128/G values
+      if constexpr (128 / G == 1) {
+        put_store<nt>(reinterpret_cast<uint16_t*>(scales) + (row * 2 + p), (uint16_t)sb[0]);
+      } else if constexpr (128 / G == 2) {
+        put_store<nt>(reinterpret_cast<uint32_t*>(scales) + (row * 2 + p), sb[0] | (sb[1] << 16));
+      } else {
+        put_store<nt>(reinterpret_cast<uint2*>(scales) + (row * 2 + p), make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)));
+      }
+    }
+  }
+}
+
+// Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
+// that R.y_chunk addresses.  lds holds 32 x 17 uint4.
+template <int G, int ROT, class Rows>
+__device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                              uint4* __restrict__ y, const Rows& R, uint4* lds, int lane) {
+  constexpr int CPR = 32;
+  const int p = lane >> 5, v = lane & 31;
+  const uint32_t kpos = lane & 31;
+  const float sigma = p ? -1.0f : 1.0f;
+  {
+    const int rows = R.rows;
+    const bool uniform = R.uniform;
+    uint32_t cw[16], sb[128 / G];
+    {
+      const size_t row = R.cache_row(v < rows ? v : 0);
+      sfor<4>([&](auto C) {
+        const uint4 q = stream_load(codes + (row * 8 + 4 * p + RTQ_CI(C)));
+        cw[4 * RTQ_CI(C) + 0] = q.x;
+        cw[4 * RTQ_CI(C) + 1] = q.y;
+        cw[4 * RTQ_CI(C) + 2] = q.z;
+        cw[4 * RTQ_CI(C) + 3] = q.w;
+      });
+      if constexpr (128 / G == 1) {
+        sb[0] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (row * 2 + p));
+      } else if constexpr (128 / G == 2) {
+        const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(scales) + (row * 2 + p));
+        sb[0] = w & 0xffffu;
+        sb[1] = w >> 16;
+      } else {
+        const uint2 w = stream_load(reinterpret_cast<const uint2*>(scales) + (row * 2 + p));
+        sb[0] = w.x & 0xffffu;
+        sb[1] = w.x >> 16;
+        sb[2] = w.y & 0xffffu;
+        sb[3] = w.y >> 16;
+      }
+    }
+    float u[128];
+    if constexpr (ROT == kSRFT) {
+      // lane 1 holds its half in mirrored order: undo on the packed form
+      uint32_t rev[16];
+      sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
+      sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
+      uint32_t sr[128 / G];
+      sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
+      sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
+      float L[128];
+      dequant_unpack<128, G>(cw, sb, 0.5f, L);  // the halving of E and t folded in
+      // P = lane v's slots (X_a), Q = lane v+32's slots (X_{128-a}, Re/Im swapped)
+      const int src0 = v, src1 = v + 32;
+      float yv[128];
+      {
+        const float p0 = __shfl(L[0], src0), q0 = __shfl(L[0], src1);
+        yv[0] = __builtin_fmaf(sigma, q0, p0);
+      }
+      sfor<63>([&](auto A) {
+        constexpr int a = RTQ_CI(A) + 1;
+        const float pr = __shfl(L[2 * a - 1], src0), pi = __shfl(L[2 * a], src0);
+        const float qr = __shfl(L[2 * a], src1), qi = __shfl(L[2 * a - 1], src1);
+        const float fr = __builtin_fmaf(sigma, qr, pr);  // E (lane 0) or t (lane 1)
+        const float fi = __builtin_fmaf(-sigma, qi, pi);
+        // lane 1: O_a = w^-a t_a with w^-a = c + i s; lane 0 multiplies by 1
+        constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);
+        const float cc = p ? c : 1.0f, ss = p ? s : 0.0f;
+        yv[2 * a - 1] = __builtin_fmaf(cc, fr, -ss * fi);
+        yv[2 * a] = __builtin_fmaf(cc, fi, ss * fr);
+      });
+      {
+        const float p64 = __shfl(L[127], src0), q64 = __shfl(L[127], src1);
+        constexpr float sq2 = 1.41421356237309504880f;  // 2 / sqrt(2): L is halved
+        yv[127] = (p ? -q64 : p64) * sq2;
+      }
+      srft_inv<128, Sqrt2>(yv, u);
+    } else {
+      float f[128];
+      dequant_unpack<128, G>(cw, sb, 1.0f / 16.0f, f);
+      fwht_f32<128>(f);
+      sfor<128>([&](auto K) {
+        const float r = __shfl_xor(f[RTQ_CI(K)], 32);
+        u[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
+      });
+    }
+    // fp16 samples out through LDS in two passes of 16 output chunks per row
+    // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
+    // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
+    // re-interleaves them on the way out.  SRHT: lane p holds output chunks
+    // 16 p .. 16 p + 15, written in pass p.
+    constexpr int LR2 = 17;
+    const int kk = lane & 15, rsub = lane >> 4;
+    sfor<2>([&](auto PH) {
+      constexpr int ph = RTQ_CI(PH);
+      if constexpr (ph > 0) {
+        wait_lds_reads();
+        lds_sync();
+      }
+      if constexpr (ROT == kSRFT) {
+        sfor<8>([&](auto C) {
+          constexpr int c = 8 * ph + RTQ_CI(C);
+          lds[v * LR2 + 8 * p + RTQ_CI(C)] =
+              make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
+                         pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+        });
+      } else {
+        if (p == ph) {
+          sfor<16>([&](auto C) {
+            constexpr int c = RTQ_CI(C);
+            lds[v * LR2 + c] =
+                make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
+                           pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+          });
+        }
+      }
+      lds_sync();
+      const uint32_t k = 16u * ph + (uint32_t)kk;  // output chunk this lane stores
+      auto get = [&](int rl) -> uint4 {
+        if constexpr (ROT == kSRFT) {
+          const uint2* row = reinterpret_cast<const uint2*>(&lds[rl * LR2]);
+          const uint2 e = row[kk], o = row[16 + kk];
+          return make_uint4(__builtin_amdgcn_perm(o.x, e.x, 0x05040100u), __builtin_amdgcn_perm(o.x, e.x, 0x07060302u),
+                            __builtin_amdgcn_perm(o.y, e.y, 0x05040100u), __builtin_amdgcn_perm(o.y, e.y, 0x07060302u));
+        } else {
+          return lds[rl * LR2 + kk];
+        }
+      };
+      if (uniform) {
+        const uint4 m = R.uniform_masks(k);
+        sfor<8>([&](auto J) {
+          const int rl = rsub + 4 * RTQ_CI(J);
+          if (rl < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
+        });
+      } else {
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+          const int rl = rsub + 4 * j;
+          if (rl < rows)
+            put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), R.row_masks(rl, k)));
+        }
+      }
+    });
+    wait_lds_reads();
+    lds_sync();
+  }
+}
+
+}  // namespace rtq

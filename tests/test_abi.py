@@ -217,7 +217,7 @@ def test_mapped_rejects_bad_arguments_without_launching(name):
                {"strides": (300, 150, -50, 1)}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
                {"c": C + 2}, {"strides": (1 << 60, 150, 50, 1)}, {"layers": 1 << 20, "streams": 1 << 10, "n": 1 << 10}):
         assert mapped_call(name, **kw) == bad, kw
-    for d, g in [(256, 32), (96, 32), (64, 128), (128, 16)]:
+    for d, g in [(256, 256), (96, 32), (64, 128), (128, 16)]:
         assert mapped_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
 
 

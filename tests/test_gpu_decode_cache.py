@@ -63,16 +63,33 @@ def test_append_layer_major(rot, d, g):
     run_append(rot, d, g, L, S, C, 7, 9, lm(S, C), 21, 2 * S * C, L)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("t0,n", [(0, 1), (2, 3), (10, 16), (0, 70)])
-def test_append_time_major(t0, n):
+def test_append_time_major(t0, n, d):
     L, S, C = 3, 4, 80
-    run_append("srft", 128, 32, L, S, C, t0, n, tm(L, S), 0x5EED * 3, 2 * S, L)
+    run_append("srft", d, 32, L, S, C, t0, n, tm(L, S), 0x5EED * 3, 2 * S, L)
 
 
-def test_append_seed_per_token_row():
+@pytest.mark.parametrize("rot,d", [("srft", 64), ("srft", 256), ("srht", 256)])
+def test_append_seed_per_token_row(rot, d):
     """A seed rule that changes inside a tile takes the per-lane sign path."""
     L, S, C = 1, 2, 50
-    run_append("srft", 64, 32, L, S, C, 3, 40, lm(S, C), 5, 7, 0)
+    run_append(rot, d, 32, L, S, C, 3, 40, lm(S, C), 5, 7, 0)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_dequant_rows_seed_per_token_row(rot):
+    """The row-mapped inverse with seeds that change inside a tile (d = 256)."""
+    L, S, C, d, g = 1, 2, 50, 256, 32
+    ch, sh, rows = run_append(rot, d, g, L, S, C, 3, 40, lm(S, C), 5, 7, 0)
+    y = torch.zeros((L * 2 * S * C, d), dtype=torch.float16, device=DEV)
+    rtq.dequant_rows(rot, torch.from_numpy(ch).to(DEV), torch.from_numpy(sh).to(DEV), y, L, S, 3, 40, lm(S, C), g, 5,
+                     7, 0)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    check_inverse(ch[rows], sh[rows], yh[rows], d, g, 5, 7, 0, rot, rows=rows)
+    others = np.setdiff1d(np.arange(L * 2 * S * C), rows)
+    assert not yh[others].any(), "rows outside the block were written"
 
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
@@ -104,7 +121,7 @@ def test_empty_block_is_a_no_op():
     assert int(codes.sum()) == 0
 
 
-@pytest.mark.parametrize("rot,d,g", [("srft", 128, 32), ("srht", 64, 64)])
+@pytest.mark.parametrize("rot,d,g", [("srft", 128, 32), ("srht", 64, 64), ("srft", 256, 32), ("srht", 256, 64)])
 def test_decode_cache_window_cycle(rot, d, g):
     """Prefill 20 tokens, append 37 one at a time with a 16-token window:
     the quantized prefix, its dequantized copy and the window match the
