@@ -150,9 +150,8 @@ rtq_status srht_dequant_inv(const void* codes_u8, const void* scales_f16, void* 
  *                 Entries must be finite and nonzero.
  *   x_f16, y_f16, scales_f16, n, d, group, seed rule, stream: as for
  *                 srft_quant_fwd / srft_dequant_inv.
- * Supported: d in {64, 128} with the groups of the common conventions; other
- * bits or d = 256 return RTQ_ERR_UNSUPPORTED.  Errors otherwise as in the
- * common conventions.
+ * Supported: every (d, group) of the common conventions; other bits return
+ * RTQ_ERR_UNSUPPORTED.  Errors otherwise as in the common conventions.
  */
 rtq_status srft_quant_fwd_ext(const void* x_f16, void* codes_u8, void* scales_f16, int64_t n, int32_t d,
                               int32_t group, int32_t bits, const void* lambda_f16, uint64_t seed,

@@ -38,9 +38,9 @@ ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32
 # (d, group) pairs of the cache-layout entry points (*_quant_append, *_dequant_rows) and of the
 # code-width / lambda entry points (*_ext)
 CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
-EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128)}
+EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 ATTN_MAX_Q_PER_KV = 8
-# code widths of the *_ext entry points (d = 64 or 128)
+# code widths of the *_ext entry points
 CODE_BITS = (3, 4, 6, 8)
 
 

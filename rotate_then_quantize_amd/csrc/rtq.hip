@@ -203,32 +203,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 // rows of a contiguous [n, 256] tensor.
 // ---------------------------------------------------------------------------
 
-// Tile rows row0 .. row0 + rows - 1 of the tensor, under the call's seed rule.
-struct TileRows {
-  uint32_t row0;
-  int rows;
-  bool uniform;
-  uint32_t b0;  // seed block of row0
-  const SeedRule& sr;
-  const SignTable& tb;
-  static constexpr bool kStreamStores = true;
-  __device__ uint4 uniform_masks(uint32_t k) const { return chunk_masks(tb, seed_offset(b0, sr), sr.seed, k); }
-  __device__ uint4 row_masks(int rl, uint32_t k) const {
-    return chunk_sign_masks(seed_of_block(seed_block(row0 + (uint32_t)rl, sr), sr), k);
-  }
-  __device__ size_t cache_row(int rl) const { return (size_t)row0 + (uint32_t)rl; }
-  __device__ uint4* y_chunk(uint4* y, int rl, uint32_t k) const {
-    return y + (size_t)row0 * 32 + ((uint32_t)(rl * 32) + k);
-  }
-};
-
-__device__ __forceinline__ TileRows tile_rows(uint32_t n, const SeedRule& sr, const SignTable& tb) {
-  const uint32_t row0 = blockIdx.x * 32u;
-  const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
-  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
-  return TileRows{row0, rows, b0 == b1, b0, sr, tb};
-}
-
 template <int G, int ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,

@@ -1,6 +1,6 @@
 // rtq_ext.hip -- forward and inverse with 3-, 4-, 6- or 8-bit codes and an
-// optional per-channel lambda (d = 64 / 128), and their C ABI entry points
-// (include/rtq.h).
+// optional per-channel lambda (d = 64 / 128 / 256), and their C ABI entry
+// points (include/rtq.h).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -11,6 +11,7 @@
 #include "rtq_host.hpp"
 #include "rtq_lane.hpp"
 #include "rtq_mem.hpp"
+#include "rtq_pair.hpp"
 
 namespace rtq {
 
@@ -162,6 +163,24 @@ __global__ __launch_bounds__(64) void inv_ext_kernel(const uint32_t* __restrict_
   });
 }
 
+// d = 256: the two-lanes-per-vector tiles of rtq_pair.hpp with B-bit codes
+// and the lambda, over a contiguous [n, 256] tensor.
+template <int G, int ROT, int B>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_ext_pair_kernel(
+    const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales,
+    const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
+  __shared__ uint4 lds[32 * 33];
+  fwd_pair_tile<G, ROT, TileRows, B>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
+}
+
+template <int G, int ROT, int B>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void inv_ext_pair_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y,
+    const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
+  __shared__ uint4 lds[32 * 17];
+  inv_pair_tile<G, ROT, TileRows, B>(codes, scales, y, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
+}
+
 template <int ROT, int B>
 KernelFn find_ext_bits(bool fwd, int d, int g) {
 #define RTQ_EXT_CASE(DD, GG)                                                           \
@@ -171,6 +190,12 @@ KernelFn find_ext_bits(bool fwd, int d, int g) {
   RTQ_EXT_CASE(64, 32) RTQ_EXT_CASE(64, 64)
   RTQ_EXT_CASE(128, 32) RTQ_EXT_CASE(128, 64) RTQ_EXT_CASE(128, 128)
 #undef RTQ_EXT_CASE
+#define RTQ_EXT_PAIR_CASE(GG)                                                          \
+  if (d == 256 && g == GG)                                                             \
+    return fwd ? reinterpret_cast<KernelFn>(&fwd_ext_pair_kernel<GG, ROT, B>)          \
+               : reinterpret_cast<KernelFn>(&inv_ext_pair_kernel<GG, ROT, B>);
+  RTQ_EXT_PAIR_CASE(32) RTQ_EXT_PAIR_CASE(64) RTQ_EXT_PAIR_CASE(128)
+#undef RTQ_EXT_PAIR_CASE
   return nullptr;
 }
 
@@ -216,18 +241,21 @@ rtq_status run_ext(bool fwd, int rot, const void* in0, const void* in1, void* ou
   uint32_t n32 = (uint32_t)n;
   SeedRule sr = make_seed_rule(seed, rps, period, n);
   const uint32_t* l = static_cast<const uint32_t*>(lam);
-  const int64_t tiles = (n + 63) / 64;
+  const int vpt = d == 256 ? 32 : 64;  // rows per tile
+  const int64_t tiles = (n + vpt - 1) / vpt;
+  SignTable tb;  // the d = 256 kernels take the sign table as a last argument
+  if (d == 256) fill_sign_table(tb, sr, n, d);
   if (fwd) {
     const void* x = in0;
     void* codes = out0;
     void* scales = out1;
-    void* kargs[] = {&x, &codes, &scales, &l, &n32, &sr};
+    void* kargs[] = {&x, &codes, &scales, &l, &n32, &sr, &tb};
     return launch(fn, tiles, kargs, stream);
   }
   const void* codes = in0;
   const void* scales = in1;
   void* y = out0;
-  void* kargs[] = {&codes, &scales, &y, &l, &n32, &sr};
+  void* kargs[] = {&codes, &scales, &y, &l, &n32, &sr, &tb};
   return launch(fn, tiles, kargs, stream);
 }
 

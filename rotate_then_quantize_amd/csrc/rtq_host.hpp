@@ -58,4 +58,8 @@ inline SeedRule make_seed_rule(uint64_t seed, int64_t rps, int32_t period, int64
   return s;
 }
 
+// Sign words of the first seeds of a call for the kernels' sign table
+// (defined with the int4 kernels in rtq.hip).
+void fill_sign_table(SignTable& tb, const SeedRule& sr, int64_t n, int d);
+
 }  // namespace rtq

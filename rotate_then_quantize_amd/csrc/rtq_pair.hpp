@@ -35,10 +35,59 @@
 #include <stdint.h>
 
 #include "rtq_device.hpp"
+#include "rtq_div.hpp"
 #include "rtq_lane.hpp"
 #include "rtq_mem.hpp"
 
 namespace rtq {
+
+// The unnormalized real-DFT bins (scale 1 on every bin), for rfft_bins.
+struct UnitBins {
+  static constexpr double s0 = 1.0, sm = 1.0, si = 1.0;
+};
+
+// u = lambda (.) (the lane's 128 samples), exact in fp32.  SRFT: lane p holds
+// the samples 2m + p, h[k] = (sample 4k + p, sample 4k + 2 + p), whose
+// weights are half p of lambda words 2k and 2k + 1.  SRHT: lane p holds
+// samples 128 p + m, h[k] = (128 p + 2k, 128 p + 2k + 1) = lambda word 64 p + k.
+template <int ROT>
+__device__ __forceinline__ void lambda_half(const uint32_t (&h)[64], const uint32_t* __restrict__ lam, int p,
+                                            float (&u)[128]) {
+  if constexpr (ROT == kSRFT) {
+    const uint32_t sh = 16u * (uint32_t)p;
+    sfor<64>([&](auto K) {
+      constexpr int k = RTQ_CI(K);
+      u[2 * k] = lo_f(h[k]) * lo_f(lam[2 * k] >> sh);
+      u[2 * k + 1] = hi_f(h[k]) * lo_f(lam[2 * k + 1] >> sh);
+    });
+  } else {
+    const uint32_t* lp = lam + 64 * p;
+    sfor<64>([&](auto K) {
+      constexpr int k = RTQ_CI(K);
+      const uint32_t l = lp[k];
+      u[2 * k] = lo_f(h[k]) * lo_f(l);
+      u[2 * k + 1] = hi_f(h[k]) * hi_f(l);
+    });
+  }
+}
+
+// u /= lambda for the lane's 128 output samples (same sample sets as above;
+// u[m] is sample 2m + p for SRFT, 128 p + m for SRHT).
+template <int ROT>
+__device__ __forceinline__ void unweight_half(float (&u)[128], const uint32_t* __restrict__ lam, int p) {
+  if constexpr (ROT == kSRFT) {
+    const uint32_t sh = 16u * (uint32_t)p;
+    sfor<128>([&](auto M) { u[RTQ_CI(M)] *= __builtin_amdgcn_rcpf(lo_f(lam[RTQ_CI(M)] >> sh)); });
+  } else {
+    const uint32_t* lp = lam + 64 * p;
+    sfor<64>([&](auto K) {
+      constexpr int k = RTQ_CI(K);
+      const uint32_t l = lp[k];
+      u[2 * k] *= __builtin_amdgcn_rcpf(lo_f(l));
+      u[2 * k + 1] *= __builtin_amdgcn_rcpf(hi_f(l));
+    });
+  }
+}
 
 // Non-temporal store for streaming tiles, ordinary (L2-merged) store for rows
 // scattered by a cache layout.
@@ -49,11 +98,13 @@ __device__ __forceinline__ void put_store(T* p, T v) {
 }
 
 // Forward tile: rows R.row0 .. R.row0 + R.rows - 1 of x (contiguous, 32
-// 16-byte chunks per row) into the codes / scales rows R.cache_row(.).  lds
-// holds 32 x 33 uint4.
-template <int G, int ROT, class Rows>
+// 16-byte chunks per row) into the codes / scales rows R.cache_row(.), with
+// B-bit codes (one little-endian bit stream per row, 32 B bytes) and an
+// optional per-channel lambda.  lds holds 32 x 33 uint4.
+template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4* __restrict__ codes,
-                                              uint8_t* __restrict__ scales, const Rows& R, uint4* lds, int lane) {
+                                              uint8_t* __restrict__ scales, const Rows& R, uint4* lds, int lane,
+                                              const uint32_t* __restrict__ lam = nullptr) {
   constexpr int D = 256, CPR = 32, LROW = CPR + 1;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
@@ -104,8 +155,14 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
     float L[128];
     float zs;
     if constexpr (ROT == kSRFT) {
-      float fr[65], fi[65];
-      rdft<128, 1, 0, 64>(h, fr, fi);  // unnormalized; sqrt(2/256) is applied by the quantizer
+      float fr[65], fi[65];  // unnormalized; sqrt(2/256) is applied by the quantizer
+      if (lam != nullptr) {
+        float uw[128];
+        lambda_half<kSRFT>(h, lam, p, uw);
+        rfft_bins<128, UnitBins>(uw, fr, fi);
+      } else {
+        rdft<128, 1, 0, 64>(h, fr, fi);
+      }
       // Partner exchange by ds_bpermute.  Every 4 bins the next addresses are
       // tied to the last result, so each group of shuffles issues only once
       // the previous group has been consumed; this keeps the exchange from
@@ -138,14 +195,31 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       zs = SrftScale<256>::value;
     } else {
       float f[128];
-      fwht_from_f16<128>(h, f);
+      if (lam != nullptr) {
+        lambda_half<kSRHT>(h, lam, p, f);
+        fwht_f32<128>(f);
+      } else {
+        fwht_from_f16<128>(h, f);
+      }
       sfor<128>([&](auto K) {
         const float r = __shfl_xor(f[RTQ_CI(K)], 32);
         L[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
       });
       zs = 1.0f / 16.0f;
     }
-    uint32_t cw[16], sb[128 / G];
+    constexpr int CWW = 4 * B;  // code words of the lane's half row
+    uint32_t cw[CWW], sb[128 / G];
+    if constexpr (B != 4) {
+      // SRFT lane 1 holds its half mirrored: put it in natural order first
+      // (a b-bit stream has no cheap field reversal), then quantize
+      if constexpr (ROT == kSRFT) {
+        float Ln[128];
+        sfor<128>([&](auto I) { Ln[RTQ_CI(I)] = p ? L[127 - RTQ_CI(I)] : L[RTQ_CI(I)]; });
+        quantize_pack_bits<128, G, B>(Ln, zs, cw, sb);
+      } else {
+        quantize_pack_bits<128, G, B>(L, zs, cw, sb);
+      }
+    } else {
     quantize_pack<128, G>(L, zs, cw, sb);
     if constexpr (ROT == kSRFT) {
       // lane 1: codes and scales are in mirrored order -> reverse them
@@ -156,11 +230,12 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
       sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
     }
+    }
     if (v < rows) {
       const size_t row = R.cache_row(v);
       constexpr bool nt = Rows::kStreamStores;
-      sfor<4>([&](auto C) {
-        put_store<nt>(codes + (row * 8 + 4 * p + RTQ_CI(C)),
+      sfor<B>([&](auto C) {
+        put_store<nt>(codes + (row * (2 * B) + B * p + RTQ_CI(C)),
                      make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]));
       });
       // this lane's half of the row's scales: 128/G values
@@ -176,10 +251,12 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
 }
 
 // Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
-// that R.y_chunk addresses.  lds holds 32 x 17 uint4.
-template <int G, int ROT, class Rows>
+// that R.y_chunk addresses, for B-bit codes and an optional lambda.  lds
+// holds 32 x 17 uint4.
+template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
-                                              uint4* __restrict__ y, const Rows& R, uint4* lds, int lane) {
+                                              uint4* __restrict__ y, const Rows& R, uint4* lds, int lane,
+                                              const uint32_t* __restrict__ lam = nullptr) {
   constexpr int CPR = 32;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
@@ -187,11 +264,11 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
   {
     const int rows = R.rows;
     const bool uniform = R.uniform;
-    uint32_t cw[16], sb[128 / G];
+    uint32_t cw[4 * B], sb[128 / G];
     {
       const size_t row = R.cache_row(v < rows ? v : 0);
-      sfor<4>([&](auto C) {
-        const uint4 q = stream_load(codes + (row * 8 + 4 * p + RTQ_CI(C)));
+      sfor<B>([&](auto C) {
+        const uint4 q = stream_load(codes + (row * (2 * B) + B * p + RTQ_CI(C)));
         cw[4 * RTQ_CI(C) + 0] = q.x;
         cw[4 * RTQ_CI(C) + 1] = q.y;
         cw[4 * RTQ_CI(C) + 2] = q.z;
@@ -213,15 +290,22 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
     }
     float u[128];
     if constexpr (ROT == kSRFT) {
-      // lane 1 holds its half in mirrored order: undo on the packed form
-      uint32_t rev[16];
-      sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
-      sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
-      uint32_t sr[128 / G];
-      sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
-      sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
+      // lane 1 keeps its half in mirrored order (the halving of E and t is
+      // folded into the dequantization)
       float L[128];
-      dequant_unpack<128, G>(cw, sb, 0.5f, L);  // the halving of E and t folded in
+      if constexpr (B == 4) {  // undo the mirror on the packed form
+        uint32_t rev[16];
+        sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
+        sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
+        uint32_t sr[128 / G];
+        sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
+        sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
+        dequant_unpack<128, G>(cw, sb, 0.5f, L);
+      } else {  // dequantize in natural order, then mirror the values
+        float Ln[128];
+        dequant_unpack_bits<128, G, B>(cw, sb, 0.5f, Ln);
+        sfor<128>([&](auto I) { L[RTQ_CI(I)] = p ? Ln[127 - RTQ_CI(I)] : Ln[RTQ_CI(I)]; });
+      }
       // P = lane v's slots (X_a), Q = lane v+32's slots (X_{128-a}, Re/Im swapped)
       const int src0 = v, src1 = v + 32;
       float yv[128];
@@ -249,13 +333,15 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
       srft_inv<128, Sqrt2>(yv, u);
     } else {
       float f[128];
-      dequant_unpack<128, G>(cw, sb, 1.0f / 16.0f, f);
+      if constexpr (B == 4) dequant_unpack<128, G>(cw, sb, 1.0f / 16.0f, f);
+      else dequant_unpack_bits<128, G, B>(cw, sb, 1.0f / 16.0f, f);
       fwht_f32<128>(f);
       sfor<128>([&](auto K) {
         const float r = __shfl_xor(f[RTQ_CI(K)], 32);
         u[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
       });
     }
+    if (lam != nullptr) unweight_half<ROT>(u, lam, p);
     // fp16 samples out through LDS in two passes of 16 output chunks per row
     // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
     // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
@@ -316,6 +402,33 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
     wait_lds_reads();
     lds_sync();
   }
+}
+
+// Row policy of the plain entry points: tile rows row0 .. row0 + rows - 1 of
+// a contiguous [n, 256] tensor, under the call's seed rule.
+struct TileRows {
+  uint32_t row0;
+  int rows;
+  bool uniform;
+  uint32_t b0;  // seed block of row0
+  const SeedRule& sr;
+  const SignTable& tb;
+  static constexpr bool kStreamStores = true;
+  __device__ uint4 uniform_masks(uint32_t k) const { return chunk_masks(tb, seed_offset(b0, sr), sr.seed, k); }
+  __device__ uint4 row_masks(int rl, uint32_t k) const {
+    return chunk_sign_masks(seed_of_block(seed_block(row0 + (uint32_t)rl, sr), sr), k);
+  }
+  __device__ size_t cache_row(int rl) const { return (size_t)row0 + (uint32_t)rl; }
+  __device__ uint4* y_chunk(uint4* y, int rl, uint32_t k) const {
+    return y + (size_t)row0 * 32 + ((uint32_t)(rl * 32) + k);
+  }
+};
+
+__device__ __forceinline__ TileRows tile_rows(uint32_t n, const SeedRule& sr, const SignTable& tb) {
+  const uint32_t row0 = blockIdx.x * 32u;
+  const int rows = (int)(n - row0 < 32u ? n - row0 : 32u);
+  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+  return TileRows{row0, rows, b0 == b1, b0, sr, tb};
 }
 
 }  // namespace rtq

@@ -250,7 +250,7 @@ def test_ext_rejects_bad_arguments_without_launching(name):
     for kw in ({"n": -1}, {"rps": -1}, {"per": -1}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
                {"c": C + 2}, {"lam": LAM + 2}, {"n": 0xFFFFFF01}):
         assert ext_call(name, **kw) == bad, kw
-    for kw in ({"bits": 2}, {"bits": 5}, {"bits": 16}, {"d": 256}, {"d": 96}, {"g": 16}):
+    for kw in ({"bits": 2}, {"bits": 5}, {"bits": 16}, {"d": 256, "g": 256}, {"d": 96}, {"g": 16}):
         assert ext_call(name, **kw) == rtq.RTQ_ERR_UNSUPPORTED, kw
 
 

@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 from tests.conftest import gpu_available
-from tests.parity import check_forward_ext, check_inverse_ext
+from tests.parity import fp16_ulp, check_forward_ext, check_inverse_ext
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -57,23 +57,34 @@ def test_widths_and_lambda(rot, d, g, bits, use_lam):
     run_case(rot, d, g, bits, use_lam)
 
 
+@pytest.mark.parametrize("d", [64, 256])
 @pytest.mark.parametrize("bits", [3, 6])
-@pytest.mark.parametrize("n", [1, 63, 64, 65, 129])
-def test_ragged_rows_and_seed_rules(bits, n):
-    run_case("srft", 64, 32, bits, True, n=n, rps=7, per=3)
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 63, 64, 65, 129])
+def test_ragged_rows_and_seed_rules(bits, n, d):
+    run_case("srft", d, 32, bits, True, n=n, rps=7, per=3)
 
 
-def test_bits4_without_lambda_equals_the_int4_kernels():
-    """The general kernel with 4-bit codes and no lambda writes the same bytes
-    as the fused int4 kernel."""
-    x = torch.from_numpy(rows(500, 128, 1)).to(DEV)
-    c1, s1 = rtq.srft_quant_fwd_ext(x, 32, 4, 9, None, 11, 4)
-    c2, s2 = rtq.srft_quant_fwd(x, 32, 9, 11, 4)
-    y1 = rtq.srft_dequant_inv_ext(c1, s1, 128, 32, 4, 9, None, 11, 4)
-    y2 = rtq.srft_dequant_inv(c2, s2, 128, 32, 9, 11, 4)
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d", [128, 256])
+def test_bits4_without_lambda_equals_the_int4_kernels(rot, d):
+    """The general kernel with 4-bit codes and no lambda writes the same codes
+    and scales as the fused int4 kernel, and the same fp16 outputs, except for
+    SRHT at d <= 128, where the two inverse kernels round the dequantized
+    values differently (each stays within the inverse tolerance of the
+    oracle; here they agree within 2e-3 times the row's largest scale)."""
+    x = torch.from_numpy(rows(500, d, 1)).to(DEV)
+    c1, s1 = rtq.quant_fwd_ext(rot, x, 32, 4, 9, None, 11, 4)
+    c2, s2 = rtq.quant_fwd(rot, x, 32, 9, 11, 4)
+    y1 = rtq.dequant_inv_ext(rot, c1, s1, d, 32, 4, 9, None, 11, 4)
+    y2 = rtq.dequant_inv(rot, c2, s2, d, 32, 9, 11, 4)
     torch.cuda.synchronize()
     assert torch.equal(c1, c2) and torch.equal(s1, s2)
-    assert torch.equal(y1, y2)
+    if rot == "srft" or d == 256:
+        assert torch.equal(y1, y2)
+    else:
+        a, b = y1.double().cpu().numpy(), y2.double().cpu().numpy()
+        s_row = s2.double().cpu().numpy().max(axis=1, keepdims=True)
+        assert np.all(np.abs(a - b) <= 2e-3 * s_row + fp16_ulp(b)), np.max(np.abs(a - b) / (2e-3 * s_row))
 
 
 def test_error_falls_with_code_width_on_the_gpu():
