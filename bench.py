@@ -155,9 +155,16 @@ def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = Fals
              f"# kernel_source_sha: {kernel_source_hash(ATTN_SOURCES if attn else KERNEL_SOURCES)}",
              "# kernel | calls | average us | min us | max us | share of GPU time",
              ]
+    others = [r for r in rows if not short_kernel_name(r["Name"]).startswith("rtq::")]
     for r in rows:
+        if r in others:
+            continue
         lines.append(f"{short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}%")
+    if others:
+        lines.append(f"other kernels (input generation, copies, baselines): {len(others)} kernels, "
+                     f"{sum(int(r['Calls']) for r in others)} calls, "
+                     f"{sum(float(r['Percentage']) for r in others):.1f}% of GPU time")
     for r in rows:
         role = kernel_role(r["Name"])
         if role and (role == "attn_decode") == attn:
