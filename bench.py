@@ -42,8 +42,16 @@ ATTN_METRIC = "decode-attention steps/s over the int4 rotated K/V cache (dequant
 _CSRC = os.path.join(ROOT, "rotate_then_quantize_amd", "csrc")
 # sources each kernel family is compiled from (a profile is current while their code is unchanged)
 KERNEL_SOURCES = [os.path.join(_CSRC, f) for f in (
-    "rtq.hip", "rtq_lane.hpp", "rtq_host.hpp", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp", "rtq_pair.hpp")]
+    "rtq.hip", "rtq_lane.hpp", "rtq_host.hpp", "rtq_device.hpp", "rtq_div.hpp", "rtq_mem.hpp")]
+PAIR_SOURCES = KERNEL_SOURCES + [os.path.join(_CSRC, "rtq_pair.hpp")]  # d = 256 kernels
 ATTN_SOURCES = [os.path.join(_CSRC, f) for f in ("rtq_attn.hip", "rtq_device.hpp", "rtq_mem.hpp")]
+
+
+def kernel_sources(role: str, d: int):
+    """The source files a kernel's code comes from (its profile summaries go stale when they change)."""
+    if role == "attn_decode":
+        return ATTN_SOURCES
+    return PAIR_SOURCES if d == 256 else KERNEL_SOURCES
 
 
 def log(*a):
@@ -66,7 +74,7 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str, rot: str, kernel: str):
+def read_traffic(workload_name: str, rot: str, kernel: str, d: int):
     """HBM bytes per launch from the committed PMC summary, if it was taken on
     the current kernel source; otherwise None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{rot}_{workload_name}.txt")
@@ -78,8 +86,7 @@ def read_traffic(workload_name: str, rot: str, kernel: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    sources = ATTN_SOURCES if kernel == "attn_decode" else KERNEL_SOURCES
-    if vals.get("kernel_source_sha") != kernel_source_hash(sources):
+    if vals.get("kernel_source_sha") != kernel_source_hash(kernel_sources(kernel, d)):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -105,8 +112,8 @@ def role_bytes(w, role: str) -> int:
     return rows * w.bytes_per_vector()
 
 
-def role_sources(role: str):
-    return ATTN_SOURCES if role == "attn_decode" else KERNEL_SOURCES
+def role_sources(role: str, d: int):
+    return kernel_sources(role, d)
 
 
 def short_kernel_name(name: str) -> str:
@@ -152,7 +159,7 @@ def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = Fals
     what = "decode attention" if attn else "forward + inverse"
     lines = [f"# rocprofv3 kernel trace, {what}, workload {w.name} (d={w.d}, group={w.group}, {rot})",
              f"# command: {command}",
-             f"# kernel_source_sha: {kernel_source_hash(ATTN_SOURCES if attn else KERNEL_SOURCES)}",
+             f"# kernel_source_sha: {kernel_source_hash(kernel_sources('attn_decode' if attn else 'quant_fwd', w.d))}",
              "# kernel | calls | average us | min us | max us | share of GPU time",
              ]
     others = [r for r in rows if not short_kernel_name(r["Name"]).startswith("rtq::")]
@@ -214,7 +221,7 @@ def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mi
         lines += [f"# command ({c}): {cmd}" for c, cmd in commands]
         lines += [
             f"kernel: {kname}",
-            f"kernel_source_sha: {kernel_source_hash(role_sources(role))}",
+            f"kernel_source_sha: {kernel_source_hash(role_sources(role, w.d))}",
             f"dispatches_fetch: {nf[kname]}",
             f"dispatches_write: {nw[kname]}",
             f"fetch_kib_per_dispatch_raw: {fetch[kname]:.1f}",
@@ -546,7 +553,7 @@ def attn_main(args, w, dev):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": read_traffic(w.name, rot, "attn_decode"),
+            "traffic": read_traffic(w.name, rot, "attn_decode", w.d),
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
@@ -923,7 +930,7 @@ def main():
     dom_ms, dom_bytes = (inv_ms, inv_bytes) if dominant == "inv" else (fwd_ms, fwd_bytes)
     achieved = dom_bytes / dom_ms / 1e6
     kname = {"fwd": "quant_fwd", "inv": "dequant_inv"}[dominant]
-    traffic = read_traffic(w.name, rot, kname)
+    traffic = read_traffic(w.name, rot, kname, w.d)
     log(f"step {ms_step * 1e3:.1f} us | fwd {fwd_ms * 1e3:.1f} us {fwd_gbps:.0f} GB/s "
         f"({100 * fwd_gbps / HBM_PEAK_GBPS:.1f}%) | inv {inv_ms * 1e3:.1f} us {inv_gbps:.0f} GB/s "
         f"({100 * inv_gbps / HBM_PEAK_GBPS:.1f}%) | step {step_gbps:.0f} GB/s")
