@@ -195,6 +195,64 @@ def pmc_per_dispatch(directory: str, counter: str):
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
+VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD",
+                 "SQ_INSTS_VMEM_WR", "SQ_INSTS_SMEM")
+SIMDS, CLOCK_HZ = 1024, 2.4e9  # MI355X: 256 CUs x 4 SIMDs, peak engine clock
+
+
+def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bool = False) -> None:
+    """Instruction mix per wave of each library kernel from one rocprofv3 --pmc
+    pass of SQ counters (chip totals per dispatch), and the VALU issue time it
+    implies: a wave64 VALU instruction occupies its SIMD for 4 cycles, so
+    busy = SQ_INSTS_VALU * 4 / (SIMDs * clock * kernel time), with the kernel
+    time from a rocprofv3 trace of the same command and the peak clock."""
+    import csv
+    per = {c: pmc_per_dispatch(pmc_dir, c) for c in VALU_COUNTERS}
+    durs = {short_kernel_name(r["Name"]): float(r["AverageNs"])
+            for r in csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv")))}
+    for kname, waves in per["SQ_WAVES"][0].items():
+        role = kernel_role(kname)
+        if not role or (role == "attn_decode") != attn or kname not in durs or waves <= 0:
+            continue
+        valu = per["SQ_INSTS_VALU"][0][kname]
+        busy = valu * 4.0 / (SIMDS * CLOCK_HZ * durs[kname] * 1e-9)
+        lines = [f"# instruction mix of {kname}, workload {w.name} (d={w.d}, group={w.group}, {rot})"]
+        lines += [f"# command ({c}): {cmd}" for c, cmd in commands]
+        lines += [f"kernel: {kname}", f"kernel_source_sha: {kernel_source_hash(role_sources(role, w.d))}",
+                  f"dispatches: {per['SQ_WAVES'][1][kname]}", f"waves_per_dispatch: {waves:.0f}"]
+        for c in VALU_COUNTERS[1:]:
+            lines.append(f"{c.lower()}_per_wave: {per[c][0][kname] / waves:.1f}")
+        lines += [f"kernel_average_us: {durs[kname] / 1e3:.2f}",
+                  f"valu_busy_estimate: {busy:.3f}",
+                  "# valu_busy_estimate = SQ_INSTS_VALU * 4 cycles / (1024 SIMDs * 2.4 GHz * kernel time)"
+                  + ("; MFMA instructions count as VALU instructions here" if attn else "")]
+        path = os.path.join(ROOT, "profiles", f"valu_{role}_{rot}_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log(f"wrote {path}")
+
+
+def read_valu(workload_name: str, rot: str, kernel: str, d: int):
+    """VALU instructions per wave and the busy estimate from the committed
+    summary, if it was taken on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"valu_{kernel}_{rot}_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash(kernel_sources(kernel, d)):
+        return None
+    try:
+        return {"valu_insts_per_wave": float(vals["sq_insts_valu_per_wave"]),
+                "busy_estimate": float(vals["valu_busy_estimate"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (KeyError, ValueError):
+        return None
+
+
 def summarize_traffic(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, cal_mib, w, rot, commands) -> None:
     """HBM bytes per launch of each kernel: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch) scaled by what the same counters read for a plain device copy of
@@ -556,6 +614,7 @@ def attn_main(args, w, dev):
             "traffic": read_traffic(w.name, rot, "attn_decode", w.d),
             "algorithmic_bytes_per_launch": nbytes,
         },
+        "valu": read_valu(w.name, rot, "attn_decode", w.d),
     }
     if not args.no_eager:
         result["unfused_baseline"] = attn_unfused_baseline(w, rot, ms_step, dev)
@@ -786,15 +845,21 @@ def main():
                     help="write profiles/kernel_trace_*.txt from a rocprofv3 --kernel-trace --stats CSV directory")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/traffic_*.txt from four rocprofv3 --pmc CSV directories")
+    ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC", "TRACE"),
+                    help="write profiles/valu_*.txt from a rocprofv3 --pmc run of SQ instruction counters and a "
+                         "kernel trace of the same command")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
     if args.workload is None:
         args.workload = 3 if (args.attn or args.decode_cache) else 2
 
-    if args.summarize_trace or args.summarize_traffic:
+    if args.summarize_trace or args.summarize_traffic or args.summarize_valu:
         from rotate_then_quantize_amd import workloads as W
         w = W.WORKLOADS[args.workload]
+        if args.summarize_valu:
+            summarize_valu(*args.summarize_valu, w, args.rot, [("SQ counters", c) for c in args.command[-1:]],
+                           args.attn)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn)
         if args.summarize_traffic:
@@ -805,8 +870,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py measures one GPU: this build has no multi-GPU path (rows are independent; "
-            "see DESIGN.md for how the work would shard). Run with --gpus 1.")
+        log("bench.py measures one GPU and has no multi-GPU path: rows are independent, so the work "
+            "shards by layer, K/V head or batch with no exchange, each GPU running the same kernels on "
+            "its share. Run with --gpus 1.")
         sys.exit(2)
 
     import torch
@@ -967,6 +1033,7 @@ def main():
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
         },
+        "valu": read_valu(w.name, rot, kname, w.d),
     }
     if not args.no_graph:
         result["graph_replay"] = graph_replay(w, sets, replicas, fwd_fn, inv_fn, args.steps, bpv)

@@ -14,7 +14,7 @@ Sources (cited by page title and section):
   [P4] "Quantization & Serving".
   [P5] "Chapter 25 - Quantization: The Hardware View".
 
-What the pages fix and what is a reading (each reading is listed in the design doc):
+What the pages fix and what is this oracle's reading where they leave a step open:
   * Each K/V vector is rotated, quantized to int4, and later dequantized and
     rotated back [P1, "First, the 17%"].
   * SRFT = flip signs with a constant pseudo-random +-1 vector, then take an FFT (rfft on the
