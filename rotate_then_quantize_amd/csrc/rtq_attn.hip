@@ -437,6 +437,61 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int6
   }
 }
 
+// This lane's source addresses for token 0 of a chunk (the same pieces as
+// issue_chunk), so that a full chunk's loads cost one 64-bit add each: chunk
+// tok0 reads base + tok0 * (bytes per token step).  Only a stream's last,
+// partial chunk goes through issue_chunk's clamped addressing.
+template <int D, int GR>
+struct ChunkSources {
+  using C = Cfg<D, GR>;
+  static constexpr int NS = C::SLOT == 8 ? 2 : 1;  // scale loads per chunk
+  const uint8_t* k[C::CODE_DMA];
+  const uint8_t* v[C::CODE_DMA];
+  const uint8_t* s[NS];
+  int64_t code_step, scale_step;  // bytes per token
+
+  __device__ __forceinline__ ChunkSources(const Params& p, int64_t row_k, int64_t row_v, int lane) {
+    constexpr int PPR = C::RB / 16, RPI = 64 / PPR;
+    sfor<C::CODE_DMA>([&](auto I) {
+      const int lr = RTQ_CI(I) * RPI + lane / PPR;
+      const int r = lrow<D>(lr);
+      const int piece = (lane % PPR) ^ swz<D>(lr);
+      const int64_t off = (int64_t)r * p.stride_token;
+      k[RTQ_CI(I)] = p.codes + (row_k + off) * C::RB + 16 * piece;
+      v[RTQ_CI(I)] = p.codes + (row_v + off) * C::RB + 16 * piece;
+    });
+    if constexpr (C::SLOT == 16) {
+      s[0] = p.scales + ((lane < 32 ? row_k : row_v) + (int64_t)(lane & 31) * p.stride_token) * 16;
+    } else if constexpr (C::SLOT == 8) {
+      const int64_t off = (int64_t)(lane / 2) * p.stride_token;
+      s[0] = p.scales + (row_k + off) * 8 + 4 * (lane & 1);
+      s[1] = p.scales + (row_v + off) * 8 + 4 * (lane & 1);
+    } else {
+      s[0] = p.scales + ((lane < 32 ? row_k : row_v) + (int64_t)(lane & 31) * p.stride_token) * (2 * C::SPR);
+    }
+    code_step = p.stride_token * C::RB;
+    scale_step = p.stride_token * 2 * C::SPR;
+  }
+
+  // Direct-to-LDS loads of the full chunk of tokens tok0 .. tok0 + 31.
+  __device__ __forceinline__ void issue(int tok0, uint8_t* buf) const {
+    const int64_t dc = (int64_t)tok0 * code_step, ds = (int64_t)tok0 * scale_step;
+    sfor<C::CODE_DMA>([&](auto I) {
+      dma_to_lds<16>(k[RTQ_CI(I)] + dc, buf + RTQ_CI(I) * 1024);
+      dma_to_lds<16>(v[RTQ_CI(I)] + dc, buf + C::CODE_BYTES + RTQ_CI(I) * 1024);
+    });
+    uint8_t* sb = buf + 2 * C::CODE_BYTES;
+    if constexpr (C::SLOT == 16) {
+      dma_to_lds<16>(s[0] + ds, sb);
+    } else if constexpr (C::SLOT == 8) {
+      dma_to_lds<4>(s[0] + ds, sb);
+      dma_to_lds<4>(s[1] + ds, sb + C::SCALE_BYTES);
+    } else {
+      dma_to_lds<2 * C::SPR>(s[0] + ds, sb);
+    }
+  }
+};
+
 template <int D, int GR, int ROT>
 __global__ void __launch_bounds__(64 * kWavesPerStream) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
 attn_decode_kernel(Params p) {
@@ -454,7 +509,7 @@ attn_decode_kernel(Params p) {
   float* const stage_all = C::DENSE_ROT ? reinterpret_cast<float*>(slot1) : stage_arr;
   float* const vt_all = reinterpret_cast<float*>(slot1 + kMaxQ * C::QROW * 4);  // d = 256: [D][kMaxQ]
 
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;
   const int G = p.q_per_kv, T = p.tokens;
   // Workgroups go to the 8 XCDs round-robin (id b to XCD b % 8).  Give XCD x
@@ -489,9 +544,15 @@ attn_decode_kernel(Params p) {
     const uint4* src = p.q + (qrow + lane) * (D / 8);
     sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
   }
-  if (c_begin < c_end) issue_chunk<D, GR>(p, row_k, row_v, c_begin * kChunk, slot0 + w * C::BUF, lane);
+  const ChunkSources<D, GR> src(p, row_k, row_v, lane);
+  // a chunk is full unless it holds the stream's last token
+  auto load_chunk = [&](int c, uint8_t* dst) {
+    if ((c + 1) * kChunk <= T) src.issue(c * kChunk, dst);
+    else issue_chunk<D, GR>(p, row_k, row_v, c * kChunk, dst, lane);
+  };
+  if (c_begin < c_end) load_chunk(c_begin, slot0 + w * C::BUF);
   if (C::BUFS > 2 && c_begin + 1 < c_end)
-    issue_chunk<D, GR>(p, row_k, row_v, (c_begin + 1) * kChunk, slot1 + w * C::BUF, lane);
+    load_chunk(c_begin + 1, slot1 + w * C::BUF);
   if constexpr (C::DENSE_ROT) {
     dense_queries<D, ROT>(p, qrow, seed_of_row(p, row_k), G, slot1, stage, qexp);
   } else if (lead) {
@@ -583,7 +644,7 @@ attn_decode_kernel(Params p) {
     if (NB > 2 && c + 1 < c_end) wait_vmcnt<C::NDMA>();
     else wait_vmcnt<0>();
     lds_sync();
-    if (c + NB - 1 < c_end) issue_chunk<D, GR>(p, row_k, row_v, (c + NB - 1) * kChunk, next, lane);
+    if (c + NB - 1 < c_end) load_chunk(c + NB - 1, next);
     const uint8_t* kc = buf;
     const uint8_t* vc = buf + C::CODE_BYTES;
     const uint8_t* ks = buf + 2 * C::CODE_BYTES;
