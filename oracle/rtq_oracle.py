@@ -496,11 +496,15 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray, rows: np.ndarray, d: int
 def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, strides, layers: int, streams: int,
                 tokens: int, q_per_kv: int, d: int, group: int, seed: int, rows_per_seed: int = 0,
                 seed_period: int = 0, rot: str = "srft", softmax_scale: float | None = None,
-                pairs=None) -> np.ndarray:
+                pairs=None, window: np.ndarray | None = None, window_tokens: int = 0) -> np.ndarray:
     """One decode step of attention for every (layer, stream): query g of
     q[layer, stream] attends over the first `tokens` cached keys and values of
     its stream (rows from cache_rows), each dequantized and rotated back
-    exactly (fp64, no fp16 rounding); softmax_scale defaults to 1/sqrt(d).
+    exactly (fp64, no fp16 rounding), followed by the first `window_tokens`
+    tokens of the fp16 window (window[layer, kv, stream, j], kept unquantized
+    in the original domain, as the method page's decode cache keeps its newest
+    tokens: "Quantization Speed Is Often a Kernel Problem", "First, the 17%");
+    one softmax runs over all of them; softmax_scale defaults to 1/sqrt(d).
     Returns o [layers, streams, q_per_kv, d] in fp64 (entries of (layer,
     stream) pairs outside `pairs`, when a list is given, stay zero)."""
     if softmax_scale is None:
@@ -512,7 +516,11 @@ def attn_decode(q_f16: np.ndarray, codes: np.ndarray, scales: np.ndarray, stride
         u = []
         for kv in (0, 1):
             rows = cache_rows(layer, kv, st, tokens, strides)
-            u.append(dequant_rows(codes, scales, rows, d, group, seed, rows_per_seed, seed_period, rot))
+            part = dequant_rows(codes, scales, rows, d, group, seed, rows_per_seed, seed_period, rot)
+            if window_tokens:
+                win = np.asarray(window[layer, kv, st, :window_tokens], dtype=np.float16).astype(np.float64)
+                part = np.concatenate([part, win])
+            u.append(part)
         keys, values = u
         for g in range(q_per_kv):
             sc = keys @ q[layer, st, g] * softmax_scale

@@ -497,6 +497,66 @@ def check_attn_cache_layout(m):
 
 
 
+def _textbook_attention(q, keys, values, scale):
+    """softmax(scale * keys q) values, written out term by term."""
+    e = [math.exp(scale * float(np.dot(q, k))) for k in keys]
+    return sum(w * v for w, v in zip(e, values)) / sum(e)
+
+
+def check_attn_window_joins_the_softmax(m):
+    """With an fp16 window, one softmax runs over the dequantized prefix and
+    the window tokens: the textbook formula over both token lists (prefix
+    rows through dequant_inv one at a time, window rows as given)."""
+    rng = np.random.default_rng(8)
+    L, S, Tc, T, W, Wc, G, d, g = 2, 2, 5, 4, 3, 4, 2, 64, 32
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 31, 2 * S * Tc, L, "srft")
+    win = (rng.standard_normal((L, 2, S, Wc, d)) * 0.7).astype(np.float16)
+    q = rng.standard_normal((L, S, G, d)).astype(np.float16)
+    o = m.attn_decode(q, codes, scales, _lm(S, Tc), L, S, T, G, d, g, 31, 2 * S * Tc, L, "srft",
+                      window=win, window_tokens=W)
+    for l in range(L):
+        for s in range(S):
+            base = l * 2 * S * Tc + s * Tc
+            k = _attn_values(m, codes, scales, range(base, base + T), d, g, 31, 2 * S * Tc, L, "srft")
+            v = _attn_values(m, codes, scales, range(base + S * Tc, base + S * Tc + T), d, g, 31, 2 * S * Tc, L,
+                             "srft")
+            keys = list(k) + list(win[l, 0, s, :W].astype(np.float64))
+            values = list(v) + list(win[l, 1, s, :W].astype(np.float64))
+            for gi in range(G):
+                want = _textbook_attention(q[l, s, gi].astype(np.float64), keys, values, 1.0 / 8.0)
+                assert np.allclose(o[l, s, gi], want, rtol=1e-12, atol=1e-12)
+
+
+def check_attn_window_alone(m):
+    """With no quantized tokens the window is the whole context: the textbook
+    formula on the window rows; rows past window_tokens are ignored."""
+    rng = np.random.default_rng(9)
+    L, S, Tc, W, Wc, d, g = 1, 2, 3, 5, 8, 128, 64
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 3, 0, 0, "srht")
+    win = rng.standard_normal((L, 2, S, Wc, d)).astype(np.float16)
+    win[:, :, :, W:] = np.float16(1e4)  # unused slots must not matter
+    q = rng.standard_normal((L, S, 1, d)).astype(np.float16)
+    o = m.attn_decode(q, codes, scales, _lm(S, Tc), L, S, 0, 1, d, g, 3, 0, 0, "srht", window=win, window_tokens=W)
+    for s in range(S):
+        want = _textbook_attention(q[0, s, 0].astype(np.float64), win[0, 0, s, :W].astype(np.float64),
+                                   win[0, 1, s, :W].astype(np.float64), 1.0 / math.sqrt(d))
+        assert np.allclose(o[0, s, 0], want, rtol=1e-12, atol=1e-12)
+
+
+def check_attn_dominant_window_key_selects_its_value(m):
+    """A query parallel to one window key, scaled far up, returns that window
+    token's value."""
+    rng = np.random.default_rng(10)
+    L, S, Tc, T, Wc, d, g = 1, 1, 4, 4, 4, 64, 64
+    codes, scales = _attn_cache(m, rng, L, S, Tc, d, g, 5, 0, 0, "srft", scale=0.01)
+    win = (rng.standard_normal((L, 2, S, Wc, d)) * 0.01).astype(np.float16)
+    key = win[0, 0, 0, 2].astype(np.float64)
+    q = (key / np.linalg.norm(key) * 4e4).astype(np.float16).reshape(1, 1, 1, d)
+    o = m.attn_decode(q, codes, scales, _lm(S, Tc), L, S, T, 1, d, g, 5, 0, 0, "srft", softmax_scale=1.0,
+                      window=win, window_tokens=3)
+    assert np.allclose(o[0, 0, 0], win[0, 1, 0, 2].astype(np.float64), rtol=0, atol=1e-9)
+
+
 # ---------------------------------------------------------------------------
 # Row lists and the decode-cache window
 # ---------------------------------------------------------------------------

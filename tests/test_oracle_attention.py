@@ -3,7 +3,9 @@
 Each pin fixes the result independently of the function's own arithmetic:
 a single token returns its value, identical keys average the values, a
 dominant key selects its value, and permuting tokens changes nothing; a
-textbook loop on a three-token case is kept as a cross-check."""
+textbook loop on a three-token case is kept as a cross-check.  With an fp16
+window, the textbook formula over the prefix and the window tokens, the
+window alone, and a dominant window key."""
 import oracle
 from tests import oracle_pins as P
 
@@ -42,3 +44,15 @@ def test_row_list_matches_single_rows():
 
 def test_window_schedule_closed_form():
     P.check_window_schedule_closed_form(oracle)
+
+
+def test_window_joins_the_softmax():
+    P.check_attn_window_joins_the_softmax(oracle)
+
+
+def test_window_alone():
+    P.check_attn_window_alone(oracle)
+
+
+def test_dominant_window_key_selects_its_value():
+    P.check_attn_dominant_window_key_selects_its_value(oracle)

@@ -49,6 +49,9 @@ def all_pins(m):
         "attn_rows": lambda: P.check_attn_dequant_rows_match_rowwise_inverse(m),
         "row_list": lambda: P.check_row_list_matches_single_rows(m),
         "window": lambda: P.check_window_schedule_closed_form(m),
+        "attn_window": lambda: P.check_attn_window_joins_the_softmax(m),
+        "attn_window_alone": lambda: P.check_attn_window_alone(m),
+        "attn_window_dominant": lambda: P.check_attn_dominant_window_key_selects_its_value(m),
         "ext_bits4": lambda: P.check_ext_bits4_without_lambda_is_the_int4_path(m),
         "ext_layout": lambda: P.check_pack_bits_layout_fixtures(m),
         "ext_roundtrip": lambda: P.check_pack_bits_exhaustive_round_trip(m),
@@ -145,6 +148,15 @@ MUTATIONS = {
     "b-bit clamp one code short": (
         "    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1\n    q = np.clip",
         "    lo, hi = -(1 << (bits - 1)) + 1, (1 << (bits - 1)) - 1\n    q = np.clip"),
+    "attention window reads keys as values": (
+        "                win = np.asarray(window[layer, kv, st, :window_tokens]",
+        "                win = np.asarray(window[layer, 0, st, :window_tokens]"),
+    "attention window drops its last token": (
+        "                win = np.asarray(window[layer, kv, st, :window_tokens]",
+        "                win = np.asarray(window[layer, kv, st, :window_tokens - 1]"),
+    "attention window rounds through fp16 after the prefix": (
+        "                part = np.concatenate([part, win])",
+        "                part = np.concatenate([part.astype(np.float16).astype(np.float64), win])"),
     "attention drops the softmax scale": (
         "            sc = keys @ q[layer, st, g] * softmax_scale",
         "            sc = keys @ q[layer, st, g]"),
