@@ -97,12 +97,14 @@ def read_traffic(workload_name: str, rot: str, kernel: str, d: int):
 KERNEL_ROLES = (("fwd_", "quant_fwd"), ("inv_", "dequant_inv"), ("attn::", "attn_decode"))
 
 
-def attn_bytes(w) -> int:
+def attn_bytes(w, window: int = 0) -> int:
     """Algorithmic HBM bytes of one decode-attention launch over workload w:
-    every K and V row's codes and scales once, plus the queries and outputs."""
+    every K and V row's codes and scales once, the fp16 K and V rows of the
+    `window` newest tokens once, plus the queries and outputs."""
     rows = w.layers * 2 * w.streams * w.tokens
     qo = 2 * w.layers * w.streams * w.q_per_kv * w.d * 2
-    return rows * (w.d // 2 + 2 * (w.d // w.group)) + qo
+    win = w.layers * 2 * w.streams * window * w.d * 2
+    return rows * (w.d // 2 + 2 * (w.d // w.group)) + qo + win
 
 
 def role_bytes(w, role: str) -> int:
@@ -519,10 +521,16 @@ def attn_cpu_baseline(w, codes_gpu, scales_gpu, q_gpu, rot, seconds, strides, rp
 def attn_main(args, w, dev):
     import torch
     import rotate_then_quantize_amd as rtq
-    rot = args.rot
+    rot, W = args.rot, args.window
     lib = rtq.library()
-    fn = lib.srft_attn_decode if rot == "srft" else lib.srht_attn_decode
+    if W:
+        fn = lib.srft_attn_decode_window if rot == "srft" else lib.srht_attn_decode_window
+    else:
+        fn = lib.srft_attn_decode if rot == "srft" else lib.srht_attn_decode
     L, S, T, G, d, g = w.layers, w.streams, w.tokens, w.q_per_kv, w.d, w.group
+    if w.kv != 2:
+        raise SystemExit(f"workload {w.wid} ({w.name}) holds no K/V pair per stream; decode attention needs one "
+                         f"(workloads 2, 3, 4 and 5 do)")
     n = w.n_rows
     if args.attn_layout == "heads":
         strides = (2 * S * T, S * T, T, 1)
@@ -532,7 +540,7 @@ def attn_main(args, w, dev):
     cache_bytes = n * (d // 2 + 2 * (d // g))
     replicas = args.replicas or max(1, math.ceil((1 << 30) / cache_bytes))
     log(f"decode attention, workload {w.name}: L={L} S={S} T={T} G={G} d={d} group={g} rot={rot}, "
-        f"{replicas} cache replica(s) of {cache_bytes / 1e6:.1f} MB")
+        f"{replicas} cache replica(s) of {cache_bytes / 1e6:.1f} MB" + (f", fp16 window of {W} tokens" if W else ""))
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     stream = torch.cuda.current_stream(dev)
@@ -549,9 +557,13 @@ def attn_main(args, w, dev):
         q = torch.randn((L, S, G, d), generator=gen, device=dev).to(torch.float16)
         out = torch.empty_like(q)
         a = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
-             ctypes.c_void_p(out.data_ptr()), L, S, T, G, d, g, *strides, w.sign_seed, rps, per, scale,
-             ws_ptr, ws_bytes, sh)
-        sets.append((a, (codes, scales, q, out)))
+             ctypes.c_void_p(out.data_ptr()), L, S, T, G, d, g, *strides, w.sign_seed, rps, per, scale)
+        keep = (codes, scales, q, out)
+        if W:
+            win = torch.randn((L, 2, S, W, d), generator=gen, device=dev).to(torch.float16)
+            a += (ctypes.c_void_p(win.data_ptr()), W, W)
+            keep += (win,)
+        sets.append((a + (ws_ptr, ws_bytes, sh), keep))
     torch.cuda.synchronize()
 
     def step(i):
@@ -577,7 +589,7 @@ def attn_main(args, w, dev):
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     k_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in sampled) / len(sampled)
-    nbytes = attn_bytes(w)
+    nbytes = attn_bytes(w, W)
     achieved = nbytes / k_ms / 1e6
     log(f"step {ms_step * 1e3:.1f} us | kernel {k_ms * 1e3:.1f} us {achieved:.0f} GB/s "
         f"({100 * achieved / HBM_PEAK_GBPS:.1f}% of {HBM_PEAK_GBPS:.0f})")
@@ -600,6 +612,7 @@ def attn_main(args, w, dev):
             "cache_strides": list(strides),
             "cache_replicas": replicas, "cache": "uniform int4 codes, |N(0,1)|*0.3 fp16 scales",
             "token_split_workspace_bytes": ws_bytes,
+            "window_tokens": W,
         },
         "kernel_us": {"attn_decode": k_ms * 1e3,
                       "timing": f"hipEvents on the launch stream, every {SAMPLE}th timed step "
@@ -611,14 +624,15 @@ def attn_main(args, w, dev):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": read_traffic(w.name, rot, "attn_decode", w.d),
+            # the counter summaries cover the launch without a window
+            "traffic": None if W else read_traffic(w.name, rot, "attn_decode", w.d),
             "algorithmic_bytes_per_launch": nbytes,
         },
-        "valu": read_valu(w.name, rot, "attn_decode", w.d),
+        "valu": None if W else read_valu(w.name, rot, "attn_decode", w.d),
     }
-    if not args.no_eager:
+    if not args.no_eager and not W:
         result["unfused_baseline"] = attn_unfused_baseline(w, rot, ms_step, dev)
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not W:
         codes, scales, q, _ = sets[0][1]
         result["cpu_baseline"] = attn_cpu_baseline(w, codes, scales, q, rot, args.cpu_seconds, strides, rps, per)
     print(json.dumps(result), flush=True)
@@ -833,6 +847,8 @@ def main():
                          "contiguous, as a per-layer [batch, heads, tokens, d] cache), 'workload' = the "
                          "workload's own row order")
     ap.add_argument("--rot", choices=["srft", "srht"], default="srft")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="with --attn: also attend to W fp16 tokens per stream (0-64)")
     ap.add_argument("--replicas", type=int, default=0, help="buffer sets cycled per step (0 = enough to exceed 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -851,6 +867,8 @@ def main():
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
+    if args.window and (not args.attn or not 0 < args.window <= 64):
+        ap.error("--window takes 1 to 64 tokens and goes with --attn")
     if args.workload is None:
         args.workload = 3 if (args.attn or args.decode_cache) else 2
 

@@ -296,6 +296,49 @@ rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void*
                             int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
                             float softmax_scale, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * srft_attn_decode_window / srht_attn_decode_window -- the same decode step
+ * over a cache whose newest tokens are still fp16: the method page's decode
+ * cache keeps the newest tokens unquantized in a small window and quantizes
+ * them only when it fills ("Quantization Speed Is Often a Kernel Problem",
+ * "First, the 17%").  One softmax runs over the `tokens` int4 tokens of each
+ * stream (as in srft_attn_decode) and its first `window_tokens` window
+ * tokens, which come after them:
+ *   out[l][s][g] = fp16( sum_t w_t v_t + sum_j w'_j wv_j ),  with the weights
+ *   w, w' of one softmax over c_t = softmax_scale * (q . k_t) and
+ *   c'_j = softmax_scale * (q . wk_j).
+ *
+ *   window_f16      in : [layers][2][streams][window_capacity][d] fp16, the
+ *                        window keys (index 1 = 0) and values (1), in the
+ *                        original domain (neither rotated nor sign-flipped);
+ *                        16-byte aligned.  Slots past window_tokens are not read.
+ *   window_capacity    : token slots per (layer, K/V, stream) of the window.
+ *   window_tokens      : window tokens that count, 0 .. window_capacity.
+ *   tokens             : may be 0 when window_tokens >= 1 (no int4 token yet).
+ * Other arguments, workspace, supported shapes and errors as for
+ * srft_attn_decode.  window_tokens > 64: RTQ_ERR_UNSUPPORTED; window_tokens >
+ * window_capacity, a NULL window with window_tokens > 0, a misaligned window,
+ * or out overlapping the window: RTQ_ERR_INVALID_ARG.  window_tokens == 0 is
+ * srft_attn_decode.
+ */
+rtq_status srft_attn_decode_window(const void* q_f16, const void* codes_u8, const void* scales_f16,
+                                   void* out_f16, int32_t layers, int32_t streams, int32_t tokens,
+                                   int32_t q_per_kv, int32_t d, int32_t group, int64_t stride_layer,
+                                   int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                                   uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                   float softmax_scale, const void* window_f16, int32_t window_capacity,
+                                   int32_t window_tokens, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+rtq_status srht_attn_decode_window(const void* q_f16, const void* codes_u8, const void* scales_f16,
+                                   void* out_f16, int32_t layers, int32_t streams, int32_t tokens,
+                                   int32_t q_per_kv, int32_t d, int32_t group, int64_t stride_layer,
+                                   int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                                   uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                   float softmax_scale, const void* window_f16, int32_t window_capacity,
+                                   int32_t window_tokens, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d);
 
 /* Static, NUL-terminated description of a status code (never NULL). */

@@ -77,6 +77,11 @@ def library():
             fn = getattr(lib, name)
             fn.argtypes = attn_args
             fn.restype = ctypes.c_int
+        win_args = attn_args[:18] + [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32] + attn_args[18:]
+        for name in ("srft_attn_decode_window", "srht_attn_decode_window"):
+            fn = getattr(lib, name)
+            fn.argtypes = win_args
+            fn.restype = ctypes.c_int
         lib.rtq_attn_workspace_bytes.argtypes = [ctypes.c_int32] * 5
         lib.rtq_attn_workspace_bytes.restype = ctypes.c_size_t
         mapped_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -210,7 +215,7 @@ def _attn_workspace(q, tokens, stream_handle):
 
 
 def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period, softmax_scale,
-          out, stream, workspace=None):
+          out, stream, workspace=None, window=None, window_tokens=0):
     import math
     import torch
     _need(q, torch.float16, "q")
@@ -226,9 +231,17 @@ def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, 
     strides = tuple(int(v) for v in strides)
     if len(strides) != 4 or min(strides) < 0:
         raise ValueError("strides must be four non-negative row counts (layer, kv, stream, token)")
-    if tokens < 1:
-        raise ValueError("tokens must be at least 1")
-    if layers and streams:
+    if window is not None:
+        _need(window, torch.float16, "window")
+        if window.dim() != 5 or tuple(window.shape[:3]) != (layers, 2, streams) or window.shape[4] != d:
+            raise ValueError(f"window must be [{layers}, 2, {streams}, capacity, {d}]")
+        if not 0 <= window_tokens <= window.shape[3]:
+            raise ValueError("window_tokens must lie in 0 .. window capacity")
+    elif window_tokens:
+        raise ValueError("window_tokens without a window")
+    if tokens < (0 if window_tokens else 1):
+        raise ValueError("tokens must be at least 1 (or 0 with a non-empty window)")
+    if layers and streams and tokens:
         max_row = (layers - 1) * strides[0] + strides[1] + (streams - 1) * strides[2] + (tokens - 1) * strides[3]
         if max_row >= codes.shape[0]:
             raise ValueError(f"the cache has {codes.shape[0]} rows; the strides reach row {max_row}")
@@ -245,31 +258,37 @@ def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, 
     else:
         _need(workspace, torch.uint8, "workspace")
         ws_ptr, ws_bytes = ctypes.c_void_p(workspace.data_ptr()), workspace.numel()
-    _check(getattr(library(), cname)(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
-        ctypes.c_void_p(out.data_ptr()), layers, streams, tokens, q_per_kv, d, group, *strides,
-        seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale), ws_ptr, ws_bytes, sh))
+    args = [ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), layers, streams, tokens, q_per_kv, d, group, *strides,
+            seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale)]
+    if window is not None:
+        args += [ctypes.c_void_p(window.data_ptr()), window.shape[3], window_tokens]
+        cname += "_window"
+    _check(getattr(library(), cname)(*args, ws_ptr, ws_bytes, sh))
     return out
 
 
 def srft_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
-                     softmax_scale=None, out=None, stream=None, workspace=None):
+                     softmax_scale=None, out=None, stream=None, workspace=None, window=None, window_tokens=0):
     """One decode step of attention over an SRFT int4 cache: q [layers, streams, q_per_kv, d] fp16
     attends over tokens 0..tokens-1 of its stream, whose key / value row is
     layer*strides[0] + kv*strides[1] + stream*strides[2] + token*strides[3] (kv 0 = K, 1 = V).
     Returns o like q (fp16); softmax_scale defaults to 1/sqrt(d).
     workspace: None = a zero-filled workspace kept per (device, stream), which lets the kernel split each
     stream's tokens over several workgroups when there are few streams; a uint8 tensor = that memory
-    (zero-filled before its first use, see attn_workspace_bytes); an empty tensor = no split."""
+    (zero-filled before its first use, see attn_workspace_bytes); an empty tensor = no split.
+    window: an fp16 [layers, 2, streams, capacity, d] window of the newest tokens (unquantized, original
+    domain) whose first window_tokens tokens join the softmax after the `tokens` int4 tokens; tokens may
+    then be 0."""
     return _attn("srft_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
-                 softmax_scale, out, stream, workspace)
+                 softmax_scale, out, stream, workspace, window, window_tokens)
 
 
 def srht_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
-                     softmax_scale=None, out=None, stream=None, workspace=None):
+                     softmax_scale=None, out=None, stream=None, workspace=None, window=None, window_tokens=0):
     """srft_attn_decode over an SRHT (Walsh-Hadamard) int4 cache."""
     return _attn("srht_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
-                 softmax_scale, out, stream, workspace)
+                 softmax_scale, out, stream, workspace, window, window_tokens)
 
 
 def attn_decode(rot, *args, **kw):

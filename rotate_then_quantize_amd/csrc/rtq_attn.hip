@@ -47,6 +47,10 @@
 //     online-softmax rescale stays in the lane that owns the query.
 //   * int4 -> fp16 takes one v_bitop3 per pair of codes (mask, bias and
 //     fp16 exponent at once) and one packed fp16 add or fma.
+//   * The method keeps the newest tokens in fp16, unquantized ("First, the
+//     17%").  The _window entry points take those tokens too: after the int4
+//     part is merged, the workgroup scores the window in the original domain
+//     and joins it to the same softmax with the online-softmax merge.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -93,7 +97,13 @@ struct Params {
   int32_t splits;
   float* part;      // [pairs][splits][PartFloats]
   uint32_t* count;  // [pairs], zero between calls
+  // fp16 window of each stream's newest tokens, unquantized and in the
+  // original domain: [layers][K, V][streams][win_cap][d], or null.
+  const uint4* win;
+  int32_t win_cap, win_tokens;
 };
+
+constexpr int kMaxWindow = 64;  // window tokens per stream
 
 // Floats of one split's partial: the unnormalized output sum of each query
 // (q_per_kv rows of d), then its running max and its softmax denominator.
@@ -437,6 +447,192 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t row_k, int6
   }
 }
 
+// DPP lane moves: x of another lane of the same row of 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// op over each aligned group of N lanes (N = 8, 16, 32 or 64), in every lane
+// of the group: quad swaps, then the mirror of each 8 and of each 16 lanes,
+// then the 16- and 32-lane swaps.  Every lane of the wave must be active.
+template <int N, class Op>
+__device__ __forceinline__ float reduce_lanes(float x, Op op) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "lane groups of 8 to 64");
+  x = op(x, dpp<0xB1>(x));   // quad_perm 1,0,3,2
+  x = op(x, dpp<0x4E>(x));   // quad_perm 2,3,0,1
+  x = op(x, dpp<0x141>(x));  // row_half_mirror: lane i <-> 7 - i
+  if constexpr (N >= 16) x = op(x, dpp<0x140>(x));  // row_mirror: lane i <-> 15 - i
+  if constexpr (N >= 32) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  if constexpr (N >= 64) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  }
+  return x;
+}
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+
+// LDS of the window part: the weights [kMaxWindow][kMaxQ] and coef[kMaxQ]
+// (in ring slot 0), and the partial value sums of every token phase
+// [planes][kMaxQ][D], whose plane 0 becomes the window output ows[g][D].
+template <int D>
+struct WindowLds {
+  static constexpr int PAIRS = D / 2;               // 4-byte dim pairs per row
+  static constexpr int PHASES = 64 * kWavesPerStream / PAIRS;  // token phases of the value loop
+  static constexpr int PLANES = PAIRS < 64 ? kWavesPerStream : PHASES;  // d = 64: one per wave
+  static constexpr int WEIGHT_BYTES = 4096;
+  static_assert((kMaxWindow * kMaxQ + kMaxQ) * 4 <= WEIGHT_BYTES, "weights and coef fit 4 KB");
+  static constexpr int RED_BYTES = PLANES * kMaxQ * D * 4;
+};
+
+// The fp16 window's share of one softmax over the int4 tokens and the
+// window tokens, by the whole workgroup.  Scores: lanes hold 16-byte pieces
+// of the window key rows (a wave's loads cover consecutive rows) and dot them
+// with the same pieces of every query; a row's pieces are summed over its
+// lanes.  Softmax: one wave per query merges the window scores with the int4
+// part's running max mq and denominator lq (the online-softmax merge).
+// Values: each thread owns a dim pair and one token phase (coalesced rows),
+// sums weight * value for every query, and the phases are summed through
+// LDS.  Leaves coef[g] (the weight of the normalized int4 output) and
+// ows[g * D + dim] (the window's part of the output, multiplied by the value
+// sign of dim, since the output is sign-flipped as a whole at the end).
+// Scores are in base-2 units like the int4 part's.  The window's K, V and
+// query loads (WindowRegs) are all issued before the first use, so the part
+// costs one memory round trip, which the caller can start early.
+template <int D>
+struct WindowRegs {
+  using WL = WindowLds<D>;
+  static constexpr int CPR = D / 8;                    // 16-byte pieces per row
+  static constexpr int RPW = 64 / CPR;                 // rows per wave per key load
+  static constexpr int RPG = RPW * kWavesPerStream;    // rows per workgroup per key load
+  static constexpr int NK = kMaxWindow / RPG;          // key loads per thread
+  static constexpr int NV = kMaxWindow / WL::PHASES;   // value loads per thread
+  uint4 qv[kMaxQ], kv[NK];
+  uint32_t vv[NV];
+
+  __device__ __forceinline__ void load(const Params& p, int64_t wrow_k, int64_t wrow_v, int64_t qrow, int G) {
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6, W = p.win_tokens;
+    const int c = lane % CPR, r0 = w * RPW + lane / CPR;
+    const int pr = t % WL::PAIRS, ph = t / WL::PAIRS;
+    const uint32_t* wv = reinterpret_cast<const uint32_t*>(p.win) + wrow_v * WL::PAIRS;
+    sfor<kMaxQ>([&](auto I) {
+      if (RTQ_CI(I) < G) qv[RTQ_CI(I)] = p.q[(qrow + RTQ_CI(I)) * CPR + c];
+    });
+    sfor<NK>([&](auto I) {
+      const int j = r0 + RTQ_CI(I) * RPG;
+      kv[RTQ_CI(I)] = j < W ? p.win[(wrow_k + j) * CPR + c] : make_uint4(0, 0, 0, 0);
+    });
+    sfor<NV>([&](auto I) {
+      const int j = ph + RTQ_CI(I) * WL::PHASES;
+      vv[RTQ_CI(I)] = j < W ? wv[(int64_t)j * WL::PAIRS + pr] : 0u;
+    });
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void window_part(const Params& p, const WindowRegs<D>& r, int G, uint64_t seed_v,
+                                            const float* mq, const float* lq, float* wts, float* coef, float* red) {
+  using WL = WindowLds<D>;
+  using WR = WindowRegs<D>;
+  constexpr int CPR = WR::CPR, RPG = WR::RPG, NK = WR::NK, NV = WR::NV;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, W = p.win_tokens;
+  const int c = lane % CPR, r0 = w * WR::RPW + lane / CPR;
+  const int pr = t % WL::PAIRS, ph = t / WL::PAIRS;
+  const uint4* qv = r.qv;
+  const uint4* kv = r.kv;
+  const uint32_t* vv = r.vv;
+
+  // scores of every (window token, query)
+  sfor<NK>([&](auto I) {
+    if (RTQ_CI(I) * RPG < W) {
+      const int j = r0 + RTQ_CI(I) * RPG;
+      const uint4 k = kv[RTQ_CI(I)];
+      sfor<kMaxQ>([&](auto Gi) {
+        constexpr int g = RTQ_CI(Gi);
+        if (g < G) {
+          const uint4 a = qv[g];
+          float acc = __builtin_amdgcn_fdot2(as_h2(a.x), as_h2(k.x), 0.0f, false);
+          acc = __builtin_amdgcn_fdot2(as_h2(a.y), as_h2(k.y), acc, false);
+          acc = __builtin_amdgcn_fdot2(as_h2(a.z), as_h2(k.z), acc, false);
+          acc = __builtin_amdgcn_fdot2(as_h2(a.w), as_h2(k.w), acc, false);
+          acc = reduce_lanes<CPR>(acc, AddOp{});
+          if (c == 0 && j < W) wts[j * kMaxQ + g] = acc * p.qscale;
+        }
+      });
+    }
+  });
+  __syncthreads();
+
+  // softmax over the int4 part and the window, one wave per query; the
+  // weights of rows past the window become 0
+  for (int g = w; g < G; g += kWavesPerStream) {
+    const float sc = lane < W ? wts[lane * kMaxQ + g] : kNegBig;
+    const float m = fmaxf(mq[g], reduce_lanes<64>(sc, MaxOp{}));
+    const float fr = __builtin_amdgcn_exp2f(mq[g] - m);  // 0 when there is no int4 token
+    const float e = lane < W ? __builtin_amdgcn_exp2f(sc - m) : 0.0f;
+    const float inv = 1.0f / __builtin_fmaf(fr, lq[g], reduce_lanes<64>(e, AddOp{}));
+    wts[lane * kMaxQ + g] = e * inv;
+    if (lane == 0) coef[g] = fr * lq[g] * inv;
+  }
+  __syncthreads();
+
+  // the weighted values: dims 2 pr, 2 pr + 1 of every query, over this phase's tokens
+  float acc[kMaxQ][2];
+  sfor<kMaxQ>([&](auto Gi) { acc[RTQ_CI(Gi)][0] = acc[RTQ_CI(Gi)][1] = 0.0f; });
+  sfor<NV>([&](auto I) {
+    if (RTQ_CI(I) * WL::PHASES < W) {
+      const int j = ph + RTQ_CI(I) * WL::PHASES;  // < kMaxWindow
+      const float4 wa = *reinterpret_cast<const float4*>(wts + j * kMaxQ);
+      const float4 wb = *reinterpret_cast<const float4*>(wts + j * kMaxQ + 4);
+      const float wg[kMaxQ] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+      const f16x2_t v = as_h2(vv[RTQ_CI(I)]);
+      const float v0 = (float)v[0], v1 = (float)v[1];
+      sfor<kMaxQ>([&](auto Gi) {
+        constexpr int g = RTQ_CI(Gi);
+        if (g < G) {
+          acc[g][0] = __builtin_fmaf(wg[g], v0, acc[g][0]);
+          acc[g][1] = __builtin_fmaf(wg[g], v1, acc[g][1]);
+        }
+      });
+    }
+  });
+  int plane = ph;
+  if constexpr (WL::PAIRS < 64) {
+    // d = 64: the wave's two phases (lanes 0-31, 32-63) are summed here
+    sfor<kMaxQ>([&](auto Gi) {
+      sfor<2>([&](auto E) {
+        const float x = acc[RTQ_CI(Gi)][RTQ_CI(E)];
+        const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        acc[RTQ_CI(Gi)][RTQ_CI(E)] = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+      });
+    });
+    plane = w;
+  }
+  if (WL::PAIRS >= 64 || lane < 32) {
+    sfor<kMaxQ>([&](auto Gi) {
+      constexpr int g = RTQ_CI(Gi);
+      if (g < G)
+        *reinterpret_cast<float2*>(red + (plane * kMaxQ + g) * D + 2 * pr) = make_float2(acc[g][0], acc[g][1]);
+    });
+  }
+  __syncthreads();
+  for (int idx = t; idx < G * D; idx += 64 * kWavesPerStream) {
+    const int g = idx / D, dim = idx - g * D;
+    float sum = 0.0f;
+    sfor<WL::PLANES>([&](auto P) { sum += red[(RTQ_CI(P) * kMaxQ + g) * D + dim]; });
+    red[g * D + dim] = sign_bit(seed_v, (uint32_t)dim) ? -sum : sum;  // plane 0 becomes ows
+  }
+  __syncthreads();
+}
+
 // This lane's source addresses for token 0 of a chunk (the same pieces as
 // issue_chunk), so that a full chunk's loads cost one 64-bit add each: chunk
 // tok0 reads base + tok0 * (bytes per token step).  Only a stream's last,
@@ -767,6 +963,15 @@ attn_decode_kernel(Params p) {
     }
   }
 
+  // The fp16 window's loads go out now when this workgroup is the only one
+  // of its stream (their latency then overlaps the merge); with token splits
+  // only the workgroup that merges them reads the window.
+  const bool has_window = p.win != nullptr && p.win_tokens > 0;
+  const int64_t wrow_k = ((int64_t)layer * 2 * p.streams + stream) * p.win_cap;
+  const int64_t wrow_v = wrow_k + (int64_t)p.streams * p.win_cap;
+  WindowRegs<D> wregs;
+  if (has_window && p.splits == 1) wregs.load(p, wrow_k, wrow_v, qrow, G);
+
   // ---- merge the partials of each stream's waves ----
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
@@ -798,6 +1003,8 @@ attn_decode_kernel(Params p) {
     if constexpr (C::DENSE_ROT) vt_all[dim * kMaxQ + g] = val;
     else stage_all[g * C::QROW + dim] = val;
   };
+  // the int4 part's running max and denominator per query (window merge)
+  __shared__ float mq[kMaxQ], lq[kMaxQ];
   float* const mine = p.splits > 1 ? p.part + ((int64_t)pair * p.splits + split) * part_floats(G, D) : nullptr;
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int g = idx / D, dim = idx % D;
@@ -810,7 +1017,12 @@ attn_decode_kernel(Params p) {
       num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
     }
     if (p.splits == 1) {
-      put_out(g, dim, num / (den * kVShift));  // den >= 1: the max score has weight 1
+      // den >= 1 when the stream has int4 tokens (the max score has weight 1)
+      put_out(g, dim, den > 0.0f ? num / (den * kVShift) : 0.0f);
+      if (dim == 0) {
+        mq[g] = mx;
+        lq[g] = den;
+      }
     } else {
       publish(mine + idx, num);
       if (dim == 0) {
@@ -846,11 +1058,30 @@ attn_decode_kernel(Params p) {
         den = __builtin_fmaf(f, collect(ps + G * D + G + g), den);
         num = __builtin_fmaf(f, collect(ps + idx), num);
       }
-      put_out(g, dim, num / (den * kVShift));
+      put_out(g, dim, den > 0.0f ? num / (den * kVShift) : 0.0f);
+      if (dim == 0) {
+        mq[g] = mx;
+        lq[g] = den;
+      }
     }
     if (threadIdx.x == 0) __hip_atomic_store(p.count + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+
+  // ---- the fp16 window's part (the merge area of ring slot 0 is free now) ----
+  // weights and coef at the start of ring slot 0; the phase sums after them
+  // at d = 256 (ring slot 1 holds the rotation area there), else in ring slot 1
+  using WL = WindowLds<D>;
+  float* const wsc = reinterpret_cast<float*>(slot0);     // [kMaxWindow][kMaxQ] weights
+  float* const coef = wsc + kMaxWindow * kMaxQ;            // [kMaxQ]
+  float* const ows = reinterpret_cast<float*>(C::DENSE_ROT ? slot0 + WL::WEIGHT_BYTES : slot1);  // [kMaxQ][D]
+  static_assert(C::DENSE_ROT ? WL::WEIGHT_BYTES + WL::RED_BYTES <= C::SLOT_ARRAY
+                             : WL::WEIGHT_BYTES <= C::SLOT_ARRAY && WL::RED_BYTES <= C::SLOT_ARRAY,
+                "the window area fits the free ring slots");
+  if (has_window) {
+    if (p.splits > 1) wregs.load(p, wrow_k, wrow_v, qrow, G);
+    window_part<D>(p, wregs, G, seed_of_row(p, row_v), mq, lq, wsc, coef, ows);
+  }
 
   // ---- rotate the outputs back: o = D_V R^T o_rot ----
   if constexpr (C::DENSE_ROT) {
@@ -860,17 +1091,21 @@ attn_decode_kernel(Params p) {
     __syncthreads();
     const float sv = sign_bit(seed_of_row(p, row_v), (uint32_t)t) ? -1.0f : 1.0f;
     _Float16* o16 = reinterpret_cast<_Float16*>(p.out);
+    auto store = [&](int g, float u) {
+      if (has_window) u = __builtin_fmaf(coef[g], u, ows[g * D + t]);
+      o16[(qrow + g) * D + t] = (_Float16)(sv * u);
+    };
     if (G <= 4) {
       float u[4];
       dense_inverse<ROT, 4>(vt_all, tw, t, u);
       sfor<4>([&](auto Gi) {
-        if (RTQ_CI(Gi) < G) o16[(qrow + RTQ_CI(Gi)) * D + t] = (_Float16)(sv * u[RTQ_CI(Gi)]);
+        if (RTQ_CI(Gi) < G) store(RTQ_CI(Gi), u[RTQ_CI(Gi)]);
       });
     } else {
       float u[kMaxQ];
       dense_inverse<ROT, kMaxQ>(vt_all, tw, t, u);
       sfor<kMaxQ>([&](auto Gi) {
-        if (RTQ_CI(Gi) < G) o16[(qrow + RTQ_CI(Gi)) * D + t] = (_Float16)(sv * u[RTQ_CI(Gi)]);
+        if (RTQ_CI(Gi) < G) store(RTQ_CI(Gi), u[RTQ_CI(Gi)]);
       });
     }
   } else if (lead) {
@@ -889,6 +1124,18 @@ attn_decode_kernel(Params p) {
       } else {
         fwht_f32<D>(z);
         sfor<D>([&](auto I) { u[RTQ_CI(I)] = z[RTQ_CI(I)] * InvSqrt<D>::value; });
+      }
+      if (has_window) {
+        const float a = coef[lane];
+        const float* wrow = ows + lane * D;
+        sfor<D / 4>([&](auto I) {
+          constexpr int i = RTQ_CI(I);
+          const float4 f = *reinterpret_cast<const float4*>(wrow + 4 * i);
+          u[4 * i] = __builtin_fmaf(a, u[4 * i], f.x);
+          u[4 * i + 1] = __builtin_fmaf(a, u[4 * i + 1], f.y);
+          u[4 * i + 2] = __builtin_fmaf(a, u[4 * i + 2], f.z);
+          u[4 * i + 3] = __builtin_fmaf(a, u[4 * i + 3], f.w);
+        });
       }
       uint4* dst = p.out + (qrow + lane) * (D / 8);
       sfor<D / 8>([&](auto I) {
@@ -972,8 +1219,8 @@ bool overlaps(const void* a, __int128 na, const void* b, __int128 nb) {
 
 rtq_status run(int rot, const void* q, const void* codes, const void* scales, void* out, int32_t layers,
                int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d, int32_t group, const int64_t (&st)[4],
-               uint64_t seed, int64_t rps, int32_t period, float softmax_scale, void* workspace,
-               size_t workspace_size, hipStream_t stream) {
+               uint64_t seed, int64_t rps, int32_t period, float softmax_scale, const void* win, int32_t win_cap,
+               int32_t win_tokens, void* workspace, size_t workspace_size, hipStream_t stream) {
   if (layers < 0 || streams < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
@@ -987,20 +1234,28 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   if (q_per_kv < 1) return RTQ_ERR_INVALID_ARG;
   if (q_per_kv > kMaxQ) return RTQ_ERR_UNSUPPORTED;
+  if (win_tokens < 0 || win_cap < 0 || (win == nullptr && win_tokens != 0)) return RTQ_ERR_INVALID_ARG;
+  if (win_tokens > kMaxWindow) return RTQ_ERR_UNSUPPORTED;
+  if (win_tokens > win_cap || (win != nullptr && !aligned16(win))) return RTQ_ERR_INVALID_ARG;
   if (layers == 0 || streams == 0) return RTQ_OK;
-  if (tokens < 1 || tokens > 0x7fffff00) return RTQ_ERR_INVALID_ARG;
+  // the int4 prefix may be empty only when the window holds the tokens
+  if (tokens < (win_tokens > 0 ? 0 : 1) || tokens > 0x7fffff00) return RTQ_ERR_INVALID_ARG;
   const int64_t wgs = (int64_t)layers * streams;
   if (wgs > 0x7fffffff) return RTQ_ERR_INVALID_ARG;
   if (!q || !codes || !scales || !out) return RTQ_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(codes) || !aligned16(scales) || !aligned16(out)) return RTQ_ERR_INVALID_ARG;
   if ((workspace == nullptr) != (workspace_size == 0) || !aligned16(workspace)) return RTQ_ERR_INVALID_ARG;
-  // largest row the kernel reads, in 128-bit arithmetic
-  const __int128 max_row = (__int128)(layers - 1) * st[0] + st[1] + (__int128)(streams - 1) * st[2] +
-                           (__int128)(tokens - 1) * st[3];
+  // largest row the kernel reads, in 128-bit arithmetic (none without int4 tokens)
+  const __int128 max_row = tokens == 0 ? -1 : (__int128)(layers - 1) * st[0] + st[1] +
+                                                  (__int128)(streams - 1) * st[2] + (__int128)(tokens - 1) * st[3];
   if (max_row >= ((__int128)1 << 56)) return RTQ_ERR_INVALID_ARG;
-  if (!seeds_constant(layers, streams, tokens, st, rps, period)) return RTQ_ERR_INVALID_ARG;
+  if (tokens > 0 && !seeds_constant(layers, streams, tokens, st, rps, period)) return RTQ_ERR_INVALID_ARG;
   const __int128 qo_bytes = (__int128)layers * streams * q_per_kv * d * 2;
   const __int128 code_bytes = (max_row + 1) * (d / 2), scale_bytes = (max_row + 1) * 2 * (d / group);
+  const __int128 win_bytes = win_tokens > 0 ? (__int128)layers * 2 * streams * win_cap * d * 2 : 0;
+  if (win_tokens > 0 && (overlaps(out, qo_bytes, win, win_bytes) ||
+                         (workspace && overlaps(workspace, workspace_size, win, win_bytes))))
+    return RTQ_ERR_INVALID_ARG;
   if (overlaps(out, qo_bytes, q, qo_bytes) || overlaps(out, qo_bytes, codes, code_bytes) ||
       overlaps(out, qo_bytes, scales, scale_bytes))
     return RTQ_ERR_INVALID_ARG;
@@ -1032,6 +1287,9 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   p.count = splits > 1 ? static_cast<uint32_t*>(workspace) : nullptr;
   p.part = splits > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ((wgs * 4 + 255) & ~(int64_t)255))
                       : nullptr;
+  p.win = win_tokens > 0 ? static_cast<const uint4*>(win) : nullptr;
+  p.win_cap = win_cap;
+  p.win_tokens = win_tokens;
   void* kargs[] = {&p};
   const hipError_t e =
       hipLaunchKernel(fn, dim3((unsigned)(wgs * splits)), dim3(64 * kWavesPerStream), kargs, 0, stream);
@@ -1051,7 +1309,22 @@ RTQ_API rtq_status srft_attn_decode(const void* q_f16, const void* codes_u8, con
                                     size_t workspace_bytes, hipStream_t stream) {
   const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
   return rtq::attn::run(0, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
-                        seed, rows_per_seed, seed_period, softmax_scale, workspace, workspace_bytes, stream);
+                        seed, rows_per_seed, seed_period, softmax_scale, nullptr, 0, 0, workspace, workspace_bytes,
+                        stream);
+}
+
+RTQ_API rtq_status srft_attn_decode_window(const void* q_f16, const void* codes_u8, const void* scales_f16,
+                                           void* out_f16, int32_t layers, int32_t streams, int32_t tokens,
+                                           int32_t q_per_kv, int32_t d, int32_t group, int64_t stride_layer,
+                                           int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                                           uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                           float softmax_scale, const void* window_f16, int32_t window_capacity,
+                                           int32_t window_tokens, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
+  return rtq::attn::run(0, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
+                        seed, rows_per_seed, seed_period, softmax_scale, window_f16, window_capacity, window_tokens,
+                        workspace, workspace_bytes, stream);
 }
 
 RTQ_API rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
@@ -1062,7 +1335,22 @@ RTQ_API rtq_status srht_attn_decode(const void* q_f16, const void* codes_u8, con
                                     size_t workspace_bytes, hipStream_t stream) {
   const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
   return rtq::attn::run(1, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
-                        seed, rows_per_seed, seed_period, softmax_scale, workspace, workspace_bytes, stream);
+                        seed, rows_per_seed, seed_period, softmax_scale, nullptr, 0, 0, workspace, workspace_bytes,
+                        stream);
+}
+
+RTQ_API rtq_status srht_attn_decode_window(const void* q_f16, const void* codes_u8, const void* scales_f16,
+                                           void* out_f16, int32_t layers, int32_t streams, int32_t tokens,
+                                           int32_t q_per_kv, int32_t d, int32_t group, int64_t stride_layer,
+                                           int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                                           uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                           float softmax_scale, const void* window_f16, int32_t window_capacity,
+                                           int32_t window_tokens, void* workspace, size_t workspace_bytes,
+                                           hipStream_t stream) {
+  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
+  return rtq::attn::run(1, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
+                        seed, rows_per_seed, seed_period, softmax_scale, window_f16, window_capacity, window_tokens,
+                        workspace, workspace_bytes, stream);
 }
 
 RTQ_API size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv,

@@ -12,8 +12,10 @@ quantized (``*_dequant_rows``); the result equals dequantizing the whole
 prefix again.
 
 Host orchestration only: every quantization and dequantization runs in the
-HIP kernels (``*_quant_append`` and ``*_dequant_rows``); PyTorch allocates
-the buffers and copies each new token into the window.
+HIP kernels (``*_quant_append`` and ``*_dequant_rows``), and ``attention``
+reads the int4 prefix and the fp16 window in one kernel
+(``*_attn_decode_window``); PyTorch allocates the buffers and copies each new
+token into the window.
 
 Layout: rows ``[layer][K, V][stream][token]`` with ``capacity`` token slots
 per stream (strides ``(2*streams*capacity, streams*capacity, capacity, 1)``),
@@ -82,6 +84,13 @@ class DecodeCache:
             self._quantize(self.window_kv, self.quantized)
             self.quantized += self.window
             self.held = 0
+
+    def attention(self, q, softmax_scale=None, out=None):
+        """One decode step of attention over everything the cache holds: q [layers, streams, q_per_kv, d]
+        fp16 attends over the int4 prefix and the fp16 window in one launch (*_attn_decode_window)."""
+        return rtq.attn_decode(self.rot, q, self.codes, self.scales, self.strides, self.quantized, self.group,
+                               self.seed, self.rows_per_seed, self.seed_period, softmax_scale, out=out,
+                               window=self.window_kv, window_tokens=self.held)
 
     def row(self, layer: int, kv: int, stream: int, token: int) -> int:
         """Cache row of (layer, kv, stream, token)."""

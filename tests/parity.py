@@ -139,6 +139,32 @@ def check_attention(o_gpu, o_orc, scales, strides, tokens, group, pairs=None):
     return worst
 
 
+def check_attention_window(o_gpu, o_orc, scales, strides, tokens, group, window, window_tokens):
+    """check_attention for attention over int4 tokens plus an fp16 window:
+    |o_gpu - o_oracle| <= 2e-3 * s_v + 1 ulp of fp16 at o_oracle + 1e-5 *
+    max |window value|.  s_v is the largest value scale of the stream's int4
+    tokens (0 without any); the window values enter exactly, so the last term
+    only covers fp32 arithmetic on them.  Returns the largest error in units
+    of the bound."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    layers, streams = o_orc.shape[:2]
+    worst = 0.0
+    for l in range(layers):
+        for s in range(streams):
+            rows = oracle.cache_rows(l, 1, s, tokens, strides)
+            sv = float(np.max(np.asarray(scales[rows], dtype=np.float64))) if tokens else 0.0
+            wmax = float(np.max(np.abs(np.asarray(window[l, 1, s, :window_tokens], dtype=np.float64)))) \
+                if window_tokens else 0.0
+            err = np.abs(o_gpu[l, s] - o_orc[l, s])
+            bound = 2e-3 * sv + fp16_ulp(o_orc[l, s]) + 1e-5 * wmax
+            if not np.all(np.isfinite(o_gpu[l, s])) or np.any(err > bound):
+                g, i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+                raise AssertionError(f"attention mismatch at layer {l} stream {s} query {g} dim {i}: gpu "
+                                     f"{o_gpu[l, s, g, i]!r} oracle {o_orc[l, s, g, i]!r} (bound {bound[g, i]:.3g})")
+            worst = max(worst, float(np.max(err / bound)))
+    return worst
+
+
 def check_forward_ext(x16, codes_gpu, scales_gpu, group, bits, lam, seed, rps=0, period=0, rot="srft"):
     """check_forward for b-bit codes and an optional lambda: scales exact (or
     one fp16 ulp apart at an fp16 rounding midpoint of absmax/2^(b-1)); codes

@@ -24,9 +24,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["rtq_attn_workspace_bytes", "rtq_status_string", "srft_attn_decode", "srft_dequant_inv",
+    assert declared_functions() == ["rtq_attn_workspace_bytes", "rtq_status_string", "srft_attn_decode",
+                                    "srft_attn_decode_window", "srft_dequant_inv",
                                     "srft_dequant_inv_ext", "srft_dequant_rows", "srft_quant_append", "srft_quant_fwd",
-                                    "srft_quant_fwd_ext", "srht_attn_decode", "srht_dequant_inv",
+                                    "srft_quant_fwd_ext", "srht_attn_decode", "srht_attn_decode_window",
+                                    "srht_dequant_inv",
                                     "srht_dequant_inv_ext", "srht_dequant_rows", "srht_quant_append", "srht_quant_fwd",
                                     "srht_quant_fwd_ext"]
 
@@ -198,6 +200,31 @@ def test_attention_workspace_size_query():
     assert f(1, 1, 2048, 8, 128) == 256 + 8 * (8 * 130) * 4       # 2048 tokens / (32 * 8)
     assert f(16, 16, 4096, 1, 64) == 1024 + 256 * 2 * 68 * 4     # 256 pairs: two per CU
     assert f(16, 17, 4096, 1, 64) == 0                            # 272 pairs: splitting needs a second round
+
+
+WIN = 0xC000000  # window (never dereferenced)
+
+
+def win_call(name, tokens=50, win=WIN, cap=16, wt=16, out=O, layers=2, streams=3, qpk=4, d=128, g=32):
+    fn = getattr(rtq.library(), name + "_window")
+    return fn(ctypes.c_void_p(Q), ctypes.c_void_p(K), ctypes.c_void_p(S_), ctypes.c_void_p(out), layers, streams,
+              tokens, qpk, d, g, 300, 150, 50, 1, 1, 0, 0, ctypes.c_float(0.125), ctypes.c_void_p(win), cap, wt,
+              ctypes.c_void_p(0), 0, None)
+
+
+@pytest.mark.parametrize("name", ATTN)
+def test_attention_window_rejects_bad_arguments(name):
+    bad = rtq.RTQ_ERR_INVALID_ARG
+    assert win_call(name, win=0, wt=4) == bad                 # window tokens without a window
+    assert win_call(name, win=WIN + 8) == bad                 # misaligned window
+    assert win_call(name, cap=8, wt=9) == bad                 # more tokens than slots
+    assert win_call(name, wt=-1) == bad
+    assert win_call(name, cap=-1, wt=0) == bad
+    assert win_call(name, tokens=0, wt=0) == bad              # no token at all
+    assert win_call(name, out=WIN + 4096) == bad              # out inside the window
+    assert win_call(name, cap=65, wt=65) == rtq.RTQ_ERR_UNSUPPORTED
+    assert win_call(name, d=96) == rtq.RTQ_ERR_UNSUPPORTED
+    assert win_call(name, layers=0) == rtq.RTQ_OK
 
 
 MAPPED = ["srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"]

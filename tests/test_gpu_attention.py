@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from tests.conftest import gpu_available
-from tests.parity import check_attention
+from tests.parity import check_attention, check_attention_window
 
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
@@ -183,6 +183,91 @@ def test_workspace_errors():
                               0, 2048, 0, 1, 1, 0, 0, 0.1, None, 64, None)  # size without a pointer
     assert st == rtq.RTQ_ERR_INVALID_ARG
     torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# The fp16 window of the newest tokens, in the same softmax as the int4 tokens.
+# ---------------------------------------------------------------------------
+
+
+def run_window_case(rot, d, g, L, S, T, W, Wc, G, seed=41, workspace=None):
+    rng = np.random.default_rng(d + g + 7 * W + T)
+    tcap = max(T, 1)
+    rps = 2 * S * tcap if L > 1 else 0
+    per = L if L > 1 else 0
+    codes, scales = make_cache(rng, L * 2 * S * tcap, d, g, seed, rps, per, rot, outliers=2)
+    win = (rng.standard_normal((L, 2, S, Wc, d)) * 1.5).astype(np.float16)
+    q16 = rng.standard_normal((L, S, G, d)).astype(np.float16)
+    print(f"window case rot={rot} d={d} g={g} L={L} S={S} T={T} W={W}/{Wc} G={G}", flush=True)
+    q = torch.from_numpy(q16).to(DEV)
+    c = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
+    sc = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
+    wt = torch.from_numpy(win).to(DEV)
+    o = rtq.attn_decode(rot, q, c, sc, lm(S, tcap), T, g, seed, rps, per, window=wt, window_tokens=W,
+                        workspace=workspace)
+    torch.cuda.synchronize()
+    o_orc = oracle.attn_decode(q16, codes, scales, lm(S, tcap), L, S, T, G, d, g, seed, rps, per, rot,
+                               window=win, window_tokens=W)
+    worst = check_attention_window(o.cpu().numpy(), o_orc, scales, lm(S, tcap), T, g, win, W)
+    print(f"  worst error / bound = {worst:.3f}", flush=True)
+    return o, (q, c, sc, wt, tcap, rps, per)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,g", ATTN)
+def test_window_joins_the_int4_tokens(rot, d, g):
+    run_window_case(rot, d, g, 2, 3, 37, 5, 16, 3)
+
+
+@pytest.mark.parametrize("d,T,W,G", [(64, 100, 64, 8), (128, 1, 16, 6), (256, 70, 1, 4), (128, 33, 63, 1)])
+def test_window_sizes(d, T, W, G):
+    run_window_case("srft", d, 32, 1, 2, T, W, max(W, 16), G)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_window_without_int4_tokens(rot, d):
+    """The first decode steps: nothing is quantized yet, the window is the whole context."""
+    run_window_case(rot, d, 32, 2, 2, 0, 7, 16, 4)
+
+
+def test_window_with_token_splits():
+    L, S, T = 1, 2, 1500
+    assert rtq.attn_workspace_bytes(L, S, T, 4, 128) > 0
+    run_window_case("srft", 128, 32, L, S, T, 16, 16, 4)
+
+
+def test_empty_window_equals_plain_attention():
+    o, (q, c, sc, wt, tcap, rps, per) = run_window_case("srft", 128, 32, 2, 2, 90, 0, 16, 5)
+    o2 = rtq.attn_decode("srft", q, c, sc, lm(2, tcap), 90, 32, 41, rps, per)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("rot,d,g", [("srft", 128, 32), ("srht", 64, 64), ("srft", 256, 32)])
+def test_decode_cache_attention(rot, d, g):
+    """DecodeCache.attention after a prefill and single-token appends: one launch over the int4 prefix
+    and the fp16 window, against the oracle on the tokens as they went in."""
+    from rotate_then_quantize_amd.decode_cache import DecodeCache
+    L, S, C, Wn, T0, K, G, seed = 2, 3, 96, 16, 20, 21, 3, 17
+    rng = np.random.default_rng(3)
+    toks = rng.standard_normal((L, 2, S, T0 + K, d)).astype(np.float16)
+    cache = DecodeCache(L, S, C, d, g, seed, rot, Wn)
+    cache.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :, :, :T0])).to(DEV))
+    for k in range(K):
+        cache.append(torch.from_numpy(np.ascontiguousarray(toks[:, :, :, T0 + k])).to(DEV))
+    q16 = rng.standard_normal((L, S, G, d)).astype(np.float16)
+    o = cache.attention(torch.from_numpy(q16).to(DEV))
+    torch.cuda.synchronize()
+    nq, held = cache.quantized, cache.held
+    print(f"decode cache attention rot={rot} d={d}: {nq} int4 tokens, {held} in the window", flush=True)
+    assert held > 0 and nq > T0
+    codes, scales = cache.codes.cpu().numpy(), cache.scales.cpu().numpy()
+    win = cache.window_kv.cpu().numpy()
+    o_orc = oracle.attn_decode(q16, codes, scales, cache.strides, L, S, nq, G, d, g, seed, cache.rows_per_seed,
+                               cache.seed_period, rot, window=win, window_tokens=held)
+    check_attention_window(o.cpu().numpy(), o_orc, scales, cache.strides, nq, g, win, held)
+    assert np.array_equal(win[:, :, :, :held], toks[:, :, :, nq:nq + held])
 
 
 def test_empty_grid_is_a_no_op():
