@@ -630,6 +630,7 @@ def attn_main(args, w, dev):
         },
         "valu": None if W else read_valu(w.name, rot, "attn_decode", w.d),
     }
+    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
     if not args.no_eager and not W:
         result["unfused_baseline"] = attn_unfused_baseline(w, rot, ms_step, dev)
     if not args.no_cpu_baseline and not W:
@@ -821,12 +822,43 @@ def ext_main(args, w, dev):
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
     }
+    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
     print(json.dumps(result), flush=True)
 
 
 def W_generate(w, dev):
     from rotate_then_quantize_amd import workloads as W
     return W.generate(w, dev)
+
+
+def measured_copy(dev, mib: int = 1024, reps: int = 10) -> dict:
+    """Achievable HBM rate: a device-to-device copy of `mib` MiB (read plus
+    written bytes over the median event-timed copy), reported beside the
+    published peak."""
+    import torch
+    nbytes = mib << 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    stream = torch.cuda.current_stream(dev)
+    b.copy_(a)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    del a, b
+    return {"GBps": 2 * nbytes / ms / 1e6, "bytes_each_way": nbytes,
+            "kind": f"torch device-to-device copy, (read + written bytes) / median of {reps} event-timed copies"}
+
+
+def with_achievable(roof: dict, copy: dict) -> dict:
+    roof["achievable"] = copy["GBps"]
+    roof["frac_of_achievable"] = roof["achieved"] / copy["GBps"]
+    return roof
 
 
 def main():
@@ -1053,6 +1085,7 @@ def main():
         },
         "valu": read_valu(w.name, rot, kname, w.d),
     }
+    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
     if not args.no_graph:
         result["graph_replay"] = graph_replay(w, sets, replicas, fwd_fn, inv_fn, args.steps, bpv)
     if not args.no_eager:
