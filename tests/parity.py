@@ -139,7 +139,7 @@ def check_attention(o_gpu, o_orc, scales, strides, tokens, group, pairs=None):
     return worst
 
 
-def check_attention_window(o_gpu, o_orc, scales, strides, tokens, group, window, window_tokens):
+def check_attention_window(o_gpu, o_orc, scales, strides, tokens, group, window, window_tokens, pairs=None):
     """check_attention for attention over int4 tokens plus an fp16 window:
     |o_gpu - o_oracle| <= 2e-3 * s_v + 1 ulp of fp16 at o_oracle + 1e-5 *
     max |window value|.  s_v is the largest value scale of the stream's int4
@@ -148,20 +148,20 @@ def check_attention_window(o_gpu, o_orc, scales, strides, tokens, group, window,
     of the bound."""
     o_gpu = np.asarray(o_gpu, dtype=np.float64)
     layers, streams = o_orc.shape[:2]
+    todo = [(l, s) for l in range(layers) for s in range(streams)] if pairs is None else pairs
     worst = 0.0
-    for l in range(layers):
-        for s in range(streams):
-            rows = oracle.cache_rows(l, 1, s, tokens, strides)
-            sv = float(np.max(np.asarray(scales[rows], dtype=np.float64))) if tokens else 0.0
-            wmax = float(np.max(np.abs(np.asarray(window[l, 1, s, :window_tokens], dtype=np.float64)))) \
-                if window_tokens else 0.0
-            err = np.abs(o_gpu[l, s] - o_orc[l, s])
-            bound = 2e-3 * sv + fp16_ulp(o_orc[l, s]) + 1e-5 * wmax
-            if not np.all(np.isfinite(o_gpu[l, s])) or np.any(err > bound):
-                g, i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
-                raise AssertionError(f"attention mismatch at layer {l} stream {s} query {g} dim {i}: gpu "
-                                     f"{o_gpu[l, s, g, i]!r} oracle {o_orc[l, s, g, i]!r} (bound {bound[g, i]:.3g})")
-            worst = max(worst, float(np.max(err / bound)))
+    for l, s in todo:
+        rows = oracle.cache_rows(l, 1, s, tokens, strides)
+        sv = float(np.max(np.asarray(scales[rows], dtype=np.float64))) if tokens else 0.0
+        wmax = float(np.max(np.abs(np.asarray(window[l, 1, s, :window_tokens], dtype=np.float64)))) \
+            if window_tokens else 0.0
+        err = np.abs(o_gpu[l, s] - o_orc[l, s])
+        bound = 2e-3 * sv + fp16_ulp(o_orc[l, s]) + 1e-5 * wmax
+        if not np.all(np.isfinite(o_gpu[l, s])) or np.any(err > bound):
+            g, i = np.unravel_index(int(np.argmax(err - bound)), err.shape)
+            raise AssertionError(f"attention mismatch at layer {l} stream {s} query {g} dim {i}: gpu "
+                                 f"{o_gpu[l, s, g, i]!r} oracle {o_orc[l, s, g, i]!r} (bound {bound[g, i]:.3g})")
+        worst = max(worst, float(np.max(err / bound)))
     return worst
 
 

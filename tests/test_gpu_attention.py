@@ -334,3 +334,36 @@ def test_workload_full_size_sampled(wid):
     print(f"  sampled pairs {pairs}: worst error / (2e-3 s_v) = {worst:.3f}", flush=True)
     del codes, scales, q, o
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wid,win", [(3, 0), (3, 16), (2, 16), (5, 16)])
+def test_bench_launch_full_size_sampled(wid, win):
+    """The launch that the attention bench times, at full size: the per-head
+    [layer][K, V][stream][token] layout with one sign seed per layer, the
+    binding's token-split workspace, and (win > 0) that many fp16 window
+    tokens per stream; sampled (layer, stream) pairs against the oracle."""
+    w = W.WORKLOADS[wid]
+    L, S, T, G, d, g = w.layers, w.streams, w.tokens, w.q_per_kv, w.d, w.group
+    strides = (2 * S * T, S * T, T, 1)
+    rps, per = (2 * S * T, L) if L > 1 else (0, 0)
+    codes, scales = random_cache(L * 2 * S * T, d, g, 300 + wid)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(400 + wid)
+    q = torch.randn((L, S, G, d), generator=gen, device=DEV).to(torch.float16)
+    window = torch.randn((L, 2, S, max(win, 1), d), generator=gen, device=DEV).to(torch.float16)
+    print(f"bench launch {w.name}: L={L} S={S} T={T} G={G} window={win} "
+          f"splits workspace={rtq.attn_workspace_bytes(L, S, T, G, d)} B", flush=True)
+    o = rtq.srft_attn_decode(q, codes, scales, strides, T, g, w.sign_seed, rps, per,
+                             window=window if win else None, window_tokens=win)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(wid + win)
+    extra = 3 if T <= 4096 else 0  # a 32768-token d = 256 stream takes the oracle a few seconds
+    pairs = [(0, 0), (L - 1, S - 1)] + [(int(rng.integers(L)), int(rng.integers(S))) for _ in range(extra)]
+    qh, ch, sh, oh = q.cpu().numpy(), codes.cpu().numpy(), scales.cpu().numpy(), o.cpu().numpy()
+    wh = window.cpu().numpy()
+    o_orc = oracle.attn_decode(qh, ch, sh, strides, L, S, T, G, d, g, w.sign_seed, rps, per, "srft", pairs=pairs,
+                               window=wh if win else None, window_tokens=win)
+    worst = check_attention_window(oh, o_orc, sh, strides, T, g, wh, win, pairs=pairs)
+    print(f"  sampled pairs {pairs}: worst error / bound = {worst:.3f}", flush=True)
+    del codes, scales, q, o, window
+    torch.cuda.empty_cache()
