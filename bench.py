@@ -643,7 +643,9 @@ def decode_cache_main(args, w, dev):
     """Per-step cost of keeping a dequantized fp16 prefix with a 16-token fp16
     window (append each token to the window; every 16th step quantize the
     window in place and dequantize just those rows), against dequantizing
-    the whole cache every step."""
+    the whole cache every step; and a whole decode step whose consumer is
+    the int4 attention (append + one attention launch, no dequantized
+    copy)."""
     import torch
     import rotate_then_quantize_amd as rtq
     from rotate_then_quantize_amd.decode_cache import DecodeCache
@@ -702,10 +704,32 @@ def decode_cache_main(args, w, dev):
     ev[1].record(stream)
     torch.cuda.synchronize()
     full_ms = ev[0].elapsed_time(ev[1]) / full_steps
+    # A whole decode step with the int4 attention as the consumer (no dequantized copy kept): append the
+    # token (every 16th step quantizes the window in place), then one attention launch over the int4
+    # prefix and the fp16 window.
+    del y
+    lean = DecodeCache(L, S, T + args.warmup + steps, d, g, w.sign_seed, rot, W, dev, keep_prefix=False)
+    lean.prefill(torch.randn((L, 2, S, T, d), generator=gen, device=dev).to(torch.float16))
+    q = torch.randn((L, S, w.q_per_kv, d), generator=gen, device=dev).to(torch.float16)
+    o = torch.empty_like(q)
+    for i in range(args.warmup):
+        lean.append(new[i])
+        lean.attention(q, out=o)
+    torch.cuda.synchronize()
+    dsteps = steps  # a multiple of 16: every phase of the window schedule equally often
+    ev[0].record(stream)
+    for i in range(dsteps):
+        lean.append(new[i])
+        lean.attention(q, out=o)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    decode_ms = ev[0].elapsed_time(ev[1]) / dsteps
+    del lean
     rows_flush = L * 2 * S * W
     bpv = w.bytes_per_vector()
     log(f"window policy {window_ms * 1e3:.1f} us/step | flush: append {append_ms * 1e3:.1f} us + refresh "
-        f"{rows_ms * 1e3:.1f} us ({rows_flush} rows) | full re-dequantize {full_ms * 1e3:.1f} us/step")
+        f"{rows_ms * 1e3:.1f} us ({rows_flush} rows) | full re-dequantize {full_ms * 1e3:.1f} us/step | "
+        f"decode step with int4 attention {decode_ms * 1e3:.1f} us")
     result = {
         "metric": "decode-step cache maintenance time, dequantized prefix + 16-token fp16 window, 1 GPU",
         "value": window_ms * 1e3,
@@ -726,6 +750,10 @@ def decode_cache_main(args, w, dev):
         "full_redequantize": {"us_per_step": full_ms * 1e3, "rows": n_all,
                               "ops": "append of the new token + dequant_inv of every cache row, each step"},
         "speedup_vs_full_redequantize": full_ms / window_ms,
+        "decode_step_with_int4_attention": {
+            "us_per_step": decode_ms * 1e3, "steps": dsteps, "q_per_kv": w.q_per_kv,
+            "ops": "append of the new token (the window quantized in place every 16th step) + one "
+                   "attention launch over the int4 prefix and the fp16 window; no dequantized copy kept"},
     }
     print(json.dumps(result), flush=True)
 

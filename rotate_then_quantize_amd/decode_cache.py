@@ -17,6 +17,11 @@ reads the int4 prefix and the fp16 window in one kernel
 (``*_attn_decode_window``); PyTorch allocates the buffers and copies each new
 token into the window.
 
+With ``keep_prefix=False`` no dequantized copy is kept: a consumer that
+reads the int4 prefix directly (``attention``) needs none, which saves its
+memory (3.5x the int4 cache at d = 128, g = 32) and the refresh on every
+flush.
+
 Layout: rows ``[layer][K, V][stream][token]`` with ``capacity`` token slots
 per stream (strides ``(2*streams*capacity, streams*capacity, capacity, 1)``),
 one sign seed per layer (``rows_per_seed = 2*streams*capacity``,
@@ -29,7 +34,7 @@ import rotate_then_quantize_amd as rtq
 
 class DecodeCache:
     def __init__(self, layers: int, streams: int, capacity: int, d: int, group: int, seed: int,
-                 rot: str = "srft", window: int = 16, device="cuda"):
+                 rot: str = "srft", window: int = 16, device="cuda", keep_prefix: bool = True):
         import torch
         if min(layers, streams, capacity, window) < 1:
             raise ValueError("layers, streams, capacity and window must be positive")
@@ -42,7 +47,8 @@ class DecodeCache:
         self.rows_per_seed, self.seed_period = (2 * streams * capacity, layers) if layers > 1 else (0, 0)
         self.codes = torch.zeros((n, d // 2), dtype=torch.uint8, device=device)
         self.scales = torch.zeros((n, d // group), dtype=torch.float16, device=device)
-        self.prefix = torch.zeros((n, d), dtype=torch.float16, device=device)  # dequantized copy
+        # dequantized copy (None without keep_prefix)
+        self.prefix = torch.zeros((n, d), dtype=torch.float16, device=device) if keep_prefix else None
         self.window_kv = torch.zeros((layers, 2, streams, window, d), dtype=torch.float16, device=device)
         self.quantized = 0  # tokens in the int4 cache (and in the dequantized copy)
         self.held = 0       # tokens in the fp16 window
@@ -53,12 +59,13 @@ class DecodeCache:
 
     def _quantize(self, block, t0: int) -> None:
         """block [layers, 2, streams, n, d] fp16 -> cache tokens t0 .. t0+n-1, then refresh their rows of the
-        dequantized copy."""
+        dequantized copy (if one is kept)."""
         n = block.shape[3]
         rtq.quant_append(self.rot, block, self.codes, self.scales, self.strides, t0, self.group, self.seed,
                          self.rows_per_seed, self.seed_period)
-        rtq.dequant_rows(self.rot, self.codes, self.scales, self.prefix, self.layers, self.streams, t0, n,
-                         self.strides, self.group, self.seed, self.rows_per_seed, self.seed_period)
+        if self.prefix is not None:
+            rtq.dequant_rows(self.rot, self.codes, self.scales, self.prefix, self.layers, self.streams, t0, n,
+                             self.strides, self.group, self.seed, self.rows_per_seed, self.seed_period)
 
     def prefill(self, kv) -> None:
         """Quantize a prompt's K/V, kv [layers, 2, streams, tokens, d] fp16, into an empty cache."""
@@ -73,7 +80,7 @@ class DecodeCache:
 
     def append(self, kv) -> None:
         """Add one token's K/V, kv [layers, 2, streams, d] fp16.  It stays in the fp16 window; when the window
-        is full, the whole window is quantized into the cache and the dequantized copy refreshed."""
+        is full, the whole window is quantized into the cache and the dequantized copy (if kept) refreshed."""
         if tuple(kv.shape) != (self.layers, 2, self.streams, self.d):
             raise ValueError(f"kv must be [{self.layers}, 2, {self.streams}, {self.d}]")
         if self.tokens + 1 > self.capacity:

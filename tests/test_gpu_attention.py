@@ -268,6 +268,16 @@ def test_decode_cache_attention(rot, d, g):
                                cache.seed_period, rot, window=win, window_tokens=held)
     check_attention_window(o.cpu().numpy(), o_orc, scales, cache.strides, nq, g, win, held)
     assert np.array_equal(win[:, :, :, :held], toks[:, :, :, nq:nq + held])
+    # without the dequantized copy: the same int4 cache, window and attention output
+    lean = DecodeCache(L, S, C, d, g, seed, rot, Wn, keep_prefix=False)
+    lean.prefill(torch.from_numpy(np.ascontiguousarray(toks[:, :, :, :T0])).to(DEV))
+    for k in range(K):
+        lean.append(torch.from_numpy(np.ascontiguousarray(toks[:, :, :, T0 + k])).to(DEV))
+    o2 = lean.attention(torch.from_numpy(q16).to(DEV))
+    torch.cuda.synchronize()
+    assert lean.prefix is None and (lean.quantized, lean.held) == (nq, held)
+    assert torch.equal(lean.codes, cache.codes) and torch.equal(lean.scales, cache.scales)
+    assert torch.equal(o2, o)
 
 
 def test_empty_grid_is_a_no_op():
