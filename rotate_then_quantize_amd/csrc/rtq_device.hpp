@@ -492,41 +492,47 @@ __device__ __forceinline__ void fwht_f32(float (&v)[N]) {
 // Symmetric absmax int4 quantizer and nibble packing.
 // ---------------------------------------------------------------------------
 
+// One group (GI) of quantize_pack below.
+template <int GI, int D, int G>
+__device__ __forceinline__ void quantize_pack_group(const float (&z)[D], float zs, uint32_t (&cw)[D / 8],
+                                                    uint32_t (&sb)[D / G]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  constexpr int g0 = GI * G;
+  float a = 0.0f;
+  sfor<G>([&](auto I) { a = fmaxf(a, fabsf(z[g0 + RTQ_CI(I)])); });
+  a *= zs;
+  uint32_t bits = __half_as_ushort(__float2half_rn(a * 0.125f));
+  bits = bits < 0x7bffu ? bits : 0x7bffu;  // saturate (inf -> 65504)
+  sb[GI] = bits;
+  const float s = __half2float(__ushort_as_half((unsigned short)bits));
+  const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
+  sfor<G / 8>([&](auto W) {
+    constexpr int base = g0 + RTQ_CI(W) * 8;
+    uint32_t b[8];
+    sfor<8>([&](auto I) {
+      const float t = __builtin_fmaf(z[base + RTQ_CI(I)], inv, kMagic);
+      b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic - 8.0f, kMagic + 7.0f));
+    });
+    // low bytes of the even codes -> E, of the odd codes -> O
+    const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) |
+                       __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
+    const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) |
+                       __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
+    cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+  });
+}
+
 // Per group of G consecutive values of (zs * z): s = fp16_rne(absmax / 8)
 // saturated at 65504; q = clamp(rne(zs * z / s), -8, 7), q = 0 when s == 0.
 // Codes: cw[w] holds values 8w .. 8w+7, value 2i in the low nibble of byte i.
 // The rounding uses fma(z, 1/s, 1.5 * 2^23): the fp32 result lies in
 // [2^23, 2^24) where the spacing is 1, so the single rounding of the fma is
 // round-half-even of z/s, and the low 4 bits of the result are q mod 16.
+// quantize_pack_group does one group (GI) of this.
 template <int D, int G>
 __device__ __forceinline__ void quantize_pack(const float (&z)[D], float zs, uint32_t (&cw)[D / 8],
                                               uint32_t (&sb)[D / G]) {
-  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
-  sfor<D / G>([&](auto GI) {
-    constexpr int g0 = RTQ_CI(GI) * G;
-    float a = 0.0f;
-    sfor<G>([&](auto I) { a = fmaxf(a, fabsf(z[g0 + RTQ_CI(I)])); });
-    a *= zs;
-    uint32_t bits = __half_as_ushort(__float2half_rn(a * 0.125f));
-    bits = bits < 0x7bffu ? bits : 0x7bffu;  // saturate (inf -> 65504)
-    sb[RTQ_CI(GI)] = bits;
-    const float s = __half2float(__ushort_as_half((unsigned short)bits));
-    const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
-    sfor<G / 8>([&](auto W) {
-      constexpr int base = g0 + RTQ_CI(W) * 8;
-      uint32_t b[8];
-      sfor<8>([&](auto I) {
-        const float t = __builtin_fmaf(z[base + RTQ_CI(I)], inv, kMagic);
-        b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic - 8.0f, kMagic + 7.0f));
-      });
-      // low bytes of the even codes -> E, of the odd codes -> O
-      const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) |
-                         __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
-      const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) |
-                         __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
-      cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
-    });
-  });
+  sfor<D / G>([&](auto GI) { quantize_pack_group<RTQ_CI(GI), D, G>(z, zs, cw, sb); });
 }
 
 // fp16 half SEL of a, times b, plus c, in fp32 with a single rounding.

@@ -154,6 +154,8 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
     lds_sync();
     float L[128];
     float zs;
+    constexpr int CWW = 4 * B;  // code words of the lane's half row
+    uint32_t cw[CWW], sb[128 / G];
     if constexpr (ROT == kSRFT) {
       float fr[65], fi[65];  // unnormalized; sqrt(2/256) is applied by the quantizer
       if (lam != nullptr) {
@@ -170,13 +172,14 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       int addr_e = v * 4, addr_o = (v + 32) * 4;
       auto shf = [](float x, int addr) { return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x))); };
       // slot 0: E_0 + sigma * O_0 (real)
-      {
+      auto bin0 = [&]() {
         const float e0 = shf(fr[0], addr_e), o0 = shf(fr[0], addr_o);
         constexpr float r2 = 0.70710678118654752440f;  // real end bins: 1/16 = sqrt(2/256) / sqrt(2)
         L[0] = __builtin_fmaf(sigma, o0, e0) * r2;
-      }
-      sfor<63>([&](auto A) {
-        constexpr int a = RTQ_CI(A) + 1;
+      };
+      // bin a = 1 .. 63: slots 2a - 1 and 2a
+      auto bin = [&](auto A) {
+        constexpr int a = RTQ_CI(A);
         const float er = shf(fr[a], addr_e), ei = shf(fi[a], addr_e);
         const float orr = shf(fr[a], addr_o), oi = shf(fi[a], addr_o);
         constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);  // w^a = c - i s
@@ -187,12 +190,36 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
         L[2 * a - 1] = p ? ri : rr;
         L[2 * a] = p ? rr : ri;
         if constexpr (a % 4 == 0) asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(L[2 * a]));
-      });
-      {  // slot 64: X_64 = E_64 - i O_64; lane 0 keeps Re, lane 1 keeps Im
+      };
+      // slot 127: X_64 = E_64 - i O_64; lane 0 keeps Re, lane 1 keeps Im
+      auto bin64 = [&]() {
         const float e64 = shf(fr[64], addr_e), o64 = shf(fr[64], addr_o);
         L[127] = p ? -o64 : e64;
-      }
+      };
+      // later shuffles wait for w
+      auto after = [&](uint32_t w) { asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(w)); };
       zs = SrftScale<256>::value;
+      if constexpr (B == 4) {
+        // Quantize each group as soon as the bins that fill it are exchanged:
+        // the finished coordinates of at most one group are then live, not
+        // all 128 (they had been spilled at three waves per SIMD).  Group gi
+        // holds slots gi*G .. gi*G+G-1; bin a fills slots 2a-1 and 2a.
+        sfor<128 / G>([&](auto GI) {
+          constexpr int gi = RTQ_CI(GI), lo = gi * G, hi = lo + G - 1;
+          constexpr int a0 = lo / 2 + 1, a1 = (hi + 1) / 2 < 63 ? (hi + 1) / 2 : 63;
+          if constexpr (gi == 0) bin0();
+          sfor<a1 - a0 + 1>([&](auto K) { bin(ic<a0 + RTQ_CI(K)>{}); });
+          if constexpr (hi == 127) bin64();
+          quantize_pack_group<gi, 128, G>(L, zs, cw, sb);
+          // the next group's shuffles wait for this group's codes (else the
+          // compiler sinks every group's quantization below all shuffles)
+          if constexpr (hi < 127) after(cw[(lo + G) / 8 - 1]);
+        });
+      } else {
+        bin0();
+        sfor<63>([&](auto A) { bin(ic<RTQ_CI(A) + 1>{}); });
+        bin64();
+      }
     } else {
       float f[128];
       if (lam != nullptr) {
@@ -207,8 +234,6 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       });
       zs = 1.0f / 16.0f;
     }
-    constexpr int CWW = 4 * B;  // code words of the lane's half row
-    uint32_t cw[CWW], sb[128 / G];
     if constexpr (B != 4) {
       // SRFT lane 1 holds its half mirrored: put it in natural order first
       // (a b-bit stream has no cheap field reversal), then quantize
@@ -219,17 +244,16 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       } else {
         quantize_pack_bits<128, G, B>(L, zs, cw, sb);
       }
-    } else {
-    quantize_pack<128, G>(L, zs, cw, sb);
-    if constexpr (ROT == kSRFT) {
-      // lane 1: codes and scales are in mirrored order -> reverse them
+    } else if constexpr (ROT == kSRFT) {
+      // (quantized above) lane 1: codes and scales are in mirrored order -> reverse them
       uint32_t rev[16];
       sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
       sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
       uint32_t sr[128 / G];
       sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
       sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
-    }
+    } else {
+      quantize_pack<128, G>(L, zs, cw, sb);
     }
     if (v < rows) {
       const size_t row = R.cache_row(v);
