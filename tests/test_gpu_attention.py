@@ -219,9 +219,13 @@ def test_window_joins_the_int4_tokens(rot, d, g):
     run_window_case(rot, d, g, 2, 3, 37, 5, 16, 3)
 
 
-@pytest.mark.parametrize("d,T,W,G", [(64, 100, 64, 8), (128, 1, 16, 6), (256, 70, 1, 4), (128, 33, 63, 1)])
-def test_window_sizes(d, T, W, G):
-    run_window_case("srft", d, 32, 1, 2, T, W, max(W, 16), G)
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,T,W,G", [(64, 100, 64, 8), (128, 1, 16, 6), (256, 70, 1, 4), (128, 33, 63, 1),
+                                     (256, 40, 64, 8), (128, 300, 64, 8)])
+def test_window_sizes(rot, d, T, W, G):
+    """Window sizes up to the 64-token limit, with up to 8 queries per K/V head (the largest window
+    work area)."""
+    run_window_case(rot, d, 32, 1, 2, T, W, max(W, 16), G)
 
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
