@@ -48,11 +48,13 @@ namespace rtq {
 
 // One forward tile: rows row0 .. row0 + rows - 1, lane l owning row row0 + l.
 // kUniform: every row has seed s (masks are scalar); otherwise s is the
-// lane's own seed.
-template <int D, int G, int ROT, bool kUniform>
+// lane's own seed.  LAM: each channel i is first multiplied by lam_i (d fp16
+// values, a per-channel scale), as in the width-and-lambda entry points.
+template <int D, int G, int ROT, bool kUniform, bool LAM = false>
 __device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint4* __restrict__ ct,
                                               uint8_t* __restrict__ st, int rows, const SignTable& tb,
-                                              uint32_t j, uint64_t s, uint4* buf, int lane) {
+                                              uint32_t j, uint64_t s, uint4* buf, int lane,
+                                              const uint32_t* __restrict__ lam = nullptr) {
   constexpr int CPR = D / 8;  // 16-byte chunks per input row
   constexpr int CW = D / 32;  // 16-byte chunks per code row
   load_tile_to_lds<CPR>(xt, rows, buf, lane);
@@ -65,7 +67,8 @@ __device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint
   if constexpr (kUniform) sg.apply(h);
   else apply_lane_signs<D>(h, s);
   uint32_t cw[D / 8], sb[D / G];
-  quantize_row<D, G, ROT>(h, cw, sb);
+  if constexpr (LAM) quantize_row_lambda<D, G, ROT>(h, lam, cw, sb);
+  else quantize_row<D, G, ROT>(h, cw, sb);
   // codes leave through LDS (the input tile is no longer needed)
   lds_sync();
   sfor<CW>([&](auto C) {
@@ -78,6 +81,28 @@ __device__ __forceinline__ void fwd_lane_tile(const uint4* __restrict__ xt, uint
     if (c / CW < rows) stream_store(ct + (uint32_t)c, buf[c]);
   });
   if (lane < rows) store_row_scales<D, G>(st, (uint32_t)lane, sb);
+}
+
+// The forward step with a per-channel lambda (the plain kernel below writes
+// the same steps out without it).
+template <int D, int G, int ROT, bool LAM>
+__device__ __forceinline__ void fwd_lane_body(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                              uint8_t* __restrict__ scales, const uint32_t* __restrict__ lam,
+                                              uint32_t n, const SeedRule& sr, const SignTable& tb) {
+  constexpr int CPR = D / 8;
+  constexpr int CW = D / 32;
+  __shared__ uint4 buf[64 * CPR];
+  const int lane = threadIdx.x;
+  const uint32_t row0 = blockIdx.x * 64u;
+  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+  const uint4* xt = x + (size_t)row0 * CPR;
+  uint4* ct = codes + (size_t)row0 * CW;
+  uint8_t* st = scales + (size_t)row0 * (2 * D / G);
+  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+  if (b0 == b1)
+    fwd_lane_tile<D, G, ROT, true, LAM>(xt, ct, st, rows, tb, seed_offset(b0, sr), sr.seed, buf, lane, lam);
+  else
+    fwd_lane_tile<D, G, ROT, false, LAM>(xt, ct, st, rows, tb, 0, lane_seed(sr, row0, rows, lane), buf, lane, lam);
 }
 
 // Forward step, one 64-row tile per wave.
@@ -96,6 +121,16 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
   const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
   if (b0 == b1) fwd_lane_tile<D, G, ROT, true>(xt, ct, st, rows, tb, seed_offset(b0, sr), sr.seed, buf, lane);
   else fwd_lane_tile<D, G, ROT, false>(xt, ct, st, rows, tb, 0, lane_seed(sr, row0, rows, lane), buf, lane);
+}
+
+// The same with a per-channel lambda (4-bit codes of the width-and-lambda
+// entry points).
+template <int D, int G, int ROT>
+__global__ __launch_bounds__(64) void fwd_lane_lambda_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales,
+                                                             const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr,
+                                                             SignTable tb) {
+  fwd_lane_body<D, G, ROT, true>(x, codes, scales, lam, n, sr, tb);
 }
 
 // Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
@@ -117,14 +152,16 @@ __device__ __forceinline__ void load_codes_to_lds(const uint4* __restrict__ ct, 
 // The code block arrives coalesced in LDS, each lane reads its own row, and
 // the fp16 output leaves through the same LDS buffer (padded rows) as
 // coalesced 16-byte stores.
-template <int D, int G, int ROT, bool kUniform>
+template <int D, int G, int ROT, bool kUniform, bool LAM = false>
 __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, const uint8_t* __restrict__ st,
                                               uint4* __restrict__ yt, int rows, const SignTable& tb, uint32_t j,
-                                              uint64_t s, uint4* lds, int lane) {
+                                              uint64_t s, uint4* lds, int lane,
+                                              const uint32_t* __restrict__ lam = nullptr, float* inv_lam = nullptr) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
   const uint32_t r = (uint32_t)(lane < rows ? lane : rows - 1);
   load_codes_to_lds<CW>(ct, rows, lds, lane);
+  if constexpr (LAM) lambda_reciprocals<D>(lam, inv_lam, lane);  // read after the barrier below
   uint32_t sb[D / G];
   load_row_scales<D, G>(st, r, sb);
   UniformSigns<D> sg;
@@ -147,6 +184,7 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
     dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
     fwht_f32<D>(u);
   }
+  if constexpr (LAM) lambda_unweight_lds<D>(u, inv_lam);  // the per-channel lambda divided out
   uint32_t h[D / 2];
   sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   if constexpr (kUniform) sg.apply(h);
@@ -177,6 +215,31 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   });
 }
 
+// The inverse step with a per-channel lambda (the plain kernel below writes
+// the same steps out without it).
+template <int D, int G, int ROT, bool LAM>
+__device__ __forceinline__ void inv_lane_body(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                              uint4* __restrict__ y, const uint32_t* __restrict__ lam, uint32_t n,
+                                              const SeedRule& sr, const SignTable& tb) {
+  constexpr int CPR = D / 8;
+  constexpr int CW = D / 32;
+  constexpr int LT = 64 * (CPR / InvPhases<D>::value + 1);  // output tile (uint4)
+  __shared__ uint4 lds[LT > 64 * CW ? LT : 64 * CW];
+  __shared__ __attribute__((aligned(16))) float inv_lam[D];  // 1 / lambda per channel
+  const int lane = threadIdx.x;
+  const uint32_t row0 = blockIdx.x * 64u;
+  const int rows = (int)(n - row0 < 64u ? n - row0 : 64u);
+  const uint4* ct = codes + (size_t)row0 * CW;
+  const uint8_t* st = scales + (size_t)row0 * (2 * D / G);
+  uint4* yt = y + (size_t)row0 * CPR;
+  const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
+  if (b0 == b1)
+    inv_lane_tile<D, G, ROT, true, LAM>(ct, st, yt, rows, tb, seed_offset(b0, sr), sr.seed, lds, lane, lam, inv_lam);
+  else
+    inv_lane_tile<D, G, ROT, false, LAM>(ct, st, yt, rows, tb, 0, lane_seed(sr, row0, rows, lane), lds, lane, lam,
+                                         inv_lam);
+}
+
 // Inverse step, one 64-row tile per wave.  At most 168 VGPRs (3 waves per
 // SIMD): d = 128 then spills a little, and still runs 5% faster than at 2.
 template <int D, int G, int ROT>
@@ -196,6 +259,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   const uint32_t b0 = seed_block(row0, sr), b1 = seed_block(row0 + (uint32_t)(rows - 1), sr);
   if (b0 == b1) inv_lane_tile<D, G, ROT, true>(ct, st, yt, rows, tb, seed_offset(b0, sr), sr.seed, lds, lane);
   else inv_lane_tile<D, G, ROT, false>(ct, st, yt, rows, tb, 0, lane_seed(sr, row0, rows, lane), lds, lane);
+}
+
+// The same with a per-channel lambda (4-bit codes of the width-and-lambda
+// entry points).
+template <int D, int G, int ROT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_lane_lambda_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y,
+    const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
+  inv_lane_body<D, G, ROT, true>(codes, scales, y, lam, n, sr, tb);
 }
 
 // ---------------------------------------------------------------------------
@@ -280,6 +352,23 @@ KernelFn find_kernel(bool fwd, int d, int g) {
   RTQ_CASE(128, 32) RTQ_CASE(128, 64) RTQ_CASE(128, 128)
   RTQ_CASE(256, 32) RTQ_CASE(256, 64) RTQ_CASE(256, 128)
 #undef RTQ_CASE
+  return nullptr;
+}
+
+// The 4-bit lambda kernels (one lane per row), for the width-and-lambda
+// entry points: null for d = 256 or an unsupported group.
+KernelFn find_lane_lambda_kernel(bool fwd, int rot, int d, int g) {
+#define RTQ_LAM_CASE(DD, GG)                                                                              \
+  if (d == DD && g == GG) {                                                                                \
+    if (rot == kSRFT)                                                                                      \
+      return fwd ? reinterpret_cast<KernelFn>(&fwd_lane_lambda_kernel<DD, GG, kSRFT>)                      \
+                 : reinterpret_cast<KernelFn>(&inv_lane_lambda_kernel<DD, GG, kSRFT>);                     \
+    return fwd ? reinterpret_cast<KernelFn>(&fwd_lane_lambda_kernel<DD, GG, kSRHT>)                        \
+               : reinterpret_cast<KernelFn>(&inv_lane_lambda_kernel<DD, GG, kSRHT>);                       \
+  }
+  RTQ_LAM_CASE(64, 32) RTQ_LAM_CASE(64, 64)
+  RTQ_LAM_CASE(128, 32) RTQ_LAM_CASE(128, 64) RTQ_LAM_CASE(128, 128)
+#undef RTQ_LAM_CASE
   return nullptr;
 }
 

@@ -25,18 +25,6 @@ namespace rtq {
 // per wave; tiles move through LDS as in the int4 kernels.
 // ---------------------------------------------------------------------------
 
-// u = lambda (.) h (fp16 pairs times fp16 pairs, exact in fp32).
-template <int D>
-__device__ __forceinline__ void lambda_weight(const uint32_t (&h)[D / 2], const uint32_t* __restrict__ lam,
-                                              float (&u)[D]) {
-  sfor<D / 2>([&](auto K) {
-    constexpr int k = RTQ_CI(K);
-    const uint32_t l = lam[k];
-    u[2 * k] = lo_f(h[k]) * lo_f(l);
-    u[2 * k + 1] = hi_f(h[k]) * hi_f(l);
-  });
-}
-
 template <int D, int G, int ROT, int B>
 __global__ __launch_bounds__(64) void fwd_ext_kernel(const uint4* __restrict__ x, uint32_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales, const uint32_t* __restrict__ lam,
@@ -102,6 +90,7 @@ __global__ __launch_bounds__(64) void inv_ext_kernel(const uint32_t* __restrict_
   constexpr int PC = CPR / PH, LR = PC + 1;
   constexpr int LT = 64 * LR;  // output staging (uint4)
   __shared__ uint4 lds[LT > 16 * CWW ? LT : 16 * CWW];
+  __shared__ __attribute__((aligned(16))) float inv_lam[D];  // 1 / lambda per channel
   uint32_t* lw = reinterpret_cast<uint32_t*>(lds);
   const int lane = threadIdx.x;
   const uint32_t row0 = blockIdx.x * 64u;
@@ -117,6 +106,7 @@ __global__ __launch_bounds__(64) void inv_ext_kernel(const uint32_t* __restrict_
   uint32_t sb[D / G];
   load_row_scales<D, G>(scales + (size_t)row0 * (2 * D / G), r, sb);
   const uint64_t s = lane_seed(sr, row0, rows, lane);
+  if (lam != nullptr) lambda_reciprocals<D>(lam, inv_lam, lane);  // read after the barrier below
   wait_lds_reads();
   lds_sync();
   uint32_t cw[CWW];
@@ -129,14 +119,7 @@ __global__ __launch_bounds__(64) void inv_ext_kernel(const uint32_t* __restrict_
     dequant_unpack_bits<D, G, B>(cw, sb, InvSqrt<D>::value, u);
     fwht_f32<D>(u);
   }
-  if (lam != nullptr) {
-    sfor<D / 2>([&](auto K) {
-      constexpr int k = RTQ_CI(K);
-      const uint32_t l = lam[k];
-      u[2 * k] *= __builtin_amdgcn_rcpf(lo_f(l));
-      u[2 * k + 1] *= __builtin_amdgcn_rcpf(hi_f(l));
-    });
-  }
+  if (lam != nullptr) lambda_unweight_lds<D>(u, inv_lam);
   uint32_t h[D / 2];
   sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   flip_signs<D>(h, s, lane);
@@ -221,8 +204,12 @@ rtq_status run_ext(bool fwd, int rot, const void* in0, const void* in1, void* ou
   if (n < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   const rtq_status shape = check_shape(d, g);
   if (shape != RTQ_OK) return shape;
-  const KernelFn fn = rot == kSRFT ? find_ext<kSRFT>(fwd, d, g, bits) : find_ext<kSRHT>(fwd, d, g, bits);
+  KernelFn fn = rot == kSRFT ? find_ext<kSRFT>(fwd, d, g, bits) : find_ext<kSRHT>(fwd, d, g, bits);
   if (!fn) return RTQ_ERR_UNSUPPORTED;
+  // 4 bits with lambda below d = 256: the int4 tiles with the lambda multiply
+  // (16-byte code moves, the int4 packer), which write the same bytes
+  const KernelFn lane_lambda = bits == 4 && lam ? find_lane_lambda_kernel(fwd, rot, d, g) : nullptr;
+  if (lane_lambda) fn = lane_lambda;
   if (n == 0) return RTQ_OK;
   if (n > kMaxRows) return RTQ_ERR_INVALID_ARG;
   const void* a = in0;
@@ -246,8 +233,8 @@ rtq_status run_ext(bool fwd, int rot, const void* in0, const void* in1, void* ou
   const uint32_t* l = static_cast<const uint32_t*>(lam);
   const int vpt = d == 256 ? 32 : 64;  // rows per tile
   const int64_t tiles = (n + vpt - 1) / vpt;
-  SignTable tb;  // the d = 256 kernels take the sign table as a last argument
-  if (d == 256) fill_sign_table(tb, sr, n, d);
+  SignTable tb;  // the d = 256 and lane-lambda kernels take the sign table as a last argument
+  if (d == 256 || lane_lambda) fill_sign_table(tb, sr, n, d);
   if (fwd) {
     const void* x = in0;
     void* codes = out0;

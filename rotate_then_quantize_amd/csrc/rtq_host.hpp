@@ -62,4 +62,9 @@ inline SeedRule make_seed_rule(uint64_t seed, int64_t rps, int32_t period, int64
 // (defined with the int4 kernels in rtq.hip).
 void fill_sign_table(SignTable& tb, const SeedRule& sr, int64_t n, int d);
 
+// The one-lane-per-row int4 kernels with a per-channel lambda (d = 64 / 128),
+// or null.  Their arguments: in, out0, out1, lambda, rows, SeedRule,
+// SignTable.
+KernelFn find_lane_lambda_kernel(bool fwd, int rot, int d, int g);
+
 }  // namespace rtq

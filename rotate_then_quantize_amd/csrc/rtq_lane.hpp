@@ -150,6 +150,62 @@ __device__ __forceinline__ void quantize_row(const uint32_t (&h)[D / 2], uint32_
   quantize_pack<D, G>(z, zs, cw, sb);
 }
 
+// u = lambda (.) h (fp16 pairs times fp16 pairs, exact in fp32); lam holds d
+// fp16 values, one per channel.
+template <int D>
+__device__ __forceinline__ void lambda_weight(const uint32_t (&h)[D / 2], const uint32_t* __restrict__ lam,
+                                              float (&u)[D]) {
+  sfor<D / 2>([&](auto K) {
+    constexpr int k = RTQ_CI(K);
+    const uint32_t l = lam[k];
+    u[2 * k] = lo_f(h[k]) * lo_f(l);
+    u[2 * k + 1] = hi_f(h[k]) * hi_f(l);
+  });
+}
+
+// inv[c] = 1 / lambda_c for the D channels, lane c mod 64 computing channel
+// c: one reciprocal per lane and 64 channels instead of one per value of
+// every row (lambda is the same for all rows).  Visible to the whole wave
+// after the caller's next LDS barrier.
+template <int D>
+__device__ __forceinline__ void lambda_reciprocals(const uint32_t* __restrict__ lam, float* inv, int lane) {
+  sfor<D / 64>([&](auto I) {
+    const int c = RTQ_CI(I) * 64 + lane;
+    const uint32_t l = lam[c / 2];
+    inv[c] = __builtin_amdgcn_rcpf((c & 1) ? hi_f(l) : lo_f(l));
+  });
+}
+
+// u *= inv, channel by channel (inv from lambda_reciprocals, read as
+// broadcasts).
+template <int D>
+__device__ __forceinline__ void lambda_unweight_lds(float (&u)[D], const float* inv) {
+  sfor<D / 4>([&](auto K) {
+    constexpr int k = RTQ_CI(K);
+    const float4 r = *reinterpret_cast<const float4*>(inv + 4 * k);
+    u[4 * k] *= r.x;
+    u[4 * k + 1] *= r.y;
+    u[4 * k + 2] *= r.z;
+    u[4 * k + 3] *= r.w;
+  });
+}
+
+// quantize_row of lambda (.) h: the transform then runs on fp32 input.
+template <int D, int G, int ROT>
+__device__ __forceinline__ void quantize_row_lambda(const uint32_t (&h)[D / 2], const uint32_t* __restrict__ lam,
+                                                    uint32_t (&cw)[D / 8], uint32_t (&sb)[D / G]) {
+  float u[D];
+  lambda_weight<D>(h, lam, u);
+  if constexpr (ROT == kSRFT) {
+    float z[D];
+    srft_fwd<D>(u, z);
+    quantize_pack<D, G>(z, 1.0f, cw, sb);
+  } else {
+    fwht_f32<D>(u);
+    quantize_pack<D, G>(u, InvSqrt<D>::value, cw, sb);
+  }
+}
+
 // scales of one row, packed as written to memory (fp16 pairs, low half first)
 template <int D, int G>
 __device__ __forceinline__ void store_row_scales(uint8_t* __restrict__ st, uint32_t r, const uint32_t (&sb)[D / G]) {

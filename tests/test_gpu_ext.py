@@ -65,6 +65,15 @@ def test_ragged_rows_and_seed_rules(bits, n, d):
 
 
 @pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 63, 65, 129])
+def test_bits4_lambda_ragged_rows(rot, d, n):
+    """4-bit codes with lambda below d = 256 run on the int4 tiles with the
+    lambda multiply: partial tiles and a per-row seed rule."""
+    run_case(rot, d, 32, 4, True, n=n, rps=5, per=3)
+
+
+@pytest.mark.parametrize("rot", ["srft", "srht"])
 @pytest.mark.parametrize("d", [128, 256])
 def test_bits4_without_lambda_equals_the_int4_kernels(rot, d):
     """The general kernel with 4-bit codes and no lambda writes the same codes
