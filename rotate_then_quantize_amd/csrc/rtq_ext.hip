@@ -164,7 +164,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y,
     const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
   __shared__ uint4 lds[32 * 17];
-  inv_pair_tile<G, ROT, TileRows, B>(codes, scales, y, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
+  __shared__ __attribute__((aligned(16))) float inv_lam[kPairLambdaFloats];
+  inv_pair_tile<G, ROT, TileRows, B>(codes, scales, y, tile_rows(n, sr, tb), lds, threadIdx.x, lam, inv_lam);
 }
 
 template <int ROT, int B>

@@ -71,22 +71,34 @@ __device__ __forceinline__ void lambda_half(const uint32_t (&h)[64], const uint3
   }
 }
 
-// u /= lambda for the lane's 128 output samples (same sample sets as above;
-// u[m] is sample 2m + p for SRFT, 128 p + m for SRHT).
+// 1/lambda of the 128 samples each half of the pair holds, as inv[p * 132 + m]
+// for half p and its sample m (SRFT: channel 2m + p, SRHT: 128p + m); rows
+// are padded to 132 floats so that the two halves read different banks.
+// One reciprocal per lane and 64 channels per tile, instead of one per value
+// (lambda is the same for every row).
 template <int ROT>
-__device__ __forceinline__ void unweight_half(float (&u)[128], const uint32_t* __restrict__ lam, int p) {
-  if constexpr (ROT == kSRFT) {
-    const uint32_t sh = 16u * (uint32_t)p;
-    sfor<128>([&](auto M) { u[RTQ_CI(M)] *= __builtin_amdgcn_rcpf(lo_f(lam[RTQ_CI(M)] >> sh)); });
-  } else {
-    const uint32_t* lp = lam + 64 * p;
-    sfor<64>([&](auto K) {
-      constexpr int k = RTQ_CI(K);
-      const uint32_t l = lp[k];
-      u[2 * k] *= __builtin_amdgcn_rcpf(lo_f(l));
-      u[2 * k + 1] *= __builtin_amdgcn_rcpf(hi_f(l));
-    });
-  }
+__device__ __forceinline__ void pair_lambda_reciprocals(const uint32_t* __restrict__ lam, float* inv, int lane) {
+  sfor<4>([&](auto I) {
+    const int idx = RTQ_CI(I) * 64 + lane, p = idx >> 7, m = idx & 127;
+    const int ch = ROT == kSRFT ? 2 * m + p : 128 * p + m;
+    const uint32_t l = lam[ch >> 1];
+    inv[p * 132 + m] = __builtin_amdgcn_rcpf((ch & 1) ? hi_f(l) : lo_f(l));
+  });
+}
+constexpr int kPairLambdaFloats = 2 * 132;
+
+// u /= lambda for the lane's 128 output samples (u[m] is sample m of half p),
+// from the reciprocal table, read as broadcasts.
+__device__ __forceinline__ void unweight_half(float (&u)[128], const float* inv, int p) {
+  const float* r = inv + p * 132;
+  sfor<32>([&](auto J) {
+    constexpr int j = RTQ_CI(J);
+    const float4 q = *reinterpret_cast<const float4*>(r + 4 * j);
+    u[4 * j] *= q.x;
+    u[4 * j + 1] *= q.y;
+    u[4 * j + 2] *= q.z;
+    u[4 * j + 3] *= q.w;
+  });
 }
 
 // Non-temporal store for streaming tiles, ordinary (L2-merged) store for rows
@@ -284,8 +296,9 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
 template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
                                               uint4* __restrict__ y, const Rows& R, uint4* lds, int lane,
-                                              const uint32_t* __restrict__ lam = nullptr) {
+                                              const uint32_t* __restrict__ lam = nullptr, float* inv_lam = nullptr) {
   constexpr int CPR = 32;
+  if (lam != nullptr) pair_lambda_reciprocals<ROT>(lam, inv_lam, lane);  // read after a barrier below
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
   const float sigma = p ? -1.0f : 1.0f;
@@ -369,7 +382,10 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
         u[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
       });
     }
-    if (lam != nullptr) unweight_half<ROT>(u, lam, p);
+    if (lam != nullptr) {
+      lds_sync();
+      unweight_half(u, inv_lam, p);
+    }
     // fp16 samples out through LDS in two passes of 16 output chunks per row
     // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
     // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
