@@ -275,11 +275,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 // rows of a contiguous [n, 256] tensor.
 // ---------------------------------------------------------------------------
 
-// The SRFT forward with groups of 32 fits three waves per SIMD without
-// spills (it quantizes each group as soon as its bins are exchanged);
-// larger groups and the SRHT would spill.
+// The forward with groups of 32 fits three waves per SIMD without spills
+// (it quantizes each group as soon as its values are complete); larger
+// groups would spill.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT && G == 32 ? 3 : 2, 8))) void fwd_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 2, 8))) void fwd_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
     SignTable tb) {
   __shared__ uint4 lds[32 * 33];

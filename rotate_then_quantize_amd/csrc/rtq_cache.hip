@@ -159,9 +159,9 @@ __device__ __forceinline__ MappedTileRows mapped_tile_rows(uint32_t n, const Row
   return MappedTileRows{row0, rows, uniform, s0, m, rs};
 }
 
-// The SRFT forward with groups of 32 fits three waves per SIMD without spills.
+// The forward with groups of 32 fits three waves per SIMD without spills.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT && G == 32 ? 3 : 2, 8))) void fwd_mapped_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 2, 8))) void fwd_mapped_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, RowMap m,
     RowSeeds rs) {
   __shared__ uint4 lds[32 * 33];

@@ -240,11 +240,25 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       } else {
         fwht_from_f16<128>(h, f);
       }
-      sfor<128>([&](auto K) {
+      zs = 1.0f / 16.0f;
+      auto combine = [&](auto K) {
         const float r = __shfl_xor(f[RTQ_CI(K)], 32);
         L[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
-      });
-      zs = 1.0f / 16.0f;
+      };
+      // a shuffle of x waits for w
+      auto after = [](float& x, uint32_t w) { asm volatile("" : "+v"(x) : "v"(w)); };
+      if constexpr (B == 4) {
+        // group by group, as for the SRFT: quantize each group once its
+        // values are combined; the next group's shuffles wait for its codes
+        sfor<128 / G>([&](auto GI) {
+          constexpr int gi = RTQ_CI(GI), lo = gi * G;
+          sfor<G>([&](auto K) { combine(ic<lo + RTQ_CI(K)>{}); });
+          quantize_pack_group<gi, 128, G>(L, zs, cw, sb);
+          if constexpr (lo + G < 128) after(f[lo + G], cw[(lo + G) / 8 - 1]);
+        });
+      } else {
+        sfor<128>([&](auto K) { combine(K); });
+      }
     }
     if constexpr (B != 4) {
       // SRFT lane 1 holds its half mirrored: put it in natural order first
@@ -264,9 +278,7 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       uint32_t sr[128 / G];
       sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
       sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
-    } else {
-      quantize_pack<128, G>(L, zs, cw, sb);
-    }
+    }  // SRHT, 4 bits: quantized above
     if (v < rows) {
       const size_t row = R.cache_row(v);
       constexpr bool nt = Rows::kStreamStores;
