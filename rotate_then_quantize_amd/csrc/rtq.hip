@@ -356,19 +356,22 @@ KernelFn find_kernel(bool fwd, int d, int g) {
 }
 
 // The 4-bit lambda kernels (one lane per row), for the width-and-lambda
-// entry points: null for d = 256 or an unsupported group.
+// entry points: null for d = 256 or an unsupported group, and for the d = 128
+// inverse, which spills about 1 KB per lane at three waves per SIMD (the
+// general kernel fits two waves without spills).
 KernelFn find_lane_lambda_kernel(bool fwd, int rot, int d, int g) {
-#define RTQ_LAM_CASE(DD, GG)                                                                              \
-  if (d == DD && g == GG) {                                                                                \
-    if (rot == kSRFT)                                                                                      \
-      return fwd ? reinterpret_cast<KernelFn>(&fwd_lane_lambda_kernel<DD, GG, kSRFT>)                      \
-                 : reinterpret_cast<KernelFn>(&inv_lane_lambda_kernel<DD, GG, kSRFT>);                     \
-    return fwd ? reinterpret_cast<KernelFn>(&fwd_lane_lambda_kernel<DD, GG, kSRHT>)                        \
-               : reinterpret_cast<KernelFn>(&inv_lane_lambda_kernel<DD, GG, kSRHT>);                       \
+#define RTQ_LAM(KERNEL, DD, GG)                                                      \
+  if (d == DD && g == GG)                                                            \
+    return rot == kSRFT ? reinterpret_cast<KernelFn>(&KERNEL<DD, GG, kSRFT>)         \
+                        : reinterpret_cast<KernelFn>(&KERNEL<DD, GG, kSRHT>);
+  if (fwd) {
+    RTQ_LAM(fwd_lane_lambda_kernel, 64, 32) RTQ_LAM(fwd_lane_lambda_kernel, 64, 64)
+    RTQ_LAM(fwd_lane_lambda_kernel, 128, 32) RTQ_LAM(fwd_lane_lambda_kernel, 128, 64)
+    RTQ_LAM(fwd_lane_lambda_kernel, 128, 128)
+  } else {
+    RTQ_LAM(inv_lane_lambda_kernel, 64, 32) RTQ_LAM(inv_lane_lambda_kernel, 64, 64)
   }
-  RTQ_LAM_CASE(64, 32) RTQ_LAM_CASE(64, 64)
-  RTQ_LAM_CASE(128, 32) RTQ_LAM_CASE(128, 64) RTQ_LAM_CASE(128, 128)
-#undef RTQ_LAM_CASE
+#undef RTQ_LAM
   return nullptr;
 }
 
