@@ -154,11 +154,13 @@ def find_csv(directory: str, suffix: str) -> str:
     return hits[0]
 
 
-def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = False) -> None:
-    """Write the rocprofv3 --kernel-trace --stats summary of a bench run."""
+def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = False, window: int = 0) -> None:
+    """Write the rocprofv3 --kernel-trace --stats summary of a bench run
+    (window: the fp16 window tokens of an --attn --window run)."""
     import csv
     rows = list(csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv"))))
-    what = "decode attention" if attn else "forward + inverse"
+    what = ("decode attention" + (f" with {window} fp16 window tokens" if window else "")) if attn \
+        else "forward + inverse"
     lines = [f"# rocprofv3 kernel trace, {what}, workload {w.name} (d={w.d}, group={w.group}, {rot})",
              f"# command: {command}",
              f"# kernel_source_sha: {kernel_source_hash(kernel_sources('attn_decode' if attn else 'quant_fwd', w.d))}",
@@ -177,10 +179,11 @@ def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = Fals
     for r in rows:
         role = kernel_role(r["Name"])
         if role and (role == "attn_decode") == attn:
-            bytes_launch = role_bytes(w, role)
+            bytes_launch = attn_bytes(w, window) if role == "attn_decode" else role_bytes(w, role)
             lines.append(f"{role}_average_us: {float(r['AverageNs']) / 1e3:.3f}")
             lines.append(f"{role}_algorithmic_GBps: {bytes_launch / float(r['AverageNs']):.1f}")
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{'attn_' if attn else ''}{rot}_{w.name}.txt")
+    suffix = f"_window{window}" if window else ""
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{'attn_' if attn else ''}{rot}_{w.name}{suffix}.txt")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     log(f"wrote {path}")
@@ -939,7 +942,7 @@ def main():
             summarize_valu(*args.summarize_valu, w, args.rot, [("SQ counters", c) for c in args.command[-1:]],
                            args.attn)
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn)
+            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn, args.window)
         if args.summarize_traffic:
             names = ("FETCH_SIZE", "WRITE_SIZE", "copy FETCH_SIZE", "copy WRITE_SIZE")
             cmds = list(zip(names, args.command[-4:])) if len(args.command) >= 4 else []
