@@ -409,6 +409,25 @@ def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warm
     }
 
 
+def host_info() -> dict:
+    """The host the oracle baseline ran on: CPU model and the cores this
+    process may use (the oracle's BLAS threads are reported as "cores")."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count() or 1
+    return {"cpu_model": model, "affinity_cores": affinity}
+
+
 def cpu_baseline(w, x_gpu, rot, seconds):
     """The oracle, as it is, on consecutive 65536-row chunks of the same
     workload until ``seconds`` of CPU time are spent (input copy excluded)."""
@@ -437,6 +456,7 @@ def cpu_baseline(w, x_gpu, rot, seconds):
         "value": done / spent,
         "unit": "vectors/s",
         "cores": threads,
+        "host": host_info(),
         "kind": "oracle",
         "sample": f"{done} rows ({where}), forward + inverse each, fp64 numpy oracle in {chunk}-row chunks, "
                   f"{spent:.1f} s of oracle time (device-to-host copies excluded)",
@@ -515,6 +535,7 @@ def attn_cpu_baseline(w, codes_gpu, scales_gpu, q_gpu, rot, seconds, strides, rp
         "value": done / spent / (L * S),
         "unit": "steps/s",
         "cores": threads,
+        "host": host_info(),
         "kind": "oracle",
         "sample": f"{done} of the {L * S} (layer, stream) pairs ({w.tokens} tokens, {w.q_per_kv} queries each), "
                   f"fp64 numpy oracle, {spent:.1f} s of oracle time; steps/s = pairs/s / {L * S}",

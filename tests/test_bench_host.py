@@ -53,3 +53,8 @@ def test_more_than_one_gpu_is_refused():
     r = run_bench("--gpus", "2")
     assert r.returncode != 0
     assert "one GPU" in (r.stdout + r.stderr) or "1 GPU" in (r.stdout + r.stderr), (r.stdout + r.stderr)[-300:]
+
+
+def test_host_info_names_the_cpu():
+    info = bench.host_info()
+    assert info["affinity_cores"] >= 1 and isinstance(info["cpu_model"], str)
