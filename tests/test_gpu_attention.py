@@ -235,10 +235,13 @@ def test_window_without_int4_tokens(rot, d):
     run_window_case(rot, d, 32, 2, 2, 0, 7, 16, 4)
 
 
-def test_window_with_token_splits():
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_with_token_splits(rot, d):
+    """Only the workgroup that merges a stream's splits reads the window."""
     L, S, T = 1, 2, 1500
-    assert rtq.attn_workspace_bytes(L, S, T, 4, 128) > 0
-    run_window_case("srft", 128, 32, L, S, T, 16, 16, 4)
+    assert rtq.attn_workspace_bytes(L, S, T, 4, d) > 0
+    run_window_case(rot, d, 32, L, S, T, 16, 16, 4)
 
 
 def test_empty_window_equals_plain_attention():
