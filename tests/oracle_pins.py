@@ -363,6 +363,119 @@ def check_group_scales(quantize_groups):
     assert q[0, 5] == -4 and q[0, 100] == 1
 
 
+# fp16(0.1) and fp16(1/3), evaluated by hand: 0.1 = 1.6 * 2^-4 and the 10-bit
+# mantissa 0.6 * 1024 = 614.4 rounds to 614, so fp16(0.1) = 1638/16384 =
+# 819/8192; 1/3 = 1.333... * 2^-2 and 0.333... * 1024 = 341.33 rounds to 341,
+# so fp16(1/3) = 1365/4096.  Neither equals the real number it stands for.
+FP16_TENTH = 819 / 8192          # 0.0999755859375
+FP16_THIRD = 1365 / 4096         # 0.333251953125
+
+
+def check_dequantize_hand_evaluated(dequantize_groups):
+    """x_hat = s * q with zero point 0, per group, with s the stored fp16 scale.
+
+    The decode rule: [P4] "Quantization & Serving" (opening: the dequantized
+    value of symmetric absmax quantization is s times the code) and [P3] "What
+    Quantization Is, Mathematically" (decode multiplies the cell index by the
+    scale; zero_point = 0 in the symmetric case).  Scales are fp16 values
+    ([P3] "How Many Numbers Should One Scale Cover").  Every product below is
+    evaluated by hand; two of the scales are not the real numbers 0.1 and 1/3
+    but their fp16 roundings, and 65504 is the largest fp16 value.
+    """
+    cases = [
+        # (codes, fp16 scales, group, expected x_hat)
+        ([[-8, 7, 3, -1]], [[2.5, 0.375]], 2, [[-20.0, 17.5, 1.125, -0.375]]),
+        # 3 * 819/8192 = 2457/8192; -8 * 819/8192 = -819/1024; scale 0 decodes to 0
+        ([[3, -8, 0, 5]], [[FP16_TENTH, 0.0]], 2, [[2457 / 8192, -819 / 1024, 0.0, 0.0]]),
+        # 7 * 1365/4096 = 9555/4096; -8 * 1365/4096 = -10920/4096; 65504 * (-8, 7, 0, 1)
+        ([[7, -8, 1, -1, -8, 7, 0, 1]], [[FP16_THIRD, 65504.0]], 4,
+         [[9555 / 4096, -10920 / 4096, 1365 / 4096, -1365 / 4096, -524032.0, 458528.0, 0.0, 65504.0]]),
+        # two rows, one group per row
+        ([[1, 2], [-3, 4]], [[0.5], [0.25]], 2, [[0.5, 1.0], [-0.75, 1.0]]),
+    ]
+    for q, s, g, want in cases:
+        s16 = np.array(s, dtype=np.float16)
+        assert np.array_equal(s16.astype(np.float64), np.array(s)), "fixture scales must be fp16 values"
+        got = dequantize_groups(np.array(q, dtype=np.int8), s16, g)
+        assert np.array_equal(np.asarray(got, dtype=np.float64), np.array(want)), (q, s, got, want)
+
+
+def check_dequant_inv_hand_evaluated(oracle):
+    """The whole inverse step on a hand-evaluated row with no rotation (R = I):
+    unpack [P5] nibbles, dequantize (s * q), flip signs, round to fp16.
+
+    Bytes 0x78 = (7 << 4) | 8 and 0xF3 = (15 << 4) | 3 hold the codes
+    -8, 7, 3, -1 (low nibble first, two's complement).  The signs of seed
+    1234567 are +1, +1, -1, +1 (from the top bits of its first published
+    SplitMix64 outputs, checked in check_sign_vector_from_published).  With
+    scales 2.5 and 0.375 over groups of 2: y = (-20, 17.5, -1.125, -0.375).
+    """
+    codes = np.array([[0x78, 0xF3]], dtype=np.uint8)
+    scales = np.array([[2.5, 0.375]], dtype=np.float16)
+    y = oracle.dequant_inv(codes, scales, 4, 2, 1234567, rot="none")
+    assert y.dtype == np.float16
+    assert y.astype(np.float64).tolist() == [[-20.0, 17.5, -1.125, -0.375]], y
+
+
+def check_quantize_dequantize_half_step(quantize_groups, dequantize_groups):
+    """Through both steps of the oracle: z_hat = dequantize(quantize(z)) lies on
+    the grid s * {-8 .. 7} of its group's stored scale, and |z_hat - z| <= s/2
+    for every value that is not clipped ([P4] "Quantization & Serving": the
+    rounding error of absmax quantization is at most s/2 before clipping);
+    a clipped value (only +absmax can clip, at 7.5 < a/s <= 8) errs by at most
+    s (1 + 8 * 2^-11) (fp16 rounding of s moves a/s by at most 2^-11 relative)."""
+    rng = np.random.default_rng(31)
+    for trial in range(60):
+        g = (32, 64, 128)[trial % 3]
+        z = rng.standard_normal((5, 256)) * rng.choice([1e-3, 1.0, 40.0])
+        z[:, rng.integers(256, size=3)] *= 25.0
+        q, s, _ = quantize_groups(z, g)
+        zhat = np.asarray(dequantize_groups(q, s, g), dtype=np.float64)
+        s_el = np.repeat(s.astype(np.float64), g, axis=-1)
+        k = zhat / s_el
+        assert np.array_equal(k, np.rint(k)) and k.min() >= -8 and k.max() <= 7, "off the code grid"
+        err = np.abs(zhat - z)
+        r = z / s_el
+        inside = (r <= 7.5) & (r >= -8.5)
+        assert np.all(err[inside] <= s_el[inside] / 2 * (1 + 1e-12)), "more than half a step"
+        assert np.all(err <= s_el * (1 + 8 * 2.0 ** -11)), "clipped error above one step"
+
+
+def check_quantize_divides_by_stored_scale(quantize_groups):
+    """Codes divide by the stored fp16 scale, not by absmax/8 before rounding.
+
+    [P3] "How Many Numbers Should One Scale Cover": scales are fp16 values that
+    are stored and moved, and the decode of [P3] "What Quantization Is,
+    Mathematically" multiplies by that stored value; dividing by the same
+    value keeps the round trip within half a step of it.
+
+    Hand-evaluated group (absmax 0.8, so absmax/8 = 0.1, stored as
+    fp16(0.1) = 819/8192):
+      0.8     / (819/8192) = 8.00195...  -> 8, clamped to 7
+      0.24995 / (819/8192) = 2.50011...  -> 3   (0.24995 / 0.1 = 2.4995 -> 2)
+     -0.34995 / (819/8192) = -3.50035... -> -4  (-0.34995 / 0.1 = -3.4995 -> -3)
+      0.0502  / (819/8192) = 0.5021...   -> 1
+    """
+    z = np.zeros((1, 32))
+    z[0, :4] = [0.8, 0.24995, -0.34995, 0.0502]
+    q, s, _ = quantize_groups(z, 32)
+    assert float(s[0, 0]) == FP16_TENTH, s
+    assert q[0, :4].tolist() == [7, 3, -4, 1], q[0, :4]
+    assert np.all(q[0, 4:] == 0)
+
+
+def check_ext_divides_by_stored_scale(m):
+    """The same rule for b-bit codes: absmax 0.1 * 2^(b-1) gives the stored
+    scale fp16(0.1) = 819/8192 for every width, and 0.24995 and -0.34995 take
+    the codes 3 and -4 (dividing by 0.1 would give 2 and -3)."""
+    for bits in m.CODE_BITS:
+        z = np.zeros((1, 32))
+        z[0, :3] = [0.1 * (1 << (bits - 1)), 0.24995, -0.34995]
+        q, s, _ = m.quantize_groups_bits(z, 32, bits)
+        assert float(s[0, 0]) == FP16_TENTH, (bits, s)
+        assert q[0, 1] == 3 and q[0, 2] == -4, (bits, q[0, :3])
+
+
 # ---------------------------------------------------------------------------
 # Attention over the compressed cache
 # ---------------------------------------------------------------------------

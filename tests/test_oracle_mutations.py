@@ -36,6 +36,12 @@ def all_pins(m):
         "scale_round": lambda: P.check_scale_rounding(m.fp16_scale_from_absmax),
         "zero_group": lambda: P.check_zero_group(m.quantize_groups, m.dequantize_groups),
         "group_scales": lambda: P.check_group_scales(m.quantize_groups),
+        "dequant_hand": lambda: P.check_dequantize_hand_evaluated(m.dequantize_groups),
+        "dequant_inv_hand": lambda: P.check_dequant_inv_hand_evaluated(m),
+        "quant_dequant_half_step": lambda: P.check_quantize_dequantize_half_step(m.quantize_groups,
+                                                                                 m.dequantize_groups),
+        "stored_scale": lambda: P.check_quantize_divides_by_stored_scale(m.quantize_groups),
+        "ext_stored_scale": lambda: P.check_ext_divides_by_stored_scale(m),
         "mse_order": lambda: P.check_mse_ordering(m.int4_roundtrip_blocks),
         "nibbles": lambda: P.check_nibbles(m.pack_nibbles, m.unpack_nibbles),
         "impulse": lambda: P.check_impulse_end_to_end(m),
@@ -163,9 +169,33 @@ MUTATIONS = {
     "cache rows swap the kv and stream strides": (
         "    return layer * sl + kv * skv + stream * ss + st * np.arange(tokens, dtype=np.int64)",
         "    return layer * sl + kv * ss + stream * skv + st * np.arange(tokens, dtype=np.int64)"),
+    "dequantize adds half a step": (
+        "return (qg * s64[..., None]).reshape(q.shape)", "return ((qg + 0.5) * s64[..., None]).reshape(q.shape)"),
+    "dequantize halves the scale": (
+        "return (qg * s64[..., None]).reshape(q.shape)", "return (qg * (s64 / 2)[..., None]).reshape(q.shape)"),
+    "dequantize uses the first group's scale for every group": (
+        "return (qg * s64[..., None]).reshape(q.shape)", "return (qg * s64[..., :1, None]).reshape(q.shape)"),
+    "quantizer divides by absmax/8 before its fp16 rounding": (
+        "    q = quantize_with_scale(zg, s[..., None])",
+        "    q = np.clip(np.rint(np.where(a[..., None] > 0, zg / np.where(a[..., None] > 0, a[..., None] / 8.0, 1.0),"
+        " 0.0)), INT4_MIN, INT4_MAX).astype(np.int8)"),
+    "b-bit quantizer divides by absmax/2^(b-1) before its fp16 rounding": (
+        "    s64 = s.astype(np.float64)[..., None]", "    s64 = (a / float(1 << (bits - 1)))[..., None]"),
     "forward rotates before the sign flip": (
         "u = D * x\n    return u @ rotation_matrix(rot, d).T",
         "return D * (x @ rotation_matrix(rot, d).T)"),
+}
+
+
+# Mistakes in the dequantize step and in the choice of the divided scale must
+# be caught by a pin written for that step, not only incidentally by a pin of
+# some other part (such as the error ordering of the code widths).
+DEDICATED = {
+    "dequantize adds half a step": {"dequant_hand", "dequant_inv_hand", "quant_dequant_half_step"},
+    "dequantize halves the scale": {"dequant_hand", "dequant_inv_hand", "quant_dequant_half_step"},
+    "dequantize uses the first group's scale for every group": {"dequant_hand", "quant_dequant_half_step"},
+    "quantizer divides by absmax/8 before its fp16 rounding": {"stored_scale"},
+    "b-bit quantizer divides by absmax/2^(b-1) before its fp16 rounding": {"ext_stored_scale"},
 }
 
 
@@ -174,6 +204,8 @@ def test_mutation_is_caught(name):
     old, new = MUTATIONS[name]
     failed = all_pins(mutated(old, new))
     assert failed, f"no pin catches the planted mistake: {name}"
+    if name in DEDICATED:
+        assert DEDICATED[name] <= set(failed), (name, sorted(failed))
 
 
 def test_unmutated_copy_passes_every_pin():

@@ -126,3 +126,23 @@ def test_oracle_is_independent_of_the_library():
 
 def test_group_scales():
     P.check_group_scales(oracle.quantize_groups)
+
+
+def test_dequantize_hand_evaluated():
+    P.check_dequantize_hand_evaluated(oracle.dequantize_groups)
+
+
+def test_dequant_inv_hand_evaluated():
+    P.check_dequant_inv_hand_evaluated(oracle)
+
+
+def test_quantize_dequantize_half_step():
+    P.check_quantize_dequantize_half_step(oracle.quantize_groups, oracle.dequantize_groups)
+
+
+def test_quantize_divides_by_stored_fp16_scale():
+    P.check_quantize_divides_by_stored_scale(oracle.quantize_groups)
+
+
+def test_ext_quantize_divides_by_stored_fp16_scale():
+    P.check_ext_divides_by_stored_scale(oracle)
