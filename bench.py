@@ -375,7 +375,7 @@ def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warm
     quantize, dequantize, inverse rotate) on the same buffers; signs are a
     precomputed tensor.  Measurement only."""
     import torch
-    from rotate_then_quantize_amd import eager
+    import eager_baseline as eager
     n_inv = w.n_rows
     n_fwd = w.new_rows if w.new_tokens else w.n_rows
     signs_inv = eager.sign_matrix(n_inv, w.d, w.sign_seed, w.rows_per_seed, w.seed_period)

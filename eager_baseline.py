@@ -9,7 +9,7 @@ kernels is not enough": the fused pair).  It follows the same contract as the C 
 rfft, absmax/8 fp16 scales, round-half-even, clamp to [-8, 7], two's
 complement nibbles, SplitMix64 signs and the per-row seed rule), using
 torch.fft on the GPU (hipFFT underneath) and elementwise torch ops.  Nothing
-in the library calls it.
+in the library calls it, and it lives outside the package beside bench.py.
 """
 from __future__ import annotations
 

@@ -23,7 +23,7 @@ __all__ = [
     "srft_attn_decode", "srht_attn_decode", "attn_workspace_bytes",
     "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
     "srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext", "CODE_BITS",
-    "RTQError", "library", "library_path", "SUPPORTED", "ATTN_SUPPORTED", "CACHE_SUPPORTED", "EXT_SUPPORTED",
+    "RTQError", "library", "library_path", "ATTN_MAX_WINDOW", "SUPPORTED", "ATTN_SUPPORTED", "CACHE_SUPPORTED", "EXT_SUPPORTED",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -40,6 +40,8 @@ ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32
 CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
 ATTN_MAX_Q_PER_KV = 8
+# fp16 window tokens per stream that *_attn_decode_window accepts
+ATTN_MAX_WINDOW = 64
 # code widths of the *_ext entry points
 CODE_BITS = (3, 4, 6, 8)
 

@@ -38,6 +38,8 @@ class DecodeCache:
         import torch
         if min(layers, streams, capacity, window) < 1:
             raise ValueError("layers, streams, capacity and window must be positive")
+        if window > rtq.ATTN_MAX_WINDOW:
+            raise ValueError(f"window must be at most {rtq.ATTN_MAX_WINDOW} tokens (the attention kernel's limit)")
         if (d, group) not in rtq.CACHE_SUPPORTED:
             raise ValueError(f"(d, group) = ({d}, {group}) is not supported for the decode cache")
         self.layers, self.streams, self.capacity, self.d, self.group = layers, streams, capacity, d, group

@@ -24,3 +24,27 @@ def gpu_available() -> bool:
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """The 1e-5 tie-mismatch rate over every code the session compared
+    (tests/parity.py keeps the tally).  A session that compared fewer than a
+    million codes cannot resolve the rate and says so; otherwise a rate above
+    1e-5 fails the session."""
+    try:
+        from tests.parity import TALLY
+    except Exception:
+        return
+    n, m = TALLY["elements"], TALLY["mismatch"]
+    if n == 0:
+        return
+    rate = m / n
+    tr = session.config.pluginmanager.get_plugin("terminalreporter")
+    msg = f"code tie mismatches over the session: {m} of {n} compared codes (rate {rate:.2e})"
+    if n < 1_000_000:
+        msg += "; too few codes to resolve a 1e-5 rate"
+    elif rate > 1e-5:
+        msg += " exceeds 1e-5"
+        session.exitstatus = pytest.ExitCode.TESTS_FAILED
+    if tr is not None:
+        tr.write_line(msg)

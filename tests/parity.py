@@ -7,8 +7,10 @@ Tolerances (the reading of the stated bar):
     scale.
   * codes: bit-exact, except elements whose oracle z/s lies within 1e-4 of
     k + 1/2, which may differ by +-1; at most 1e-5 of all elements may differ.
-    The rate is counted over every element compared in the session (TALLY,
-    asserted by the last GPU test); a single call may exceed it by at most two
+    The rate is asserted over a dedicated sample of 4 M codes per rotation
+    (test_code_tie_rate_on_its_own_sample) and over every element compared in
+    the session (TALLY, checked when the session ends); a single call may
+    exceed it by at most two
     elements, since exact ties (SRHT of fp16 inputs gives dyadic values, about
     3.5e-6 of elements) make small inputs too noisy to resolve a 1e-5 rate.
     ``allow_ties`` lifts the count for inputs built to sit on ties.

@@ -227,6 +227,18 @@ def test_attention_window_rejects_bad_arguments(name):
     assert win_call(name, layers=0) == rtq.RTQ_OK
 
 
+def test_decode_cache_rejects_windows_the_attention_cannot_read():
+    """A DecodeCache whose window exceeds what *_attn_decode_window accepts
+    fails at construction, not at its 65th append."""
+    from rotate_then_quantize_amd.decode_cache import DecodeCache
+    lim = rtq.ATTN_MAX_WINDOW
+    assert win_call("srft_attn_decode", cap=lim + 1, wt=lim + 1) == rtq.RTQ_ERR_UNSUPPORTED
+    with pytest.raises(ValueError):
+        DecodeCache(1, 1, 256, 64, 32, 1, window=lim + 1, device="cpu")
+    cache = DecodeCache(1, 1, 256, 64, 32, 1, window=lim, device="cpu")
+    assert cache.window_kv.shape[3] == lim
+
+
 MAPPED = ["srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows"]
 
 

@@ -1,4 +1,4 @@
-"""The eager four-operation baseline (rotate_then_quantize_amd.eager) is held
+"""The eager four-operation baseline (eager_baseline.py, beside bench.py) is held
 to the same parity bar as the fused kernels: it is measured beside them, so
 it must compute the same thing.  CPU cases run here; the GPU case checks the
 torch.fft / GPU elementwise path that bench.py times."""
@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 import torch
 
-from rotate_then_quantize_amd import eager
+import eager_baseline as eager
 from rotate_then_quantize_amd import workloads as W
 from tests import parity
 

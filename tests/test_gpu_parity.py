@@ -215,11 +215,21 @@ def test_workload_full_size_sampled(wid, rot):
     torch.cuda.empty_cache()
 
 
-def test_zz_code_tie_rate_over_the_suite():
-    """Across every element compared above, tie mismatches stay <= 1e-5."""
-    from tests.parity import TALLY
-    if TALLY["elements"] < 1_000_000:
-        pytest.skip("too few elements compared in this session to resolve a 1e-5 rate")
-    rate = TALLY["mismatch"] / TALLY["elements"]
-    print("tie mismatches", TALLY, f"rate {rate:.2e}")
-    assert rate <= 1e-5, TALLY
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+def test_code_tie_rate_on_its_own_sample(rot):
+    """The 1e-5 bound on tie mismatches, measured over this test's own sample
+    (2^19 codes of every supported (d, group): N(0,1) rows with three x20
+    outlier channels, per-row seed rule), so it holds whatever else ran.  The
+    rate over every element the session compares is also checked when the
+    session ends (tests/conftest.py)."""
+    mism, elements = 0, 0
+    for i, (d, g) in enumerate(SHAPES):
+        n = (1 << 19) // d
+        x = outlier_rows(n, d, seed=4000 + 10 * i + (rot == "srht"))
+        codes, scales = gpu_fwd(rot, x, g, 0xC0DE + i, 97, 5)
+        st = check_forward(x, codes, scales, g, 0xC0DE + i, 97, 5, rot)
+        mism += st["code_ties"]
+        elements += st["elements"]
+    print(rot, "tie mismatches", mism, "of", elements, f"rate {mism / elements:.2e}")
+    assert elements >= (1 << 19) * len(SHAPES)
+    assert mism <= 1e-5 * elements, (mism, elements)
