@@ -5,12 +5,15 @@ One step = one pass of the whole path over one batch of synthetic K/V input:
 the forward launch (sign flip, SRFT, per-group absmax, int4 rounding, nibble
 packing) over every row, then the inverse launch (unpack, dequantize, inverse
 SRFT, sign flip, fp16 store) over every row.  The default workload is the
-SmolLM2-360M-shaped prefill KV cache (32 layers x 2 x 5 KV heads x 4096
-tokens, d = 64, groups of 32, per-layer sign seeds): 1,310,720 vectors.
+largest configuration that fits one GPU, the Gemma-3-1B-shaped long-context
+KV cache (26 layers x 2 x 16 sequences x 32768 tokens, d = 256, groups of
+32, per-layer sign seeds): 27,262,976 vectors, 17.9 GB per direction.
 
-Inputs are resident in HBM before timing starts.  Several replicas of the
-buffers are cycled so the 256 MB last-level cache cannot hold a step's data.
-Prints one JSON line on stdout (human-readable notes go to stderr).
+Inputs are resident in HBM before timing starts.  Workloads smaller than
+1 GiB cycle several replicas of the buffers so the 256 MB last-level cache
+cannot hold a step's data.  Each kernel's duration is the median of 21
+event-timed launches in a pass of its own after the timed steps.  Prints one
+JSON line on stdout (human-readable notes go to stderr).
 
   python bench.py [--steps K] [--warmup W] [--workload 1..5] [--rot srft|srht]
 
@@ -154,34 +157,84 @@ def find_csv(directory: str, suffix: str) -> str:
     return hits[0]
 
 
-def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = False, window: int = 0) -> None:
+def find_profile(directory: str, csv_suffix: str):
+    """('csv', path) when rocprofv3 wrote CSV files, else ('db', path) of its
+    SQLite (rocpd) database, the default output format."""
+    csvs, dbs = [], []
+    for root, _, files in os.walk(directory):
+        csvs += [os.path.join(root, f) for f in files if f.endswith(csv_suffix)]
+        dbs += [os.path.join(root, f) for f in files if f.endswith(".db")]
+    if len(csvs) == 1:
+        return "csv", csvs[0]
+    if len(dbs) == 1:
+        return "db", dbs[0]
+    raise SystemExit(f"expected one *{csv_suffix} or one *.db under {directory}, found {csvs + dbs}")
+
+
+def trace_dispatches(trace_dir: str):
+    """{kernel short name: [duration ns of each dispatch, in launch order]}
+    from a rocprofv3 --kernel-trace run (CSV or rocpd database)."""
+    kind, path = find_profile(trace_dir, "kernel_trace.csv")
+    if kind == "db":
+        import sqlite3
+        con = sqlite3.connect(path)
+        rows = [(n, int(b), int(e)) for n, b, e in con.execute("select name, start, end from kernels")]
+        con.close()
+    else:
+        import csv
+        raw = list(csv.DictReader(open(path)))
+        if not raw:
+            return {}
+        keys = raw[0].keys()
+        name_k = next(k for k in ("Kernel_Name", "KernelName", "Name") if k in keys)
+        beg_k = next(k for k in ("Start_Timestamp", "BeginNs", "Start") if k in keys)
+        end_k = next(k for k in ("End_Timestamp", "EndNs", "End") if k in keys)
+        rows = [(r[name_k], int(r[beg_k]), int(r[end_k])) for r in raw]
+    out = {}
+    for name, b, e in sorted(rows, key=lambda r: r[1]):
+        out.setdefault(short_kernel_name(name), []).append(e - b)
+    return out
+
+
+def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = False, window: int = 0,
+                    skip: int = 0) -> None:
     """Write the rocprofv3 --kernel-trace --stats summary of a bench run
-    (window: the fp16 window tokens of an --attn --window run)."""
-    import csv
-    rows = list(csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv"))))
+    (window: the fp16 window tokens of an --attn --window run).  The first
+    `skip` dispatches of each library kernel (the bench's set-up and warm-up
+    launches) are left out of its figures."""
+    per = trace_dispatches(trace_dir)
     what = ("decode attention" + (f" with {window} fp16 window tokens" if window else "")) if attn \
         else "forward + inverse"
     lines = [f"# rocprofv3 kernel trace, {what}, workload {w.name} (d={w.d}, group={w.group}, {rot})",
              f"# command: {command}",
              f"# kernel_source_sha: {kernel_source_hash(kernel_sources('attn_decode' if attn else 'quant_fwd', w.d))}",
-             "# kernel | calls | average us | min us | max us | share of GPU time",
+             f"# per library kernel, its first {skip} dispatch(es) (set-up and warm-up) are left out",
+             "# kernel | dispatches used (skipped) | average us | median us | min us | max us",
              ]
-    others = [r for r in rows if not short_kernel_name(r["Name"]).startswith("rtq::")]
-    for r in rows:
-        if r in others:
+    others = {k: v for k, v in per.items() if not k.startswith("rtq::")}
+    total_ns = sum(sum(v) for v in per.values()) or 1
+    used = {}
+    for name, durs in per.items():
+        if not name.startswith("rtq::"):
             continue
-        lines.append(f"{short_kernel_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}%")
+        kept = durs[skip:] if len(durs) > skip else durs
+        used[name] = kept
+        srt = sorted(kept)
+        lines.append(f"{name} | {len(kept)} ({len(durs) - len(kept)}) | {sum(kept) / len(kept) / 1e3:.2f} | "
+                     f"{srt[len(srt) // 2] / 1e3:.2f} | {srt[0] / 1e3:.2f} | {srt[-1] / 1e3:.2f}")
     if others:
         lines.append(f"other kernels (input generation, copies, baselines): {len(others)} kernels, "
-                     f"{sum(int(r['Calls']) for r in others)} calls, "
-                     f"{sum(float(r['Percentage']) for r in others):.1f}% of GPU time")
-    for r in rows:
-        role = kernel_role(r["Name"])
+                     f"{sum(len(v) for v in others.values())} calls, "
+                     f"{100.0 * sum(sum(v) for v in others.values()) / total_ns:.1f}% of GPU time")
+    for name, kept in used.items():
+        role = kernel_role(name)
         if role and (role == "attn_decode") == attn:
             bytes_launch = attn_bytes(w, window) if role == "attn_decode" else role_bytes(w, role)
-            lines.append(f"{role}_average_us: {float(r['AverageNs']) / 1e3:.3f}")
-            lines.append(f"{role}_algorithmic_GBps: {bytes_launch / float(r['AverageNs']):.1f}")
+            avg = sum(kept) / len(kept)
+            med = sorted(kept)[len(kept) // 2]
+            lines.append(f"{role}_average_us: {avg / 1e3:.3f}")
+            lines.append(f"{role}_median_us: {med / 1e3:.3f}")
+            lines.append(f"{role}_algorithmic_GBps: {bytes_launch / avg:.1f}")
     suffix = f"_window{window}" if window else ""
     path = os.path.join(ROOT, "profiles", f"kernel_trace_{'attn_' if attn else ''}{rot}_{w.name}{suffix}.txt")
     with open(path, "w") as f:
@@ -190,13 +243,27 @@ def summarize_trace(trace_dir: str, w, rot: str, command: str, attn: bool = Fals
 
 
 def pmc_per_dispatch(directory: str, counter: str):
-    """{kernel short name: mean counter value per dispatch} from a rocprofv3 --pmc run."""
-    import csv
+    """({kernel short name: mean counter value per dispatch}, {kernel: dispatches})
+    from a rocprofv3 --pmc run (CSV or rocpd database); a counter's value of
+    one dispatch is its sum over the rows recorded for that dispatch."""
+    kind, path = find_profile(directory, "counter_collection.csv")
+    per_dispatch = {}
+    if kind == "db":
+        import sqlite3
+        con = sqlite3.connect(path)
+        rows = con.execute("select kernel_name, dispatch_id, value from counters_collection where counter_name = ?",
+                           (counter,)).fetchall()
+        con.close()
+    else:
+        import csv
+        rows = [(r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")), r["Counter_Value"])
+                for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+    for name, did, val in rows:
+        key = (short_kernel_name(name), did)
+        per_dispatch[key] = per_dispatch.get(key, 0.0) + float(val)
     acc = {}
-    for r in csv.DictReader(open(find_csv(directory, "counter_collection.csv"))):
-        if r["Counter_Name"] != counter:
-            continue
-        acc.setdefault(short_kernel_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    for (name, _), v in per_dispatch.items():
+        acc.setdefault(name, []).append(v)
     return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
@@ -205,16 +272,17 @@ VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "
 SIMDS, CLOCK_HZ = 1024, 2.4e9  # MI355X: 256 CUs x 4 SIMDs, peak engine clock
 
 
-def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bool = False) -> None:
+def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bool = False, skip: int = 0) -> None:
     """Instruction mix per wave of each library kernel from one rocprofv3 --pmc
     pass of SQ counters (chip totals per dispatch), and the VALU issue time it
     implies: a wave64 VALU instruction occupies its SIMD for 4 cycles, so
     busy = SQ_INSTS_VALU * 4 / (SIMDs * clock * kernel time), with the kernel
     time from a rocprofv3 trace of the same command and the peak clock."""
-    import csv
     per = {c: pmc_per_dispatch(pmc_dir, c) for c in VALU_COUNTERS}
-    durs = {short_kernel_name(r["Name"]): float(r["AverageNs"])
-            for r in csv.DictReader(open(find_csv(trace_dir, "kernel_stats.csv")))}
+    durs = {}
+    for name, ds in trace_dispatches(trace_dir).items():
+        kept = ds[skip:] if len(ds) > skip else ds
+        durs[name] = sum(kept) / len(kept)
     for kname, waves in per["SQ_WAVES"][0].items():
         role = kernel_role(kname)
         if not role or (role == "attn_decode") != attn or kname not in durs or waves <= 0:
@@ -370,23 +438,55 @@ def graph_replay(w, sets, replicas, fwd_fn, inv_fn, steps, bpv, replays=5):
     }
 
 
-def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warmup=3):
+def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=3, warmup=1):
     """The same step as four separate torch operations (rotate with torch.fft,
-    quantize, dequantize, inverse rotate) on the same buffers; signs are a
-    precomputed tensor.  Measurement only."""
+    quantize, dequantize, inverse rotate) on the same buffers; signs are
+    precomputed.  Workloads whose fp32 intermediates would not fit are run in
+    row chunks of whole seed blocks (each chunk's signs are one broadcast
+    row), every chunk still as the four operations.  Measurement only."""
     import torch
     import eager_baseline as eager
     n_inv = w.n_rows
     n_fwd = w.new_rows if w.new_tokens else w.n_rows
-    signs_inv = eager.sign_matrix(n_inv, w.d, w.sign_seed, w.rows_per_seed, w.seed_period)
-    signs_fwd = signs_inv[n_inv - n_fwd:] if w.new_tokens else signs_inv
+    budget = 1 << 30  # bytes of one fp32 [rows, d] intermediate per chunk
+    rps, per = w.rows_per_seed, w.seed_period
+    if n_inv * w.d * 4 <= 4 * budget:
+        chunk_rows, repeat = n_inv, False
+    elif rps and per and rps * per * w.d * 4 <= budget:
+        # whole cycles of the seed rule: every chunk has the first chunk's signs
+        chunk_rows, repeat = rps * per * max(1, budget // (rps * per * w.d * 4)), True
+    elif rps and rps * w.d * 4 <= budget:
+        chunk_rows, repeat = rps, False  # one seed block per chunk: its signs are one row
+    else:
+        raise SystemExit("eager baseline: no chunking rule for this workload")
+    chunks, first = [], None
+    for r0 in range(0, n_inv, chunk_rows):
+        r1 = min(n_inv, r0 + chunk_rows)
+        if chunk_rows == n_inv:
+            sg = eager.sign_matrix(n_inv, w.d, w.sign_seed, rps, per)
+        elif repeat:
+            if first is None:
+                first = eager.sign_matrix(chunk_rows, w.d, w.sign_seed, rps, per)
+            sg = first[:r1 - r0]
+        else:
+            sg = eager.sign_matrix(1, w.d, w.sign_seed, rps, per, row0=r0)
+        chunks.append((r0, r1, sg))
+    if w.new_tokens:  # the decode step quantizes only the new token's rows
+        fwd_chunks = [(n_inv - n_fwd, n_inv,
+                       eager.sign_matrix(n_fwd, w.d, w.sign_seed, rps, per, row0=n_inv - n_fwd))]
+    else:
+        fwd_chunks = chunks
 
     def step(i):
         x, codes, scales, _ = sets[i % replicas][2]
-        xin = x[n_inv - n_fwd:] if w.new_tokens else x
-        c, s = eager.quant_fwd(xin, w.group, 0, rot=rot, signs=signs_fwd)
         _, codes2, scales2, _ = sets[(i + 1) % replicas][2]
-        return c, s, eager.dequant_inv(codes2, scales2, w.d, w.group, 0, rot=rot, signs=signs_inv)
+        out = []
+        for r0, r1, sg in fwd_chunks:
+            out.append(eager.quant_fwd(x[r0:r1], w.group, 0, rot=rot, signs=sg))
+        for r0, r1, sg in chunks:
+            out.append(eager.dequant_inv(codes2[r0:r1], scales2[r0:r1], w.d, w.group, 0, rot=rot, signs=sg))
+            del out[-1]
+        return out
 
     for i in range(warmup):
         step(i)
@@ -398,12 +498,15 @@ def eager_baseline(w, sets, replicas, rot, fused_ms_step, stream, steps=20, warm
     ev[1].record(stream)
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / steps
+    torch.cuda.empty_cache()
     return {
         "ms_per_step": ms,
         "value": max(n_fwd, n_inv) / (ms * 1e-3),
         "unit": "vectors/s",
         "fused_speedup": ms / fused_ms_step,
         "steps": steps,
+        "row_chunks": len(chunks),
+        "chunk_rows": chunk_rows,
         "ops": "rotate (torch.fft.rfft or Hadamard matmul), quantize, dequantize, inverse rotate (irfft): "
                "separate torch operations on the GPU, fp32 intermediates in HBM",
     }
@@ -654,7 +757,7 @@ def attn_main(args, w, dev):
         },
         "valu": None if W else read_valu(w.name, rot, "attn_decode", w.d),
     }
-    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
+    result["hbm_copy"] = measured_copy(dev)
     if not args.no_eager and not W:
         result["unfused_baseline"] = attn_unfused_baseline(w, rot, ms_step, dev)
     if not args.no_cpu_baseline and not W:
@@ -874,7 +977,7 @@ def ext_main(args, w, dev):
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
     }
-    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
+    result["hbm_copy"] = measured_copy(dev)
     print(json.dumps(result), flush=True)
 
 
@@ -907,10 +1010,33 @@ def measured_copy(dev, mib: int = 1024, reps: int = 10) -> dict:
             "kind": f"torch device-to-device copy, (read + written bytes) / median of {reps} event-timed copies"}
 
 
-def with_achievable(roof: dict, copy: dict) -> dict:
-    roof["achievable"] = copy["GBps"]
-    roof["frac_of_achievable"] = roof["achieved"] / copy["GBps"]
-    return roof
+def time_launches(fn, arg_sets, stream, min_ms: float = 1.0):
+    """Median, min and max duration in ms of one launch of fn(*a), a cycling
+    through arg_sets: each of len(arg_sets) samples is R back-to-back launches
+    between two events recorded on `stream` (the launch stream), divided by R.
+    R = 1 when one launch takes at least min_ms; shorter kernels take enough
+    launches per sample to fill min_ms, so the few microseconds an event
+    marker costs do not count as kernel time."""
+    import torch
+
+    def sample(r, k0):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for j in range(r):
+            st = fn(*arg_sets[(k0 + j) % len(arg_sets)])
+            if st:
+                raise RuntimeError(f"launch failed with status {st}")
+        e1.record(stream)
+        return e0, e1
+
+    torch.cuda.synchronize()
+    e0, e1 = sample(1, 0)
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(min_ms / max(e0.elapsed_time(e1), 1e-3)))
+    evs = [sample(reps, k) for k in range(len(arg_sets))]
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) / reps for e0, e1 in evs)
+    return ms[len(ms) // 2], (ms[0], ms[-1]), reps
 
 
 def main():
@@ -919,7 +1045,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", type=int, default=None, choices=[1, 2, 3, 4, 5],
-                    help="workload id (default 2; 3 with --attn)")
+                    help="workload id (default 5; 3 with --attn or --decode-cache)")
     ap.add_argument("--attn", action="store_true",
                     help="measure decode attention over the int4 cache instead of forward + inverse")
     ap.add_argument("--ext", action="store_true",
@@ -943,6 +1069,8 @@ def main():
                     help="only run a plain device copy of MIB MiB a few times (PMC counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="write profiles/kernel_trace_*.txt from a rocprofv3 --kernel-trace --stats CSV directory")
+    ap.add_argument("--trace-skip", type=int, default=0, metavar="N",
+                    help="with --summarize-trace: leave each library kernel's first N dispatches out")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/traffic_*.txt from four rocprofv3 --pmc CSV directories")
     ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC", "TRACE"),
@@ -954,16 +1082,17 @@ def main():
     if args.window and (not args.attn or not 0 < args.window <= 64):
         ap.error("--window takes 1 to 64 tokens and goes with --attn")
     if args.workload is None:
-        args.workload = 3 if (args.attn or args.decode_cache) else 2
+        args.workload = 3 if (args.attn or args.decode_cache) else 5
 
     if args.summarize_trace or args.summarize_traffic or args.summarize_valu:
         from rotate_then_quantize_amd import workloads as W
         w = W.WORKLOADS[args.workload]
         if args.summarize_valu:
             summarize_valu(*args.summarize_valu, w, args.rot, [("SQ counters", c) for c in args.command[-1:]],
-                           args.attn)
+                           args.attn, args.trace_skip)
         if args.summarize_trace:
-            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn, args.window)
+            summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn, args.window,
+                            args.trace_skip)
         if args.summarize_traffic:
             names = ("FETCH_SIZE", "WRITE_SIZE", "copy FETCH_SIZE", "copy WRITE_SIZE")
             cmds = list(zip(names, args.command[-4:])) if len(args.command) >= 4 else []
@@ -1069,26 +1198,22 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # Kernel durations come from events on every SAMPLE-th timed step: one
-    # before the forward, one between the two launches, one after the inverse.
-    # An event marker costs a few microseconds of GPU idle time, so the other
-    # steps run without markers.
-    SAMPLE = 20
-    sampled = [i for i in range(args.steps) if i % SAMPLE == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in sampled}
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev = evs.get(i)
-        step(args.warmup + i, ev[0] if ev else None, ev[1] if ev else None)
-        if ev:
-            ev[2].record(stream)
+        step(args.warmup + i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
     ms_step = (t1 - t0) * 1e3 / args.steps
-    fwd_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in sampled) / len(sampled)
-    inv_ms = sum(evs[i][1].elapsed_time(evs[i][2]) for i in sampled) / len(sampled)
+
+    # Kernel durations: KERNEL_REPS event-timed samples of each kernel on its
+    # own, after the timed steps (so --steps does not change how many samples
+    # there are); the median of the per-launch durations (time_launches).
+    # Launches cycle the replicas as the steps do.
+    KERNEL_REPS = 21
+    fwd_ms, fwd_spread, fwd_reps = time_launches(fwd_fn, [sets[i % replicas][0] for i in range(KERNEL_REPS)],
+                                                 stream)
+    inv_ms, inv_spread, inv_reps = time_launches(inv_fn, [sets[(i + 1) % replicas][1] for i in range(KERNEL_REPS)],
+                                                 stream)
     fwd_bytes, inv_bytes = n_fwd * bpv, n_inv * bpv
     fwd_gbps, inv_gbps = fwd_bytes / fwd_ms / 1e6, inv_bytes / inv_ms / 1e6
     vectors = max(n_fwd, n_inv)
@@ -1124,8 +1249,12 @@ def main():
         "hbm_gbps": {"step": step_gbps, "forward": fwd_gbps, "inverse": inv_gbps,
                      "peak": HBM_PEAK_GBPS, "bytes_per_vector": bpv},
         "kernel_us": {"forward": fwd_ms * 1e3, "inverse": inv_ms * 1e3,
-                      "timing": f"hipEvents on the launch stream, every {SAMPLE}th timed step "
-                                f"({len(sampled)} of {args.steps})"},
+                      "forward_min_max": [fwd_spread[0] * 1e3, fwd_spread[1] * 1e3],
+                      "inverse_min_max": [inv_spread[0] * 1e3, inv_spread[1] * 1e3],
+                      "launches_per_sample": [fwd_reps, inv_reps],
+                      "timing": f"median of {KERNEL_REPS} samples per kernel, each sample a run of back-to-back "
+                                "launches (one launch when a launch takes 1 ms or more) between two hipEvents on "
+                                "the launch stream, in a pass after the timed steps"},
         "roofline": {
             "kernel": f"{rot}_{kname} d={w.d} g={w.group}",
             "bound": "hbm",
@@ -1137,7 +1266,7 @@ def main():
         },
         "valu": read_valu(w.name, rot, kname, w.d),
     }
-    result["roofline"] = with_achievable(result["roofline"], measured_copy(dev))
+    result["hbm_copy"] = measured_copy(dev)
     if not args.no_graph:
         result["graph_replay"] = graph_replay(w, sets, replicas, fwd_fn, inv_fn, args.steps, bpv)
     if not args.no_eager:

@@ -35,9 +35,9 @@ def _splitmix_sign_bits(seeds: np.ndarray, d: int) -> np.ndarray:
 
 
 def sign_matrix(n: int, d: int, seed: int, rows_per_seed: int = 0, seed_period: int = 0,
-                device="cuda") -> torch.Tensor:
-    """[n, d] float32 +-1 signs of rows 0..n-1 under the per-row seed rule."""
-    rows = np.arange(n, dtype=np.int64)
+                device="cuda", row0: int = 0) -> torch.Tensor:
+    """[n, d] float32 +-1 signs of rows row0 .. row0+n-1 under the per-row seed rule."""
+    rows = np.arange(row0, row0 + n, dtype=np.int64)
     if rows_per_seed:
         block = rows // rows_per_seed
         if seed_period:

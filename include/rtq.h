@@ -257,7 +257,7 @@ rtq_status srht_dequant_rows(const void* codes_u8, const void* scales_f16, void*
  *   otherwise RTQ_ERR_INVALID_ARG.
  *
  * Supported: (d, group) in {(64,32), (64,64), (128,32), (128,64), (128,128),
- * (256,32), (256,64), (256,128)} and 1 <= q_per_kv <= 8, else
+ * (256,32), (256,64), (256,128), (256,256)} and 1 <= q_per_kv <= 8, else
  * RTQ_ERR_UNSUPPORTED.  tokens >= 1, strides >= 0,
  * layers * streams < 2^31, softmax_scale finite, else RTQ_ERR_INVALID_ARG; layers == 0
  * or streams == 0 returns RTQ_OK and touches nothing.  The caller guarantees

@@ -32,13 +32,13 @@ _lib = None
 
 RTQ_OK, RTQ_ERR_INVALID_ARG, RTQ_ERR_UNSUPPORTED, RTQ_ERR_HIP = 0, 1, 2, 3
 # (d, group) pairs the library is built for
-SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128), (256, 256)}
 # (d, group) pairs of the decode-attention kernels; at most 8 query heads per K/V head
-ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+ATTN_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128), (256, 256)}
 # (d, group) pairs of the cache-layout entry points (*_quant_append, *_dequant_rows) and of the
 # code-width / lambda entry points (*_ext)
-CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
-EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128)}
+CACHE_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128), (256, 256)}
+EXT_SUPPORTED = {(64, 32), (64, 64), (128, 32), (128, 64), (128, 128), (256, 32), (256, 64), (256, 128), (256, 256)}
 ATTN_MAX_Q_PER_KV = 8
 # fp16 window tokens per stream that *_attn_decode_window accepts
 ATTN_MAX_WINDOW = 64

@@ -275,21 +275,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
 // rows of a contiguous [n, 256] tensor.
 // ---------------------------------------------------------------------------
 
-// The forward with groups of 32 fits three waves per SIMD without spills
-// (it quantizes each group as soon as its values are complete); larger
-// groups would spill.
+// Three waves per SIMD (at most 168 VGPRs): every group size fits without
+// spills.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 2, 8))) void fwd_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void fwd_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, SeedRule sr,
     SignTable tb) {
   __shared__ uint4 lds[32 * 33];
   fwd_pair_tile<G, ROT>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x);
 }
 
-// The SRFT inverse fits three waves per SIMD with a few spilled registers,
-// which measured 4-5% faster than two; the SRHT inverse would spill far more.
+// Three waves per SIMD: the SRHT inverse fits without spills, the SRFT
+// inverse spills a few addresses that are used only by the final stores.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT ? 3 : 2, 8))) void inv_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_pair_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y, uint32_t n,
     SeedRule sr, SignTable tb) {
   __shared__ uint4 lds[32 * 17];
@@ -350,7 +349,7 @@ KernelFn find_kernel(bool fwd, int d, int g) {
   if (d == DD && g == GG) return fwd ? pick_fwd<DD, GG, ROT>() : pick_inv<DD, GG, ROT>();
   RTQ_CASE(64, 32) RTQ_CASE(64, 64)
   RTQ_CASE(128, 32) RTQ_CASE(128, 64) RTQ_CASE(128, 128)
-  RTQ_CASE(256, 32) RTQ_CASE(256, 64) RTQ_CASE(256, 128)
+  RTQ_CASE(256, 32) RTQ_CASE(256, 64) RTQ_CASE(256, 128) RTQ_CASE(256, 256)
 #undef RTQ_CASE
   return nullptr;
 }

@@ -736,9 +736,11 @@ attn_decode_kernel(Params p) {
 
   // ---- prologue: queries (lead waves) and the first two chunks (every wave) ----
   uint4 qv[C::DENSE_ROT ? 1 : D / 8];
-  if (!C::DENSE_ROT && lead && lane < G) {
-    const uint4* src = p.q + (qrow + lane) * (D / 8);
-    sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
+  if constexpr (!C::DENSE_ROT) {
+    if (lead && lane < G) {
+      const uint4* src = p.q + (qrow + lane) * (D / 8);
+      sfor<D / 8>([&](auto I) { qv[RTQ_CI(I)] = src[RTQ_CI(I)]; });
+    }
   }
   const ChunkSources<D, GR> src(p, row_k, row_v, lane);
   // a chunk is full unless it holds the stream's last token
@@ -1162,7 +1164,7 @@ KernelFn find_kernel(int d, int g) {
   if (d == DD && g == GG) return reinterpret_cast<KernelFn>(&attn_decode_kernel<DD, GG, ROT>);
   RTQ_ATTN_CASE(64, 32) RTQ_ATTN_CASE(64, 64)
   RTQ_ATTN_CASE(128, 32) RTQ_ATTN_CASE(128, 64) RTQ_ATTN_CASE(128, 128)
-  RTQ_ATTN_CASE(256, 32) RTQ_ATTN_CASE(256, 64) RTQ_ATTN_CASE(256, 128)
+  RTQ_ATTN_CASE(256, 32) RTQ_ATTN_CASE(256, 64) RTQ_ATTN_CASE(256, 128) RTQ_ATTN_CASE(256, 256)
 #undef RTQ_ATTN_CASE
   return nullptr;
 }

@@ -159,19 +159,18 @@ __device__ __forceinline__ MappedTileRows mapped_tile_rows(uint32_t n, const Row
   return MappedTileRows{row0, rows, uniform, s0, m, rs};
 }
 
-// The forward with groups of 32 fits three waves per SIMD without spills.
+// Three waves per SIMD, as the plain forward.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(G == 32 ? 3 : 2, 8))) void fwd_mapped_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void fwd_mapped_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, RowMap m,
     RowSeeds rs) {
   __shared__ uint4 lds[32 * 33];
   fwd_pair_tile<G, ROT>(x, codes, scales, mapped_tile_rows(n, m, rs), lds, threadIdx.x);
 }
 
-// The SRFT inverse runs three waves per SIMD with a few spilled registers
-// (4-5% faster than two); the SRHT one would spill far more.
+// Three waves per SIMD, as the plain inverse.
 template <int G, int ROT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT ? 3 : 2, 8))) void inv_mapped_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_mapped_pair_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y, uint32_t n, RowMap m,
     RowSeeds rs) {
   __shared__ uint4 lds[32 * 17];
@@ -191,7 +190,7 @@ KernelFn find_mapped(bool fwd, int d, int g) {
   if (d == 256 && g == GG)                                                             \
     return fwd ? reinterpret_cast<KernelFn>(&fwd_mapped_pair_kernel<GG, ROT>)          \
                : reinterpret_cast<KernelFn>(&inv_mapped_pair_kernel<GG, ROT>);
-  RTQ_MAPPED_PAIR_CASE(32) RTQ_MAPPED_PAIR_CASE(64) RTQ_MAPPED_PAIR_CASE(128)
+  RTQ_MAPPED_PAIR_CASE(32) RTQ_MAPPED_PAIR_CASE(64) RTQ_MAPPED_PAIR_CASE(128) RTQ_MAPPED_PAIR_CASE(256)
 #undef RTQ_MAPPED_PAIR_CASE
   return nullptr;
 }

@@ -156,11 +156,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   fwd_pair_tile<G, ROT, TileRows, B>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
 }
 
-// The 4-bit SRFT inverse runs three waves per SIMD with a few spilled
-// registers (4-5% faster than two); the other widths and SRHT would spill
-// far more.
+// Three waves per SIMD (the SRFT inverses spill a few addresses that only
+// the final stores use).
 template <int G, int ROT, int B>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(ROT == kSRFT && B == 4 ? 3 : 2, 8))) void inv_ext_pair_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_ext_pair_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y,
     const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
   __shared__ uint4 lds[32 * 17];
@@ -181,7 +180,7 @@ KernelFn find_ext_bits(bool fwd, int d, int g) {
   if (d == 256 && g == GG)                                                             \
     return fwd ? reinterpret_cast<KernelFn>(&fwd_ext_pair_kernel<GG, ROT, B>)          \
                : reinterpret_cast<KernelFn>(&inv_ext_pair_kernel<GG, ROT, B>);
-  RTQ_EXT_PAIR_CASE(32) RTQ_EXT_PAIR_CASE(64) RTQ_EXT_PAIR_CASE(128)
+  RTQ_EXT_PAIR_CASE(32) RTQ_EXT_PAIR_CASE(64) RTQ_EXT_PAIR_CASE(128) RTQ_EXT_PAIR_CASE(256)
 #undef RTQ_EXT_PAIR_CASE
   return nullptr;
 }

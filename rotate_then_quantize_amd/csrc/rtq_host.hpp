@@ -36,13 +36,12 @@ inline bool ranges_overlap(const void* a, int64_t na, const void* b, int64_t nb)
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Supported (d, group): d in {64,128,256}; group in {32,64,128,256}, group <= d.
-// (d = 256, group = 256) is a per-token scale over two lanes and is not built.
+// Supported (d, group): d in {64,128,256}; group in {32,64,128,256}, group <= d
+// (group == d is one scale per vector, the per-token recipe).
 inline rtq_status check_shape(int32_t d, int32_t g) {
   if (d != 64 && d != 128 && d != 256) return RTQ_ERR_UNSUPPORTED;
   if (g != 32 && g != 64 && g != 128 && g != 256) return RTQ_ERR_UNSUPPORTED;
   if (g > d) return RTQ_ERR_UNSUPPORTED;
-  if (d == 256 && g == 256) return RTQ_ERR_UNSUPPORTED;
   return RTQ_OK;
 }
 

@@ -1,8 +1,9 @@
 // rtq_pair.hpp -- d = 256 tiles of the fused rotate-then-quantize kernels
-// (MI355X, gfx950): two lanes per vector (lane v and lane v + 32), 32
-// vectors per tile.  The tiles are written once and used by the plain
-// entry points (rows of a contiguous [n, 256] tensor) and by the cache-layout
-// entry points (rows placed by strides), through a row policy:
+// (MI355X, gfx950): two lanes per vector (lane v and lane v + 32, "half 0"
+// and "half 1" of the pair), 32 vectors per tile.  The tiles are written once
+// and used by the plain entry points (rows of a contiguous [n, 256] tensor)
+// and by the cache-layout entry points (rows placed by strides), through a
+// row policy:
 //
 //   struct Rows {
 //     uint32_t row0;  // first row of the tile in the input numbering
@@ -15,15 +16,38 @@
 //     uint4* y_chunk(uint4* y, int rl, uint32_t k) const;  // 16-byte chunk k of row rl of y
 //   };
 //
-//   SRFT: lane p holds the samples u_{2m+p} (m = 0..127), computes their real
-//     DFT of length 128 (E for p = 0, O for p = 1), both lanes exchange E and O
-//     (ds_bpermute), and combine X_a = E_a + w^a O_a (lane 0, bins 0..64) and
-//     X_{128-a} = conj(E_a - w^a O_a) (lane 1, bins 64..128).  Lane 1 keeps its
-//     coordinates mirrored (local index 127 - i) with Re/Im swapped, which
-//     makes its register layout identical to lane 0's; the mirror is undone
-//     on the packed codes and scales.
-//   SRHT: lane p holds the contiguous half p; H_256 = H_2 (x) H_128, so each
-//     lane applies H_128 and the halves combine as F0 + F1 / F0 - F1.
+// Coordinates of the packed rotated vector each half holds, as two segments
+// of 64 (its registers L[0..63] and L[64..127], in order):
+//   SRFT: half 0 coordinates [0, 64) and [192, 256), half 1 [64, 128) and [128, 192);
+//   SRHT: half 0 coordinates [0, 64) and [128, 192), half 1 [64, 128) and [192, 256).
+// A group of 32 or 64 coordinates lies in one lane, and a lane's codes and
+// scales are whole runs of the row's bytes; a group of 128 or 256 spans the
+// pair and its absmax is reduced across it.  Both halves run the same
+// instructions on their own data.
+//
+// The halves exchange values with v_permlane32_swap (one VALU instruction per
+// register pair, no LDS).  Swapping registers A and B leaves lane v with
+// (A of lane v, A of lane v + 32) and lane v + 32 with (B of lane v, B of
+// lane v + 32) in (A, B).
+//
+//   SRFT forward: half p holds the samples u_{2m+p} (m = 0..127) and computes
+//     the unnormalized real DFT of its 128 samples, E (p = 0) or O (p = 1),
+//     bins 0..64.  With w = exp(-2 pi i / 256), X_b = E_b + w^b O_b and
+//     X_{128-b} = conj(E_b - w^b O_b).  For a = 1..31, half 0 forms bins a and
+//     128 - a, half 1 bins a + 32 and 96 - a: one swap of bin registers a and
+//     a + 32 gives half 0 (E_a, O_a) and half 1 (E_{a+32}, O_{a+32}), and each
+//     half reads its own twiddle w^b from an LDS table.  Bins 0, 32 and 64 are
+//     formed in both halves and each keeps the coordinates it owns.
+//   SRFT inverse: the same exchange backwards: each half forms E and O of its
+//     bins from X_b and X_{128-b}, one swap gives half 0 every E_b and half 1
+//     every O_b, and each half runs the inverse real DFT of 128 points.
+//   SRHT: H_256 = H_2 (x) H_128.  Forward: half p holds the contiguous half p
+//     of the samples and applies H_128 (F_p); one swap of registers k and
+//     k + 64 gives half 0 (F_0[k], F_1[k]) and half 1 (F_0[k+64], F_1[k+64]),
+//     whose sum and difference are the coordinates each owns.  Inverse: each
+//     half forms z_i + z_{128+i} and z_i - z_{128+i} of its coordinates, one
+//     swap gives half 0 every sum and half 1 every difference, and each
+//     applies H_128.
 //
 // Method: "Quantization Speed Is Often a Kernel Problem", "First, the 17%"
 // and "Fusing four steps into two kernels is not enough" (rotate + quantize
@@ -101,6 +125,13 @@ __device__ __forceinline__ void unweight_half(float (&u)[128], const float* inv,
   });
 }
 
+// Words Q .. Q + 3 of w count as computed here (an empty asm that claims to
+// change them): later code cannot move their computation past this point.
+template <int Q, int N>
+__device__ __forceinline__ void pin_words(uint32_t (&w)[N]) {
+  asm volatile("" : "+v"(w[Q]), "+v"(w[Q + 1]), "+v"(w[Q + 2]), "+v"(w[Q + 3]));
+}
+
 // Non-temporal store for streaming tiles, ordinary (L2-merged) store for rows
 // scattered by a cache layout.
 template <bool NT, class T>
@@ -108,6 +139,335 @@ __device__ __forceinline__ void put_store(T* p, T v) {
   if constexpr (NT) stream_store(p, v);
   else *p = v;
 }
+
+// ---------------------------------------------------------------------------
+// Lane-pair exchange
+// ---------------------------------------------------------------------------
+
+// (a, b) <- v_permlane32_swap(a, b): lane v ends with (a of lane v, a of lane
+// v + 32), lane v + 32 with (b of lane v, b of lane v + 32).
+__device__ __forceinline__ void pair_swap(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// x of lane v (lo) and of lane v + 32 (hi), in both lanes of the pair.
+__device__ __forceinline__ void pair_both(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+// Block of 64 packed coordinates that segment s (0 or 1) of half p holds.
+template <int ROT>
+__device__ __forceinline__ uint32_t seg_block(int p, int s) {
+  if constexpr (ROT == kSRFT) return p ? 1u + (uint32_t)s : 3u * (uint32_t)s;  // half 0: 0, 3; half 1: 1, 2
+  else return (uint32_t)p + 2u * (uint32_t)s;                                   // half 0: 0, 2; half 1: 1, 3
+}
+
+// cos and sin of 2 pi b / 256 for b = 0 .. 63 (the twiddles w^b = c - i s of
+// the pair exchange), from the same compile-time evaluation as the
+// transforms' constants.  Copied into LDS once per tile; half p reads entry
+// a + 32 p.
+struct PairTwiddles {
+  float cs[128];
+};
+consteval PairTwiddles make_pair_twiddles() {
+  PairTwiddles t{};
+  for (int b = 0; b < 64; ++b) {
+    t.cs[2 * b] = (float)cos2pi(b, 256);
+    t.cs[2 * b + 1] = (float)sin2pi(b, 256);
+  }
+  return t;
+}
+static __constant__ PairTwiddles kPairTwiddles = make_pair_twiddles();
+
+__device__ __forceinline__ void load_pair_twiddles(float* tw, int lane) {
+  reinterpret_cast<float2*>(tw)[lane] = reinterpret_cast<const float2*>(kPairTwiddles.cs)[lane];
+}
+
+// ---------------------------------------------------------------------------
+// Groups of a lane's 128 coordinates
+// ---------------------------------------------------------------------------
+
+// Local groups: LG coordinates each (G for groups of 32 and 64; 64 for the
+// groups of 128 and 256 that span the pair).
+template <int G> struct PairGroups {
+  static constexpr int LG = G <= 64 ? G : 64;
+  static constexpr int NLG = 128 / LG;
+};
+
+// max |L[i]| over local group GI.
+template <int GI, int LG>
+__device__ __forceinline__ float local_absmax(const float (&L)[128]) {
+  float a = 0.0f;
+  sfor<LG>([&](auto I) { a = fmaxf(a, fabsf(L[GI * LG + RTQ_CI(I)])); });
+  return a;
+}
+
+// Quantize local group GI of (zs * L) with the group's absmax a_raw (of the
+// unscaled values, over the whole group wherever it lies): s = fp16_rne(
+// zs * a_raw / 2^(B-1)) saturated at 65504, q = clamp(rne(zs * L / s),
+// -2^(B-1), 2^(B-1) - 1), q = 0 when s == 0.  Codes form the lane's bit
+// stream (code j at bits [j B, (j + 1) B) of cw; for B = 4 the nibble
+// layout, two codes per byte, even code low).  The rounding is
+// fma(L, 1/s', 1.5 * 2^23): its fp32 result lies in [2^23, 2^24), where the
+// spacing is 1, so the fma's single rounding is round-half-even of L / s'
+// and the low bits are q in two's complement.  For B != 4 the caller zeroes
+// cw first.
+template <int GI, int LG, int B>
+__device__ __forceinline__ void quantize_local_group(const float (&L)[128], float zs, float a_raw,
+                                                     uint32_t (&cw)[4 * B], uint32_t (&sb)[128 / LG]) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  constexpr float kLo = -(float)(1 << (B - 1)), kHi = (float)((1 << (B - 1)) - 1);
+  constexpr float kInvRange = 1.0f / (float)(1 << (B - 1));
+  constexpr int g0 = GI * LG;
+  const float a = a_raw * zs;
+  uint32_t bits = __half_as_ushort(__float2half_rn(a * kInvRange));
+  bits = bits < 0x7bffu ? bits : 0x7bffu;  // saturate (inf -> 65504)
+  sb[GI] = bits;
+  const float s = __half2float(__ushort_as_half((unsigned short)bits));
+  const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
+  if constexpr (B == 4) {
+    sfor<LG / 8>([&](auto W) {
+      constexpr int base = g0 + RTQ_CI(W) * 8;
+      uint32_t b[8];
+      sfor<8>([&](auto I) {
+        const float t = __builtin_fmaf(L[base + RTQ_CI(I)], inv, kMagic);
+        b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic + kLo, kMagic + kHi));
+      });
+      // low bytes of the even codes -> e, of the odd codes -> o
+      const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
+      const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
+      cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+    });
+  } else {
+    constexpr uint32_t kMask = (1u << B) - 1u;
+    sfor<LG>([&](auto I) {
+      constexpr int i = g0 + RTQ_CI(I);
+      constexpr int pos = i * B, w = pos / 32, sh = pos % 32;
+      const float t = __builtin_amdgcn_fmed3f(__builtin_fmaf(L[i], inv, kMagic), kMagic + kLo, kMagic + kHi);
+      const uint32_t f = __float_as_uint(t) & kMask;
+      cw[w] |= f << sh;
+      if constexpr (sh + B > 32) cw[w + 1] |= f >> (32 - sh);
+    });
+  }
+}
+
+// Quantize every local group of a lane (groups of G, B-bit codes), with the
+// absmax of groups that span the pair (G = 128, 256) reduced across it.
+template <int G, int B>
+__device__ __forceinline__ void quantize_pair_groups(const float (&L)[128], float zs, uint32_t (&cw)[4 * B],
+                                                     uint32_t (&sb)[PairGroups<G>::NLG]) {
+  constexpr int LG = PairGroups<G>::LG;
+  if constexpr (G <= 64) {
+    sfor<128 / LG>([&](auto GI) {
+      constexpr int gi = RTQ_CI(GI);
+      quantize_local_group<gi, LG, B>(L, zs, local_absmax<gi, LG>(L), cw, sb);
+    });
+  } else {
+    // local group k lies in global group k (G = 128) or 0 (G = 256) in both halves
+    float a0 = local_absmax<0, 64>(L), a1 = local_absmax<1, 64>(L);
+    float m0, m1;
+    if constexpr (G == 128) {
+      pair_swap(a0, a1);                  // lane v: (a0, a0 of v + 32); lane v + 32: (a1 of v, a1)
+      pair_both(fmaxf(a0, a1), m0, m1);   // group 0's absmax from lane v, group 1's from lane v + 32
+    } else {
+      float lo, hi;
+      pair_both(fmaxf(a0, a1), lo, hi);
+      m0 = m1 = fmaxf(lo, hi);
+    }
+    quantize_local_group<0, 64, B>(L, zs, m0, cw, sb);
+    quantize_local_group<1, 64, B>(L, zs, m1, cw, sb);
+  }
+}
+
+// A lane's codes (two segments of 64 B-bit codes, 8 B bytes each) to or from
+// its row of 32 B bytes: segment s goes to bytes 8 B seg_block(p, s).  Even
+// B moves 16-byte pieces, B = 3 8-byte pieces.
+template <int ROT, int B, bool NT>
+__device__ __forceinline__ void store_pair_codes(uint4* codes, size_t row, int p, const uint32_t (&cw)[4 * B]) {
+  if constexpr (B % 2 == 0) {
+    constexpr int PS = B / 2;  // 16-byte pieces per segment
+    sfor<2>([&](auto S) {
+      uint4* dst = codes + row * (2 * B) + seg_block<ROT>(p, RTQ_CI(S)) * PS;
+      sfor<PS>([&](auto C) {
+        constexpr int w = (RTQ_CI(S) * PS + RTQ_CI(C)) * 4;
+        put_store<NT>(dst + RTQ_CI(C), make_uint4(cw[w], cw[w + 1], cw[w + 2], cw[w + 3]));
+      });
+    });
+  } else {
+    uint2* base = reinterpret_cast<uint2*>(codes);
+    sfor<2>([&](auto S) {
+      uint2* dst = base + row * (4 * B) + seg_block<ROT>(p, RTQ_CI(S)) * B;
+      sfor<B>([&](auto C) {
+        constexpr int w = (RTQ_CI(S) * B + RTQ_CI(C)) * 2;
+        put_store<NT>(dst + RTQ_CI(C), make_uint2(cw[w], cw[w + 1]));
+      });
+    });
+  }
+}
+
+template <int ROT, int B>
+__device__ __forceinline__ void load_pair_codes(const uint4* codes, size_t row, int p, uint32_t (&cw)[4 * B]) {
+  if constexpr (B % 2 == 0) {
+    constexpr int PS = B / 2;
+    sfor<2>([&](auto S) {
+      const uint4* src = codes + row * (2 * B) + seg_block<ROT>(p, RTQ_CI(S)) * PS;
+      sfor<PS>([&](auto C) {
+        constexpr int w = (RTQ_CI(S) * PS + RTQ_CI(C)) * 4;
+        const uint4 q = stream_load(src + RTQ_CI(C));
+        cw[w] = q.x;
+        cw[w + 1] = q.y;
+        cw[w + 2] = q.z;
+        cw[w + 3] = q.w;
+      });
+    });
+  } else {
+    const uint2* base = reinterpret_cast<const uint2*>(codes);
+    sfor<2>([&](auto S) {
+      const uint2* src = base + row * (4 * B) + seg_block<ROT>(p, RTQ_CI(S)) * B;
+      sfor<B>([&](auto C) {
+        constexpr int w = (RTQ_CI(S) * B + RTQ_CI(C)) * 2;
+        const uint2 q = stream_load(src + RTQ_CI(C));
+        cw[w] = q.x;
+        cw[w + 1] = q.y;
+      });
+    });
+  }
+}
+
+// A lane's scales to or from its row of 512 / G bytes.  G = 32: local groups
+// 2s, 2s + 1 are global groups 2 b, 2 b + 1 of block b = seg_block(p, s) (a
+// 4-byte word each); G = 64: local group s is global group b (2 bytes each);
+// G = 128 and 256: the row's scales, identical in both halves, written by
+// half 0.
+template <int ROT, int G, bool NT>
+__device__ __forceinline__ void store_pair_scales(uint8_t* scales, size_t row, int p,
+                                                  const uint32_t (&sb)[PairGroups<G>::NLG]) {
+  if constexpr (G == 32) {
+    uint32_t* r = reinterpret_cast<uint32_t*>(scales) + row * 4;
+    put_store<NT>(r + seg_block<ROT>(p, 0), sb[0] | (sb[1] << 16));
+    put_store<NT>(r + seg_block<ROT>(p, 1), sb[2] | (sb[3] << 16));
+  } else if constexpr (G == 64) {
+    uint16_t* r = reinterpret_cast<uint16_t*>(scales) + row * 4;
+    put_store<NT>(r + seg_block<ROT>(p, 0), (uint16_t)sb[0]);
+    put_store<NT>(r + seg_block<ROT>(p, 1), (uint16_t)sb[1]);
+  } else if constexpr (G == 128) {
+    if (p == 0) put_store<NT>(reinterpret_cast<uint32_t*>(scales) + row, sb[0] | (sb[1] << 16));
+  } else {
+    if (p == 0) put_store<NT>(reinterpret_cast<uint16_t*>(scales) + row, (uint16_t)sb[0]);
+  }
+}
+
+template <int ROT, int G>
+__device__ __forceinline__ void load_pair_scales(const uint8_t* scales, size_t row, int p,
+                                                 uint32_t (&sb)[PairGroups<G>::NLG]) {
+  if constexpr (G == 32) {
+    const uint32_t* r = reinterpret_cast<const uint32_t*>(scales) + row * 4;
+    const uint32_t w0 = stream_load(r + seg_block<ROT>(p, 0)), w1 = stream_load(r + seg_block<ROT>(p, 1));
+    sb[0] = w0 & 0xffffu;
+    sb[1] = w0 >> 16;
+    sb[2] = w1 & 0xffffu;
+    sb[3] = w1 >> 16;
+  } else if constexpr (G == 64) {
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(scales) + row * 4;
+    sb[0] = stream_load(r + seg_block<ROT>(p, 0));
+    sb[1] = stream_load(r + seg_block<ROT>(p, 1));
+  } else if constexpr (G == 128) {
+    const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(scales) + row);
+    sb[0] = w & 0xffffu;
+    sb[1] = w >> 16;
+  } else {
+    sb[0] = sb[1] = stream_load(reinterpret_cast<const uint16_t*>(scales) + row);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// SRFT exchange of the pair
+// ---------------------------------------------------------------------------
+
+// One bin of the forward exchange (a = 1..31): bins a and a + 32 of E and O
+// (fr, fi: the lane's own real DFT) become coordinates 2b-1, 2b (X_b) and
+// 255-2b, 256-2b (X_{128-b}) of the lane's bin b = a + 32 p, as local
+// registers L[2a-1], L[2a], L[127-2a], L[128-2a].
+template <int A>
+__device__ __forceinline__ void srft_fwd_bin(float (&fr)[65], float (&fi)[65], const float2* twl, float (&L)[128]) {
+  constexpr int a = A;
+  pair_swap(fr[a], fr[a + 32]);  // (E_b, O_b) re in both halves
+  pair_swap(fi[a], fi[a + 32]);
+  const float2 t = twl[a];       // w^b = t.x - i t.y
+  const float er = fr[a], ei = fi[a], orr = fr[a + 32], oi = fi[a + 32];
+  const float xr = __builtin_fmaf(t.x, orr, __builtin_fmaf(t.y, oi, er));   // X_b = E + w^b O
+  const float xi = __builtin_fmaf(t.x, oi, __builtin_fmaf(-t.y, orr, ei));
+  L[2 * a - 1] = xr;
+  L[2 * a] = xi;
+  L[127 - 2 * a] = __builtin_fmaf(2.0f, er, -xr);  // Re X_{128-b} = 2 Re E - Re X_b
+  L[128 - 2 * a] = __builtin_fmaf(-2.0f, ei, xi);  // Im X_{128-b} = Im X_b - 2 Im E
+}
+
+// Bins 0, 32 and 64 of the forward exchange.  Half 0 owns X_0 (L[0]), X_128
+// (L[127]), Re X_32 (L[63]) and Im X_96 (L[64]); half 1 owns Im X_32 (L[0]),
+// Re X_96 (L[127]) and X_64 = E_64 - i O_64 (L[63], L[64]).  The real end
+// bins carry 1/sqrt2 (their orthonormal scale is 1/16, the others'
+// sqrt(2/256), which the quantizer applies).
+__device__ __forceinline__ void srft_fwd_edges(float (&fr)[65], float (&fi)[65], int p, float (&L)[128]) {
+  pair_swap(fr[0], fr[64]);  // half 0: (E_0, O_0), half 1: (E_64, O_64)
+  float e32r, o32r, e32i, o32i;
+  pair_both(fr[32], e32r, o32r);
+  pair_both(fi[32], e32i, o32i);
+  constexpr float h = 0.70710678118654752440f;  // w^32 = h - i h
+  const float xr = __builtin_fmaf(h, o32r, __builtin_fmaf(h, o32i, e32r));
+  const float xi = __builtin_fmaf(h, o32i, __builtin_fmaf(-h, o32r, e32i));
+  const float yr = __builtin_fmaf(2.0f, e32r, -xr), yi = __builtin_fmaf(-2.0f, e32i, xi);  // X_96
+  const float P = fr[0], Q = fr[64];
+  constexpr float r2 = 0.70710678118654752440f;
+  L[0] = p ? xi : (P + Q) * r2;
+  L[127] = p ? yr : (P - Q) * r2;
+  L[63] = p ? P : xr;
+  L[64] = p ? -Q : yi;
+}
+
+// The inverse exchange: from the lane's coordinates L (halved: z / 2), the
+// packed 128-point spectrum yv of the lane's own samples (E for half 0, O for
+// half 1) in the convention of srft_inv<128, Sqrt2>.
+__device__ __forceinline__ void srft_inv_exchange(const float (&L)[128], const float2* twl, int p, float (&yv)[128]) {
+  const float sigma = p ? -1.0f : 1.0f;
+  {
+    float x0, imx32, x128, rex96, rex32, rex64, imx96, imx64;
+    pair_both(L[0], x0, imx32);
+    pair_both(L[127], x128, rex96);
+    pair_both(L[63], rex32, rex64);
+    pair_both(L[64], imx96, imx64);
+    yv[0] = __builtin_fmaf(sigma, x128, x0);  // E_0 or O_0
+    const float er = rex32 + rex96, ei = imx32 - imx96, dr = rex32 - rex96, di = imx32 + imx96;
+    constexpr float h = 0.70710678118654752440f;  // w^-32 = h + i h
+    yv[63] = p ? h * (dr - di) : er;
+    yv[64] = p ? h * (di + dr) : ei;
+    constexpr float sq2 = 1.41421356237309504880f;  // E_64 = Re X_64, O_64 = -Im X_64
+    yv[127] = (p ? -imx64 : rex64) * sq2;
+  }
+  sfor<31>([&](auto A) {
+    constexpr int a = RTQ_CI(A) + 1;
+    const float ar = L[2 * a - 1], ai = L[2 * a], br = L[127 - 2 * a], bi = L[128 - 2 * a];
+    float er = ar + br, ei = ai - bi;           // E_b = (X_b + conj X_{128-b}) / 2
+    const float dr = ar - br, di = ai + bi;     // w^b O_b
+    const float2 t = twl[a];                    // w^-b = t.x + i t.y
+    float orr = __builtin_fmaf(t.x, dr, -t.y * di);
+    float oi = __builtin_fmaf(t.x, di, t.y * dr);
+    pair_swap(er, orr);  // half 0: (E_a, E_{a+32}); half 1: (O_a, O_{a+32})
+    pair_swap(ei, oi);
+    yv[2 * a - 1] = er;
+    yv[2 * a] = ei;
+    yv[2 * a + 63] = orr;
+    yv[2 * a + 64] = oi;
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Forward tile
+// ---------------------------------------------------------------------------
 
 // Forward tile: rows R.row0 .. R.row0 + R.rows - 1 of x (contiguous, 32
 // 16-byte chunks per row) into the codes / scales rows R.cache_row(.), with
@@ -117,10 +477,12 @@ template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4* __restrict__ codes,
                                               uint8_t* __restrict__ scales, const Rows& R, uint4* lds, int lane,
                                               const uint32_t* __restrict__ lam = nullptr) {
-  constexpr int D = 256, CPR = 32, LROW = CPR + 1;
+  constexpr int CPR = 32, LROW = CPR + 1;
+  constexpr int NLG = PairGroups<G>::NLG;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
-  const float sigma = p ? -1.0f : 1.0f;
+  __shared__ float tw[128];
+  if constexpr (ROT == kSRFT) load_pair_twiddles(tw, lane);  // read after the barrier below
   {
     const uint32_t row0 = R.row0;
     const int rows = R.rows;
@@ -166,8 +528,8 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
     lds_sync();
     float L[128];
     float zs;
-    constexpr int CWW = 4 * B;  // code words of the lane's half row
-    uint32_t cw[CWW], sb[128 / G];
+    uint32_t cw[4 * B], sb[NLG];
+    if constexpr (B != 4) sfor<4 * B>([&](auto K) { cw[RTQ_CI(K)] = 0u; });
     if constexpr (ROT == kSRFT) {
       float fr[65], fi[65];  // unnormalized; sqrt(2/256) is applied by the quantizer
       if (lam != nullptr) {
@@ -177,60 +539,21 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
       } else {
         rdft<128, 1, 0, 64>(h, fr, fi);
       }
-      // Partner exchange by ds_bpermute.  Every 4 bins the next addresses are
-      // tied to the last result, so each group of shuffles issues only once
-      // the previous group has been consumed; this keeps the exchange from
-      // holding all 260 shuffled values at once (register pressure).
-      int addr_e = v * 4, addr_o = (v + 32) * 4;
-      auto shf = [](float x, int addr) { return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(x))); };
-      // slot 0: E_0 + sigma * O_0 (real)
-      auto bin0 = [&]() {
-        const float e0 = shf(fr[0], addr_e), o0 = shf(fr[0], addr_o);
-        constexpr float r2 = 0.70710678118654752440f;  // real end bins: 1/16 = sqrt(2/256) / sqrt(2)
-        L[0] = __builtin_fmaf(sigma, o0, e0) * r2;
-      };
-      // bin a = 1 .. 63: slots 2a - 1 and 2a
-      auto bin = [&](auto A) {
-        constexpr int a = RTQ_CI(A);
-        const float er = shf(fr[a], addr_e), ei = shf(fi[a], addr_e);
-        const float orr = shf(fr[a], addr_o), oi = shf(fi[a], addr_o);
-        constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);  // w^a = c - i s
-        const float tr = __builtin_fmaf(c, orr, s * oi);
-        const float ti = __builtin_fmaf(c, oi, -s * orr);
-        const float rr = __builtin_fmaf(sigma, tr, er);
-        const float ri = __builtin_fmaf(sigma, ei, ti);
-        L[2 * a - 1] = p ? ri : rr;
-        L[2 * a] = p ? rr : ri;
-        if constexpr (a % 4 == 0) asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(L[2 * a]));
-      };
-      // slot 127: X_64 = E_64 - i O_64; lane 0 keeps Re, lane 1 keeps Im
-      auto bin64 = [&]() {
-        const float e64 = shf(fr[64], addr_e), o64 = shf(fr[64], addr_o);
-        L[127] = p ? -o64 : e64;
-      };
-      // later shuffles wait for w
-      auto after = [&](uint32_t w) { asm volatile("" : "+v"(addr_e), "+v"(addr_o) : "v"(w)); };
       zs = SrftScale<256>::value;
-      if constexpr (B == 4) {
-        // Quantize each group as soon as the bins that fill it are exchanged:
-        // the finished coordinates of at most one group are then live, not
-        // all 128 (they had been spilled at three waves per SIMD).  Group gi
-        // holds slots gi*G .. gi*G+G-1; bin a fills slots 2a-1 and 2a.
-        sfor<128 / G>([&](auto GI) {
-          constexpr int gi = RTQ_CI(GI), lo = gi * G, hi = lo + G - 1;
-          constexpr int a0 = lo / 2 + 1, a1 = (hi + 1) / 2 < 63 ? (hi + 1) / 2 : 63;
-          if constexpr (gi == 0) bin0();
-          sfor<a1 - a0 + 1>([&](auto K) { bin(ic<a0 + RTQ_CI(K)>{}); });
-          if constexpr (hi == 127) bin64();
-          quantize_pack_group<gi, 128, G>(L, zs, cw, sb);
-          // the next group's shuffles wait for this group's codes (else the
-          // compiler sinks every group's quantization below all shuffles)
-          if constexpr (hi < 127) after(cw[(lo + G) / 8 - 1]);
-        });
+      const float2* twl = reinterpret_cast<const float2*>(tw) + 32 * p;
+      srft_fwd_edges(fr, fi, p, L);
+      if constexpr (G == 32) {
+        // bins 1..16 complete local groups 0 and 3, bins 17..31 groups 1 and 2:
+        // quantize each pair of groups as soon as it is complete
+        sfor<16>([&](auto A) { srft_fwd_bin<RTQ_CI(A) + 1>(fr, fi, twl, L); });
+        quantize_local_group<0, 32, B>(L, zs, local_absmax<0, 32>(L), cw, sb);
+        quantize_local_group<3, 32, B>(L, zs, local_absmax<3, 32>(L), cw, sb);
+        sfor<15>([&](auto A) { srft_fwd_bin<RTQ_CI(A) + 17>(fr, fi, twl, L); });
+        quantize_local_group<1, 32, B>(L, zs, local_absmax<1, 32>(L), cw, sb);
+        quantize_local_group<2, 32, B>(L, zs, local_absmax<2, 32>(L), cw, sb);
       } else {
-        bin0();
-        sfor<63>([&](auto A) { bin(ic<RTQ_CI(A) + 1>{}); });
-        bin64();
+        sfor<31>([&](auto A) { srft_fwd_bin<RTQ_CI(A) + 1>(fr, fi, twl, L); });
+        quantize_pair_groups<G, B>(L, zs, cw, sb);
       }
     } else {
       float f[128];
@@ -241,66 +564,39 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
         fwht_from_f16<128>(h, f);
       }
       zs = 1.0f / 16.0f;
+      // coordinates k (half 0) or 64 + k (half 1), and 128 + k or 192 + k
       auto combine = [&](auto K) {
-        const float r = __shfl_xor(f[RTQ_CI(K)], 32);
-        L[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
+        constexpr int k = RTQ_CI(K);
+        pair_swap(f[k], f[k + 64]);
+        L[k] = f[k] + f[k + 64];
+        L[k + 64] = f[k] - f[k + 64];
       };
-      // a shuffle of x waits for w
-      auto after = [](float& x, uint32_t w) { asm volatile("" : "+v"(x) : "v"(w)); };
-      if constexpr (B == 4) {
-        // group by group, as for the SRFT: quantize each group once its
-        // values are combined; the next group's shuffles wait for its codes
-        sfor<128 / G>([&](auto GI) {
-          constexpr int gi = RTQ_CI(GI), lo = gi * G;
-          sfor<G>([&](auto K) { combine(ic<lo + RTQ_CI(K)>{}); });
-          quantize_pack_group<gi, 128, G>(L, zs, cw, sb);
-          if constexpr (lo + G < 128) after(f[lo + G], cw[(lo + G) / 8 - 1]);
-        });
+      if constexpr (G == 32) {
+        sfor<32>([&](auto K) { combine(K); });
+        quantize_local_group<0, 32, B>(L, zs, local_absmax<0, 32>(L), cw, sb);
+        quantize_local_group<2, 32, B>(L, zs, local_absmax<2, 32>(L), cw, sb);
+        sfor<32>([&](auto K) { combine(ic<RTQ_CI(K) + 32>{}); });
+        quantize_local_group<1, 32, B>(L, zs, local_absmax<1, 32>(L), cw, sb);
+        quantize_local_group<3, 32, B>(L, zs, local_absmax<3, 32>(L), cw, sb);
       } else {
-        sfor<128>([&](auto K) { combine(K); });
+        sfor<64>([&](auto K) { combine(K); });
+        quantize_pair_groups<G, B>(L, zs, cw, sb);
       }
     }
-    if constexpr (B != 4) {
-      // SRFT lane 1 holds its half mirrored: put it in natural order first
-      // (a b-bit stream has no cheap field reversal), then quantize
-      if constexpr (ROT == kSRFT) {
-        float Ln[128];
-        sfor<128>([&](auto I) { Ln[RTQ_CI(I)] = p ? L[127 - RTQ_CI(I)] : L[RTQ_CI(I)]; });
-        quantize_pack_bits<128, G, B>(Ln, zs, cw, sb);
-      } else {
-        quantize_pack_bits<128, G, B>(L, zs, cw, sb);
-      }
-    } else if constexpr (ROT == kSRFT) {
-      // (quantized above) lane 1: codes and scales are in mirrored order -> reverse them
-      uint32_t rev[16];
-      sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
-      sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
-      uint32_t sr[128 / G];
-      sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
-      sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
-    }  // SRHT, 4 bits: quantized above
     if (v < rows) {
       const size_t row = R.cache_row(v);
-      constexpr bool nt = Rows::kStreamStores;
-      // Each lane writes its half row in 16-byte pieces, so one store
-      // instruction leaves one or two pieces in each 128-byte line: ordinary
-      // stores let L2 merge them into full lines.  (With the non-temporal
-      // hint 8-bit codes ran 2.2x slower, and int4 codes 1-2% slower.)
-      sfor<B>([&](auto C) {
-        put_store<false>(codes + (row * (2 * B) + B * p + RTQ_CI(C)),
-                     make_uint4(cw[4 * RTQ_CI(C)], cw[4 * RTQ_CI(C) + 1], cw[4 * RTQ_CI(C) + 2], cw[4 * RTQ_CI(C) + 3]));
-      });
-      // this lane's half of the row's scales: 128/G values
-      if constexpr (128 / G == 1) {
-        put_store<nt>(reinterpret_cast<uint16_t*>(scales) + (row * 2 + p), (uint16_t)sb[0]);
-      } else if constexpr (128 / G == 2) {
-        put_store<nt>(reinterpret_cast<uint32_t*>(scales) + (row * 2 + p), sb[0] | (sb[1] << 16));
-      } else {
-        put_store<nt>(reinterpret_cast<uint2*>(scales) + (row * 2 + p), make_uint2(sb[0] | (sb[1] << 16), sb[2] | (sb[3] << 16)));
-      }
+      // Each lane writes two runs of its row in 16- or 8-byte pieces, so one
+      // store instruction leaves one or two pieces in each 128-byte line:
+      // ordinary stores let L2 merge them into full lines.
+      store_pair_codes<ROT, B, false>(codes, row, p, cw);
+      store_pair_scales<ROT, G, Rows::kStreamStores>(scales, row, p, sb);
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Inverse tile
+// ---------------------------------------------------------------------------
 
 // Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
 // that R.y_chunk addresses, for B-bit codes and an optional lambda.  lds
@@ -309,95 +605,53 @@ template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
                                               uint4* __restrict__ y, const Rows& R, uint4* lds, int lane,
                                               const uint32_t* __restrict__ lam = nullptr, float* inv_lam = nullptr) {
-  constexpr int CPR = 32;
+  constexpr int NLG = PairGroups<G>::NLG, LG = PairGroups<G>::LG;
   if (lam != nullptr) pair_lambda_reciprocals<ROT>(lam, inv_lam, lane);  // read after a barrier below
+  __shared__ float tw[128];
+  if constexpr (ROT == kSRFT) load_pair_twiddles(tw, lane);  // read after the first barrier below
   const int p = lane >> 5, v = lane & 31;
-  const uint32_t kpos = lane & 31;
-  const float sigma = p ? -1.0f : 1.0f;
   {
     const int rows = R.rows;
     const bool uniform = R.uniform;
-    uint32_t cw[4 * B], sb[128 / G];
+    uint32_t cw[4 * B], sb[NLG];
     {
       const size_t row = R.cache_row(v < rows ? v : 0);
-      sfor<B>([&](auto C) {
-        const uint4 q = stream_load(codes + (row * (2 * B) + B * p + RTQ_CI(C)));
-        cw[4 * RTQ_CI(C) + 0] = q.x;
-        cw[4 * RTQ_CI(C) + 1] = q.y;
-        cw[4 * RTQ_CI(C) + 2] = q.z;
-        cw[4 * RTQ_CI(C) + 3] = q.w;
-      });
-      if constexpr (128 / G == 1) {
-        sb[0] = stream_load(reinterpret_cast<const uint16_t*>(scales) + (row * 2 + p));
-      } else if constexpr (128 / G == 2) {
-        const uint32_t w = stream_load(reinterpret_cast<const uint32_t*>(scales) + (row * 2 + p));
-        sb[0] = w & 0xffffu;
-        sb[1] = w >> 16;
-      } else {
-        const uint2 w = stream_load(reinterpret_cast<const uint2*>(scales) + (row * 2 + p));
-        sb[0] = w.x & 0xffffu;
-        sb[1] = w.x >> 16;
-        sb[2] = w.y & 0xffffu;
-        sb[3] = w.y >> 16;
-      }
+      load_pair_codes<ROT, B>(codes, row, p, cw);
+      load_pair_scales<ROT, G>(scales, row, p, sb);
     }
     float u[128];
     if constexpr (ROT == kSRFT) {
-      // lane 1 keeps its half in mirrored order (the halving of E and t is
-      // folded into the dequantization)
-      float L[128];
-      if constexpr (B == 4) {  // undo the mirror on the packed form
-        uint32_t rev[16];
-        sfor<16>([&](auto W) { rev[RTQ_CI(W)] = nibble_reverse(cw[15 - RTQ_CI(W)]); });
-        sfor<16>([&](auto W) { cw[RTQ_CI(W)] = p ? rev[RTQ_CI(W)] : cw[RTQ_CI(W)]; });
-        uint32_t sr[128 / G];
-        sfor<128 / G>([&](auto W) { sr[RTQ_CI(W)] = sb[128 / G - 1 - RTQ_CI(W)]; });
-        sfor<128 / G>([&](auto W) { sb[RTQ_CI(W)] = p ? sr[RTQ_CI(W)] : sb[RTQ_CI(W)]; });
-        dequant_unpack<128, G>(cw, sb, 0.5f, L);
-      } else {  // dequantize in natural order, then mirror the values
-        float Ln[128];
-        dequant_unpack_bits<128, G, B>(cw, sb, 0.5f, Ln);
-        sfor<128>([&](auto I) { L[RTQ_CI(I)] = p ? Ln[127 - RTQ_CI(I)] : Ln[RTQ_CI(I)]; });
-      }
-      // P = lane v's slots (X_a), Q = lane v+32's slots (X_{128-a}, Re/Im swapped)
-      const int src0 = v, src1 = v + 32;
-      float yv[128];
-      {
-        const float p0 = __shfl(L[0], src0), q0 = __shfl(L[0], src1);
-        yv[0] = __builtin_fmaf(sigma, q0, p0);
-      }
-      sfor<63>([&](auto A) {
-        constexpr int a = RTQ_CI(A) + 1;
-        const float pr = __shfl(L[2 * a - 1], src0), pi = __shfl(L[2 * a], src0);
-        const float qr = __shfl(L[2 * a], src1), qi = __shfl(L[2 * a - 1], src1);
-        const float fr = __builtin_fmaf(sigma, qr, pr);  // E (lane 0) or t (lane 1)
-        const float fi = __builtin_fmaf(-sigma, qi, pi);
-        // lane 1: O_a = w^-a t_a with w^-a = c + i s; lane 0 multiplies by 1
-        constexpr float c = (float)cos2pi(a, 256), s = (float)sin2pi(a, 256);
-        const float cc = p ? c : 1.0f, ss = p ? s : 0.0f;
-        yv[2 * a - 1] = __builtin_fmaf(cc, fr, -ss * fi);
-        yv[2 * a] = __builtin_fmaf(cc, fi, ss * fr);
-      });
-      {
-        const float p64 = __shfl(L[127], src0), q64 = __shfl(L[127], src1);
-        constexpr float sq2 = 1.41421356237309504880f;  // 2 / sqrt(2): L is halved
-        yv[127] = (p ? -q64 : p64) * sq2;
-      }
+      float L[128], yv[128];  // L = z / 2: the halving of E and O is folded in here
+      if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, 0.5f, L);
+      else dequant_unpack_bits<128, LG, B>(cw, sb, 0.5f, L);
+      lds_sync();  // the twiddle table is written
+      srft_inv_exchange(L, reinterpret_cast<const float2*>(tw) + 32 * p, p, yv);
       srft_inv<128, Sqrt2>(yv, u);
     } else {
-      float f[128];
-      if constexpr (B == 4) dequant_unpack<128, G>(cw, sb, 1.0f / 16.0f, f);
-      else dequant_unpack_bits<128, G, B>(cw, sb, 1.0f / 16.0f, f);
-      fwht_f32<128>(f);
-      sfor<128>([&](auto K) {
-        const float r = __shfl_xor(f[RTQ_CI(K)], 32);
-        u[RTQ_CI(K)] = __builtin_fmaf(sigma, f[RTQ_CI(K)], r);
+      float L[128];
+      if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, 1.0f / 16.0f, L);
+      else dequant_unpack_bits<128, LG, B>(cw, sb, 1.0f / 16.0f, L);
+      // half 0: z_k + z_{128+k}, half 1: z_k - z_{128+k}, k = 0 .. 127
+      sfor<64>([&](auto K) {
+        constexpr int k = RTQ_CI(K);
+        float s = L[k] + L[k + 64], d = L[k] - L[k + 64];
+        pair_swap(s, d);
+        u[k] = s;
+        u[k + 64] = d;
       });
+      fwht_f32<128>(u);
     }
     if (lam != nullptr) {
       lds_sync();
       unweight_half(u, inv_lam, p);
     }
+    // Every sample rounded to fp16 pairs before the output passes begin, so
+    // that no transform value stays live across them (the compiler would
+    // otherwise finish the last butterflies lazily inside the second pass and
+    // spill around the first).
+    uint32_t hw[64];
+    sfor<64>([&](auto M) { hw[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+    sfor<16>([&](auto Q) { pin_words<4 * RTQ_CI(Q)>(hw); });
     // fp16 samples out through LDS in two passes of 16 output chunks per row
     // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
     // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
@@ -414,17 +668,13 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
       if constexpr (ROT == kSRFT) {
         sfor<8>([&](auto C) {
           constexpr int c = 8 * ph + RTQ_CI(C);
-          lds[v * LR2 + 8 * p + RTQ_CI(C)] =
-              make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
-                         pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+          lds[v * LR2 + 8 * p + RTQ_CI(C)] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
         });
       } else {
         if (p == ph) {
           sfor<16>([&](auto C) {
             constexpr int c = RTQ_CI(C);
-            lds[v * LR2 + c] =
-                make_uint4(pack_f16x2(u[8 * c + 0], u[8 * c + 1]), pack_f16x2(u[8 * c + 2], u[8 * c + 3]),
-                           pack_f16x2(u[8 * c + 4], u[8 * c + 5]), pack_f16x2(u[8 * c + 6], u[8 * c + 7]));
+            lds[v * LR2 + c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
           });
         }
       }

@@ -67,7 +67,7 @@ def test_rejects_bad_arguments_without_launching(name):
     assert call(name, A, B, C, -1, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
     assert call(name, A, B, C, 10, 64, 32, rps=-1) == rtq.RTQ_ERR_INVALID_ARG
     assert call(name, A, B, C, 10, 64, 32, per=-1) == rtq.RTQ_ERR_INVALID_ARG
-    for d, g in [(96, 32), (32, 32), (512, 32), (64, 16), (64, 128), (128, 256), (64, 48), (256, 256)]:
+    for d, g in [(96, 32), (32, 32), (512, 32), (64, 16), (64, 128), (128, 256), (64, 48), (256, 512)]:
         assert call(name, A, B, C, 10, d, g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
     # null and misaligned pointers
     assert call(name, 0, B, C, 10, 64, 32) == rtq.RTQ_ERR_INVALID_ARG
@@ -138,7 +138,7 @@ def test_attention_rejects_bad_arguments_without_launching(name):
     # rows past 2^56
     assert attn_call(name, strides=(1 << 60, 150, 50, 1)) == bad
     # unsupported shapes and head ratios
-    for d, g in [(256, 256), (64, 128), (128, 16), (96, 32), (512, 32)]:
+    for d, g in [(256, 512), (64, 128), (128, 16), (96, 32), (512, 32)]:
         assert attn_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
     assert attn_call(name, qpk=9) == rtq.RTQ_ERR_UNSUPPORTED
 
@@ -256,7 +256,7 @@ def test_mapped_rejects_bad_arguments_without_launching(name):
                {"strides": (300, 150, -50, 1)}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
                {"c": C + 2}, {"strides": (1 << 60, 150, 50, 1)}, {"layers": 1 << 20, "streams": 1 << 10, "n": 1 << 10}):
         assert mapped_call(name, **kw) == bad, kw
-    for d, g in [(256, 256), (96, 32), (64, 128), (128, 16)]:
+    for d, g in [(256, 512), (96, 32), (64, 128), (128, 16)]:
         assert mapped_call(name, d=d, g=g) == rtq.RTQ_ERR_UNSUPPORTED, (d, g)
 
 
@@ -289,7 +289,7 @@ def test_ext_rejects_bad_arguments_without_launching(name):
     for kw in ({"n": -1}, {"rps": -1}, {"per": -1}, {"a": 0}, {"b": 0}, {"c": 0}, {"a": A + 8}, {"b": B + 4},
                {"c": C + 2}, {"lam": LAM + 2}, {"n": 0xFFFFFF01}):
         assert ext_call(name, **kw) == bad, kw
-    for kw in ({"bits": 2}, {"bits": 5}, {"bits": 16}, {"d": 256, "g": 256}, {"d": 96}, {"g": 16}):
+    for kw in ({"bits": 2}, {"bits": 5}, {"bits": 16}, {"d": 256, "g": 512}, {"d": 96}, {"g": 16}):
         assert ext_call(name, **kw) == rtq.RTQ_ERR_UNSUPPORTED, kw
 
 

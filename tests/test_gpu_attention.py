@@ -310,9 +310,9 @@ def test_argument_errors():
         rtq.srft_attn_decode(q9, c, s, (0, 32, 0, 1), 8, 32, 1)         # 9 query heads per K/V head
     q256 = torch.zeros((1, 1, 1, 256), dtype=torch.float16, device=DEV)
     c256 = torch.zeros((64, 128), dtype=torch.uint8, device=DEV)
-    s256 = torch.zeros((64, 1), dtype=torch.float16, device=DEV)
+    s256 = torch.zeros((64, 16), dtype=torch.float16, device=DEV)
     with pytest.raises(rtq.RTQError):
-        rtq.srft_attn_decode(q256, c256, s256, (0, 32, 0, 1), 8, 256, 1)  # groups of 256 not built
+        rtq.srft_attn_decode(q256, c256, s256, (0, 32, 0, 1), 8, 16, 1)  # groups of 16 not built
 
 
 # ---------------------------------------------------------------------------
