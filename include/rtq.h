@@ -341,6 +341,33 @@ rtq_status srht_attn_decode_window(const void* q_f16, const void* codes_u8, cons
 
 size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d);
 
+/*
+ * srft_attn_decode_noalloc -- srft_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation, arguments, checks
+ * and results as srft_attn_decode with a workspace of
+ * rtq_attn_workspace_bytes(...) bytes, but the token-split workspace is a
+ * static device array of the library (4,228,096 bytes: the largest one the
+ * split policy asks for), so the caller passes none and nothing is
+ * allocated, by the library or by the caller.
+ *   Scratch: each GPU the library runs on holds its own copy until the
+ *   process ends.  The first call on a device looks up its address and
+ *   clears it with a kernel launched on `stream` (after the argument
+ *   checks); every call that completes leaves it cleared again.
+ *   Concurrency: every call on one GPU shares that GPU's scratch, so calls
+ *   that may overlap in time on one GPU (other streams, other host threads)
+ *   race and give wrong results; serialize them, or use srft_attn_decode
+ *   with workspaces of their own.
+ *   Errors: as srft_attn_decode; RTQ_ERR_HIP if the scratch cannot be set up
+ *   on the current device; RTQ_ERR_UNSUPPORTED if a call's split plan needed
+ *   more scratch than the array holds (none does under the current policy).
+ */
+rtq_status srft_attn_decode_noalloc(const void* q_f16, const void* codes_u8, const void* scales_f16, void* out_f16,
+                                    int32_t layers, int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d,
+                                    int32_t group, int64_t stride_layer, int64_t stride_kv, int64_t stride_stream,
+                                    int64_t stride_token, uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                    float softmax_scale, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* rtq_status_string(rtq_status status);
 

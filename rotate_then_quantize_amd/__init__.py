@@ -20,7 +20,7 @@ import os
 
 __all__ = [
     "srft_quant_fwd", "srft_dequant_inv", "srht_quant_fwd", "srht_dequant_inv",
-    "srft_attn_decode", "srht_attn_decode", "attn_workspace_bytes",
+    "srft_attn_decode", "srht_attn_decode", "srft_attn_decode_noalloc", "attn_workspace_bytes",
     "srft_quant_append", "srht_quant_append", "srft_dequant_rows", "srht_dequant_rows",
     "srft_quant_fwd_ext", "srht_quant_fwd_ext", "srft_dequant_inv_ext", "srht_dequant_inv_ext", "CODE_BITS",
     "RTQError", "library", "library_path", "ATTN_MAX_WINDOW", "SUPPORTED", "ATTN_SUPPORTED", "CACHE_SUPPORTED", "EXT_SUPPORTED",
@@ -84,6 +84,8 @@ def library():
             fn = getattr(lib, name)
             fn.argtypes = win_args
             fn.restype = ctypes.c_int
+        lib.srft_attn_decode_noalloc.argtypes = attn_args[:18] + [ctypes.c_void_p]
+        lib.srft_attn_decode_noalloc.restype = ctypes.c_int
         lib.rtq_attn_workspace_bytes.argtypes = [ctypes.c_int32] * 5
         lib.rtq_attn_workspace_bytes.restype = ctypes.c_size_t
         mapped_args = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -217,7 +219,7 @@ def _attn_workspace(q, tokens, stream_handle):
 
 
 def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period, softmax_scale,
-          out, stream, workspace=None, window=None, window_tokens=0):
+          out, stream, workspace=None, window=None, window_tokens=0, noalloc=False):
     import math
     import torch
     _need(q, torch.float16, "q")
@@ -253,6 +255,12 @@ def _attn(cname, q, codes, scales, strides, tokens, group, seed, rows_per_seed, 
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
     sh = _stream_handle(q, stream)
+    if noalloc:  # the library's static scratch holds the split partials
+        args = [ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                ctypes.c_void_p(out.data_ptr()), layers, streams, tokens, q_per_kv, d, group, *strides,
+                seed & ((1 << 64) - 1), rows_per_seed, seed_period, float(softmax_scale)]
+        _check(library().srft_attn_decode_noalloc(*args, sh))
+        return out
     if workspace is None:
         workspace = _attn_workspace(q, tokens, sh)
     if workspace is None or workspace.numel() == 0:
@@ -284,6 +292,15 @@ def srft_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_se
     then be 0."""
     return _attn("srft_attn_decode", q, codes, scales, strides, tokens, group, seed, rows_per_seed, seed_period,
                  softmax_scale, out, stream, workspace, window, window_tokens)
+
+
+def srft_attn_decode_noalloc(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,
+                             softmax_scale=None, out=None, stream=None):
+    """srft_attn_decode whose token-split partials live in the library's static device scratch: the
+    library allocates nothing (pass `out` to allocate nothing here either).  Calls that may overlap in
+    time on one GPU share the scratch and race."""
+    return _attn("srft_attn_decode_noalloc", q, codes, scales, strides, tokens, group, seed, rows_per_seed,
+                 seed_period, softmax_scale, out, stream, noalloc=True)
 
 
 def srht_attn_decode(q, codes, scales, strides, tokens, group, seed, rows_per_seed=0, seed_period=0,

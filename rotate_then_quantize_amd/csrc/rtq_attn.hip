@@ -53,6 +53,7 @@
 //     and joins it to the same softmax with the online-softmax merge.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <stdint.h>
 
 #include "rtq.h"
@@ -1219,10 +1220,16 @@ bool overlaps(const void* a, __int128 na, const void* b, __int128 nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+rtq_status scratch_on_current_device(hipStream_t stream, void** out);
+extern const size_t kScratchBytesExtern;
+
+// use_scratch: the split workspace is the library's static scratch (set up
+// here, after every argument check), and workspace must be null.
 rtq_status run(int rot, const void* q, const void* codes, const void* scales, void* out, int32_t layers,
                int32_t streams, int32_t tokens, int32_t q_per_kv, int32_t d, int32_t group, const int64_t (&st)[4],
                uint64_t seed, int64_t rps, int32_t period, float softmax_scale, const void* win, int32_t win_cap,
-               int32_t win_tokens, void* workspace, size_t workspace_size, hipStream_t stream) {
+               int32_t win_tokens, void* workspace, size_t workspace_size, hipStream_t stream,
+               bool use_scratch = false) {
   if (layers < 0 || streams < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (st[i] < 0) return RTQ_ERR_INVALID_ARG;
@@ -1265,6 +1272,12 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
                     overlaps(workspace, workspace_size, codes, code_bytes) ||
                     overlaps(workspace, workspace_size, scales, scale_bytes)))
     return RTQ_ERR_INVALID_ARG;
+  if (use_scratch) {
+    if (workspace != nullptr) return RTQ_ERR_INVALID_ARG;
+    const rtq_status s = scratch_on_current_device(stream, &workspace);
+    if (s != RTQ_OK) return s;
+    workspace_size = kScratchBytesExtern;
+  }
   // as many splits as the policy asks for and the workspace holds
   int splits = workspace ? choose_splits(wgs, tokens) : 1;
   while (splits > 1 && (workspace_bytes(wgs, splits, q_per_kv, d) > workspace_size || wgs * splits > 0x7fffffff))
@@ -1296,6 +1309,52 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   const hipError_t e =
       hipLaunchKernel(fn, dim3((unsigned)(wgs * splits)), dim3(64 * kWavesPerStream), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of srft_attn_decode_noalloc: the split workspace in a file-scope
+// device array, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+// The largest workspace the split policy asks for: splits happen only with
+// at most kResidentWorkgroups / 2 (layer, stream) pairs (counters padded to
+// 256 bytes), and pairs * splits <= kResidentWorkgroups partials of at most
+// kMaxQ queries at d = 256.
+constexpr size_t kScratchBytes =
+    (size_t)(((kResidentWorkgroups / 2) * 4 + 255) & ~(int64_t)255) +
+    (size_t)kResidentWorkgroups * (size_t)part_floats(kMaxQ, 256) * 4;
+static_assert(kScratchBytes == 4228096, "4 MiB + 8 KiB");
+const size_t kScratchBytesExtern = kScratchBytes;
+
+// Each GPU the library runs on holds its own copy until the process ends.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch[kMaxDevices];  // device address of `scratch` on each device, once set up
+
+__global__ void zero_words(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The device address of `scratch` on the current device.  The first call on
+// a device looks it up (the array's name is a host-side stand-in, not a
+// device address) and clears it with a kernel on `stream` (not a memset, so
+// that a graph capture records a kernel node).
+rtq_status scratch_on_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RTQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return RTQ_ERR_HIP;
+    hipLaunchKernelGGL(zero_words, dim3(64), dim3(256), 0, stream, static_cast<uint4*>(ptr), kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return RTQ_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return RTQ_OK;
 }
 
 }  // namespace attn
@@ -1364,4 +1423,19 @@ RTQ_API size_t rtq_attn_workspace_bytes(int32_t layers, int32_t streams, int32_t
   int splits = rtq::attn::choose_splits(pairs, tokens);
   while (splits > 1 && pairs * splits > 0x7fffffff) --splits;
   return (size_t)rtq::attn::workspace_bytes(pairs, splits, q_per_kv, d);
+}
+
+RTQ_API rtq_status srft_attn_decode_noalloc(const void* q_f16, const void* codes_u8, const void* scales_f16,
+                                            void* out_f16, int32_t layers, int32_t streams, int32_t tokens,
+                                            int32_t q_per_kv, int32_t d, int32_t group, int64_t stride_layer,
+                                            int64_t stride_kv, int64_t stride_stream, int64_t stride_token,
+                                            uint64_t seed, int64_t rows_per_seed, int32_t seed_period,
+                                            float softmax_scale, hipStream_t stream) {
+  // the split plan's workspace must fit the scratch (by construction every plan does)
+  if (rtq_attn_workspace_bytes(layers, streams, tokens, q_per_kv, d) > rtq::attn::kScratchBytes)
+    return RTQ_ERR_UNSUPPORTED;
+  const int64_t st[4] = {stride_layer, stride_kv, stride_stream, stride_token};
+  return rtq::attn::run(0, q_f16, codes_u8, scales_f16, out_f16, layers, streams, tokens, q_per_kv, d, group, st,
+                        seed, rows_per_seed, seed_period, softmax_scale, nullptr, 0, 0, nullptr, 0, stream,
+                        /*use_scratch=*/true);
 }

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["rtq_attn_workspace_bytes", "rtq_status_string", "srft_attn_decode",
-                                    "srft_attn_decode_window", "srft_dequant_inv",
+                                    "srft_attn_decode_noalloc", "srft_attn_decode_window", "srft_dequant_inv",
                                     "srft_dequant_inv_ext", "srft_dequant_rows", "srft_quant_append", "srft_quant_fwd",
                                     "srft_quant_fwd_ext", "srht_attn_decode", "srht_attn_decode_window",
                                     "srht_dequant_inv",
