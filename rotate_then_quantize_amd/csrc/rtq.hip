@@ -124,9 +124,10 @@ __global__ __launch_bounds__(64) void fwd_lane_kernel(const uint4* __restrict__ 
 }
 
 // The same with a per-channel lambda (4-bit codes of the width-and-lambda
-// entry points).
+// entry points).  Two waves per SIMD, the most a 16 KB tile leaves room for
+// at d = 128, and a register budget (256) that keeps them.
 template <int D, int G, int ROT>
-__global__ __launch_bounds__(64) void fwd_lane_lambda_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_lane_lambda_kernel(const uint4* __restrict__ x, uint4* __restrict__ codes,
                                                              uint8_t* __restrict__ scales,
                                                              const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr,
                                                              SignTable tb) {
@@ -176,17 +177,23 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
     cw[4 * RTQ_CI(C) + 2] = q.z;
     cw[4 * RTQ_CI(C) + 3] = q.w;
   });
-  float z[D], u[D];
-  if constexpr (ROT == kSRFT) {
-    dequant_unpack<D, G>(cw, sb, 1.0f, z);
-    srft_inv<D, One>(z, u);
-  } else {
-    dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
-    fwht_f32<D>(u);
-  }
-  if constexpr (LAM) lambda_unweight_lds<D>(u, inv_lam);  // the per-channel lambda divided out
   uint32_t h[D / 2];
-  sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+  if constexpr (ROT == kSRFT && !LAM) {
+    float z[D];
+    dequant_unpack<D, G>(cw, sb, HartleyIn<D>::value, z);
+    srft_inv_hartley_packed<D>(z, h);
+  } else {
+    float z[D], u[D];
+    if constexpr (ROT == kSRFT) {
+      dequant_unpack<D, G>(cw, sb, HartleyIn<D>::value, z);
+      srft_inv_hartley<D>(z, u);
+    } else {
+      dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
+      fwht_f32<D>(u);
+    }
+    if constexpr (LAM) lambda_unweight_lds<D>(u, inv_lam);  // the per-channel lambda divided out
+    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+  }
   if constexpr (kUniform) sg.apply(h);
   else apply_lane_signs<D>(h, s);
   // Own row into LDS (the code block has been read), then coalesced chunks

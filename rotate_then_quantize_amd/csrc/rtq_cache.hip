@@ -109,16 +109,17 @@ __global__ __launch_bounds__(64) void inv_mapped_kernel(const uint4* __restrict_
   });
   load_row_scales<D, G>(scales + src * (2 * D / G), 0u, sb);
   const uint64_t s = row_seed(rs.seed, src, rs.rps, rs.period);
-  float z[D], u[D];
+  uint32_t h[D / 2];
   if constexpr (ROT == kSRFT) {
-    dequant_unpack<D, G>(cw, sb, 1.0f, z);
-    srft_inv<D, One>(z, u);
+    float z[D];
+    dequant_unpack<D, G>(cw, sb, HartleyIn<D>::value, z);
+    srft_inv_hartley_packed<D>(z, h);
   } else {
+    float u[D];
     dequant_unpack<D, G>(cw, sb, InvSqrt<D>::value, u);
     fwht_f32<D>(u);
+    sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   }
-  uint32_t h[D / 2];
-  sfor<D / 2>([&](auto M) { h[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
   flip_signs<D>(h, s, lane);
   if (lane < rows) {
     uint4* out = y + src * CPR;  // ordinary stores, merged per line in L2

@@ -115,9 +115,13 @@ __device__ __forceinline__ float hi_f(uint32_t w) {
   return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
 }
 // Two floats to packed fp16 (round to nearest even): low half = a.
+// (v_cvt_pk_f16_f32 written out: left to itself the compiler fuses an fma
+// that feeds the conversion into v_fma_mix{lo,hi}_f16, which issue at half
+// rate.)
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const __half2 h = __floats2half2_rn(a, b);
-  return __builtin_bit_cast(uint32_t, h);
+  uint32_t r;
+  asm("v_cvt_pk_f16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
 }
 
 // fp16 + fp16 and fp16 - fp16 into fp32 with one v_fma_mix_f32 each (the sum
@@ -311,6 +315,40 @@ __device__ __forceinline__ void rdft(const uint32_t (&h)[H], float (&xr)[N / 2 +
   }
 }
 
+// The same recursion on fp32 samples g_{OFF}, g_{OFF+S}, ... (the leaf adds
+// and subtracts fp32 values).
+template <int N, int S, int OFF, int L>
+__device__ __forceinline__ void rdft_f32(const float (&g)[L], float (&xr)[N / 2 + 1], float (&xi)[N / 2 + 1]) {
+  if constexpr (N == 4) {
+    constexpr int a = OFF, b = OFF + S, c = OFF + 2 * S, d = OFF + 3 * S;
+    const float t0 = g[a] + g[c], t1 = g[a] - g[c], t2 = g[b] + g[d], t3 = g[b] - g[d];
+    xr[0] = t0 + t2;
+    xr[2] = t0 - t2;
+    xr[1] = t1;
+    xi[1] = -t3;
+    xi[0] = 0.0f;
+    xi[2] = 0.0f;
+  } else {
+    float er[N / 4 + 1], ei[N / 4 + 1], orr[N / 4 + 1], oi[N / 4 + 1];
+    rdft_f32<N / 2, 2 * S, OFF, L>(g, er, ei);
+    rdft_f32<N / 2, 2 * S, OFF + S, L>(g, orr, oi);
+    xr[0] = er[0] + orr[0];
+    xi[0] = 0.0f;
+    xr[N / 2] = er[0] - orr[0];
+    xi[N / 2] = 0.0f;
+    xr[N / 4] = er[N / 4];
+    xi[N / 4] = -orr[N / 4];
+    sfor<N / 4 - 1>([&](auto K) {
+      constexpr int k = RTQ_CI(K) + 1;
+      constexpr float c = (float)cos2pi(k, N), s = (float)sin2pi(k, N);
+      xr[k] = __builtin_fmaf(c, orr[k], __builtin_fmaf(s, oi[k], er[k]));
+      xi[k] = __builtin_fmaf(c, oi[k], __builtin_fmaf(-s, orr[k], ei[k]));
+      xr[N / 2 - k] = __builtin_fmaf(2.0f, er[k], -xr[k]);
+      xi[N / 2 - k] = __builtin_fmaf(-2.0f, ei[k], xi[k]);
+    });
+  }
+}
+
 // Packed orthonormal SRFT of length D (one lane), returned divided by
 // sqrt(2/D): the quantizer multiplies it back (zs = SrftScale<D>), so the
 // interior bins cost nothing extra and only the two real end bins (scale
@@ -439,6 +477,128 @@ __device__ __forceinline__ void srft_inv(const float (&z)[D], float (&u)[D]) {
   });
 }
 
+// The discrete Hartley transform u_n = sum_m g_m (cos + sin)(2 pi m n / D)
+// of D real samples, from the real DFTs E and O (length D/2) of the even
+// and odd samples.  With G = DFT(g), u_n = Re G_n - Im G_n and u_{D-n} =
+// Re G_n + Im G_n; the last even/odd step of the real DFT and this
+// combination fold together: with A = Re E_k - Im E_k, B = Re E_k + Im E_k
+// and w^k = c - i s,
+//   u_k       = A + (c + s) Re O_k + (s - c) Im O_k,
+//   u_{D-k}   = B + (c - s) Re O_k + (c + s) Im O_k,
+//   u_{D/2-k} = 2 B - u_{D-k},   u_{D/2+k} = 2 A - u_k,
+// eight operations per four samples (k = 1 .. D/4 - 1); k = 0 and D/4 take
+// the sums and differences of the real end bins.
+template <int D>
+__device__ __forceinline__ void hartley_f32(const float (&g)[D], float (&u)[D]) {
+  constexpr int M = D / 2, Q = D / 4;
+  float er[Q + 1], ei[Q + 1], orr[Q + 1], oi[Q + 1];
+  rdft_f32<M, 2, 0, D>(g, er, ei);
+  rdft_f32<M, 2, 1, D>(g, orr, oi);
+  u[0] = er[0] + orr[0];
+  u[M] = er[0] - orr[0];
+  u[Q] = er[Q] + orr[Q];  // G_{D/4} = E_{D/4} - i O_{D/4}, both real
+  u[D - Q] = er[Q] - orr[Q];
+  sfor<Q - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    constexpr double c = cos2pi(k, D), s = sin2pi(k, D);
+    constexpr float cps = (float)(c + s), smc = (float)(s - c), cms = (float)(c - s);
+    const float A = er[k] - ei[k], B = er[k] + ei[k];
+    u[k] = __builtin_fmaf(cps, orr[k], __builtin_fmaf(smc, oi[k], A));
+    u[D - k] = __builtin_fmaf(cms, orr[k], __builtin_fmaf(cps, oi[k], B));
+    u[M - k] = __builtin_fmaf(2.0f, B, -u[D - k]);
+    u[M + k] = __builtin_fmaf(2.0f, A, -u[k]);
+  });
+}
+
+// Step of hartley_f32 that forms sample n (0 for the end bins).
+template <int D>
+constexpr int hartley_step(int n) {
+  constexpr int M = D / 2, Q = D / 4;
+  if (n == 0 || n == M || n == Q || n == D - Q) return 0;
+  if (n < Q) return n;           // u_k
+  if (n < M) return M - n;       // u_{M-k}
+  if (n < D - Q) return n - M;   // u_{M+k}
+  return D - n;                  // u_{D-k}
+}
+
+// hartley_f32 with the samples rounded to fp16 pairs, hw[m] = (u_{2m},
+// u_{2m+1}), each pair as soon as the step that completes it has run, so
+// that few unpacked samples are live at once.
+template <int D>
+__device__ __forceinline__ void hartley_f32_packed(const float (&g)[D], uint32_t (&hw)[D / 2]) {
+  constexpr int M = D / 2, Q = D / 4;
+  float er[Q + 1], ei[Q + 1], orr[Q + 1], oi[Q + 1];
+  rdft_f32<M, 2, 0, D>(g, er, ei);
+  rdft_f32<M, 2, 1, D>(g, orr, oi);
+  float u[D];
+  auto pack_done = [&](auto K) {
+    constexpr int k = RTQ_CI(K);
+    sfor<M>([&](auto W) {
+      constexpr int m = RTQ_CI(W);
+      constexpr int t0 = hartley_step<D>(2 * m), t1 = hartley_step<D>(2 * m + 1);
+      if constexpr ((t0 > t1 ? t0 : t1) == k) hw[m] = pack_f16x2(u[2 * m], u[2 * m + 1]);
+    });
+  };
+  u[0] = er[0] + orr[0];
+  u[M] = er[0] - orr[0];
+  u[Q] = er[Q] + orr[Q];
+  u[D - Q] = er[Q] - orr[Q];
+  pack_done(ic<0>{});
+  sfor<Q - 1>([&](auto K) {
+    constexpr int k = RTQ_CI(K) + 1;
+    constexpr double c = cos2pi(k, D), s = sin2pi(k, D);
+    constexpr float cps = (float)(c + s), smc = (float)(s - c), cms = (float)(c - s);
+    const float A = er[k] - ei[k], B = er[k] + ei[k];
+    u[k] = __builtin_fmaf(cps, orr[k], __builtin_fmaf(smc, oi[k], A));
+    u[D - k] = __builtin_fmaf(cms, orr[k], __builtin_fmaf(cps, oi[k], B));
+    u[M - k] = __builtin_fmaf(2.0f, B, -u[D - k]);
+    u[M + k] = __builtin_fmaf(2.0f, A, -u[k]);
+    pack_done(ic<k>{});
+  });
+}
+
+// u = sqrt2 * R^T z for the packed orthonormal SRFT of length D (the
+// srft_inv<D, Sqrt2> result), given yk = z / sqrt(D) (the caller folds that
+// factor into its dequantization), through the Hartley transform: with
+// g_0 = sqrt2 yk_0, g_{D/2} = sqrt2 yk_{D-1}, g_m = yk_{2m-1} - yk_{2m} and
+// g_{D-m} = yk_{2m-1} + yk_{2m} (m = 1 .. D/2-1), the inverse is
+// sum_m g_m (cos + sin)(2 pi m n / D) (hartley_f32).  This costs about the
+// forward recursion plus one operation per coordinate, against the complex
+// FFT of length D/2 plus its pre-processing for srft_inv.
+template <int D>
+__device__ __forceinline__ void srft_inv_hartley(const float (&yk)[D], float (&u)[D]) {
+  constexpr int M = D / 2;
+  constexpr float sq2 = 1.41421356237309504880f;
+  float g[D];
+  g[0] = sq2 * yk[0];
+  g[M] = sq2 * yk[D - 1];
+  sfor<M - 1>([&](auto K) {
+    constexpr int m = RTQ_CI(K) + 1;
+    g[m] = yk[2 * m - 1] - yk[2 * m];
+    g[D - m] = yk[2 * m - 1] + yk[2 * m];
+  });
+  hartley_f32<D>(g, u);
+}
+
+// srft_inv_hartley with the samples rounded to fp16 pairs (hartley_f32_packed).
+template <int D>
+__device__ __forceinline__ void srft_inv_hartley_packed(const float (&yk)[D], uint32_t (&hw)[D / 2]) {
+  constexpr int M = D / 2;
+  constexpr float sq2 = 1.41421356237309504880f;
+  float g[D];
+  g[0] = sq2 * yk[0];
+  g[M] = sq2 * yk[D - 1];
+  sfor<M - 1>([&](auto K) {
+    constexpr int m = RTQ_CI(K) + 1;
+    g[m] = yk[2 * m - 1] - yk[2 * m];
+    g[D - m] = yk[2 * m - 1] + yk[2 * m];
+  });
+  hartley_f32_packed<D>(g, hw);
+}
+
+// The factor on z for which srft_inv_hartley<D> returns u = R^T z.
+template <int D> struct HartleyIn { static constexpr float value = (float)(1.0 / csqrt(2.0 * (double)D)); };
+
 struct One { static constexpr double value = 1.0; };
 
 // 1/sqrt(D) as a compile-time fp32 constant (the SRHT normalization).
@@ -492,11 +652,38 @@ __device__ __forceinline__ void fwht_f32(float (&v)[N]) {
 // Symmetric absmax int4 quantizer and nibble packing.
 // ---------------------------------------------------------------------------
 
+// Eight int4 codes of (z * inv) packed into one word: nibble i = code i, two's
+// complement, q_i = clamp(rne(z_i * inv), -8, 7).  The rounding is
+// fma(z_i, inv, 1.5 * 2^23): the fp32 result lies in [2^23, 2^24), where the
+// spacing is 1, so the fma's single rounding is round-half-even of z_i * inv,
+// v_med3 clamps it, and the low 4 bits of the pattern are q_i mod 16.
+// (Forms that round z_i * inv + 248 with v_cvt_pk_u8_f32, or into an fp16
+// half with v_fma_mix{lo,hi}_f16, take fewer instructions but are not
+// faster: the first rounds twice, the second issues at half rate.)
+__device__ __forceinline__ uint32_t pack8_int4(const float* z, float inv) {
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
+  uint32_t b[8];
+  sfor<8>([&](auto I) {
+    const float t = __builtin_fmaf(z[RTQ_CI(I)], inv, kMagic);
+    b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic - 8.0f, kMagic + 7.0f));
+  });
+  // low bytes of the even codes -> e, of the odd codes -> o
+  const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
+  const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
+  return (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+}
+
+// Words Q .. Q + 3 of w count as computed here (an empty asm that claims to
+// change them): later code cannot move their computation past this point.
+template <int Q, int N>
+__device__ __forceinline__ void pin_words(uint32_t (&w)[N]) {
+  asm volatile("" : "+v"(w[Q]), "+v"(w[Q + 1]), "+v"(w[Q + 2]), "+v"(w[Q + 3]));
+}
+
 // One group (GI) of quantize_pack below.
 template <int GI, int D, int G>
 __device__ __forceinline__ void quantize_pack_group(const float (&z)[D], float zs, uint32_t (&cw)[D / 8],
                                                     uint32_t (&sb)[D / G]) {
-  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23
   constexpr int g0 = GI * G;
   float a = 0.0f;
   sfor<G>([&](auto I) { a = fmaxf(a, fabsf(z[g0 + RTQ_CI(I)])); });
@@ -508,27 +695,14 @@ __device__ __forceinline__ void quantize_pack_group(const float (&z)[D], float z
   const float inv = bits == 0u ? 0.0f : __builtin_amdgcn_rcpf(s) * zs;
   sfor<G / 8>([&](auto W) {
     constexpr int base = g0 + RTQ_CI(W) * 8;
-    uint32_t b[8];
-    sfor<8>([&](auto I) {
-      const float t = __builtin_fmaf(z[base + RTQ_CI(I)], inv, kMagic);
-      b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic - 8.0f, kMagic + 7.0f));
-    });
-    // low bytes of the even codes -> E, of the odd codes -> O
-    const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) |
-                       __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
-    const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) |
-                       __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
-    cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+    cw[base / 8] = pack8_int4(&z[base], inv);
   });
 }
 
 // Per group of G consecutive values of (zs * z): s = fp16_rne(absmax / 8)
 // saturated at 65504; q = clamp(rne(zs * z / s), -8, 7), q = 0 when s == 0.
-// Codes: cw[w] holds values 8w .. 8w+7, value 2i in the low nibble of byte i.
-// The rounding uses fma(z, 1/s, 1.5 * 2^23): the fp32 result lies in
-// [2^23, 2^24) where the spacing is 1, so the single rounding of the fma is
-// round-half-even of z/s, and the low 4 bits of the result are q mod 16.
-// quantize_pack_group does one group (GI) of this.
+// Codes: cw[w] holds values 8w .. 8w+7, value 2i in the low nibble of byte i
+// (pack8_int4).  quantize_pack_group does one group (GI) of this.
 template <int D, int G>
 __device__ __forceinline__ void quantize_pack(const float (&z)[D], float zs, uint32_t (&cw)[D / 8],
                                               uint32_t (&sb)[D / G]) {
@@ -547,12 +721,17 @@ __device__ __forceinline__ float mix_fma(uint32_t a, float b, float c) {
 }
 
 // z = s' * q for every value, s' = zs * s (inverse of quantize_pack's codes).
-// Two codes at a time become an fp16 pair: nibble j of a code word (value
-// 8w + j) and nibble j + 4 (value 8w + j + 4) are masked into the low and
-// high halves, biased to q + 8 by an xor with 8, and placed under the fp16
-// exponent of 1024 (0x6400), so each half reads 1024 + 8 + q.  One v_fma_mix
-// per value then gives (1032 + q) s' - 1032 s' = s' q.  For zs = 1 (and any
-// power of two) 1032 s' is exact in fp32 and so is the result.
+// Two codes at a time become an fp16 pair, biased to q + 8 by flipping the
+// nibble's top bit and placed under a fixed fp16 exponent:
+//   * nibbles j and j + 4 of a code word (values 8w + j, 8w + j + 4) with
+//     j = 0 (and j = 2 after one 8-bit shift) sit in mantissa bits 0..3 of
+//     the low and high halves under the exponent of 1024 (0x6400): each half
+//     reads 1024 + 8 + q, and one v_fma_mix gives (1032 + q) s' - 1032 s';
+//   * nibbles j = 1 (and 3) sit in mantissa bits 4..7 under the exponent of
+//     16384 (0x7400), where the mantissa unit is 16: each half reads
+//     16384 + 256 (q + 8), and (72 + q) (s' / 256) * 256 - 72 s' = s' q.
+// One shift, four mask-and-bias operations and eight v_fma_mix per word.
+// For a power-of-two zs every product and sum is exact in fp32.
 template <int D, int G>
 __device__ __forceinline__ void dequant_unpack(const uint32_t (&cw)[D / 8], const uint32_t (&sb)[D / G],
                                                float zs, float (&z)[D]) {
@@ -560,15 +739,22 @@ __device__ __forceinline__ void dequant_unpack(const uint32_t (&cw)[D / 8], cons
     constexpr int g0 = RTQ_CI(GI) * G;
     const float s = __half2float(__ushort_as_half((unsigned short)sb[RTQ_CI(GI)])) * zs;
     const float c = -1032.0f * s;
+    const float s16 = s * (1.0f / 256.0f), c16 = -72.0f * s;
     sfor<G / 8>([&](auto W) {
       constexpr int base = g0 + RTQ_CI(W) * 8;
-      const uint32_t x = cw[base / 8];
-      sfor<4>([&](auto J) {
-        constexpr int j = RTQ_CI(J);
-        const uint32_t pr = ((x >> (4 * j)) & 0x000f000fu) ^ 0x64086408u;
-        z[base + j] = mix_fma<0>(pr, s, c);
-        z[base + j + 4] = mix_fma<1>(pr, s, c);
-      });
+      const uint32_t x = cw[base / 8], y = x >> 8;
+      const uint32_t p0 = (x & 0x000f000fu) ^ 0x64086408u;  // nibbles 0 and 4
+      const uint32_t p1 = (x & 0x00f000f0u) ^ 0x74807480u;  // nibbles 1 and 5
+      const uint32_t p2 = (y & 0x000f000fu) ^ 0x64086408u;  // nibbles 2 and 6
+      const uint32_t p3 = (y & 0x00f000f0u) ^ 0x74807480u;  // nibbles 3 and 7
+      z[base + 0] = mix_fma<0>(p0, s, c);
+      z[base + 4] = mix_fma<1>(p0, s, c);
+      z[base + 1] = mix_fma<0>(p1, s16, c16);
+      z[base + 5] = mix_fma<1>(p1, s16, c16);
+      z[base + 2] = mix_fma<0>(p2, s, c);
+      z[base + 6] = mix_fma<1>(p2, s, c);
+      z[base + 3] = mix_fma<0>(p3, s16, c16);
+      z[base + 7] = mix_fma<1>(p3, s16, c16);
     });
   });
 }

@@ -113,8 +113,8 @@ __global__ __launch_bounds__(64) void inv_ext_kernel(const uint32_t* __restrict_
   sfor<CWW>([&](auto K) { cw[RTQ_CI(K)] = lw[r * CWW + RTQ_CI(K)]; });
   float z[D], u[D];
   if constexpr (ROT == kSRFT) {
-    dequant_unpack_bits<D, G, B>(cw, sb, 1.0f, z);
-    srft_inv<D, One>(z, u);
+    dequant_unpack_bits<D, G, B>(cw, sb, HartleyIn<D>::value, z);
+    srft_inv_hartley<D>(z, u);
   } else {
     dequant_unpack_bits<D, G, B>(cw, sb, InvSqrt<D>::value, u);
     fwht_f32<D>(u);

@@ -125,13 +125,6 @@ __device__ __forceinline__ void unweight_half(float (&u)[128], const float* inv,
   });
 }
 
-// Words Q .. Q + 3 of w count as computed here (an empty asm that claims to
-// change them): later code cannot move their computation past this point.
-template <int Q, int N>
-__device__ __forceinline__ void pin_words(uint32_t (&w)[N]) {
-  asm volatile("" : "+v"(w[Q]), "+v"(w[Q + 1]), "+v"(w[Q + 2]), "+v"(w[Q + 3]));
-}
-
 // Non-temporal store for streaming tiles, ordinary (L2-merged) store for rows
 // scattered by a cache layout.
 template <bool NT, class T>
@@ -167,24 +160,47 @@ __device__ __forceinline__ uint32_t seg_block(int p, int s) {
 }
 
 // cos and sin of 2 pi b / 256 for b = 0 .. 63 (the twiddles w^b = c - i s of
-// the pair exchange), from the same compile-time evaluation as the
+// the pair exchange), and c - s, c + s (the inverse exchange with the
+// Hartley step folded in), from the same compile-time evaluation as the
 // transforms' constants.  Copied into LDS once per tile; half p reads entry
 // a + 32 p.
 struct PairTwiddles {
   float cs[128];
+  float hd[128];
 };
 consteval PairTwiddles make_pair_twiddles() {
   PairTwiddles t{};
   for (int b = 0; b < 64; ++b) {
-    t.cs[2 * b] = (float)cos2pi(b, 256);
-    t.cs[2 * b + 1] = (float)sin2pi(b, 256);
+    const double c = cos2pi(b, 256), sn = sin2pi(b, 256);
+    t.cs[2 * b] = (float)c;
+    t.cs[2 * b + 1] = (float)sn;
+    t.hd[2 * b] = (float)(c - sn);
+    t.hd[2 * b + 1] = (float)(c + sn);
   }
   return t;
 }
 static __constant__ PairTwiddles kPairTwiddles = make_pair_twiddles();
 
+// The forward's table, (c, s) per entry.
 __device__ __forceinline__ void load_pair_twiddles(float* tw, int lane) {
   reinterpret_cast<float2*>(tw)[lane] = reinterpret_cast<const float2*>(kPairTwiddles.cs)[lane];
+}
+
+// The inverse's table, (c, s, c - s, c + s) per entry.
+__device__ __forceinline__ void load_pair_twiddles_inv(float* tw, int lane) {
+  const float2 a = reinterpret_cast<const float2*>(kPairTwiddles.cs)[lane];
+  const float2 b = reinterpret_cast<const float2*>(kPairTwiddles.hd)[lane];
+  reinterpret_cast<float4*>(tw)[lane] = make_float4(a.x, a.y, b.x, b.y);
+}
+
+// The twiddle tables' LDS copies (one object per kernel).
+__device__ __forceinline__ float* pair_twiddle_lds() {
+  __shared__ float tw[128];
+  return tw;
+}
+__device__ __forceinline__ float* pair_twiddle_lds_inv() {
+  __shared__ float tw[256];
+  return tw;
 }
 
 // ---------------------------------------------------------------------------
@@ -211,11 +227,11 @@ __device__ __forceinline__ float local_absmax(const float (&L)[128]) {
 // zs * a_raw / 2^(B-1)) saturated at 65504, q = clamp(rne(zs * L / s),
 // -2^(B-1), 2^(B-1) - 1), q = 0 when s == 0.  Codes form the lane's bit
 // stream (code j at bits [j B, (j + 1) B) of cw; for B = 4 the nibble
-// layout, two codes per byte, even code low).  The rounding is
-// fma(L, 1/s', 1.5 * 2^23): its fp32 result lies in [2^23, 2^24), where the
-// spacing is 1, so the fma's single rounding is round-half-even of L / s'
-// and the low bits are q in two's complement.  For B != 4 the caller zeroes
-// cw first.
+// layout, two codes per byte, even code low).  B = 4 rounds and packs with
+// pack8_int4; other widths round with fma(L, 1/s',
+// 1.5 * 2^23), whose fp32 result lies in [2^23, 2^24) where the spacing is 1,
+// so the fma's single rounding is round-half-even of L / s' and the low bits
+// are q in two's complement, and the caller zeroes cw first.
 template <int GI, int LG, int B>
 __device__ __forceinline__ void quantize_local_group(const float (&L)[128], float zs, float a_raw,
                                                      uint32_t (&cw)[4 * B], uint32_t (&sb)[128 / LG]) {
@@ -232,15 +248,7 @@ __device__ __forceinline__ void quantize_local_group(const float (&L)[128], floa
   if constexpr (B == 4) {
     sfor<LG / 8>([&](auto W) {
       constexpr int base = g0 + RTQ_CI(W) * 8;
-      uint32_t b[8];
-      sfor<8>([&](auto I) {
-        const float t = __builtin_fmaf(L[base + RTQ_CI(I)], inv, kMagic);
-        b[RTQ_CI(I)] = __float_as_uint(__builtin_amdgcn_fmed3f(t, kMagic + kLo, kMagic + kHi));
-      });
-      // low bytes of the even codes -> e, of the odd codes -> o
-      const uint32_t e = __builtin_amdgcn_perm(b[2], b[0], 0x0c0c0400u) | __builtin_amdgcn_perm(b[6], b[4], 0x04000c0cu);
-      const uint32_t o = __builtin_amdgcn_perm(b[3], b[1], 0x0c0c0400u) | __builtin_amdgcn_perm(b[7], b[5], 0x04000c0cu);
-      cw[base / 8] = (e & 0x0f0f0f0fu) | ((o << 4) & 0xf0f0f0f0u);
+      cw[base / 8] = pack8_int4(&L[base], inv);
     });
   } else {
     constexpr uint32_t kMask = (1u << B) - 1u;
@@ -429,31 +437,37 @@ __device__ __forceinline__ void srft_fwd_edges(float (&fr)[65], float (&fi)[65],
   L[64] = p ? -Q : yi;
 }
 
-// The inverse exchange: from the lane's coordinates L (halved: z / 2), the
-// packed 128-point spectrum yv of the lane's own samples (E for half 0, O for
-// half 1) in the convention of srft_inv<128, Sqrt2>.
-__device__ __forceinline__ void srft_inv_exchange(const float (&L)[128], const float2* twl, int p, float (&yv)[128]) {
+// The inverse exchange's bins 0, 32, 64 and 96: yv[0], yv[63], yv[64] and
+// yv[127] of srft_inv_exchange.
+__device__ __forceinline__ void srft_inv_edges(const float (&L)[128], int p, float& y0, float& y63, float& y64,
+                                               float& y127) {
   const float sigma = p ? -1.0f : 1.0f;
-  {
-    float x0, imx32, x128, rex96, rex32, rex64, imx96, imx64;
-    pair_both(L[0], x0, imx32);
-    pair_both(L[127], x128, rex96);
-    pair_both(L[63], rex32, rex64);
-    pair_both(L[64], imx96, imx64);
-    yv[0] = __builtin_fmaf(sigma, x128, x0);  // E_0 or O_0
-    const float er = rex32 + rex96, ei = imx32 - imx96, dr = rex32 - rex96, di = imx32 + imx96;
-    constexpr float h = 0.70710678118654752440f;  // w^-32 = h + i h
-    yv[63] = p ? h * (dr - di) : er;
-    yv[64] = p ? h * (di + dr) : ei;
-    constexpr float sq2 = 1.41421356237309504880f;  // E_64 = Re X_64, O_64 = -Im X_64
-    yv[127] = (p ? -imx64 : rex64) * sq2;
-  }
+  float x0, imx32, x128, rex96, rex32, rex64, imx96, imx64;
+  pair_both(L[0], x0, imx32);
+  pair_both(L[127], x128, rex96);
+  pair_both(L[63], rex32, rex64);
+  pair_both(L[64], imx96, imx64);
+  y0 = __builtin_fmaf(sigma, x128, x0);  // E_0 or O_0
+  const float er = rex32 + rex96, ei = imx32 - imx96, dr = rex32 - rex96, di = imx32 + imx96;
+  constexpr float h = 0.70710678118654752440f;  // w^-32 = h + i h
+  y63 = p ? h * (dr - di) : er;
+  y64 = p ? h * (di + dr) : ei;
+  constexpr float sq2 = 1.41421356237309504880f;  // E_64 = Re X_64, O_64 = -Im X_64
+  y127 = (p ? -imx64 : rex64) * sq2;
+}
+
+// The inverse exchange: from the lane's coordinates L (z / 2, times any
+// common factor), the packed 128-point spectrum yv of the lane's own samples
+// (E for half 0, O for half 1) in the convention of srft_inv<128, Sqrt2>,
+// times the same factor.  twl: the lane's half of the inverse table.
+__device__ __forceinline__ void srft_inv_exchange(const float (&L)[128], const float4* twl, int p, float (&yv)[128]) {
+  srft_inv_edges(L, p, yv[0], yv[63], yv[64], yv[127]);
   sfor<31>([&](auto A) {
     constexpr int a = RTQ_CI(A) + 1;
     const float ar = L[2 * a - 1], ai = L[2 * a], br = L[127 - 2 * a], bi = L[128 - 2 * a];
     float er = ar + br, ei = ai - bi;           // E_b = (X_b + conj X_{128-b}) / 2
     const float dr = ar - br, di = ai + bi;     // w^b O_b
-    const float2 t = twl[a];                    // w^-b = t.x + i t.y
+    const float4 t = twl[a];                    // w^-b = t.x + i t.y
     float orr = __builtin_fmaf(t.x, dr, -t.y * di);
     float oi = __builtin_fmaf(t.x, di, t.y * dr);
     pair_swap(er, orr);  // half 0: (E_a, E_{a+32}); half 1: (O_a, O_{a+32})
@@ -462,6 +476,39 @@ __device__ __forceinline__ void srft_inv_exchange(const float (&L)[128], const f
     yv[2 * a] = ei;
     yv[2 * a + 63] = orr;
     yv[2 * a + 64] = oi;
+  });
+}
+
+// srft_inv_exchange followed by srft_inv_hartley's first step, folded
+// together: g_m = Re Y_m - Im Y_m and g_{128-m} = Re Y_m + Im Y_m of the
+// lane's spectrum Y (m = 1 .. 63), g_0 = sqrt2 Y_0, g_64 = sqrt2 Y_64.  For
+// the O half, Re - Im and Re + Im of w^-b (dr + i di) come straight from
+// c - s and c + s: (c - s) dr - (c + s) di and (c + s) dr + (c - s) di.
+__device__ __forceinline__ void srft_inv_exchange_hartley(const float (&L)[128], const float4* twl, int p,
+                                                          float (&g)[128]) {
+  constexpr float sq2 = 1.41421356237309504880f;
+  {
+    float y0, y63, y64, y127;
+    srft_inv_edges(L, p, y0, y63, y64, y127);
+    g[0] = sq2 * y0;
+    g[64] = sq2 * y127;
+    g[32] = y63 - y64;
+    g[96] = y63 + y64;
+  }
+  sfor<31>([&](auto A) {
+    constexpr int a = RTQ_CI(A) + 1;
+    const float ar = L[2 * a - 1], ai = L[2 * a], br = L[127 - 2 * a], bi = L[128 - 2 * a];
+    const float er = ar + br, ei = ai - bi;
+    const float dr = ar - br, di = ai + bi;
+    const float4 t = twl[a];  // (c, s, c - s, c + s) of w^-b = c + i s
+    float em = er - ei, ep = er + ei;
+    float om = __builtin_fmaf(t.z, dr, -t.w * di), op = __builtin_fmaf(t.w, dr, t.z * di);
+    pair_swap(em, om);  // half 0: bins a and a + 32 of E; half 1: of O
+    pair_swap(ep, op);
+    g[a] = em;
+    g[128 - a] = ep;
+    g[a + 32] = om;
+    g[96 - a] = op;
   });
 }
 
@@ -481,7 +528,7 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
   constexpr int NLG = PairGroups<G>::NLG;
   const int p = lane >> 5, v = lane & 31;
   const uint32_t kpos = lane & 31;
-  __shared__ float tw[128];
+  float* tw = pair_twiddle_lds();
   if constexpr (ROT == kSRFT) load_pair_twiddles(tw, lane);  // read after the barrier below
   {
     const uint32_t row0 = R.row0;
@@ -607,8 +654,8 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
                                               const uint32_t* __restrict__ lam = nullptr, float* inv_lam = nullptr) {
   constexpr int NLG = PairGroups<G>::NLG, LG = PairGroups<G>::LG;
   if (lam != nullptr) pair_lambda_reciprocals<ROT>(lam, inv_lam, lane);  // read after a barrier below
-  __shared__ float tw[128];
-  if constexpr (ROT == kSRFT) load_pair_twiddles(tw, lane);  // read after the first barrier below
+  float* tw = pair_twiddle_lds_inv();
+  if constexpr (ROT == kSRFT) load_pair_twiddles_inv(tw, lane);  // read after the first barrier below
   const int p = lane >> 5, v = lane & 31;
   {
     const int rows = R.rows;
@@ -619,16 +666,36 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
       load_pair_codes<ROT, B>(codes, row, p, cw);
       load_pair_scales<ROT, G>(scales, row, p, sb);
     }
-    float u[128];
+    // Every sample is rounded to fp16 pairs before the output passes begin,
+    // so that no transform value stays live across them (the compiler would
+    // otherwise finish the last butterflies lazily inside the second pass and
+    // spill around the first).
+    uint32_t hw[64];
+    auto pack_all = [&](const float (&u)[128]) {
+      sfor<64>([&](auto M) { hw[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
+    };
     if constexpr (ROT == kSRFT) {
-      float L[128], yv[128];  // L = z / 2: the halving of E and O is folded in here
-      if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, 0.5f, L);
-      else dequant_unpack_bits<128, LG, B>(cw, sb, 0.5f, L);
+      // L = z / 2 (the halving of E and O) times 1/sqrt(128), the factor
+      // srft_inv_hartley expects on its input
+      constexpr float kDeq = (float)(0.5 / csqrt(128.0));
+      float L[128], yv[128];
+      if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, kDeq, L);
+      else dequant_unpack_bits<128, LG, B>(cw, sb, kDeq, L);
       lds_sync();  // the twiddle table is written
-      srft_inv_exchange(L, reinterpret_cast<const float2*>(tw) + 32 * p, p, yv);
-      srft_inv<128, Sqrt2>(yv, u);
+      const float4* twl = reinterpret_cast<const float4*>(tw) + 32 * p;
+      if (lam == nullptr) {
+        srft_inv_exchange_hartley(L, twl, p, yv);
+        hartley_f32_packed<128>(yv, hw);
+      } else {
+        float u[128];
+        srft_inv_exchange(L, twl, p, yv);
+        srft_inv_hartley<128>(yv, u);
+        lds_sync();
+        unweight_half(u, inv_lam, p);
+        pack_all(u);
+      }
     } else {
-      float L[128];
+      float L[128], u[128];
       if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, 1.0f / 16.0f, L);
       else dequant_unpack_bits<128, LG, B>(cw, sb, 1.0f / 16.0f, L);
       // half 0: z_k + z_{128+k}, half 1: z_k - z_{128+k}, k = 0 .. 127
@@ -640,17 +707,12 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
         u[k + 64] = d;
       });
       fwht_f32<128>(u);
+      if (lam != nullptr) {
+        lds_sync();
+        unweight_half(u, inv_lam, p);
+      }
+      pack_all(u);
     }
-    if (lam != nullptr) {
-      lds_sync();
-      unweight_half(u, inv_lam, p);
-    }
-    // Every sample rounded to fp16 pairs before the output passes begin, so
-    // that no transform value stays live across them (the compiler would
-    // otherwise finish the last butterflies lazily inside the second pass and
-    // spill around the first).
-    uint32_t hw[64];
-    sfor<64>([&](auto M) { hw[RTQ_CI(M)] = pack_f16x2(u[2 * RTQ_CI(M)], u[2 * RTQ_CI(M) + 1]); });
     sfor<16>([&](auto Q) { pin_words<4 * RTQ_CI(Q)>(hw); });
     // fp16 samples out through LDS in two passes of 16 output chunks per row
     // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
