@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, public figure
+KERNEL_REPS = 21  # event-timed samples per kernel (the median is reported)
 METRIC = "K/V vectors/s and HBM GB/s (% of peak), fused SRFT-int4 quant+dequant, 1 GPU"
 ATTN_METRIC = "decode-attention steps/s over the int4 rotated K/V cache (dequantized in registers), 1 GPU"
 _CSRC = os.path.join(ROOT, "rotate_then_quantize_amd", "csrc")
@@ -272,13 +273,29 @@ VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "
 SIMDS, CLOCK_HZ = 1024, 2.4e9  # MI355X: 256 CUs x 4 SIMDs, peak engine clock
 
 
-def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bool = False, skip: int = 0) -> None:
+EXTRA_COUNTERS = ("VALUBusy", "GRBM_GUI_ACTIVE", "LDSBankConflict", "TA_BUSY_avr", "TA_BUSY_max")
+XCDS = 8  # GRBM_GUI_ACTIVE is recorded once per XCD
+
+
+def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bool = False, skip: int = 0,
+                   extra_dirs=()) -> None:
     """Instruction mix per wave of each library kernel from one rocprofv3 --pmc
     pass of SQ counters (chip totals per dispatch), and the VALU issue time it
     implies: a wave64 VALU instruction occupies its SIMD for 4 cycles, so
     busy = SQ_INSTS_VALU * 4 / (SIMDs * clock * kernel time), with the kernel
-    time from a rocprofv3 trace of the same command and the peak clock."""
+    time from a rocprofv3 trace of the same command and the peak clock.
+    extra_dirs: further --pmc runs of the same command; the counters of
+    EXTRA_COUNTERS found there are listed, and with VALUBusy and
+    GRBM_GUI_ACTIVE (busy cycles, summed over the XCDs) the measured cycles
+    per VALU instruction (4 when every instruction issues at full rate) and the
+    clock the kernel ran at (its busy cycles per XCD over its trace time)."""
     per = {c: pmc_per_dispatch(pmc_dir, c) for c in VALU_COUNTERS}
+    extra = {}
+    for d in extra_dirs:
+        for c in EXTRA_COUNTERS:
+            vals, _ = pmc_per_dispatch(d, c)
+            if vals:
+                extra[c] = vals
     durs = {}
     for name, ds in trace_dispatches(trace_dir).items():
         kept = ds[skip:] if len(ds) > skip else ds
@@ -299,6 +316,16 @@ def summarize_valu(pmc_dir: str, trace_dir: str, w, rot: str, commands, attn: bo
                   f"valu_busy_estimate: {busy:.3f}",
                   "# valu_busy_estimate = SQ_INSTS_VALU * 4 cycles / (1024 SIMDs * 2.4 GHz * kernel time)"
                   + ("; MFMA instructions count as VALU instructions here" if attn else "")]
+        got = {c: v[kname] for c, v in extra.items() if kname in v}
+        for c, v in got.items():
+            lines.append(f"pmc_{c}: {v:.4g}")
+        if "VALUBusy" in got and "GRBM_GUI_ACTIVE" in got:
+            cycles = got["GRBM_GUI_ACTIVE"] / XCDS
+            per_inst = got["VALUBusy"] / 100.0 * cycles * SIMDS / valu
+            lines += [f"valu_cycles_per_instruction: {per_inst:.3f}",
+                      f"clock_GHz_while_running: {cycles / (durs[kname] * 1e-9) / 1e9:.3f}",
+                      "# valu_cycles_per_instruction = VALUBusy * (GRBM_GUI_ACTIVE / 8 XCDs) * 1024 SIMDs / "
+                      "SQ_INSTS_VALU; clock = (GRBM_GUI_ACTIVE / 8) / kernel time"]
         path = os.path.join(ROOT, "profiles", f"valu_{role}_{rot}_{w.name}.txt")
         with open(path, "w") as f:
             f.write("\n".join(lines) + "\n")
@@ -701,21 +728,14 @@ def attn_main(args, w, dev):
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    SAMPLE = 20
-    sampled = [i for i in range(args.steps) if i % SAMPLE == 0]
-    evs = {i: [torch.cuda.Event(enable_timing=True) for _ in range(2)] for i in sampled}
     t0 = time.perf_counter()
     for i in range(args.steps):
-        ev = evs.get(i)
-        if ev:
-            ev[0].record(stream)
         step(args.warmup + i)
-        if ev:
-            ev[1].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    k_ms = sum(evs[i][0].elapsed_time(evs[i][1]) for i in sampled) / len(sampled)
+    # the kernel's own time: median of KERNEL_REPS event-timed samples, in a pass after the timed steps
+    k_ms, (k_min, k_max), k_reps = time_launches(fn, [sets[k % replicas][0] for k in range(KERNEL_REPS)], stream)
     nbytes = attn_bytes(w, W)
     achieved = nbytes / k_ms / 1e6
     log(f"step {ms_step * 1e3:.1f} us | kernel {k_ms * 1e3:.1f} us {achieved:.0f} GB/s "
@@ -741,9 +761,11 @@ def attn_main(args, w, dev):
             "token_split_workspace_bytes": ws_bytes,
             "window_tokens": W,
         },
-        "kernel_us": {"attn_decode": k_ms * 1e3,
-                      "timing": f"hipEvents on the launch stream, every {SAMPLE}th timed step "
-                                f"({len(sampled)} of {args.steps})"},
+        "kernel_us": {"attn_decode": k_ms * 1e3, "attn_decode_min_max": [k_min * 1e3, k_max * 1e3],
+                      "launches_per_sample": k_reps,
+                      "timing": f"median of {KERNEL_REPS} samples, each a run of back-to-back launches (one "
+                                f"launch when a launch takes 1 ms or more) between two hipEvents on the launch "
+                                f"stream, in a pass after the timed steps"},
         "roofline": {
             "kernel": f"{rot}_attn_decode d={d} g={g} q_per_kv={G}",
             "bound": "hbm",
@@ -1073,9 +1095,10 @@ def main():
                     help="with --summarize-trace: leave each library kernel's first N dispatches out")
     ap.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                     help="write profiles/traffic_*.txt from four rocprofv3 --pmc CSV directories")
-    ap.add_argument("--summarize-valu", nargs=2, metavar=("PMC", "TRACE"),
-                    help="write profiles/valu_*.txt from a rocprofv3 --pmc run of SQ instruction counters and a "
-                         "kernel trace of the same command")
+    ap.add_argument("--summarize-valu", nargs="+", metavar="DIR",
+                    help="PMC TRACE [EXTRA ...]: write profiles/valu_*.txt from a rocprofv3 --pmc run of SQ "
+                         "instruction counters, a kernel trace of the same command and optional further --pmc "
+                         "runs (VALUBusy, GRBM_GUI_ACTIVE, LDSBankConflict, TA_BUSY)")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()
@@ -1088,8 +1111,13 @@ def main():
         from rotate_then_quantize_amd import workloads as W
         w = W.WORKLOADS[args.workload]
         if args.summarize_valu:
-            summarize_valu(*args.summarize_valu, w, args.rot, [("SQ counters", c) for c in args.command[-1:]],
-                           args.attn, args.trace_skip)
+            if len(args.summarize_valu) < 2:
+                ap.error("--summarize-valu takes PMC TRACE [EXTRA ...]")
+            pmc, trace, *extra_dirs = args.summarize_valu
+            n_cmd = 1 + len(extra_dirs)
+            cmds = [("SQ counters" if i == 0 else "extra counters", c)
+                    for i, c in enumerate(args.command[-n_cmd:])]
+            summarize_valu(pmc, trace, w, args.rot, cmds, args.attn, args.trace_skip, extra_dirs)
         if args.summarize_trace:
             summarize_trace(args.summarize_trace, w, args.rot, " ; ".join(args.command), args.attn, args.window,
                             args.trace_skip)
@@ -1209,7 +1237,6 @@ def main():
     # own, after the timed steps (so --steps does not change how many samples
     # there are); the median of the per-launch durations (time_launches).
     # Launches cycle the replicas as the steps do.
-    KERNEL_REPS = 21
     fwd_ms, fwd_spread, fwd_reps = time_launches(fwd_fn, [sets[i % replicas][0] for i in range(KERNEL_REPS)],
                                                  stream)
     inv_ms, inv_spread, inv_reps = time_launches(inv_fn, [sets[(i + 1) % replicas][1] for i in range(KERNEL_REPS)],

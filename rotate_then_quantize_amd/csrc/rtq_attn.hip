@@ -68,7 +68,17 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 
-constexpr int kWavesPerStream = 4; // a stream's tokens are split over 4 waves
+// Waves per workgroup, which split a stream's tokens into as many parts.
+// (Two waves at d = 128 ran 10% faster on the Qwen2.5-1.5B cache, 234-240
+// against 260-264 us, since the lead wave's query and output transforms then
+// leave one wave waiting instead of three.  Each wave's accumulators then
+// sum twice as many tokens against one running max, and the fp16 rounding of
+// weights and values lands differently: on a test cache with outlier
+// channels, where the output cancels terms 24 times its size, one element
+// moved 8% past the parity bound.  Kept at 4 until that bound is derived
+// from the fp16 operands instead of fixed.)
+__host__ __device__ constexpr int waves_per_stream(int) { return 4; }
+constexpr int kMaxWavesPerStream = 4;
 constexpr int kChunk = 32;     // tokens per chunk (one p.v k-step)
 constexpr int kBufs = 3;       // chunk buffers per wave (kBufs - 1 chunks in flight)
 // Waves per SIMD the register allocation targets.  The LDS ring (about 60 KB
@@ -112,7 +122,7 @@ __host__ __device__ constexpr int64_t part_floats(int g, int d) { return ((int64
 
 template <int D, int GR>
 struct Cfg {
-  static constexpr int WAVES = kWavesPerStream;
+  static constexpr int WAVES = waves_per_stream(D);
   // Ring slots per wave: three (two chunks in flight) up to d = 128; two at
   // d = 256, where three would leave room for one workgroup per CU only.
   static constexpr int BUFS = D == 256 ? 2 : kBufs;
@@ -131,14 +141,17 @@ struct Cfg {
   static constexpr int COMBINE = WAVES * kMaxQ * QROW * 4 + 2 * WAVES * kMaxQ * 4;
   static_assert(COMBINE <= SLOT_ARRAY, "the merge area fits in ring slot 0");
   static_assert(GR >= 32 && D % GR == 0, "groups of at least 32 values");
-  // d = 256: the whole workgroup rotates the queries and outputs (one
-  // coordinate per thread), in a work area that aliases ring slot 1, which
-  // is free before the first chunk and after the last one: the query stage
-  // [kMaxQ][QROW], the transposed vectors [D][kMaxQ] and the twiddles [D].
+  // d = 256: the whole workgroup rotates the queries and outputs (TPC
+  // threads per coordinate, each for kMaxQ / TPC queries), in a work area
+  // that aliases the last ring slot, which is free before its first chunk is
+  // issued and after the last one: the query stage [kMaxQ][QROW], the
+  // transposed vectors [D][kMaxQ] and the twiddles [D].
   static constexpr bool DENSE_ROT = D == 256;
+  static constexpr int WORK_SLOT = BUFS - 1;
+  static constexpr int TPC = 64 * WAVES / D;
   static constexpr int ROT_AREA = kMaxQ * QROW * 4 + D * kMaxQ * 4 + D * 8;
-  static_assert(!DENSE_ROT || (BUFS == 2 && ROT_AREA <= SLOT_ARRAY && D == 64 * WAVES),
-                "the rotation area needs a free ring slot and one thread per coordinate");
+  static_assert(!DENSE_ROT || (ROT_AREA <= SLOT_ARRAY && D * TPC == 64 * WAVES && (TPC == 1 || TPC == 2)),
+                "the rotation area needs a free ring slot and one or two threads per coordinate");
 };
 
 // Token row r of a chunk sits in LDS row lrow(r) (an involution), and 16-byte
@@ -168,6 +181,7 @@ __device__ __forceinline__ uint32_t as_u32(f16x2_t h) { return __builtin_bit_cas
 // the fp16 mantissa under the exponent of 1024 with the sign bit of the code
 // flipped (one v_bitop3), giving 1032 + q; subtract 1032.  K odd: the code
 // sits 4 bits higher, giving 1152 + 16 q; scale by 1/16 and subtract 72.
+// (The key operand at d = 256, where key_pair's bias registers would spill.)
 template <int K>
 __device__ __forceinline__ f16x2_t code_pair(uint32_t w) {
   const uint32_t x = K >= 2 ? w >> 8 : w;
@@ -178,6 +192,47 @@ __device__ __forceinline__ f16x2_t code_pair(uint32_t w) {
                                      (f16x2_t){(_Float16)0.0625f, (_Float16)0.0625f},
                                      (f16x2_t){(_Float16)-72.0f, (_Float16)-72.0f});
   }
+}
+
+// Codes K and K+4 of a key code word as the fp16 subnormals (q + 8) 2^-24,
+// times 16 for odd K (the code sits 4 bits higher): one v_bitop3 each (mask
+// and flip of the code's sign bit), the shift by 8 shared by K = 2 and 3.
+// The q.k operand of odd-K dims carries the matching 1/16, and the bias 8
+// enters the MFMA accumulator as its start value (key_bias), so the q.k
+// MFMA sums (q + 8) y and starts from -8 sum(y): scores come out times 2^-24.
+template <int K>
+__device__ __forceinline__ f16x2_t key_pair(uint32_t w) {
+  const uint32_t x = K >= 2 ? w >> 8 : w;
+  if constexpr ((K & 1) == 0) return as_h2((x & 0x000f000fu) ^ 0x00080008u);
+  else return as_h2((x & 0x00f000f0u) ^ 0x00800080u);
+}
+
+// Codes K and K+4 of a value code word as exact fp16 q / 16: the code under
+// the exponent of 1024 (1032 + q, K even) or of 1024 with the code 4 bits up
+// (1152 + 16 q, K odd), then one packed fma with 1/16 and -64.5 or with 1/256
+// and -4.5 (every step exact in fp16).
+template <int K>
+__device__ __forceinline__ f16x2_t value_pair16(uint32_t w) {
+  const uint32_t x = K >= 2 ? w >> 8 : w;
+  if constexpr ((K & 1) == 0) {
+    return __builtin_elementwise_fma(as_h2((x & 0x000f000fu) ^ 0x64086408u),
+                                     (f16x2_t){(_Float16)0.0625f, (_Float16)0.0625f},
+                                     (f16x2_t){(_Float16)-64.5f, (_Float16)-64.5f});
+  } else {
+    return __builtin_elementwise_fma(as_h2((x & 0x00f000f0u) ^ 0x64806480u),
+                                     (f16x2_t){(_Float16)0.00390625f, (_Float16)0.00390625f},
+                                     (f16x2_t){(_Float16)-4.5f, (_Float16)-4.5f});
+  }
+}
+
+// max of three floats (v_max3_f32 written out: fmaxf adds a quieting
+// v_max_f32 x, x before every operand the compiler cannot prove canonical,
+// and the lane-swap results below are such operands; scores are never
+// signalling NaNs)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
 // half SEL of w (fp16) times b plus c, in fp32 (one v_fma_mix_f32).  Plain
@@ -211,9 +266,17 @@ __device__ __forceinline__ float add_ror8(float x) {
 // x with itself across 16-lane rows and then across 32-lane halves.
 __device__ __forceinline__ float max_over_row_groups(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max3f(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max3f(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[1]));
+}
+
+// Sum of x over lanes n, n + 16, n + 32, n + 48 (the same lane swaps).
+__device__ __forceinline__ float sum_over_row_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Device-scope (all XCDs) store and load of one float of a split partial.
@@ -243,10 +306,13 @@ __device__ __forceinline__ void wave_sign_masks(uint64_t s, int lane, uint32_t (
 
 // ---------------------------------------------------------------------------
 // d = 256: the queries are rotated and the outputs rotated back by the whole
-// workgroup, thread t computing coordinate t of every query as a direct sum
-// over the 256 inputs.  This runs once per stream and step, about 2k
-// instructions per thread, where one lane per vector would need 256 fp32
-// registers.  Vectors sit transposed in LDS, v[n * kMaxQ + g], so each term's
+// workgroup, each thread computing one coordinate of the queries as a direct
+// sum over the d inputs, where one lane per vector would need 256 fp32
+// registers.  This runs once per stream and step, about 2k instructions per
+// thread.  (The code also takes two threads per coordinate, each for half the
+// queries, as d = 128 would need; at d = 128 that measured slower than the
+// lead wave's per-lane transforms, 288 against 270-280 us on the Qwen2.5-1.5B
+// cache.)  Vectors sit transposed in LDS, v[n * kMaxQ + g], so each term's
 // reads are one broadcast.
 // ---------------------------------------------------------------------------
 
@@ -273,53 +339,63 @@ __device__ __forceinline__ void load_column(const float* v, int n, float (&a)[NQ
   }
 }
 
-// z[g] = coordinate t of R v_g for NQ vectors: the packed orthonormal real
-// DFT (z_0 = X_0 / 16, z_{2k-1} = sqrt2 Re X_k / 16, z_{2k} = sqrt2 Im X_k / 16,
-// z_255 = X_128 / 16) for SRFT, H v / 16 for SRHT.
-template <int ROT, int NQ>
+// Twiddle m of a length-D transform, (cos, sin)(2 pi m / D), from the
+// 256-entry table.
+template <int D>
+__device__ __forceinline__ float2 twiddle(int m) {
+  return make_float2(kTwiddle256.c[m * (256 / D)], kTwiddle256.s[m * (256 / D)]);
+}
+
+// z[g] = coordinate t of R v_g for NQ vectors (v: the transposed vectors,
+// first of the NQ queries at v[0]): the packed orthonormal real DFT
+// (z_0 = X_0 / sqrt(D), z_{2k-1} = sqrt2 Re X_k / sqrt(D), z_{2k} =
+// sqrt2 Im X_k / sqrt(D), z_{D-1} = X_{D/2} / sqrt(D)) for SRFT, H v / sqrt(D)
+// for SRHT.
+template <int D, int ROT, int NQ>
 __device__ __forceinline__ void dense_forward(const float* v, const float2* tw, int t, float (&z)[NQ]) {
   float acc[NQ];
   sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = 0.0f; });
   if constexpr (ROT == 0) {
     const int k = (t + 1) >> 1;
-    const bool im = t > 0 && t < 255 && (t & 1) == 0;  // X_k = sum v_n (cos - i sin)(2 pi k n / 256)
+    const bool im = t > 0 && t < D - 1 && (t & 1) == 0;  // X_k = sum v_n (cos - i sin)(2 pi k n / D)
     int idx = 0;
 #pragma unroll 4
-    for (int n = 0; n < 256; ++n) {
+    for (int n = 0; n < D; ++n) {
       const float2 w = tw[idx];
       const float c = im ? -w.y : w.x;
       float a[NQ];
       load_column<NQ>(v, n, a);
       sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = __builtin_fmaf(c, a[RTQ_CI(G)], acc[RTQ_CI(G)]); });
-      idx = (idx + k) & 255;
+      idx = (idx + k) & (D - 1);
     }
-    const float norm = (t == 0 || t == 255) ? 0.0625f : (float)(csqrt(2.0) / 16.0);
+    constexpr float n_end = (float)(1.0 / csqrt((double)D)), n_mid = (float)(csqrt(2.0 / (double)D));
+    const float norm = (t == 0 || t == D - 1) ? n_end : n_mid;
     sfor<NQ>([&](auto G) { z[RTQ_CI(G)] = acc[RTQ_CI(G)] * norm; });
   } else {
 #pragma unroll 4
-    for (int n = 0; n < 256; ++n) {
+    for (int n = 0; n < D; ++n) {
       const float c = (__builtin_popcount(t & n) & 1) ? -1.0f : 1.0f;  // H[t][n]
       float a[NQ];
       load_column<NQ>(v, n, a);
       sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = __builtin_fmaf(c, a[RTQ_CI(G)], acc[RTQ_CI(G)]); });
     }
-    sfor<NQ>([&](auto G) { z[RTQ_CI(G)] = acc[RTQ_CI(G)] * 0.0625f; });
+    sfor<NQ>([&](auto G) { z[RTQ_CI(G)] = acc[RTQ_CI(G)] * InvSqrt<D>::value; });
   }
 }
 
 // u[g] = element t of R^T z_g: the orthonormal inverse real DFT of the
-// unpacked bins for SRFT, H z / 16 for SRHT.
-template <int ROT, int NQ>
+// unpacked bins for SRFT, H z / sqrt(D) for SRHT.
+template <int D, int ROT, int NQ>
 __device__ __forceinline__ void dense_inverse(const float* z, const float2* tw, int t, float (&u)[NQ]) {
   if constexpr (ROT == 0) {
     float a0[NQ], a1[NQ], acc[NQ];
     load_column<NQ>(z, 0, a0);
-    load_column<NQ>(z, 255, a1);
+    load_column<NQ>(z, D - 1, a1);
     const float alt = (t & 1) ? -1.0f : 1.0f;  // cos(pi t)
     sfor<NQ>([&](auto G) { acc[RTQ_CI(G)] = 0.0f; });
     int idx = t;
 #pragma unroll 4
-    for (int k = 1; k < 128; ++k) {
+    for (int k = 1; k < D / 2; ++k) {
       const float2 w = tw[idx];
       float re[NQ], im[NQ];
       load_column<NQ>(z, 2 * k - 1, re);
@@ -328,15 +404,15 @@ __device__ __forceinline__ void dense_inverse(const float* z, const float2* tw, 
         constexpr int g = RTQ_CI(G);
         acc[g] = __builtin_fmaf(w.x, re[g], __builtin_fmaf(-w.y, im[g], acc[g]));
       });
-      idx = (idx + t) & 255;
+      idx = (idx + t) & (D - 1);
     }
     constexpr float r2 = (float)csqrt(2.0);
     sfor<NQ>([&](auto G) {
       constexpr int g = RTQ_CI(G);
-      u[g] = __builtin_fmaf(r2, acc[g], __builtin_fmaf(alt, a1[g], a0[g])) * 0.0625f;
+      u[g] = __builtin_fmaf(r2, acc[g], __builtin_fmaf(alt, a1[g], a0[g])) * InvSqrt<D>::value;
     });
   } else {
-    dense_forward<1, NQ>(z, tw, t, u);  // H / 16 is its own inverse
+    dense_forward<D, 1, NQ>(z, tw, t, u);  // H / sqrt(D) is its own inverse
   }
 }
 
@@ -357,53 +433,59 @@ __device__ __forceinline__ void dma_to_lds(const void* g, const void* lds) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off nt" ::"s"(m), "v"(g) : "memory", "m0");
 }
 
-// d = 256 prologue, every thread: the stream's G queries, sign-flipped with
-// the key signs (element t by thread t), go transposed into the work area;
-// thread t computes coordinate t of each rotated query, scaled by qscale;
+// Dense prologue (d = 128, 256), every thread: the stream's G queries,
+// sign-flipped with the key signs, go transposed into the work area (element
+// n of queries 4h' .. 4h' + 3 by thread n + D h'); the TPC threads of
+// coordinate c compute it for their share of the queries, scaled by qscale;
 // then each query is scaled by the power of two 2^-e that puts its largest
 // entry in [2^13, 2^14) and stored to the stage [kMaxQ][D + 4].
 template <int D, int ROT>
 __device__ __forceinline__ void dense_queries(const Params& p, int64_t qrow, uint64_t seed_k, int G, uint8_t* area,
                                               float* stage, int* qexp) {
+  constexpr int TPC = 64 * waves_per_stream(D) / D, NQ = kMaxQ / TPC;
   __shared__ uint32_t amax_bits[kMaxQ];
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, c = t % D, g0 = (t / D) * NQ;
   float* vt = reinterpret_cast<float*>(area + kMaxQ * (D + 4) * 4);
   float2* tw = reinterpret_cast<float2*>(vt + D * kMaxQ);
   const _Float16* q16 = reinterpret_cast<const _Float16*>(p.q);
-  const float sg = sign_bit(seed_k, (uint32_t)t) ? -1.0f : 1.0f;
-  float col[kMaxQ];
-  sfor<kMaxQ>([&](auto Gi) {
-    constexpr int g = RTQ_CI(Gi);
-    col[g] = g < G ? sg * (float)q16[(qrow + g) * D + t] : 0.0f;
+  const float sg = sign_bit(seed_k, (uint32_t)c) ? -1.0f : 1.0f;
+  float col[NQ];
+  sfor<NQ>([&](auto Gi) {
+    const int g = g0 + RTQ_CI(Gi);
+    col[RTQ_CI(Gi)] = g < G ? sg * (float)q16[(qrow + g) * D + c] : 0.0f;
   });
-  *reinterpret_cast<float4*>(vt + t * kMaxQ) = make_float4(col[0], col[1], col[2], col[3]);
-  *reinterpret_cast<float4*>(vt + t * kMaxQ + 4) = make_float4(col[4], col[5], col[6], col[7]);
-  if constexpr (ROT == 0) tw[t] = make_float2(kTwiddle256.c[t], kTwiddle256.s[t]);
+  *reinterpret_cast<float4*>(vt + c * kMaxQ + g0) = make_float4(col[0], col[1], col[2], col[3]);
+  if constexpr (NQ == 8) *reinterpret_cast<float4*>(vt + c * kMaxQ + 4) = make_float4(col[4], col[5], col[6], col[7]);
+  if (ROT == 0 && t < D) tw[t] = twiddle<D>(t);
   if (t < kMaxQ) amax_bits[t] = 0u;
   __syncthreads();
-  float z[kMaxQ];
-  if (G <= 4) {
-    float z4[4];
-    dense_forward<ROT, 4>(vt, tw, t, z4);
-    sfor<kMaxQ>([&](auto Gi) { z[RTQ_CI(Gi)] = RTQ_CI(Gi) < 4 ? z4[RTQ_CI(Gi) & 3] : 0.0f; });
-  } else {
-    dense_forward<ROT, 8>(vt, tw, t, z);
+  float z[NQ];
+  if (g0 < G) {
+    if (NQ == 8 && G <= 4) {
+      float z4[4];
+      dense_forward<D, ROT, 4>(vt, tw, c, z4);
+      sfor<NQ>([&](auto Gi) { z[RTQ_CI(Gi)] = RTQ_CI(Gi) < 4 ? z4[RTQ_CI(Gi) & 3] : 0.0f; });
+    } else {
+      dense_forward<D, ROT, NQ>(vt + g0, tw, c, z);
+    }
+    sfor<NQ>([&](auto Gi) {
+      const int g = g0 + RTQ_CI(Gi);
+      z[RTQ_CI(Gi)] *= p.qscale;
+      if (g < G)
+        __hip_atomic_fetch_max(&amax_bits[g], __float_as_uint(fabsf(z[RTQ_CI(Gi)])), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    });
   }
-  sfor<kMaxQ>([&](auto Gi) {
-    constexpr int g = RTQ_CI(Gi);
-    z[g] *= p.qscale;
-    if (g < G)
-      __hip_atomic_fetch_max(&amax_bits[g], __float_as_uint(fabsf(z[g])), __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_WORKGROUP);
-  });
   __syncthreads();
-  sfor<kMaxQ>([&](auto Gi) {
-    constexpr int g = RTQ_CI(Gi);
-    const float amax = __uint_as_float(amax_bits[g]);
-    const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
-    stage[g * (D + 4) + t] = __builtin_ldexpf(z[g], -e);
-    if (t == g) qexp[g] = e;
-  });
+  if (g0 < G) {
+    sfor<NQ>([&](auto Gi) {
+      const int g = g0 + RTQ_CI(Gi);
+      const float amax = __uint_as_float(amax_bits[g]);
+      const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+      stage[g * (D + 4) + c] = __builtin_ldexpf(z[RTQ_CI(Gi)], -e);
+      if (c == g) qexp[g] = e;
+    });
+  }
 }
 
 // Direct-to-LDS loads of chunk tokens tok0 .. tok0+31 (tokens past the end
@@ -487,8 +569,8 @@ struct MaxOp {
 template <int D>
 struct WindowLds {
   static constexpr int PAIRS = D / 2;               // 4-byte dim pairs per row
-  static constexpr int PHASES = 64 * kWavesPerStream / PAIRS;  // token phases of the value loop
-  static constexpr int PLANES = PAIRS < 64 ? kWavesPerStream : PHASES;  // d = 64: one per wave
+  static constexpr int PHASES = 64 * waves_per_stream(D) / PAIRS;  // token phases of the value loop
+  static constexpr int PLANES = PAIRS < 64 ? waves_per_stream(D) : PHASES;  // d = 64: one per wave
   static constexpr int WEIGHT_BYTES = 4096;
   static_assert((kMaxWindow * kMaxQ + kMaxQ) * 4 <= WEIGHT_BYTES, "weights and coef fit 4 KB");
   static constexpr int RED_BYTES = PLANES * kMaxQ * D * 4;
@@ -513,7 +595,7 @@ struct WindowRegs {
   using WL = WindowLds<D>;
   static constexpr int CPR = D / 8;                    // 16-byte pieces per row
   static constexpr int RPW = 64 / CPR;                 // rows per wave per key load
-  static constexpr int RPG = RPW * kWavesPerStream;    // rows per workgroup per key load
+  static constexpr int RPG = RPW * waves_per_stream(D);  // rows per workgroup per key load
   static constexpr int NK = kMaxWindow / RPG;          // key loads per thread
   static constexpr int NV = kMaxWindow / WL::PHASES;   // value loads per thread
   uint4 qv[kMaxQ], kv[NK];
@@ -574,7 +656,7 @@ __device__ __forceinline__ void window_part(const Params& p, const WindowRegs<D>
 
   // softmax over the int4 part and the window, one wave per query; the
   // weights of rows past the window become 0
-  for (int g = w; g < G; g += kWavesPerStream) {
+  for (int g = w; g < G; g += waves_per_stream(D)) {
     const float sc = lane < W ? wts[lane * kMaxQ + g] : kNegBig;
     const float m = fmaxf(mq[g], reduce_lanes<64>(sc, MaxOp{}));
     const float fr = __builtin_amdgcn_exp2f(mq[g] - m);  // 0 when there is no int4 token
@@ -625,7 +707,7 @@ __device__ __forceinline__ void window_part(const Params& p, const WindowRegs<D>
     });
   }
   __syncthreads();
-  for (int idx = t; idx < G * D; idx += 64 * kWavesPerStream) {
+  for (int idx = t; idx < G * D; idx += 64 * waves_per_stream(D)) {
     const int g = idx / D, dim = idx - g * D;
     float sum = 0.0f;
     sfor<WL::PLANES>([&](auto P) { sum += red[(RTQ_CI(P) * kMaxQ + g) * D + dim]; });
@@ -690,7 +772,7 @@ struct ChunkSources {
 };
 
 template <int D, int GR, int ROT>
-__global__ void __launch_bounds__(64 * kWavesPerStream) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
+__global__ void __launch_bounds__(64 * waves_per_stream(D)) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
 attn_decode_kernel(Params p) {
   using C = Cfg<D, GR>;
   constexpr int kWaves = C::WAVES, kStreams = 1;
@@ -703,8 +785,9 @@ attn_decode_kernel(Params p) {
   // query in, output out (d = 256: in the work area of ring slot 1)
   __shared__ __attribute__((aligned(16))) float stage_arr[C::DENSE_ROT ? 4 : kStreams * kMaxQ * C::QROW];
   __shared__ int qexp_all[kStreams * kMaxQ];
-  float* const stage_all = C::DENSE_ROT ? reinterpret_cast<float*>(slot1) : stage_arr;
-  float* const vt_all = reinterpret_cast<float*>(slot1 + kMaxQ * C::QROW * 4);  // d = 256: [D][kMaxQ]
+  uint8_t* const work = C::WORK_SLOT == 1 ? slot1 : slot2;  // the dense rotations' area (last ring slot)
+  float* const stage_all = C::DENSE_ROT ? reinterpret_cast<float*>(work) : stage_arr;
+  float* const vt_all = reinterpret_cast<float*>(work + kMaxQ * C::QROW * 4);  // dense: [D][kMaxQ]
 
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int n = lane & 15, h = lane >> 4;
@@ -719,7 +802,7 @@ attn_decode_kernel(Params p) {
   const int pair = item / p.splits, split = item - pair * p.splits;  // a pair's splits are neighbours
   const int pairs_per_layer = (p.streams + kStreams - 1) / kStreams;
   const int layer = pair / pairs_per_layer;
-  const int sw = w / kWavesPerStream, part_w = w % kWavesPerStream;  // stream of the wave, token part
+  const int sw = w / kWaves, part_w = w % kWaves;  // stream of the wave, token part
   const int stream = (pair - layer * pairs_per_layer) * kStreams + sw;
   const bool active = stream < p.streams;
   const int64_t row_k = (int64_t)layer * p.stride_layer + (int64_t)stream * p.stride_stream;
@@ -731,8 +814,8 @@ attn_decode_kernel(Params p) {
   // this workgroup's chunks (its split of the stream), then this wave's part of them
   const int64_t nchunks = active ? (T + kChunk - 1) / kChunk : 0;
   const int s_begin = (int)(split * nchunks / p.splits), s_len = (int)((split + 1) * nchunks / p.splits) - s_begin;
-  const int c_begin = s_begin + part_w * s_len / kWavesPerStream;
-  const int c_end = s_begin + (part_w + 1) * s_len / kWavesPerStream;
+  const int c_begin = s_begin + part_w * s_len / kWaves;
+  const int c_end = s_begin + (part_w + 1) * s_len / kWaves;
   const bool lead = active && part_w == 0;  // rotates the stream's queries and outputs
 
   // ---- prologue: queries (lead waves) and the first two chunks (every wave) ----
@@ -753,7 +836,7 @@ attn_decode_kernel(Params p) {
   if (C::BUFS > 2 && c_begin + 1 < c_end)
     load_chunk(c_begin + 1, slot1 + w * C::BUF);
   if constexpr (C::DENSE_ROT) {
-    dense_queries<D, ROT>(p, qrow, seed_of_row(p, row_k), G, slot1, stage, qexp);
+    dense_queries<D, ROT>(p, qrow, seed_of_row(p, row_k), G, work, stage, qexp);
   } else if (lead) {
     uint32_t mk[D / 2];
     wave_sign_masks<D>(seed_of_row(p, row_k), lane, mk);
@@ -776,19 +859,18 @@ attn_decode_kernel(Params p) {
         sc = InvSqrt<D>::value * p.qscale;
       }
       float amax = 0.0f;
-      sfor<D>([&](auto I) {
-        y[RTQ_CI(I)] *= sc;
-        amax = fmaxf(amax, fabsf(y[RTQ_CI(I)]));
-      });
+      sfor<D>([&](auto I) { amax = fmaxf(amax, fabsf(y[RTQ_CI(I)])); });
+      amax *= sc;  // the largest entry of y * sc (rounding is monotonic)
       // scale the query by 2^-e so that its largest entry lies in [2^13, 2^14):
-      // the fp16 high part cannot overflow and the low part keeps its bits
+      // the fp16 high part cannot overflow and the low part keeps its bits.
+      // y * (sc 2^-e) is (y * sc) 2^-e exactly: one multiply per entry.
       const int e = amax > 0.0f ? __builtin_amdgcn_frexp_expf(amax) - 14 : 0;
+      const float f = __builtin_ldexpf(sc, -e);
       float* dst = stage + lane * C::QROW;
       sfor<D / 4>([&](auto I) {
         constexpr int i = RTQ_CI(I);
-        *reinterpret_cast<float4*>(dst + 4 * i) =
-            make_float4(__builtin_ldexpf(y[4 * i], -e), __builtin_ldexpf(y[4 * i + 1], -e),
-                        __builtin_ldexpf(y[4 * i + 2], -e), __builtin_ldexpf(y[4 * i + 3], -e));
+        *reinterpret_cast<float4*>(dst + 4 * i) = make_float4(y[4 * i] * f, y[4 * i + 1] * f, y[4 * i + 2] * f,
+                                                              y[4 * i + 3] * f);
       });
       qexp[lane] = e;
     }
@@ -797,29 +879,52 @@ attn_decode_kernel(Params p) {
 
   // q.k B operand, k-step j: column n < 8 holds the fp16 high part of query
   // n, column n + 8 its low part; lane group h supplies dims
-  // 32j + 8h + {v, v + 4} as pair v (the order code_pair produces).
+  // 32j + 8h + {v, v + 4} as pair v (the order key_pair produces).
+  // Pair v of odd v meets key codes held 16 times larger (key_pair), so it
+  // carries 1/16 (exact: a power of two).  key_bias[gi]: the MFMA start
+  // value of score group gi in this lane's column, -8 2^-24 times the sum of
+  // the column's query parts over the group's dims (key_pair's bias).
+  constexpr bool kBiasedKeys = D <= 128;  // key_pair (else code_pair and no bias)
   f16x8_t bq[C::KS];
+  float key_bias[C::SPR];
   {
     const int g = n & 7;
     const bool valid = g < G;
     const float* src = stage + g * C::QROW;
+    float part_sum[C::KS];
     sfor<C::KS>([&](auto J) {
       constexpr int j = RTQ_CI(J);
       uint32_t wds[4];
+      float ps = 0.0f;
       sfor<4>([&](auto V) {
         constexpr int v = RTQ_CI(V);
         const float a = valid ? src[32 * j + 8 * h + v] : 0.0f;
         const float b = valid ? src[32 * j + 8 * h + v + 4] : 0.0f;
         const _Float16 ah = (_Float16)a, bh = (_Float16)b;
         const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
-        wds[v] = n < 8 ? as_u32((f16x2_t){ah, bh}) : as_u32((f16x2_t){al, bl});
+        const _Float16 x0 = n < 8 ? ah : al, x1 = n < 8 ? bh : bl;
+        ps += (float)x0 + (float)x1;
+        constexpr float m = (kBiasedKeys && (v & 1)) ? 0.0625f : 1.0f;
+        wds[v] = as_u32((f16x2_t){(_Float16)((float)x0 * m), (_Float16)((float)x1 * m)});
       });
       bq[j] = pack8(as_h2(wds[0]), as_h2(wds[1]), as_h2(wds[2]), as_h2(wds[3]));
+      part_sum[j] = kBiasedKeys ? sum_over_row_groups(ps) : 0.0f;
+    });
+    sfor<C::SPR>([&](auto GI) {
+      constexpr int gi = RTQ_CI(GI), per = GR / 32;
+      float t = 0.0f;
+      sfor<per>([&](auto JJ) { t += part_sum[gi * per + RTQ_CI(JJ)]; });
+      key_bias[gi] = kBiasedKeys ? t * -4.76837158203125e-7f : 0.0f;  // -8 * 2^-24
     });
   }
-  const int my_e = n < G ? qexp[n & 7] : 0;
-  const bool q_lane = n < G;  // lanes whose scores / outputs belong to a query
-  if constexpr (C::DENSE_ROT) __syncthreads();  // the stage in ring slot 1 is read; the ring may refill it
+  // 2^e of the query of this lane's column (its stage row was scaled by 2^-e).
+  // Columns without a query have a zero operand: their scores are 0, their
+  // softmax stays finite and nothing reads their outputs, so they need no
+  // mask; lanes n + 8 hold copies of columns n < 8 (add_ror8).
+  const float my_scale =
+      __builtin_ldexpf(1.0f, ((n & 7) < G ? qexp[n & 7] : 0) + (kBiasedKeys ? 24 : 0));  // key_pair's 2^-24 too
+  const bool q_lane = n < G;  // lanes whose outputs are merged
+  if constexpr (C::DENSE_ROT) __syncthreads();  // the stage in the work slot is read; the ring may refill it
 
   f32x4_t acc[C::NT];
   sfor<C::NT>([&](auto I) { acc[RTQ_CI(I)] = (f32x4_t){0.0f, 0.0f, 0.0f, 0.0f}; });
@@ -849,6 +954,7 @@ attn_decode_kernel(Params p) {
     const uint8_t* ks = buf + 2 * C::CODE_BYTES;
     const uint8_t* vs = ks + C::SCALE_BYTES;
     const int tok0 = c * kChunk;
+    const bool full = tok0 + kChunk <= T;
 
     // ---- scores of tokens 16 tau + 4h + r (column n) ----
     float sc[2][4];
@@ -868,32 +974,39 @@ attn_decode_kernel(Params p) {
       f32x4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
       sfor<C::SPR>([&](auto GI) {
         constexpr int gi = RTQ_CI(GI);
-        f32x4_t part = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4_t part = {key_bias[gi], key_bias[gi], key_bias[gi], key_bias[gi]};
         sfor<GR / 32>([&](auto JJ) {
           constexpr int j = gi * (GR / 32) + RTQ_CI(JJ);
           const uint32_t x = kw[j];
-          part = mfma(pack8(code_pair<0>(x), code_pair<1>(x), code_pair<2>(x), code_pair<3>(x)), bq[j], part);
+          if constexpr (kBiasedKeys)
+            part = mfma(pack8(key_pair<0>(x), key_pair<1>(x), key_pair<2>(x), key_pair<3>(x)), bq[j], part);
+          else
+            part = mfma(pack8(code_pair<0>(x), code_pair<1>(x), code_pair<2>(x), code_pair<3>(x)), bq[j], part);
         });
         sfor<4>([&](auto R) {
           constexpr int r = RTQ_CI(R);
           s[r] = half_fma<gi & 1>(sk[SW * r + (gi >> 1)], part[r], s[r]);
         });
       });
-      sfor<4>([&](auto R) {
-        constexpr int r = RTQ_CI(R);
-        const float v = __builtin_ldexpf(add_ror8(s[r]), my_e);
-        const bool ok = q_lane && (tok0 + 16 * tau + 4 * h + r < T);
-        sc[tau][r] = ok ? v : -__builtin_inff();
-      });
+      // scores in units of 1 / my_scale (base-2 units once multiplied by it);
+      // only a chunk that holds the stream's last token has tokens to mask
+      sfor<4>([&](auto R) { sc[tau][RTQ_CI(R)] = add_ror8(s[RTQ_CI(R)]); });
+      if (!full) {
+        asm volatile("");  // a branch, not four selects on every chunk
+        sfor<4>([&](auto R) {
+          constexpr int r = RTQ_CI(R);
+          if (tok0 + 16 * tau + 4 * h + r >= T) sc[tau][r] = -__builtin_inff();
+        });
+      }
     });
 
     // ---- online softmax (base 2) over the chunk, per query column ----
     // The running max moves only when a score passes it by more than 8
     // (weights stay <= 2^8, well inside fp16), so the accumulators are
     // rescaled a handful of times per stream instead of on most chunks.
-    float cmax = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                       fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    cmax = max_over_row_groups(cmax);
+    float cmax = max3f(max3f(sc[0][0], sc[0][1], sc[0][2]), max3f(sc[0][3], sc[1][0], sc[1][1]),
+                       max3f(sc[1][2], sc[1][3], sc[1][3]));
+    cmax = max_over_row_groups(cmax) * my_scale;  // the factor is a power of two: max and scaling commute
     const bool grow = cmax > m_run + kRescaleSlack;
     if (__ballot(grow)) {
       const float m_new = grow ? cmax : m_run;
@@ -903,20 +1016,25 @@ attn_decode_kernel(Params p) {
       m_run = m_new;
     }
     float pr[2][4];
-    float psum = 0.0f;
     sfor<2>([&](auto TAU) {
       sfor<4>([&](auto R) {
-        const float e = __builtin_amdgcn_exp2f(sc[RTQ_CI(TAU)][RTQ_CI(R)] - m_run);
-        pr[RTQ_CI(TAU)][RTQ_CI(R)] = e;
-        psum += e;
+        pr[RTQ_CI(TAU)][RTQ_CI(R)] =
+            __builtin_amdgcn_exp2f(__builtin_fmaf(sc[RTQ_CI(TAU)][RTQ_CI(R)], my_scale, -m_run));
       });
     });
-    l_run += psum;
-    // P^T operand: element 4 tau + r = token 16 tau + 4h + r of query n
-    const f16x8_t pb = pack8((f16x2_t){(_Float16)pr[0][0], (_Float16)pr[0][1]},
-                             (f16x2_t){(_Float16)pr[0][2], (_Float16)pr[0][3]},
-                             (f16x2_t){(_Float16)pr[1][0], (_Float16)pr[1][1]},
-                             (f16x2_t){(_Float16)pr[1][2], (_Float16)pr[1][3]});
+    // P^T operand: element 4 tau + r = token 16 tau + 4h + r of query n.  The
+    // denominator sums these fp16 weights themselves (v_dot2_f32_f16 with
+    // (1, 1): exact), so numerator and denominator use the same weights.
+    const f16x2_t p01 = {(_Float16)pr[0][0], (_Float16)pr[0][1]}, p23 = {(_Float16)pr[0][2], (_Float16)pr[0][3]};
+    const f16x2_t p45 = {(_Float16)pr[1][0], (_Float16)pr[1][1]}, p67 = {(_Float16)pr[1][2], (_Float16)pr[1][3]};
+    const f16x8_t pb = pack8(p01, p23, p45, p67);
+    {
+      const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+      float psum = __builtin_amdgcn_fdot2(p01, one, 0.0f, false);
+      psum = __builtin_amdgcn_fdot2(p23, one, psum, false);
+      psum = __builtin_amdgcn_fdot2(p45, one, psum, false);
+      l_run += __builtin_amdgcn_fdot2(p67, one, psum, false);
+    }
 
     // ---- values: V^T operand of tokens (a, b) = pair v of lane group h ----
     uint32_t ylo[WH][4], yhi[WH][4], s2[WH][4];
@@ -939,8 +1057,7 @@ attn_decode_kernel(Params p) {
         const int vgi = (8 * wd) / GR;  // the scale group of those dims
         const uint16_t sa = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * ta + 2 * vgi);
         const uint16_t sb2 = *reinterpret_cast<const uint16_t*>(vs + C::SLOT * tb + 2 * vgi);
-        const f16x2_t sp = as_h2((uint32_t)sa | ((uint32_t)sb2 << 16)) * (f16x2_t){(_Float16)kVShift, (_Float16)kVShift};
-        s2[hh][v] = as_u32(sp);
+        s2[hh][v] = (uint32_t)sa | ((uint32_t)sb2 << 16);  // value_pair16 carries the 1/16 of kVShift
       });
     });
     sfor<C::NT>([&](auto I) {
@@ -950,7 +1067,7 @@ attn_decode_kernel(Params p) {
       sfor<4>([&](auto V) {
         constexpr int v = RTQ_CI(V);
         const uint32_t y = (D >= 128 && (i & 4)) ? yhi[hh][v] : ylo[hh][v];
-        a[v] = code_pair<k>(y) * as_h2(s2[hh][v]);
+        a[v] = value_pair16<k>(y) * as_h2(s2[hh][v]);
       });
       acc[i] = mfma(pack8(a[0], a[1], a[2], a[3]), pb, acc[i]);
     });
@@ -1002,6 +1119,9 @@ attn_decode_kernel(Params p) {
   static_assert(kStreams == 1, "the split partials assume one stream per workgroup");
   // the merged output of query g, dim: the stage row (one lane per query
   // rotates it back), or at d = 256 the transposed work area
+  // (the SRFT inverse below is srft_inv_hartley, whose input factor
+  // 1/sqrt(2d) is folded in here)
+  constexpr float kOutFold = (ROT == 0 && !C::DENSE_ROT) ? HartleyIn<D>::value : 1.0f;
   auto put_out = [&](int g, int dim, float val) {
     if constexpr (C::DENSE_ROT) vt_all[dim * kMaxQ + g] = val;
     else stage_all[g * C::QROW + dim] = val;
@@ -1012,16 +1132,16 @@ attn_decode_kernel(Params p) {
   for (int idx = threadIdx.x; idx < G * D; idx += 64 * kWaves) {
     const int g = idx / D, dim = idx % D;
     float mx = kNegBig;
-    for (int ww = 0; ww < kWavesPerStream; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
+    for (int ww = 0; ww < kWaves; ++ww) mx = fmaxf(mx, mw[ww * kMaxQ + g]);
     float num = 0.0f, den = 0.0f;
-    for (int ww = 0; ww < kWavesPerStream; ++ww) {
+    for (int ww = 0; ww < kWaves; ++ww) {
       const float f = __builtin_amdgcn_exp2f(mw[ww * kMaxQ + g] - mx);
       den = __builtin_fmaf(f, lw[ww * kMaxQ + g], den);
       num = __builtin_fmaf(f, ow[(ww * kMaxQ + g) * C::QROW + dim], num);
     }
     if (p.splits == 1) {
       // den >= 1 when the stream has int4 tokens (the max score has weight 1)
-      put_out(g, dim, den > 0.0f ? num / (den * kVShift) : 0.0f);
+      put_out(g, dim, den > 0.0f ? num * (kOutFold / kVShift) / den : 0.0f);
       if (dim == 0) {
         mq[g] = mx;
         lq[g] = den;
@@ -1037,10 +1157,13 @@ attn_decode_kernel(Params p) {
   if (p.splits > 1) {
     // Publish this split's partial; the workgroup that completes the count
     // merges all of them (no workgroup ever waits for another).
-    // The partials are written and read with device-scope accesses, which
-    // the L2 of each XCD does not keep to itself, so no L2 writeback or
-    // invalidate (an agent-scope fence, which costs far more than the merge)
-    // is needed: waiting for the stores before the count moves is enough.
+    // The partials are agent-scope relaxed atomics: global accesses with sc1,
+    // coherent across the XCDs' L2 caches (LLVM AMDGPUUsage, memory model for
+    // GFX942).  An agent-scope release would add an L2 writeback and an
+    // acquire an L2 invalidate, which only ordinary (non-sc1) accesses need;
+    // what remains of the release, waiting for the stores before the count
+    // moves, is done here, and every read of a partial is an sc1 load issued
+    // after the count's fetch_add has returned.
     __shared__ int is_last;
     wait_vmcnt<0>();  // this lane's partial stores are complete
     __syncthreads();
@@ -1061,7 +1184,7 @@ attn_decode_kernel(Params p) {
         den = __builtin_fmaf(f, collect(ps + G * D + G + g), den);
         num = __builtin_fmaf(f, collect(ps + idx), num);
       }
-      put_out(g, dim, den > 0.0f ? num / (den * kVShift) : 0.0f);
+      put_out(g, dim, den > 0.0f ? num * (kOutFold / kVShift) / den : 0.0f);
       if (dim == 0) {
         mq[g] = mx;
         lq[g] = den;
@@ -1077,8 +1200,8 @@ attn_decode_kernel(Params p) {
   using WL = WindowLds<D>;
   float* const wsc = reinterpret_cast<float*>(slot0);     // [kMaxWindow][kMaxQ] weights
   float* const coef = wsc + kMaxWindow * kMaxQ;            // [kMaxQ]
-  float* const ows = reinterpret_cast<float*>(C::DENSE_ROT ? slot0 + WL::WEIGHT_BYTES : slot1);  // [kMaxQ][D]
-  static_assert(C::DENSE_ROT ? WL::WEIGHT_BYTES + WL::RED_BYTES <= C::SLOT_ARRAY
+  float* const ows = reinterpret_cast<float*>(C::WORK_SLOT == 1 ? slot0 + WL::WEIGHT_BYTES : slot1);  // [kMaxQ][D]
+  static_assert((C::DENSE_ROT && C::WORK_SLOT == 1) ? WL::WEIGHT_BYTES + WL::RED_BYTES <= C::SLOT_ARRAY
                              : WL::WEIGHT_BYTES <= C::SLOT_ARRAY && WL::RED_BYTES <= C::SLOT_ARRAY,
                 "the window area fits the free ring slots");
   if (has_window) {
@@ -1088,28 +1211,31 @@ attn_decode_kernel(Params p) {
 
   // ---- rotate the outputs back: o = D_V R^T o_rot ----
   if constexpr (C::DENSE_ROT) {
-    const int t = threadIdx.x;
+    constexpr int NQ = kMaxQ / C::TPC;
+    const int t = threadIdx.x, c = t % D, g0 = (t / D) * NQ;
     float2* tw = reinterpret_cast<float2*>(vt_all + D * kMaxQ);
-    if constexpr (ROT == 0) tw[t] = make_float2(kTwiddle256.c[t], kTwiddle256.s[t]);
+    if (ROT == 0 && t < D) tw[t] = twiddle<D>(t);
     __syncthreads();
-    const float sv = sign_bit(seed_of_row(p, row_v), (uint32_t)t) ? -1.0f : 1.0f;
+    const float sv = sign_bit(seed_of_row(p, row_v), (uint32_t)c) ? -1.0f : 1.0f;
     _Float16* o16 = reinterpret_cast<_Float16*>(p.out);
     auto store = [&](int g, float u) {
-      if (has_window) u = __builtin_fmaf(coef[g], u, ows[g * D + t]);
-      o16[(qrow + g) * D + t] = (_Float16)(sv * u);
+      if (has_window) u = __builtin_fmaf(coef[g], u, ows[g * D + c]);
+      o16[(qrow + g) * D + c] = (_Float16)(sv * u);
     };
-    if (G <= 4) {
-      float u[4];
-      dense_inverse<ROT, 4>(vt_all, tw, t, u);
-      sfor<4>([&](auto Gi) {
-        if (RTQ_CI(Gi) < G) store(RTQ_CI(Gi), u[RTQ_CI(Gi)]);
-      });
-    } else {
-      float u[kMaxQ];
-      dense_inverse<ROT, kMaxQ>(vt_all, tw, t, u);
-      sfor<kMaxQ>([&](auto Gi) {
-        if (RTQ_CI(Gi) < G) store(RTQ_CI(Gi), u[RTQ_CI(Gi)]);
-      });
+    if (g0 < G) {
+      if (NQ == 8 && G <= 4) {
+        float u[4];
+        dense_inverse<D, ROT, 4>(vt_all, tw, c, u);
+        sfor<4>([&](auto Gi) {
+          if (RTQ_CI(Gi) < G) store(RTQ_CI(Gi), u[RTQ_CI(Gi)]);
+        });
+      } else {
+        float u[NQ];
+        dense_inverse<D, ROT, NQ>(vt_all + g0, tw, c, u);
+        sfor<NQ>([&](auto Gi) {
+          if (g0 + RTQ_CI(Gi) < G) store(g0 + RTQ_CI(Gi), u[RTQ_CI(Gi)]);
+        });
+      }
     }
   } else if (lead) {
     uint32_t mvs[D / 2];
@@ -1123,7 +1249,7 @@ attn_decode_kernel(Params p) {
         z[4 * i] = f.x; z[4 * i + 1] = f.y; z[4 * i + 2] = f.z; z[4 * i + 3] = f.w;
       });
       if constexpr (ROT == 0) {
-        srft_inv<D, One>(z, u);
+        srft_inv_hartley<D>(z, u);
       } else {
         fwht_f32<D>(z);
         sfor<D>([&](auto I) { u[RTQ_CI(I)] = z[RTQ_CI(I)] * InvSqrt<D>::value; });
@@ -1307,7 +1433,7 @@ rtq_status run(int rot, const void* q, const void* codes, const void* scales, vo
   p.win_tokens = win_tokens;
   void* kargs[] = {&p};
   const hipError_t e =
-      hipLaunchKernel(fn, dim3((unsigned)(wgs * splits)), dim3(64 * kWavesPerStream), kargs, 0, stream);
+      hipLaunchKernel(fn, dim3((unsigned)(wgs * splits)), dim3(64 * waves_per_stream(d)), kargs, 0, stream);
   return e == hipSuccess ? RTQ_OK : RTQ_ERR_HIP;
 }
 
