@@ -292,8 +292,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
   fwd_pair_tile<G, ROT>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x);
 }
 
-// Three waves per SIMD: the SRHT inverse fits without spills, the SRFT
-// inverse spills a few addresses that are used only by the final stores.
+// Three waves per SIMD (at most 168 VGPRs): both rotations fit without
+// spills.
 template <int G, int ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_pair_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y, uint32_t n,

@@ -523,9 +523,11 @@ constexpr int hartley_step(int n) {
 
 // hartley_f32 with the samples rounded to fp16 pairs, hw[m] = (u_{2m},
 // u_{2m+1}), each pair as soon as the step that completes it has run, so
-// that few unpacked samples are live at once.
-template <int D>
-__device__ __forceinline__ void hartley_f32_packed(const float (&g)[D], uint32_t (&hw)[D / 2]) {
+// that few unpacked samples are live at once.  Weighted: sample n is first
+// multiplied by w[n] (w 8-byte aligned).
+template <int D, bool Weighted = false>
+__device__ __forceinline__ void hartley_f32_packed(const float (&g)[D], uint32_t (&hw)[D / 2],
+                                                   const float* w = nullptr) {
   constexpr int M = D / 2, Q = D / 4;
   float er[Q + 1], ei[Q + 1], orr[Q + 1], oi[Q + 1];
   rdft_f32<M, 2, 0, D>(g, er, ei);
@@ -536,7 +538,14 @@ __device__ __forceinline__ void hartley_f32_packed(const float (&g)[D], uint32_t
     sfor<M>([&](auto W) {
       constexpr int m = RTQ_CI(W);
       constexpr int t0 = hartley_step<D>(2 * m), t1 = hartley_step<D>(2 * m + 1);
-      if constexpr ((t0 > t1 ? t0 : t1) == k) hw[m] = pack_f16x2(u[2 * m], u[2 * m + 1]);
+      if constexpr ((t0 > t1 ? t0 : t1) == k) {
+        if constexpr (Weighted) {
+          const float2 q = *reinterpret_cast<const float2*>(w + 2 * m);
+          hw[m] = pack_f16x2(u[2 * m] * q.x, u[2 * m + 1] * q.y);
+        } else {
+          hw[m] = pack_f16x2(u[2 * m], u[2 * m + 1]);
+        }
+      }
     });
   };
   u[0] = er[0] + orr[0];

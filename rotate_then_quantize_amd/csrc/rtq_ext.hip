@@ -156,19 +156,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   fwd_pair_tile<G, ROT, TileRows, B>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
 }
 
-// Three waves per SIMD (the SRFT inverses spill a few addresses that only
-// the final stores use).
-template <int G, int ROT, int B>
+// Three waves per SIMD, one kernel per lambda case (inv_pair_tile's LAM).
+template <int G, int ROT, int B, bool LAM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void inv_ext_pair_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, uint4* __restrict__ y,
     const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
   __shared__ uint4 lds[32 * 17];
-  __shared__ __attribute__((aligned(16))) float inv_lam[kPairLambdaFloats];
-  inv_pair_tile<G, ROT, TileRows, B>(codes, scales, y, tile_rows(n, sr, tb), lds, threadIdx.x, lam, inv_lam);
+  __shared__ __attribute__((aligned(16))) float inv_lam[LAM ? kPairLambdaFloats : 2];
+  inv_pair_tile<G, ROT, TileRows, B, LAM>(codes, scales, y, tile_rows(n, sr, tb), lds, threadIdx.x, lam, inv_lam);
 }
 
 template <int ROT, int B>
-KernelFn find_ext_bits(bool fwd, int d, int g) {
+KernelFn find_ext_bits(bool fwd, int d, int g, bool lam) {
 #define RTQ_EXT_CASE(DD, GG)                                                           \
   if (d == DD && g == GG)                                                              \
     return fwd ? reinterpret_cast<KernelFn>(&fwd_ext_kernel<DD, GG, ROT, B>)           \
@@ -179,19 +178,20 @@ KernelFn find_ext_bits(bool fwd, int d, int g) {
 #define RTQ_EXT_PAIR_CASE(GG)                                                          \
   if (d == 256 && g == GG)                                                             \
     return fwd ? reinterpret_cast<KernelFn>(&fwd_ext_pair_kernel<GG, ROT, B>)          \
-               : reinterpret_cast<KernelFn>(&inv_ext_pair_kernel<GG, ROT, B>);
+           : lam ? reinterpret_cast<KernelFn>(&inv_ext_pair_kernel<GG, ROT, B, true>)  \
+                 : reinterpret_cast<KernelFn>(&inv_ext_pair_kernel<GG, ROT, B, false>);
   RTQ_EXT_PAIR_CASE(32) RTQ_EXT_PAIR_CASE(64) RTQ_EXT_PAIR_CASE(128) RTQ_EXT_PAIR_CASE(256)
 #undef RTQ_EXT_PAIR_CASE
   return nullptr;
 }
 
 template <int ROT>
-KernelFn find_ext(bool fwd, int d, int g, int bits) {
+KernelFn find_ext(bool fwd, int d, int g, int bits, bool lam) {
   switch (bits) {
-    case 3: return find_ext_bits<ROT, 3>(fwd, d, g);
-    case 4: return find_ext_bits<ROT, 4>(fwd, d, g);
-    case 6: return find_ext_bits<ROT, 6>(fwd, d, g);
-    case 8: return find_ext_bits<ROT, 8>(fwd, d, g);
+    case 3: return find_ext_bits<ROT, 3>(fwd, d, g, lam);
+    case 4: return find_ext_bits<ROT, 4>(fwd, d, g, lam);
+    case 6: return find_ext_bits<ROT, 6>(fwd, d, g, lam);
+    case 8: return find_ext_bits<ROT, 8>(fwd, d, g, lam);
     default: return nullptr;
   }
 }
@@ -204,7 +204,8 @@ rtq_status run_ext(bool fwd, int rot, const void* in0, const void* in1, void* ou
   if (n < 0 || rps < 0 || period < 0) return RTQ_ERR_INVALID_ARG;
   const rtq_status shape = check_shape(d, g);
   if (shape != RTQ_OK) return shape;
-  KernelFn fn = rot == kSRFT ? find_ext<kSRFT>(fwd, d, g, bits) : find_ext<kSRHT>(fwd, d, g, bits);
+  KernelFn fn = rot == kSRFT ? find_ext<kSRFT>(fwd, d, g, bits, lam != nullptr)
+                              : find_ext<kSRHT>(fwd, d, g, bits, lam != nullptr);
   if (!fn) return RTQ_ERR_UNSUPPORTED;
   // 4 bits with lambda below d = 256: the int4 tiles with the lambda multiply
   // (16-byte code moves, the int4 packer), which write the same bytes

@@ -437,8 +437,11 @@ __device__ __forceinline__ void srft_fwd_edges(float (&fr)[65], float (&fi)[65],
   L[64] = p ? -Q : yi;
 }
 
-// The inverse exchange's bins 0, 32, 64 and 96: yv[0], yv[63], yv[64] and
-// yv[127] of srft_inv_exchange.
+// The inverse exchange takes the lane's coordinates L (z / 2, times any
+// common factor) to the packed 128-point spectrum Y of the lane's own samples
+// (E for half 0, O for half 1) in the convention of srft_inv<128, Sqrt2>,
+// times the same factor.  This gives its entries 0, 63, 64 and 127 (bins 0,
+// 32, 64 and 96).
 __device__ __forceinline__ void srft_inv_edges(const float (&L)[128], int p, float& y0, float& y63, float& y64,
                                                float& y127) {
   const float sigma = p ? -1.0f : 1.0f;
@@ -456,30 +459,7 @@ __device__ __forceinline__ void srft_inv_edges(const float (&L)[128], int p, flo
   y127 = (p ? -imx64 : rex64) * sq2;
 }
 
-// The inverse exchange: from the lane's coordinates L (z / 2, times any
-// common factor), the packed 128-point spectrum yv of the lane's own samples
-// (E for half 0, O for half 1) in the convention of srft_inv<128, Sqrt2>,
-// times the same factor.  twl: the lane's half of the inverse table.
-__device__ __forceinline__ void srft_inv_exchange(const float (&L)[128], const float4* twl, int p, float (&yv)[128]) {
-  srft_inv_edges(L, p, yv[0], yv[63], yv[64], yv[127]);
-  sfor<31>([&](auto A) {
-    constexpr int a = RTQ_CI(A) + 1;
-    const float ar = L[2 * a - 1], ai = L[2 * a], br = L[127 - 2 * a], bi = L[128 - 2 * a];
-    float er = ar + br, ei = ai - bi;           // E_b = (X_b + conj X_{128-b}) / 2
-    const float dr = ar - br, di = ai + bi;     // w^b O_b
-    const float4 t = twl[a];                    // w^-b = t.x + i t.y
-    float orr = __builtin_fmaf(t.x, dr, -t.y * di);
-    float oi = __builtin_fmaf(t.x, di, t.y * dr);
-    pair_swap(er, orr);  // half 0: (E_a, E_{a+32}); half 1: (O_a, O_{a+32})
-    pair_swap(ei, oi);
-    yv[2 * a - 1] = er;
-    yv[2 * a] = ei;
-    yv[2 * a + 63] = orr;
-    yv[2 * a + 64] = oi;
-  });
-}
-
-// srft_inv_exchange followed by srft_inv_hartley's first step, folded
+// The inverse exchange followed by srft_inv_hartley's first step, folded
 // together: g_m = Re Y_m - Im Y_m and g_{128-m} = Re Y_m + Im Y_m of the
 // lane's spectrum Y (m = 1 .. 63), g_0 = sqrt2 Y_0, g_64 = sqrt2 Y_64.  For
 // the O half, Re - Im and Re + Im of w^-b (dr + i di) come straight from
@@ -498,9 +478,9 @@ __device__ __forceinline__ void srft_inv_exchange_hartley(const float (&L)[128],
   sfor<31>([&](auto A) {
     constexpr int a = RTQ_CI(A) + 1;
     const float ar = L[2 * a - 1], ai = L[2 * a], br = L[127 - 2 * a], bi = L[128 - 2 * a];
-    const float er = ar + br, ei = ai - bi;
-    const float dr = ar - br, di = ai + bi;
-    const float4 t = twl[a];  // (c, s, c - s, c + s) of w^-b = c + i s
+    const float er = ar + br, ei = ai - bi;  // E_b = (X_b + conj X_{128-b}) / 2
+    const float dr = ar - br, di = ai + bi;  // w^b O_b
+    const float4 t = twl[a];                 // (c, s, c - s, c + s) of w^-b = c + i s
     float em = er - ei, ep = er + ei;
     float om = __builtin_fmaf(t.z, dr, -t.w * di), op = __builtin_fmaf(t.w, dr, t.z * di);
     pair_swap(em, om);  // half 0: bins a and a + 32 of E; half 1: of O
@@ -646,14 +626,16 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
 // ---------------------------------------------------------------------------
 
 // Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
-// that R.y_chunk addresses, for B-bit codes and an optional lambda.  lds
-// holds 32 x 17 uint4.
-template <int G, int ROT, class Rows, int B = 4>
+// that R.y_chunk addresses, for B-bit codes, divided by lambda when LAM.
+// lds holds 32 x 17 uint4.  The lambda case is a template parameter: with
+// both transform paths behind a run-time branch the compiler merges their
+// common steps and spills about 130 registers.
+template <int G, int ROT, class Rows, int B = 4, bool LAM = false>
 __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
                                               uint4* __restrict__ y, const Rows& R, uint4* lds, int lane,
                                               const uint32_t* __restrict__ lam = nullptr, float* inv_lam = nullptr) {
   constexpr int NLG = PairGroups<G>::NLG, LG = PairGroups<G>::LG;
-  if (lam != nullptr) pair_lambda_reciprocals<ROT>(lam, inv_lam, lane);  // read after a barrier below
+  if constexpr (LAM) pair_lambda_reciprocals<ROT>(lam, inv_lam, lane);  // read after a barrier below
   float* tw = pair_twiddle_lds_inv();
   if constexpr (ROT == kSRFT) load_pair_twiddles_inv(tw, lane);  // read after the first barrier below
   const int p = lane >> 5, v = lane & 31;
@@ -681,19 +663,10 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
       float L[128], yv[128];
       if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, kDeq, L);
       else dequant_unpack_bits<128, LG, B>(cw, sb, kDeq, L);
-      lds_sync();  // the twiddle table is written
+      lds_sync();  // the twiddle and reciprocal tables are written
       const float4* twl = reinterpret_cast<const float4*>(tw) + 32 * p;
-      if (lam == nullptr) {
-        srft_inv_exchange_hartley(L, twl, p, yv);
-        hartley_f32_packed<128>(yv, hw);
-      } else {
-        float u[128];
-        srft_inv_exchange(L, twl, p, yv);
-        srft_inv_hartley<128>(yv, u);
-        lds_sync();
-        unweight_half(u, inv_lam, p);
-        pack_all(u);
-      }
+      srft_inv_exchange_hartley(L, twl, p, yv);
+      hartley_f32_packed<128, LAM>(yv, hw, LAM ? inv_lam + p * 132 : nullptr);  // u / lambda when LAM
     } else {
       float L[128], u[128];
       if constexpr (B == 4) dequant_unpack<128, LG>(cw, sb, 1.0f / 16.0f, L);
@@ -707,7 +680,7 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
         u[k + 64] = d;
       });
       fwht_f32<128>(u);
-      if (lam != nullptr) {
+      if constexpr (LAM) {
         lds_sync();
         unweight_half(u, inv_lam, p);
       }
