@@ -80,12 +80,17 @@ typedef uint32_t u32x4v_t __attribute__((ext_vector_type(4)));
 __host__ __device__ constexpr int waves_per_stream(int) { return 4; }
 constexpr int kMaxWavesPerStream = 4;
 constexpr int kChunk = 32;     // tokens per chunk (one p.v k-step)
-constexpr int kBufs = 3;       // chunk buffers per wave (kBufs - 1 chunks in flight)
-// Waves per SIMD the register allocation targets.  The LDS ring (about 60 KB
-// per workgroup at d = 128) allows two workgroups per CU; a two-slot ring at
-// three waves per SIMD measured no faster (423 vs 417 us on the Qwen2.5-1.5B
-// decode cache).
-constexpr int kWavesPerEU = 2;
+// Chunk buffers per wave (one fewer chunks in flight) and the waves per SIMD
+// the register allocation targets, by head dimension.  d = 128: two slots
+// (41 KB of LDS per workgroup) and three waves per SIMD, so three
+// workgroups share a CU; against three slots (60 KB, two workgroups per CU)
+// this took 226 instead of 256 us on the Qwen2.5-1.5B decode cache, the
+// third resident wave hiding more of each chunk's load and LDS latency than
+// the second chunk in flight did.  d = 64: three slots at two waves (the
+// compiler stays at 138 VGPRs, so three waves per SIMD run anyway).  d = 256:
+// two slots (three would leave room for one workgroup per CU) at two waves.
+__host__ __device__ constexpr int ring_slots(int d) { return d == 64 ? 3 : 2; }
+__host__ __device__ constexpr int waves_per_eu(int d) { return d == 128 ? 3 : 2; }
 constexpr int kMaxQ = 8;       // query heads per K/V head
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, below any score
 constexpr float kVShift = 0.0625f;   // V is decoded as q * s / 16
@@ -123,9 +128,7 @@ __host__ __device__ constexpr int64_t part_floats(int g, int d) { return ((int64
 template <int D, int GR>
 struct Cfg {
   static constexpr int WAVES = waves_per_stream(D);
-  // Ring slots per wave: three (two chunks in flight) up to d = 128; two at
-  // d = 256, where three would leave room for one workgroup per CU only.
-  static constexpr int BUFS = D == 256 ? 2 : kBufs;
+  static constexpr int BUFS = ring_slots(D);  // ring slots per wave
   static constexpr int KS = D / 32;       // q.k k-steps = 16-byte pieces per code row
   static constexpr int NT = D / 16;       // p.v output tiles of 16 dims
   static constexpr int RB = D / 2;        // code bytes per row
@@ -772,7 +775,7 @@ struct ChunkSources {
 };
 
 template <int D, int GR, int ROT>
-__global__ void __launch_bounds__(64 * waves_per_stream(D)) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, 8)))
+__global__ void __launch_bounds__(64 * waves_per_stream(D)) __attribute__((amdgpu_waves_per_eu(waves_per_eu(D), 8)))
 attn_decode_kernel(Params p) {
   using C = Cfg<D, GR>;
   constexpr int kWaves = C::WAVES, kStreams = 1;
