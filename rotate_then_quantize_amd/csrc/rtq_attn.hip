@@ -228,6 +228,16 @@ __device__ __forceinline__ f16x2_t value_pair16(uint32_t w) {
   }
 }
 
+// a - (half SEL of h as fp16), in fp32 (one v_fma_mix_f32; exact when that
+// half is a rounding of a)
+template <int SEL>
+__device__ __forceinline__ float residual_of_half(float a, uint32_t h) {
+  float r;
+  if constexpr (SEL == 0) asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+  else asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(a));
+  return r;
+}
+
 // max of three floats (v_max3_f32 written out: fmaxf adds a quieting
 // v_max_f32 x, x before every operand the compiler cannot prove canonical,
 // and the lane-swap results below are such operands; scores are never
@@ -895,20 +905,25 @@ attn_decode_kernel(Params p) {
     const bool valid = g < G;
     const float* src = stage + g * C::QROW;
     float part_sum[C::KS];
+    const f16x2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
     sfor<C::KS>([&](auto J) {
       constexpr int j = RTQ_CI(J);
       uint32_t wds[4];
       float ps = 0.0f;
+      const float4 lo4 = valid ? *reinterpret_cast<const float4*>(src + 32 * j + 8 * h) : make_float4(0, 0, 0, 0);
+      const float4 hi4 = valid ? *reinterpret_cast<const float4*>(src + 32 * j + 8 * h + 4) : make_float4(0, 0, 0, 0);
+      const float av[4] = {lo4.x, lo4.y, lo4.z, lo4.w}, bv[4] = {hi4.x, hi4.y, hi4.z, hi4.w};
       sfor<4>([&](auto V) {
         constexpr int v = RTQ_CI(V);
-        const float a = valid ? src[32 * j + 8 * h + v] : 0.0f;
-        const float b = valid ? src[32 * j + 8 * h + v + 4] : 0.0f;
-        const _Float16 ah = (_Float16)a, bh = (_Float16)b;
-        const _Float16 al = (_Float16)(a - (float)ah), bl = (_Float16)(b - (float)bh);
-        const _Float16 x0 = n < 8 ? ah : al, x1 = n < 8 ? bh : bl;
-        ps += (float)x0 + (float)x1;
-        constexpr float m = (kBiasedKeys && (v & 1)) ? 0.0625f : 1.0f;
-        wds[v] = as_u32((f16x2_t){(_Float16)((float)x0 * m), (_Float16)((float)x1 * m)});
+        // the high parts (a, b) and the residuals a - high, b - high (exact in
+        // fp32: one v_fma_mix each), both rounded to fp16 pairs
+        const float a = av[v], b = bv[v];
+        const uint32_t hp = pack_f16x2(a, b);
+        const uint32_t lp = pack_f16x2(residual_of_half<0>(a, hp), residual_of_half<1>(b, hp));
+        uint32_t x = n < 8 ? hp : lp;
+        ps = __builtin_amdgcn_fdot2(as_h2(x), ones, ps, false);
+        if constexpr (kBiasedKeys && (v & 1)) x = as_u32(as_h2(x) * (f16x2_t){(_Float16)0.0625f, (_Float16)0.0625f});
+        wds[v] = x;
       });
       bq[j] = pack8(as_h2(wds[0]), as_h2(wds[1]), as_h2(wds[2]), as_h2(wds[3]));
       part_sum[j] = kBiasedKeys ? sum_over_row_groups(ps) : 0.0f;
