@@ -30,9 +30,9 @@
 //     whose partials the last one to finish merges (the online-softmax merge
 //     again).
 //   * Each chunk's code and scale rows arrive by direct-to-LDS loads
-//     (global_load_lds) into a three-slot ring, two chunks ahead of the one
-//     being computed.  Rows may sit anywhere (the cache layout is given by
-//     strides).
+//     (global_load_lds) into a ring of ring_slots(d) chunk buffers per wave,
+//     filled ahead of the chunk being computed.  Rows may sit anywhere (the
+//     cache layout is given by strides).
 //   * q.k is a [16 tokens x 32 dims] x [32 dims x 16 columns] MFMA
 //     (v_mfma_f32_16x16x32_f16) per group of 32 dims.  The A operand is the
 //     exact int4 code value as fp16 (no scale), so each group's partial dot

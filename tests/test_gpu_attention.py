@@ -88,7 +88,7 @@ def test_time_major_decode_layout(d, g, qpk):
 
 @pytest.mark.parametrize("d,g", [(128, 32), (64, 64), (256, 32)])
 def test_many_chunks_per_wave(d, g):
-    S, T = 2, 1000  # 32 chunks: eight per wave, the three-slot ring wraps
+    S, T = 2, 1000  # 32 chunks: eight per wave, the ring wraps several times
     run_case("srft", d, g, 1, S, T, 4, lm(S, T), 2 * S * T, seed=3)
 
 
