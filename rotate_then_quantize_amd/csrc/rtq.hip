@@ -214,11 +214,18 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
       lds[lane * LR + RTQ_CI(C)] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
     });
     lds_sync();
-    sfor<PC>([&](auto J) {
+    auto out = [&](auto J) {
       const int idx = RTQ_CI(J) * 64 + lane;
       const int rl = idx / PC, kk = idx % PC;
-      if (rl < rows) stream_store(yt + (uint32_t)(rl * CPR + ph * PC + kk), lds[rl * LR + kk]);
-    });
+      return stream_store(yt + (uint32_t)(rl * CPR + ph * PC + kk), lds[rl * LR + kk]);
+    };
+    if (rows == 64) {  // a full tile stores without per-row guards
+      sfor<PC>([&](auto J) { out(J); });
+    } else {
+      sfor<PC>([&](auto J) {
+        if ((RTQ_CI(J) * 64 + lane) / PC < rows) out(J);
+      });
+    }
   });
 }
 

@@ -534,10 +534,14 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
     if (uniform) {
       const uint4* xt = x + (size_t)row0 * CPR;
       uint4 in[16];
-      sfor<16>([&](auto J) {
-        const int rl = 2 * RTQ_CI(J) + p;
-        in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
-      });
+      if (rows == 32) {  // a full tile loads without per-row guards (about 100 instructions less)
+        sfor<16>([&](auto J) { in[RTQ_CI(J)] = stream_load(xt + ((uint32_t)((2 * RTQ_CI(J) + p) * CPR) + kpos)); });
+      } else {
+        sfor<16>([&](auto J) {
+          const int rl = 2 * RTQ_CI(J) + p;
+          in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
+        });
+      }
       sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cm)); });
     } else {
 #pragma unroll 1
@@ -730,7 +734,13 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
           return lds[rl * LR2 + kk];
         }
       };
-      if (uniform) {
+      if (uniform && rows == 32) {  // a full tile stores without per-row guards
+        const uint4 m = R.uniform_masks(k);
+        sfor<8>([&](auto J) {
+          const int rl = rsub + 4 * RTQ_CI(J);
+          put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
+        });
+      } else if (uniform) {
         const uint4 m = R.uniform_masks(k);
         sfor<8>([&](auto J) {
           const int rl = rsub + 4 * RTQ_CI(J);
