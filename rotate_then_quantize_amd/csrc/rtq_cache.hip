@@ -165,7 +165,7 @@ template <int G, int ROT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void fwd_mapped_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales, uint32_t n, RowMap m,
     RowSeeds rs) {
-  __shared__ uint4 lds[32 * 33];
+  __shared__ uint4 lds[16 * 33];
   fwd_pair_tile<G, ROT>(x, codes, scales, mapped_tile_rows(n, m, rs), lds, threadIdx.x);
 }
 

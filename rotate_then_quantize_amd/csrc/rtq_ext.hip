@@ -152,7 +152,7 @@ template <int G, int ROT, int B>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void fwd_ext_pair_kernel(
     const uint4* __restrict__ x, uint4* __restrict__ codes, uint8_t* __restrict__ scales,
     const uint32_t* __restrict__ lam, uint32_t n, SeedRule sr, SignTable tb) {
-  __shared__ uint4 lds[32 * 33];
+  __shared__ uint4 lds[16 * 33];
   fwd_pair_tile<G, ROT, TileRows, B>(x, codes, scales, tile_rows(n, sr, tb), lds, threadIdx.x, lam);
 }
 

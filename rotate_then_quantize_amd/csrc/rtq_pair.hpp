@@ -504,7 +504,7 @@ __device__ __forceinline__ void srft_inv_exchange_hartley(const float (&L)[128],
 // Forward tile: rows R.row0 .. R.row0 + R.rows - 1 of x (contiguous, 32
 // 16-byte chunks per row) into the codes / scales rows R.cache_row(.), with
 // B-bit codes (one little-endian bit stream per row, 32 B bytes) and an
-// optional per-channel lambda.  lds holds 32 x 33 uint4.
+// optional per-channel lambda.  lds holds 16 x 33 uint4.
 template <int G, int ROT, class Rows, int B = 4>
 __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4* __restrict__ codes,
                                               uint8_t* __restrict__ scales, const Rows& R, uint4* lds, int lane,
@@ -531,6 +531,20 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
         lds[rl * LROW + kpos] = q;
       }
     };
+    // The tile reaches LDS in two passes of 16 rows (rows 0..15, then 16..31),
+    // each read back by the lanes of its rows: a 16-row buffer leaves room
+    // for three waves per SIMD.
+    uint32_t h[64];
+    auto fetch = [&]() {
+      const int lr = v & 15;
+      sfor<16>([&](auto C) {
+        const uint4 q = lds[lr * LROW + 16 * p + RTQ_CI(C)];
+        h[4 * RTQ_CI(C) + 0] = q.x;
+        h[4 * RTQ_CI(C) + 1] = q.y;
+        h[4 * RTQ_CI(C) + 2] = q.z;
+        h[4 * RTQ_CI(C) + 3] = q.w;
+      });
+    };
     if (uniform) {
       const uint4* xt = x + (size_t)row0 * CPR;
       uint4 in[16];
@@ -542,24 +556,33 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
           in[RTQ_CI(J)] = rl < rows ? stream_load(xt + ((uint32_t)(rl * CPR) + kpos)) : make_uint4(0, 0, 0, 0);
         });
       }
-      sfor<16>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[RTQ_CI(J)], cm)); });
+      sfor<2>([&](auto P) {
+        constexpr int ps = RTQ_CI(P);
+        if constexpr (ps > 0) {
+          wait_lds_reads();
+          lds_sync();
+        }
+        sfor<8>([&](auto J) { put(2 * RTQ_CI(J) + p, xor4(in[8 * ps + RTQ_CI(J)], cm)); });
+        lds_sync();
+        if ((v >> 4) == ps) fetch();
+      });
     } else {
+      sfor<2>([&](auto P) {
+        constexpr int ps = RTQ_CI(P);
+        if constexpr (ps > 0) {
+          wait_lds_reads();
+          lds_sync();
+        }
 #pragma unroll 1
-      for (int j = 0; j < 16; ++j) {
-        const int rl = 2 * j + p;
-        const uint4 q = rl < rows ? stream_load(x + ((size_t)(row0 + rl) * CPR + kpos)) : make_uint4(0, 0, 0, 0);
-        put(rl, xor4(q, R.row_masks(rl, kpos)));
-      }
+        for (int j = 0; j < 8; ++j) {
+          const int rl = 16 * ps + 2 * j + p;
+          const uint4 q = rl < rows ? stream_load(x + ((size_t)(row0 + rl) * CPR + kpos)) : make_uint4(0, 0, 0, 0);
+          put(2 * j + p, xor4(q, R.row_masks(rl, kpos)));
+        }
+        lds_sync();
+        if ((v >> 4) == ps) fetch();
+      });
     }
-    lds_sync();
-    uint32_t h[64];
-    sfor<16>([&](auto C) {
-      const uint4 q = lds[v * LROW + 16 * p + RTQ_CI(C)];
-      h[4 * RTQ_CI(C) + 0] = q.x;
-      h[4 * RTQ_CI(C) + 1] = q.y;
-      h[4 * RTQ_CI(C) + 2] = q.z;
-      h[4 * RTQ_CI(C) + 3] = q.w;
-    });
     wait_lds_reads();
     lds_sync();
     float L[128];
