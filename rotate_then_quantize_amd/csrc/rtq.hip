@@ -197,33 +197,38 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   if constexpr (kUniform) sg.apply(h);
   else apply_lane_signs<D>(h, s);
   // Own row into LDS (the code block has been read), then coalesced chunks
-  // out.  d = 128 goes in two halves of 8 chunks per row, which halves the
-  // LDS tile (9 KB) so that LDS does not cap the resident waves.
+  // out.  d = 128 goes in two passes of 32 whole rows (a 9 KB LDS tile, so
+  // that LDS does not cap the resident waves): in pass ph the lanes of rows
+  // 32 ph .. 32 ph + 31 write their rows, and each store instruction then
+  // writes four whole rows (1 KB of contiguous output).
   wait_lds_reads();
   lds_sync();
   constexpr int PH = InvPhases<D>::value;
-  constexpr int PC = CPR / PH, LR = PC + 1;
+  constexpr int RP = 64 / PH, LR = CPR + 1;  // rows per pass, LDS row stride (uint4)
   sfor<PH>([&](auto P) {
     constexpr int ph = RTQ_CI(P);
     if constexpr (ph > 0) {
       wait_lds_reads();
       lds_sync();
     }
-    sfor<PC>([&](auto C) {
-      constexpr int c = ph * PC + RTQ_CI(C);
-      lds[lane * LR + RTQ_CI(C)] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
-    });
+    if (PH == 1 || lane / RP == ph) {
+      sfor<CPR>([&](auto C) {
+        constexpr int c = RTQ_CI(C);
+        lds[(lane % RP) * LR + c] = make_uint4(h[4 * c], h[4 * c + 1], h[4 * c + 2], h[4 * c + 3]);
+      });
+    }
     lds_sync();
     auto out = [&](auto J) {
       const int idx = RTQ_CI(J) * 64 + lane;
-      const int rl = idx / PC, kk = idx % PC;
-      return stream_store(yt + (uint32_t)(rl * CPR + ph * PC + kk), lds[rl * LR + kk]);
+      const int rl = idx / CPR, kk = idx % CPR;  // row of this pass, chunk
+      return stream_store(yt + (uint32_t)((RP * ph + rl) * CPR + kk), lds[rl * LR + kk]);
     };
+    constexpr int NJ = RP * CPR / 64;  // store instructions per pass
     if (rows == 64) {  // a full tile stores without per-row guards
-      sfor<PC>([&](auto J) { out(J); });
+      sfor<NJ>([&](auto J) { out(J); });
     } else {
-      sfor<PC>([&](auto J) {
-        if ((RTQ_CI(J) * 64 + lane) / PC < rows) out(J);
+      sfor<NJ>([&](auto J) {
+        if (RP * ph + (RTQ_CI(J) * 64 + lane) / CPR < rows) out(J);
       });
     }
   });
@@ -237,7 +242,7 @@ __device__ __forceinline__ void inv_lane_body(const uint4* __restrict__ codes, c
                                               const SeedRule& sr, const SignTable& tb) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
-  constexpr int LT = 64 * (CPR / InvPhases<D>::value + 1);  // output tile (uint4)
+  constexpr int LT = 64 / InvPhases<D>::value * (CPR + 1);  // output tile (uint4)
   __shared__ uint4 lds[LT > 64 * CW ? LT : 64 * CW];
   __shared__ __attribute__((aligned(16))) float inv_lam[D];  // 1 / lambda per channel
   const int lane = threadIdx.x;
@@ -262,7 +267,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 8))) void
     SeedRule sr, SignTable tb) {
   constexpr int CPR = D / 8;
   constexpr int CW = D / 32;
-  constexpr int LT = 64 * (CPR / InvPhases<D>::value + 1);  // output tile (uint4)
+  constexpr int LT = 64 / InvPhases<D>::value * (CPR + 1);  // output tile (uint4)
   __shared__ uint4 lds[LT > 64 * CW ? LT : 64 * CW];
   const int lane = threadIdx.x;
   const uint32_t row0 = blockIdx.x * 64u;

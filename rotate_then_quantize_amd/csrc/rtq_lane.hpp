@@ -235,7 +235,7 @@ __device__ __forceinline__ void load_row_scales(const uint8_t* __restrict__ st, 
   }
 }
 
-// Output transpose passes of the inverse: d = 128 in two halves.
+// Output transpose passes of the inverse: d = 128 in two passes of 32 rows.
 template <int D> struct InvPhases { static constexpr int value = D == 128 ? 2 : 1; };
 
 // Flip the sign bits of h by the lane's seed s: one ballot per 64 elements

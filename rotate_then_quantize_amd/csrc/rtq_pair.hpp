@@ -659,9 +659,10 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
 
 // Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
 // that R.y_chunk addresses, for B-bit codes, divided by lambda when LAM.
-// lds holds 32 x 17 uint4.  The lambda case is a template parameter: with
-// both transform paths behind a run-time branch the compiler merges their
-// common steps and spills about 130 registers.
+// lds holds 544 uint4 (16 x 34 for SRFT, 32 x 17 for SRHT).  The lambda
+// case is a template parameter: with both transform paths behind a run-time
+// branch the compiler merges their common steps and spills about 130
+// registers.
 template <int G, int ROT, class Rows, int B = 4, bool LAM = false>
 __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, const uint8_t* __restrict__ scales,
                                               uint4* __restrict__ y, const Rows& R, uint4* lds, int lane,
@@ -719,65 +720,96 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
       pack_all(u);
     }
     sfor<16>([&](auto Q) { pin_words<4 * RTQ_CI(Q)>(hw); });
-    // fp16 samples out through LDS in two passes of 16 output chunks per row
-    // (a 9 KB tile).  SRFT: lane p's samples are u_{2m+p}; pass ph takes its
-    // 64 samples 64 ph .. 64 ph + 63 into the p-th half of the LDS row and
-    // re-interleaves them on the way out.  SRHT: lane p holds output chunks
-    // 16 p .. 16 p + 15, written in pass p.
-    constexpr int LR2 = 17;
-    const int kk = lane & 15, rsub = lane >> 4;
-    sfor<2>([&](auto PH) {
-      constexpr int ph = RTQ_CI(PH);
-      if constexpr (ph > 0) {
-        wait_lds_reads();
+    // fp16 samples out through LDS in two passes (a 9 KB tile).
+    //   SRFT: lane p holds the samples u_{2m+p}.  Pass ph takes whole rows
+    //   16 ph .. 16 ph + 15: their lanes write their samples of parity p to
+    //   part p of the LDS row, and the wave re-interleaves the even and odd
+    //   samples and stores two whole rows (1 KB of contiguous output) per
+    //   instruction.
+    //   SRHT: lane p holds output chunks 16 p .. 16 p + 15, written in pass p
+    //   for every row (whole-row passes measured slower here).
+    if constexpr (ROT == kSRFT) {
+      constexpr int LR3 = 34;  // uint4 per LDS row: evens, a pad, odds, a pad
+      const uint32_t k = (uint32_t)(lane & 31);  // output chunk this lane stores
+      const int rh = lane >> 5;
+      auto get = [&](int r) -> uint4 {  // chunk k of local row r
+        const uint2* row = reinterpret_cast<const uint2*>(&lds[r * LR3]);
+        const uint2 e = row[k], o = row[34 + k];
+        return make_uint4(__builtin_amdgcn_perm(o.x, e.x, 0x05040100u), __builtin_amdgcn_perm(o.x, e.x, 0x07060302u),
+                          __builtin_amdgcn_perm(o.y, e.y, 0x05040100u), __builtin_amdgcn_perm(o.y, e.y, 0x07060302u));
+      };
+      sfor<2>([&](auto PH) {
+        constexpr int ph = RTQ_CI(PH);
+        if constexpr (ph > 0) {
+          wait_lds_reads();
+          lds_sync();
+        }
+        if ((v >> 4) == ph) {
+          sfor<16>([&](auto C) {
+            constexpr int c = RTQ_CI(C);
+            lds[(v & 15) * LR3 + 17 * p + c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
+          });
+        }
         lds_sync();
-      }
-      if constexpr (ROT == kSRFT) {
-        sfor<8>([&](auto C) {
-          constexpr int c = 8 * ph + RTQ_CI(C);
-          lds[v * LR2 + 8 * p + RTQ_CI(C)] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
-        });
-      } else {
+        if (uniform && rows == 32) {  // a full tile stores without per-row guards
+          const uint4 m = R.uniform_masks(k);
+          sfor<8>([&](auto J) {
+            const int r = 2 * RTQ_CI(J) + rh;
+            put_store<Rows::kStreamStores>(R.y_chunk(y, 16 * ph + r, k), xor4(get(r), m));
+          });
+        } else if (uniform) {
+          const uint4 m = R.uniform_masks(k);
+          sfor<8>([&](auto J) {
+            const int r = 2 * RTQ_CI(J) + rh;
+            if (16 * ph + r < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, 16 * ph + r, k), xor4(get(r), m));
+          });
+        } else {
+#pragma unroll 1
+          for (int j = 0; j < 8; ++j) {
+            const int r = 2 * j + rh, rl = 16 * ph + r;
+            if (rl < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(r), R.row_masks(rl, k)));
+          }
+        }
+      });
+    } else {
+      constexpr int LR2 = 17;
+      const int kk = lane & 15, rsub = lane >> 4;
+      sfor<2>([&](auto PH) {
+        constexpr int ph = RTQ_CI(PH);
+        if constexpr (ph > 0) {
+          wait_lds_reads();
+          lds_sync();
+        }
         if (p == ph) {
           sfor<16>([&](auto C) {
             constexpr int c = RTQ_CI(C);
             lds[v * LR2 + c] = make_uint4(hw[4 * c], hw[4 * c + 1], hw[4 * c + 2], hw[4 * c + 3]);
           });
         }
-      }
-      lds_sync();
-      const uint32_t k = 16u * ph + (uint32_t)kk;  // output chunk this lane stores
-      auto get = [&](int rl) -> uint4 {
-        if constexpr (ROT == kSRFT) {
-          const uint2* row = reinterpret_cast<const uint2*>(&lds[rl * LR2]);
-          const uint2 e = row[kk], o = row[16 + kk];
-          return make_uint4(__builtin_amdgcn_perm(o.x, e.x, 0x05040100u), __builtin_amdgcn_perm(o.x, e.x, 0x07060302u),
-                            __builtin_amdgcn_perm(o.y, e.y, 0x05040100u), __builtin_amdgcn_perm(o.y, e.y, 0x07060302u));
+        lds_sync();
+        const uint32_t k = 16u * ph + (uint32_t)kk;  // output chunk this lane stores
+        auto get = [&](int rl) -> uint4 { return lds[rl * LR2 + kk]; };
+        if (uniform && rows == 32) {  // a full tile stores without per-row guards
+          const uint4 m = R.uniform_masks(k);
+          sfor<8>([&](auto J) {
+            const int rl = rsub + 4 * RTQ_CI(J);
+            put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
+          });
+        } else if (uniform) {
+          const uint4 m = R.uniform_masks(k);
+          sfor<8>([&](auto J) {
+            const int rl = rsub + 4 * RTQ_CI(J);
+            if (rl < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
+          });
         } else {
-          return lds[rl * LR2 + kk];
-        }
-      };
-      if (uniform && rows == 32) {  // a full tile stores without per-row guards
-        const uint4 m = R.uniform_masks(k);
-        sfor<8>([&](auto J) {
-          const int rl = rsub + 4 * RTQ_CI(J);
-          put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
-        });
-      } else if (uniform) {
-        const uint4 m = R.uniform_masks(k);
-        sfor<8>([&](auto J) {
-          const int rl = rsub + 4 * RTQ_CI(J);
-          if (rl < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), m));
-        });
-      } else {
 #pragma unroll 1
-        for (int j = 0; j < 8; ++j) {
-          const int rl = rsub + 4 * j;
-          if (rl < rows)
-            put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), R.row_masks(rl, k)));
+          for (int j = 0; j < 8; ++j) {
+            const int rl = rsub + 4 * j;
+            if (rl < rows) put_store<Rows::kStreamStores>(R.y_chunk(y, rl, k), xor4(get(rl), R.row_masks(rl, k)));
+          }
         }
-      }
-    });
+      });
+    }
     wait_lds_reads();
     lds_sync();
   }
