@@ -71,6 +71,24 @@ def test_small_and_ragged_n(rot, d, g, n):
     roundtrip_check(rot, outlier_rows(n, d, n), g, seed=77)
 
 
+# Tiles whose last rows fall around the kernels' pass boundaries: the d = 256
+# forward stages its 32-row tile in two passes of 16 rows and the SRFT inverse
+# stores 16 whole rows per pass; the d = 128 inverse stores 32 rows per pass.
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,g,n", [(256, 32, 15), (256, 32, 16), (256, 32, 17), (256, 64, 48), (256, 32, 49),
+                                   (256, 128, 80), (128, 32, 32), (128, 64, 95), (128, 32, 97)])
+def test_pass_boundaries(rot, d, g, n):
+    roundtrip_check(rot, outlier_rows(n, d, 1000 + n), g, seed=0xB0B + n)
+
+
+# The same boundaries on tiles whose rows change seed inside the tile (the
+# per-row sign path of both passes).
+@pytest.mark.parametrize("rot", ["srft", "srht"])
+@pytest.mark.parametrize("d,n,rps", [(256, 49, 10), (256, 81, 7), (128, 97, 24)])
+def test_pass_boundaries_per_row_seeds(rot, d, n, rps):
+    roundtrip_check(rot, outlier_rows(n, d, 2000 + n), 32, seed=0xC0C + n, rps=rps, per=3)
+
+
 @pytest.mark.parametrize("rot", ["srft", "srht"])
 @pytest.mark.parametrize("d,g", [(64, 32), (128, 64), (256, 32)])
 def test_zero_rows(rot, d, g):
