@@ -273,7 +273,8 @@ VALU_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "
 SIMDS, CLOCK_HZ = 1024, 2.4e9  # MI355X: 256 CUs x 4 SIMDs, peak engine clock
 
 
-EXTRA_COUNTERS = ("VALUBusy", "GRBM_GUI_ACTIVE", "LDSBankConflict", "TA_BUSY_avr", "TA_BUSY_max")
+EXTRA_COUNTERS = ("VALUBusy", "GRBM_GUI_ACTIVE", "LDSBankConflict", "TA_BUSY_avr", "TA_BUSY_max", "MemUnitBusy",
+                  "MemUnitStalled")
 XCDS = 8  # GRBM_GUI_ACTIVE is recorded once per XCD
 
 
@@ -1098,7 +1099,7 @@ def main():
     ap.add_argument("--summarize-valu", nargs="+", metavar="DIR",
                     help="PMC TRACE [EXTRA ...]: write profiles/valu_*.txt from a rocprofv3 --pmc run of SQ "
                          "instruction counters, a kernel trace of the same command and optional further --pmc "
-                         "runs (VALUBusy, GRBM_GUI_ACTIVE, LDSBankConflict, TA_BUSY)")
+                         "runs (VALUBusy, GRBM_GUI_ACTIVE, LDSBankConflict, TA_BUSY, MemUnitBusy / MemUnitStalled)")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the profile directories, recorded in the summary")
     args = ap.parse_args()

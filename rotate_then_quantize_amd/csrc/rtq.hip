@@ -134,8 +134,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2, 8))) void
   fwd_lane_body<D, G, ROT, true>(x, codes, scales, lam, n, sr, tb);
 }
 
+// Chunk k of code row r sits at slot r * CW + (k ^ code_swizzle<CW>(r)) of
+// the staged code block: the 16 lanes of one LDS access, reading chunk k of
+// rows r .. r + 15, then hit 16 different groups of 4 banks (without the xor
+// the rows 16 / CW apart share a group).
+template <int CW>
+__device__ __forceinline__ int code_swizzle(int r) {
+  static_assert(CW == 2 || CW == 4, "code chunks per row");
+  return (r >> (CW == 4 ? 2 : 3)) & (CW - 1);
+}
+
 // Direct-to-LDS staging of a tile's code block (CW 16-byte chunks per row, in
-// row order): load instruction j of lane i fills slot 64j + i with chunk
+// row order, swizzled as above): load instruction j of lane i fills slot
 // 64j + i, a partial tile repeating its last row.
 template <int CW>
 __device__ __forceinline__ void load_codes_to_lds(const uint4* __restrict__ ct, int rows, uint4* buf, int lane) {
@@ -143,7 +153,7 @@ __device__ __forceinline__ void load_codes_to_lds(const uint4* __restrict__ ct, 
     const int c = RTQ_CI(J) * 64 + lane;
     const int r = c / CW;
     const int rr = r < rows ? r : rows - 1;
-    const uint32_t off = (uint32_t)(rr * CW + c % CW) * 16u;
+    const uint32_t off = (uint32_t)(rr * CW + ((c % CW) ^ code_swizzle<CW>(r))) * 16u;
     __builtin_amdgcn_global_load_lds((gbl_void_t*)((const char*)ct + off), (lds_void_t*)(buf + RTQ_CI(J) * 64), 16,
                                      0, kCachePolicyNT);
   });
@@ -171,7 +181,7 @@ __device__ __forceinline__ void inv_lane_tile(const uint4* __restrict__ ct, cons
   lds_sync();
   uint32_t cw[D / 8];
   sfor<CW>([&](auto C) {
-    const uint4 q = lds[r * CW + RTQ_CI(C)];
+    const uint4 q = lds[r * CW + (RTQ_CI(C) ^ code_swizzle<CW>((int)r))];
     cw[4 * RTQ_CI(C) + 0] = q.x;
     cw[4 * RTQ_CI(C) + 1] = q.y;
     cw[4 * RTQ_CI(C) + 2] = q.z;

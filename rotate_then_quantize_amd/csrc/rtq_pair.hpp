@@ -659,7 +659,7 @@ __device__ __forceinline__ void fwd_pair_tile(const uint4* __restrict__ x, uint4
 
 // Inverse tile: the codes / scales rows R.cache_row(.) into the rows of y
 // that R.y_chunk addresses, for B-bit codes, divided by lambda when LAM.
-// lds holds 544 uint4 (16 x 34 for SRFT, 32 x 17 for SRHT).  The lambda
+// lds holds 544 uint4 (16 x 33 used for SRFT, 32 x 17 for SRHT).  The lambda
 // case is a template parameter: with both transform paths behind a run-time
 // branch the compiler merges their common steps and spills about 130
 // registers.
@@ -729,7 +729,9 @@ __device__ __forceinline__ void inv_pair_tile(const uint4* __restrict__ codes, c
     //   SRHT: lane p holds output chunks 16 p .. 16 p + 15, written in pass p
     //   for every row (whole-row passes measured slower here).
     if constexpr (ROT == kSRFT) {
-      constexpr int LR3 = 34;  // uint4 per LDS row: evens, a pad, odds, a pad
+      // uint4 per LDS row: 16 of evens, a pad, 16 of odds.  An odd row stride
+      // puts the 16 rows one access writes in 16 different groups of 4 banks.
+      constexpr int LR3 = 33;
       const uint32_t k = (uint32_t)(lane & 31);  // output chunk this lane stores
       const int rh = lane >> 5;
       auto get = [&](int r) -> uint4 {  // chunk k of local row r
